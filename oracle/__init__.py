@@ -1,0 +1,225 @@
+"""fp64 CPU oracle for paged grouped-query decode attention (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package; the library's product
+path never does.  It wraps ``oracle.c`` (plain C, fp64), which shares no code
+with the HIP path.  What it computes follows the page
+"vllm.v1.attention.ops.flydsl_kernels.tq_decode" (build_tq_decode_module and
+the STEPs of tq_decode_kernel); the comment block of ``oracle.c`` states the
+definition and the readings taken where that page is silent.
+
+Array conventions (numpy, C-contiguous):
+  q_bits        uint16 [S][Hkv*QG][D]   bfloat16 bit patterns
+  k_codes       uint8  [NB][BS][Hkv][D] OCP e4m3fn codes
+  v_codes       uint8  [NB][BS][Hkv][D]
+  kv_scales     float32 [NB][Hkv][2][BS] (field 0 = K, field 1 = V)
+  block_tables  int32  [S][max_blocks_per_seq]
+  seq_lens      int32  [S]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+ORC_OK, ORC_ERR_ARGS, ORC_ERR_BLOCK, ORC_ERR_NOMEM = 0, 1, 2, 3
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm", "-lpthread"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class Oracle:
+    """ctypes view of one build of oracle.c (the default build, or a test's mutated copy)."""
+
+    def __init__(self, lib_path: str):
+        lib = ctypes.CDLL(lib_path)
+        P = ctypes.c_void_p
+        i32 = ctypes.c_int32
+        lib.orc_dec_e4m3fn.argtypes = [ctypes.c_uint8]
+        lib.orc_dec_e4m3fn.restype = ctypes.c_double
+        lib.orc_dec_bf16.argtypes = [ctypes.c_uint16]
+        lib.orc_dec_bf16.restype = ctypes.c_double
+        lib.orc_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                   ctypes.c_float, P, i32, P, i32]
+        lib.orc_decode.restype = ctypes.c_int
+        lib.orc_partials.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                     ctypes.c_float, i32, i32, P, P, P]
+        lib.orc_partials.restype = ctypes.c_int
+        lib.orc_merge.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
+        lib.orc_merge.restype = ctypes.c_int
+        self.lib = lib
+        self.path = lib_path
+
+    def decode(self, q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens, softmax_scale,
+               units=None, nthreads: int = 1) -> np.ndarray:
+        """Unsplit decode attention in fp64.
+
+        Returns [S][Hkv*QG][D] when ``units`` is None, else [len(units)][QG][D]
+        for the listed (s, h) pairs."""
+        q, k, v, sc, bt, sl, (S, Hkv, QG, D, BS, NB, MB) = _problem(
+            q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens)
+        if units is None:
+            u = None
+            n = S * Hkv
+        else:
+            u = np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+            n = u.shape[0]
+        out = np.empty((n, QG, D), dtype=np.float64)
+        rc = self.lib.orc_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(sc), _ptr(bt), _ptr(sl), S, Hkv, QG,
+                                 D, BS, NB, MB, float(softmax_scale),
+                                 None if u is None else _ptr(u), n, _ptr(out), int(nthreads))
+        if rc:
+            raise OracleError("orc_decode failed with code %d" % rc)
+        if units is None:
+            return out.reshape(S, Hkv * QG, D)
+        return out
+
+    def partials(self, q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens, softmax_scale,
+                 num_partitions: int, partition_tokens: int):
+        """Split-K partials (o [S][Hkv][P][QG][D], m, l [S][Hkv][P][QG]); dead entries are NaN."""
+        q, k, v, sc, bt, sl, (S, Hkv, QG, D, BS, NB, MB) = _problem(
+            q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens)
+        P, E = int(num_partitions), int(partition_tokens)
+        o = np.full((S, Hkv, P, QG, D), np.nan)
+        m = np.full((S, Hkv, P, QG), np.nan)
+        l = np.full((S, Hkv, P, QG), np.nan)
+        rc = self.lib.orc_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(sc), _ptr(bt), _ptr(sl), S, Hkv,
+                                   QG, D, BS, NB, MB, float(softmax_scale), P, E, _ptr(o), _ptr(m),
+                                   _ptr(l))
+        if rc:
+            raise OracleError("orc_partials failed with code %d" % rc)
+        return o, m, l
+
+    def merge(self, o, m, l, seq_lens, partition_tokens: int) -> np.ndarray:
+        """Log-sum-exp merge of partials into [S][Hkv*QG][D]."""
+        o = np.ascontiguousarray(o, dtype=np.float64)
+        m = np.ascontiguousarray(m, dtype=np.float64)
+        l = np.ascontiguousarray(l, dtype=np.float64)
+        sl = _np(seq_lens, np.int32)
+        S, Hkv, P, QG, D = o.shape
+        out = np.empty((S, Hkv * QG, D), dtype=np.float64)
+        rc = self.lib.orc_merge(_ptr(o), _ptr(m), _ptr(l), _ptr(sl), S, Hkv, QG, D, P,
+                                int(partition_tokens), _ptr(out))
+        if rc:
+            raise OracleError("orc_merge failed with code %d" % rc)
+        return out
+
+    def dec_e4m3fn(self, codes) -> np.ndarray:
+        """Decode OCP e4m3fn codes to float64 (closed form in oracle.c)."""
+        table = np.array([self.lib.orc_dec_e4m3fn(c) for c in range(256)], dtype=np.float64)
+        return table[_np(codes, np.uint8)]
+
+    def dec_bf16(self, bits) -> np.ndarray:
+        """Decode bfloat16 bit patterns to float64."""
+        b = _np(bits, np.uint16)
+        flat = np.array([self.lib.orc_dec_bf16(int(x)) for x in b.reshape(-1)], dtype=np.float64)
+        return flat.reshape(b.shape)
+
+
+_default = None
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c (compiled on first use if missing or stale)."""
+    global _default
+    if _default is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        _default = Oracle(_LIB)
+    return _default
+
+
+def build_variant(source_text: str, out_path: str) -> Oracle:
+    """Compile a given C source text (e.g. a mutated copy of oracle.c) and load it."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(source_text)
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-w", "-o",
+                    out_path, src, "-lm", "-lpthread"], check=True)
+    return Oracle(out_path)
+
+
+def source_text() -> str:
+    with open(_SRC) as f:
+        return f.read()
+
+
+def _np(x, dtype):
+    """torch tensor (CPU) or array -> C-contiguous numpy array of `dtype` (bit view for bf16)."""
+    try:
+        import torch  # noqa: WPS433
+        if isinstance(x, torch.Tensor):
+            x = x.detach().cpu()
+            if x.dtype == torch.bfloat16:
+                x = x.view(torch.int16)
+            elif x.dtype == torch.float8_e4m3fn:
+                x = x.view(torch.uint8)
+            x = x.numpy()
+    except ImportError:
+        pass
+    x = np.asarray(x)
+    if x.dtype != np.dtype(dtype):
+        if x.dtype.itemsize == np.dtype(dtype).itemsize and x.dtype.kind in "iu" and np.dtype(dtype).kind in "iu":
+            x = x.view(dtype)
+        else:
+            x = x.astype(dtype)
+    return np.ascontiguousarray(x)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _problem(q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens):
+    q = _np(q_bits, np.uint16)
+    k = _np(k_codes, np.uint8)
+    v = _np(v_codes, np.uint8)
+    sc = _np(kv_scales, np.float32)
+    bt = _np(block_tables, np.int32)
+    sl = _np(seq_lens, np.int32)
+    NB, BS, Hkv, D = k.shape
+    S, Hq, Dq = q.shape
+    if v.shape != k.shape or sc.shape != (NB, Hkv, 2, BS) or Dq != D or Hq % Hkv:
+        raise OracleError("inconsistent shapes")
+    if bt.ndim != 2 or bt.shape[0] != S or sl.shape != (S,):
+        raise OracleError("inconsistent block table / seq_lens shapes")
+    return q, k, v, sc, bt, sl, (S, Hkv, Hq // Hkv, D, BS, NB, bt.shape[1])
+
+
+def decode(*a, **k):
+    return default().decode(*a, **k)
+
+
+def partials(*a, **k):
+    return default().partials(*a, **k)
+
+
+def merge(*a, **k):
+    return default().merge(*a, **k)
+
+
+def dec_e4m3fn(codes):
+    return default().dec_e4m3fn(codes)
+
+
+def dec_bf16(bits):
+    return default().dec_bf16(bits)

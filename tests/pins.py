@@ -1,0 +1,305 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises (AssertionError or
+OracleError) when that build of the oracle disagrees with:
+  * the e4m3fn / bf16 format definitions (closed-form code values) and torch's
+    own fp8 / bf16 conversions (a library routine, run, not retyped);
+  * brute-force dense attention computed with torch float64 library ops
+    (softmax, matmul, scaled_dot_product_attention) over a gather written
+    here, on tiny inputs;
+  * closed forms: one cached token returns its V row; a zero query returns
+    the mean of V; constant V returns V; a hand-derived two-token example;
+  * invariants: physical-block permutation with a consistent table, split-K
+    merge == unsplit for many partition counts, V-scale linearity, an
+    isolated dominant token returns that token's V row.
+
+``test_oracle_pins.py`` runs them against the oracle; ``test_oracle_mutants.py``
+plants plausible mistakes in copies of oracle.c and checks that every planted
+mistake fails at least one pin.
+"""
+
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ----------------------------------------------------------------------------
+# tiny problem builder (test-local, independent of the generator module)
+# ----------------------------------------------------------------------------
+
+def tiny_problem(S=3, Hkv=2, QG=4, D=32, BS=4, lens=(1, 7, 13), extra_blocks=3, seed=0,
+                 max_blocks=None):
+    rng = np.random.default_rng(seed)
+    need = [-(-L // BS) for L in lens]
+    NB = sum(need) + extra_blocks
+    MB = max_blocks or max(max(need), 1) + 1
+    perm = rng.permutation(NB).astype(np.int32)
+    bt = np.zeros((S, MB), dtype=np.int32)
+    pos = 0
+    for s in range(S):
+        bt[s, :need[s]] = perm[pos:pos + need[s]]
+        pos += need[s]
+    q = torch.from_numpy(rng.standard_normal((S, Hkv * QG, D)).astype(np.float32)).to(torch.bfloat16)
+    def codes():
+        x = torch.from_numpy(rng.standard_normal((NB, BS, Hkv, D)).astype(np.float32) * 100)
+        return x.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+    k = codes()
+    v = codes()
+    sc = torch.from_numpy(rng.uniform(0.001, 0.02, size=(NB, Hkv, 2, BS)).astype(np.float32))
+    sl = torch.tensor(lens, dtype=torch.int32)
+    return dict(q=q, k=k, v=v, sc=sc, bt=torch.from_numpy(bt), sl=sl,
+                scale=float(np.float32(1.0 / math.sqrt(D))))
+
+
+def dense_rows(p, s, h, field):
+    """Gathered, dequantized K (field 0) or V (field 1) rows of (s, h) as float64 [L][D]."""
+    cache = p["k"] if field == 0 else p["v"]
+    BS = cache.shape[1]
+    L = int(p["sl"][s])
+    rows = []
+    for t in range(L):
+        b = int(p["bt"][s, t // BS])
+        j = t % BS
+        vals = cache[b, j, h].view(torch.float8_e4m3fn).to(torch.float64)
+        rows.append(vals * float(p["sc"][b, h, field, j]))
+    D = cache.shape[3]
+    return torch.stack(rows) if rows else torch.zeros((0, D), dtype=torch.float64)
+
+
+def run(orc, p, **kw):
+    return orc.decode(p["q"], p["k"], p["v"], p["sc"], p["bt"], p["sl"], p["scale"], **kw)
+
+
+def assert_close(a, b, rel, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    ref = max(np.max(np.abs(b)) if b.size else 0.0, 1e-300)
+    assert err <= rel * ref, f"{what}: max abs err {err:.3e} > {rel:.1e} * {ref:.3e}"
+
+
+# ----------------------------------------------------------------------------
+# format pins
+# ----------------------------------------------------------------------------
+
+def pin_e4m3fn_points(orc):
+    """Closed-form values of the OCP e4m3fn format: bias 7, 3 mantissa bits, no inf."""
+    want = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x0F: 1.875 * 2.0 ** -6,
+            0x38: 1.0, 0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0x77: 240.0, 0xB8: -1.0, 0xFE: -448.0,
+            0x81: -(2.0 ** -9)}
+    got = orc.dec_e4m3fn(np.array(sorted(want), dtype=np.uint8))
+    for c, g in zip(sorted(want), got):
+        assert g == want[c], f"code {c:#x}: {g} != {want[c]}"
+    nan = orc.dec_e4m3fn(np.array([0x7F, 0xFF], dtype=np.uint8))
+    assert np.all(np.isnan(nan)), "0x7F / 0xFF must decode to NaN"
+    neg0 = orc.dec_e4m3fn(np.array([0x80], dtype=np.uint8))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) < 0, "0x80 is -0"
+    pos = orc.dec_e4m3fn(np.arange(0, 0x7F, dtype=np.uint8))
+    assert np.all(np.diff(pos) > 0), "positive codes must be strictly increasing"
+    negs = orc.dec_e4m3fn(np.arange(0x80, 0xFF, dtype=np.uint8))
+    assert np.array_equal(negs, -pos), "sign bit must negate"
+
+
+def pin_e4m3fn_library(orc):
+    """All 256 codes against torch's float8_e4m3fn -> float64 conversion."""
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.dec_e4m3fn(codes)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), f"e4m3fn mismatch at codes {np.nonzero(~same)[0][:8]}"
+
+
+def pin_bf16_library(orc):
+    """bfloat16 bit patterns against torch's bfloat16 -> float64 conversion."""
+    rng = np.random.default_rng(7)
+    bits = np.concatenate([rng.integers(0, 1 << 16, size=4000), [0, 0x8000, 0x3F80, 0xBF80, 0x7F7F,
+                                                                 0x0001, 0x0080, 0x7F80, 0xFF80]])
+    bits = bits.astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.dec_bf16(bits)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), "bf16 decode mismatch"
+
+
+# ----------------------------------------------------------------------------
+# attention pins
+# ----------------------------------------------------------------------------
+
+def _bruteforce(p):
+    S, Hq, D = p["q"].shape
+    Hkv = p["k"].shape[2]
+    QG = Hq // Hkv
+    out = torch.zeros((S, Hq, D), dtype=torch.float64)
+    for s in range(S):
+        if int(p["sl"][s]) == 0:
+            continue
+        for h in range(Hkv):
+            K = dense_rows(p, s, h, 0)
+            V = dense_rows(p, s, h, 1)
+            Q = p["q"][s, h * QG:(h + 1) * QG].to(torch.float64)
+            logits = (Q @ K.T) * p["scale"]
+            out[s, h * QG:(h + 1) * QG] = torch.softmax(logits, dim=-1) @ V
+    return out.numpy()
+
+
+def pin_dense_bruteforce(orc):
+    """Against softmax(q K^T * scale) V with torch float64 ops on gathered rows."""
+    for seed, kw in ((0, {}), (1, dict(BS=8, lens=(9, 16, 1), QG=6)), (2, dict(S=2, Hkv=3, QG=2, lens=(40, 3)))):
+        p = tiny_problem(seed=seed, **kw)
+        assert_close(run(orc, p), _bruteforce(p), 1e-12, f"bruteforce seed {seed}")
+
+
+def pin_sdpa(orc):
+    """Against torch.nn.functional.scaled_dot_product_attention in float64."""
+    p = tiny_problem(S=2, Hkv=2, QG=3, D=64, BS=16, lens=(33, 50), seed=5)
+    got = run(orc, p)
+    for s in range(2):
+        for h in range(2):
+            K = dense_rows(p, s, h, 0)[None]
+            V = dense_rows(p, s, h, 1)[None]
+            Q = p["q"][s, h * 3:(h + 1) * 3].to(torch.float64)[None]
+            ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=p["scale"])[0]
+            assert_close(got[s, h * 3:(h + 1) * 3], ref.numpy(), 1e-12, "sdpa")
+
+
+def pin_single_token(orc):
+    """One cached token: the output is exactly that token's dequantized V row."""
+    p = tiny_problem(S=2, Hkv=2, QG=3, lens=(1, 1), seed=3)
+    got = run(orc, p)
+    for s in range(2):
+        for h in range(2):
+            v0 = dense_rows(p, s, h, 1)[0].numpy()
+            for g in range(3):
+                assert np.array_equal(got[s, h * 3 + g], v0), "L=1 must return v_0 exactly"
+
+
+def pin_zero_query(orc):
+    """q = 0: all logits 0, the output is the mean of the V rows."""
+    p = tiny_problem(seed=4, lens=(5, 12, 30))
+    p["q"] = torch.zeros_like(p["q"])
+    got = run(orc, p)
+    QG = 4
+    for s in range(3):
+        for h in range(2):
+            mean = dense_rows(p, s, h, 1).mean(dim=0).numpy()
+            for g in range(QG):
+                assert_close(got[s, h * QG + g], mean, 1e-13, "q=0 mean")
+
+
+def pin_constant_v(orc):
+    """V rows all equal: the output is that row whatever the weights."""
+    p = tiny_problem(seed=6, lens=(3, 17, 25))
+    p["v"] = torch.full_like(p["v"], 0x44)  # 3.0
+    p["sc"][:, :, 1, :] = 0.25
+    got = run(orc, p)
+    assert_close(got, np.full(got.shape, 0.75), 1e-14, "constant V")
+
+
+def pin_two_token_golden(orc):
+    """The hand-derived worked example stored under tests/golden/."""
+    with open(os.path.join(GOLDEN, "two_token_example.json")) as f:
+        ex = json.load(f)
+    D, BS = ex["head_dim"], ex["kv_block_size"]
+    q = torch.zeros((1, 1, D), dtype=torch.int16)
+    q[0, 0, 0] = ex["q_d0_bf16_bits"]
+    q = q.view(torch.bfloat16)
+    k = torch.zeros((1, BS, 1, D), dtype=torch.uint8)
+    k[0, 1, 0, 0] = ex["k_token1_d0_code"]
+    v = torch.zeros((1, BS, 1, D), dtype=torch.uint8)
+    v[0, 0, 0, :] = ex["v_token0_code"]
+    v[0, 1, 0, :] = ex["v_token1_code"]
+    sc = torch.ones((1, 1, 2, BS), dtype=torch.float32)
+    sc[0, 0, 1, 0] = ex["v_token0_scale"]
+    sc[0, 0, 1, 1] = ex["v_token1_scale"]
+    out = orc.decode(q, k, v, sc, torch.zeros((1, 1), dtype=torch.int32),
+                     torch.tensor([2], dtype=torch.int32), 1.0)
+    want = (2 - math.e / 2) / (1 + math.e)
+    assert abs(want - ex["expected_value"]) < 1e-15
+    assert_close(out[0, 0], np.full(D, want), 1e-14, "two-token closed form")
+
+
+def pin_block_permutation(orc):
+    """Relabel physical blocks (move the data, rewrite the table): bit-identical output."""
+    p = tiny_problem(seed=8, lens=(13, 29, 4), BS=4)
+    ref = run(orc, p)
+    NB = p["k"].shape[0]
+    perm = torch.from_numpy(np.random.default_rng(9).permutation(NB).astype(np.int64))
+    q = dict(p)
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(NB)
+    q["k"] = p["k"][inv].contiguous()  # new block perm[b] holds old block b
+    q["v"] = p["v"][inv].contiguous()
+    q["sc"] = p["sc"][inv].contiguous()
+    q["bt"] = perm[p["bt"].long()].to(torch.int32)
+    got = run(orc, q)
+    assert np.array_equal(got, ref), "block permutation changed the output bits"
+
+
+def pin_split_merge(orc):
+    """Split-K partials merged by log-sum-exp equal the unsplit result for any partition count."""
+    p = tiny_problem(seed=10, lens=(1, 37, 64, 95), S=4, BS=4, max_blocks=25)
+    ref = run(orc, p)
+    for P, E in ((1, 100), (2, 48), (3, 32), (7, 14), (32, 3), (95, 1), (13, 8)):
+        o, m, l = orc.partials(p["q"], p["k"], p["v"], p["sc"], p["bt"], p["sl"], p["scale"], P, E)
+        sl = p["sl"].numpy()
+        for s, L in enumerate(sl):
+            live = -(-int(L) // E)
+            assert np.all(np.isfinite(m[s, :, :live])) and np.all(np.isnan(m[s, :, live:])), "live/dead"
+            assert np.all(l[s, :, :live] >= 1.0), "l_p >= 1 (the max term contributes exp(0))"
+        out = orc.merge(o, m, l, p["sl"], E)
+        assert_close(out, ref, 1e-13, f"split merge P={P} E={E}")
+
+
+def pin_v_scale_linearity(orc):
+    """Doubling every V scale doubles the output exactly (power-of-two scaling)."""
+    p = tiny_problem(seed=11, lens=(6, 19, 2))
+    ref = run(orc, p)
+    p2 = dict(p)
+    sc = p["sc"].clone()
+    sc[:, :, 1, :] *= 2
+    p2["sc"] = sc
+    assert np.array_equal(run(orc, p2), 2 * ref)
+
+
+def pin_dominant_token(orc):
+    """K zero except at token t* where K is parallel to q (logit margin >= 80): out = V[t*]."""
+    D, BS, Hkv, QG = 32, 4, 2, 2
+    L = 23
+    for tstar in (0, 3, 4, 11, 22):
+        p = tiny_problem(S=1, Hkv=Hkv, QG=QG, D=D, BS=BS, lens=(L,), seed=12)
+        q = torch.zeros((1, Hkv * QG, D))
+        q[0, :, :] = 1.0
+        p["q"] = q.to(torch.bfloat16)
+        k = torch.zeros_like(p["k"])
+        b = int(p["bt"][0, tstar // BS])
+        k[b, tstar % BS, :, :] = 0x48  # 4.0
+        p["k"] = k
+        p["sc"][:, :, 0, :] = 1.0
+        p["scale"] = 1.0  # logit of t* = 128, others 0
+        got = run(orc, p)
+        for h in range(Hkv):
+            vt = dense_rows(p, 0, h, 1)[tstar].numpy()
+            for g in range(QG):
+                assert_close(got[0, h * QG + g], vt, 1e-30, f"dominant token t*={tstar}")
+
+
+def pin_zero_length(orc):
+    p = tiny_problem(seed=13, lens=(0, 5, 0))
+    got = run(orc, p)
+    assert np.all(got[0] == 0) and np.all(got[2] == 0)
+    assert np.any(got[1] != 0)
+
+
+ALL_PINS = [pin_e4m3fn_points, pin_e4m3fn_library, pin_bf16_library, pin_dense_bruteforce, pin_sdpa,
+            pin_single_token, pin_zero_query, pin_constant_v, pin_two_token_golden,
+            pin_block_permutation, pin_split_merge, pin_v_scale_linearity, pin_dominant_token,
+            pin_zero_length]

@@ -1,0 +1,52 @@
+"""Plant plausible mistakes in copies of oracle.c (on the CPU) and check that
+each one fails at least one of the oracle's pins.  This is what makes the pins
+worth trusting: a dropped term, a wrong sign, index or operand anywhere in the
+oracle shows up."""
+
+import os
+
+import pytest
+
+import oracle
+import pins
+
+# (name, text in oracle.c, replacement)
+MUTANTS = [
+    ("e4m3_exponent_bias", "ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
+    ("e4m3_subnormal_scale", "ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    ("e4m3_sign_dropped", "return sign ? -mag : mag;", "return mag;"),
+    ("e4m3_nan_missing", "if (e == 15 && m == 7) return NAN;", ""),
+    ("bf16_shift", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    ("block_index_wrong_divisor", "t / pb->BS]", "t / (pb->BS + 1)]"),
+    ("slot_off_by_one", "orc_kv(pb, 0, blk, t % pb->BS, h, d)", "orc_kv(pb, 0, blk, (t + 1) % pb->BS, h, d)"),
+    ("cache_head_ignored", "* pb->Hkv + h;", "* pb->Hkv + 0;"),
+    ("scale_field_ignored", "* 2 + field) * pb->BS + slot]", "* 2 + 0) * pb->BS + slot]"),
+    ("scale_slot_ignored", "* 2 + field) * pb->BS + slot]", "* 2 + field) * pb->BS + 0]"),
+    ("q_row_group_ignored", "(int64_t)h * pb->QG + g) * pb->D", "(int64_t)h * pb->QG + 0) * pb->D"),
+    ("softmax_scale_dropped", "*x = pb->scale * dot;", "*x = dot;"),
+    ("no_normalisation", "for (int d = 0; d < pb->D; ++d) o[d] /= l;", ""),
+    ("weights_not_exponentiated", "double w = exp(xbuf[t - t0] - m);", "double w = xbuf[t - t0] - m;"),
+    ("k_operand_is_v", "orc_kv(pb, 0, blk, t % pb->BS, h, d)", "orc_kv(pb, 1, blk, t % pb->BS, h, d)"),
+    ("partition_end_off_by_one", "int t0 = p * E, t1 = (p + 1) * E < L ? (p + 1) * E : L;",
+     "int t0 = p * E, t1 = (p + 1) * E < L ? (p + 1) * E - 1 : L;"),
+    ("merge_weight_no_exp", "double w = l[r] * exp(m[r] - M);", "double w = l[r];"),
+    ("merge_weight_no_l", "double w = l[r] * exp(m[r] - M);", "double w = exp(m[r] - M);"),
+    ("merge_first_partition_only", "for (int p = 0; p < live; ++p) {\n          int64_t r",
+     "for (int p = 0; p < 1; ++p) {\n          int64_t r"),
+    ("merge_no_division", "for (int d = 0; d < D; ++d) dst[d] /= W;", ""),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = oracle.source_text()
+    assert src.count(old) >= 1, f"mutation site for {name} not found in oracle.c"
+    mutated = src.replace(old, new, 1)
+    orc = oracle.build_variant(mutated, os.path.join(str(tmp_path), f"mut_{name}.so"))
+    failed = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(orc)
+        except Exception as e:  # any failure of the pin counts as caught
+            failed.append((pin.__name__, type(e).__name__))
+    assert failed, f"mutant {name} passed every pin"

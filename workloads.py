@@ -1,0 +1,237 @@
+"""Seeded synthetic inputs for paged grouped-query decode attention.
+
+This module only draws inputs: queries, the fp8-quantized paged K/V cache with
+its per-(token, kv head) scales, block tables and sequence lengths.  It holds
+none of the attention arithmetic, so both the HIP path and the fp64 oracle can
+consume what it produces without sharing code with each other.
+
+Recipe (the same for every workload):
+  * numpy ``default_rng(seed)`` draws the sequence lengths, the permutation of
+    the physical block pool and the outlier channels;
+  * torch's generator (seed+1 for q, seed+2 for K, seed+3 for V), on the
+    requested device, draws N(0, 1) values; K and V are drawn in slabs of at
+    most ``SLAB_BLOCKS`` cache blocks, K slab then V slab;
+  * q: bf16 round-to-nearest-even of N(0, 1), optionally with a seeded set of
+    outlier (q head, dim) channels multiplied by 20 before rounding;
+  * K, V: per (block, slot, kv head) row of head_dim values, scale =
+    fp32(absmax / 448) and codes = e4m3fn(x / scale) rounded to nearest even
+    (torch's cast, after clamping to +-448); an all-zero row has scale 0 and
+    codes 0;
+  * block tables: a random permutation of the pool handed out to the sequences
+    in order, ceil(L / BS) blocks each; unused table entries are 0.
+
+Layouts (all C-contiguous):
+  q             bf16   [S][Hkv*QG][D]
+  k_cache       uint8  [NB][BS][Hkv][D]  (e4m3fn codes)
+  v_cache       uint8  [NB][BS][Hkv][D]
+  kv_scales     fp32   [NB][Hkv][2][BS]  (field 0 = K, field 1 = V)
+  block_tables  int32  [S][max_blocks_per_seq]
+  seq_lens      int32  [S]
+"""
+
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+import torch
+
+FP8_E4M3FN_MAX = 448.0
+TOKENS_PER_TILE_GROUP = 256  # 16 tiles of 16 tokens
+SLAB_BLOCKS = 4096
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    num_seqs: int
+    num_kv_heads: int
+    query_group_size: int
+    kv_block_size: int
+    seq_len_lo: int
+    seq_len_hi: int
+    tile_groups_per_partition: int
+    max_blocks_per_seq: int
+    seed: int
+    head_dim: int = 128
+    num_partitions: Optional[int] = None  # None: sized to the longest sequence
+    num_blocks: Optional[int] = None  # None: exactly the blocks the sequences use
+    outlier_frac: float = 0.0
+    outlier_mult: float = 20.0
+    permute_pool: bool = True
+
+    @property
+    def num_q_heads(self) -> int:
+        return self.num_kv_heads * self.query_group_size
+
+    @property
+    def partition_tokens(self) -> int:
+        return TOKENS_PER_TILE_GROUP * self.tile_groups_per_partition
+
+
+def _W(**kw) -> Workload:
+    return Workload(**kw)
+
+
+# The five workloads: shapes, length mixes and data distributions of the decode
+# configurations this library is specified against.
+WORKLOADS = {
+    "w1_tiny": _W(name="w1_tiny", num_seqs=1, num_kv_heads=1, query_group_size=8, kv_block_size=16,
+                  seq_len_lo=256, seq_len_hi=256, tile_groups_per_partition=1,
+                  max_blocks_per_seq=16, num_blocks=16, num_partitions=1, seed=0x5EED0001),
+    "w2_s32_ctx4k": _W(name="w2_s32_ctx4k", num_seqs=32, num_kv_heads=8, query_group_size=8,
+                       kv_block_size=16, seq_len_lo=4096, seq_len_hi=4096,
+                       tile_groups_per_partition=1, max_blocks_per_seq=256, num_blocks=8192,
+                       num_partitions=16, seed=0x5EED0002),
+    "w3_s64_ragged": _W(name="w3_s64_ragged", num_seqs=64, num_kv_heads=8, query_group_size=6,
+                        kv_block_size=32, seq_len_lo=1024, seq_len_hi=8192,
+                        tile_groups_per_partition=1, max_blocks_per_seq=256, seed=0x5EED0003),
+    "w4_s128_ctx8k": _W(name="w4_s128_ctx8k", num_seqs=128, num_kv_heads=8, query_group_size=8,
+                        kv_block_size=32, seq_len_lo=8192, seq_len_hi=8192,
+                        tile_groups_per_partition=1, max_blocks_per_seq=256, num_blocks=32768,
+                        num_partitions=32, seed=0x5EED0004),
+    "w5_s16_long": _W(name="w5_s16_long", num_seqs=16, num_kv_heads=4, query_group_size=16,
+                      kv_block_size=32, seq_len_lo=16384, seq_len_hi=40960,
+                      tile_groups_per_partition=5, max_blocks_per_seq=1280, seed=0x5EED0005,
+                      outlier_frac=0.01),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    wl: Workload
+    q: torch.Tensor
+    k_cache: torch.Tensor
+    v_cache: torch.Tensor
+    kv_scales: torch.Tensor
+    block_tables: torch.Tensor
+    seq_lens: torch.Tensor
+    num_partitions: int
+    num_blocks: int
+    softmax_scale: float
+
+    def to(self, device) -> "Inputs":
+        f = lambda t: t.to(device)  # noqa: E731
+        return dataclasses.replace(self, q=f(self.q), k_cache=f(self.k_cache), v_cache=f(self.v_cache),
+                                   kv_scales=f(self.kv_scales), block_tables=f(self.block_tables),
+                                   seq_lens=f(self.seq_lens))
+
+    def kv_bytes(self) -> int:
+        """Bytes of live K/V codes plus scales: sum over sequences and kv heads of L * (2*D + 8)."""
+        D = self.wl.head_dim
+        return int(self.seq_lens.to(torch.int64).sum().item()) * self.wl.num_kv_heads * (2 * D + 8)
+
+
+def draw_seq_lens(wl: Workload, rng: np.random.Generator) -> np.ndarray:
+    if wl.seq_len_lo == wl.seq_len_hi:
+        return np.full(wl.num_seqs, wl.seq_len_lo, dtype=np.int32)
+    return rng.integers(wl.seq_len_lo, wl.seq_len_hi + 1, size=wl.num_seqs).astype(np.int32)
+
+
+def quantize_rows(x: torch.Tensor):
+    """fp32 [..., D] -> (e4m3fn codes uint8 [..., D], fp32 scale [...]) with scale = absmax / 448."""
+    absmax = x.abs().amax(dim=-1)
+    scale = absmax / FP8_E4M3FN_MAX
+    div = torch.where(scale > 0, scale, torch.ones_like(scale))
+    y = (x / div.unsqueeze(-1)).clamp_(-FP8_E4M3FN_MAX, FP8_E4M3FN_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
+                softmax_scale: Optional[float] = None) -> Inputs:
+    """Draw the inputs of workload `wl` on `device` (deterministic per device)."""
+    dev = torch.device(device)
+    rng = np.random.default_rng(wl.seed)
+    sl = draw_seq_lens(wl, rng) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    S, Hkv, QG, D, BS = wl.num_seqs, wl.num_kv_heads, wl.query_group_size, wl.head_dim, wl.kv_block_size
+    assert sl.shape == (S,)
+    need = [-(-int(L) // BS) for L in sl]
+    NB = wl.num_blocks if wl.num_blocks is not None else max(1, sum(need))
+    assert NB >= sum(need), "block pool smaller than the sequences need"
+    assert max(need) <= wl.max_blocks_per_seq
+    pool = rng.permutation(NB).astype(np.int32) if wl.permute_pool else np.arange(NB, dtype=np.int32)
+    bt = np.zeros((S, wl.max_blocks_per_seq), dtype=np.int32)
+    pos = 0
+    for s in range(S):
+        bt[s, :need[s]] = pool[pos:pos + need[s]]
+        pos += need[s]
+    if num_partitions is None:
+        num_partitions = wl.num_partitions
+    if num_partitions is None:
+        num_partitions = max(1, -(-int(sl.max()) // wl.partition_tokens))
+
+    gq = torch.Generator(device=dev).manual_seed(wl.seed + 1)
+    q = torch.randn((S, Hkv * QG, D), generator=gq, device=dev, dtype=torch.float32)
+    if wl.outlier_frac > 0:
+        n_out = int(round(wl.outlier_frac * Hkv * QG * D))
+        chans = rng.choice(Hkv * QG * D, size=n_out, replace=False)
+        mult = torch.ones(Hkv * QG * D, dtype=torch.float32)
+        mult[torch.from_numpy(chans.astype(np.int64))] = wl.outlier_mult
+        q = q * mult.view(1, Hkv * QG, D).to(dev)
+    q = q.to(torch.bfloat16)
+
+    k_codes = torch.empty((NB, BS, Hkv, D), dtype=torch.uint8, device=dev)
+    v_codes = torch.empty((NB, BS, Hkv, D), dtype=torch.uint8, device=dev)
+    scales = torch.empty((NB, Hkv, 2, BS), dtype=torch.float32, device=dev)
+    gk = torch.Generator(device=dev).manual_seed(wl.seed + 2)
+    gv = torch.Generator(device=dev).manual_seed(wl.seed + 3)
+    for b0 in range(0, NB, SLAB_BLOCKS):
+        b1 = min(NB, b0 + SLAB_BLOCKS)
+        for field, (gen, dst) in enumerate(((gk, k_codes), (gv, v_codes))):
+            x = torch.randn((b1 - b0, BS, Hkv, D), generator=gen, device=dev, dtype=torch.float32)
+            codes, sc = quantize_rows(x)
+            dst[b0:b1] = codes
+            scales[b0:b1, :, field, :] = sc.permute(0, 2, 1)
+            del x, codes, sc
+    if softmax_scale is None:
+        softmax_scale = float(np.float32(1.0 / math.sqrt(D)))
+    return Inputs(wl=wl, q=q, k_cache=k_codes, v_cache=v_codes, kv_scales=scales,
+                  block_tables=torch.from_numpy(bt).to(dev), seq_lens=torch.from_numpy(sl).to(dev),
+                  num_partitions=int(num_partitions), num_blocks=NB, softmax_scale=softmax_scale)
+
+
+def small_workload(name="small", num_seqs=3, num_kv_heads=2, query_group_size=8, kv_block_size=16,
+                   seq_lens=(1, 17, 300), tile_groups_per_partition=1, max_blocks_per_seq=None,
+                   extra_blocks=3, seed=1234, outlier_frac=0.0) -> Workload:
+    """A small workload for parity sweeps: explicit lengths via make_inputs(seq_lens=...)."""
+    BS = kv_block_size
+    mb = max_blocks_per_seq or max(1, max(-(-int(L) // BS) for L in seq_lens) + 2)
+    nb = sum(-(-int(L) // BS) for L in seq_lens) + extra_blocks
+    return Workload(name=name, num_seqs=num_seqs, num_kv_heads=num_kv_heads,
+                    query_group_size=query_group_size, kv_block_size=BS, seq_len_lo=0,
+                    seq_len_hi=0, tile_groups_per_partition=tile_groups_per_partition,
+                    max_blocks_per_seq=mb, seed=seed, num_blocks=max(1, nb),
+                    outlier_frac=outlier_frac)
+
+
+def poison(inp: Inputs, seed: int = 99) -> Inputs:
+    """Copy of `inp` with garbage wherever a correct reader must not look.
+
+    * cache slots past each sequence's length inside its last block: K/V codes
+      0x7F (NaN) and NaN scales;
+    * block-table entries past ceil(L / BS): other valid block ids of the pool
+      (never out of range, so a wrong reader gives wrong numbers, not a fault).
+    """
+    rng = np.random.default_rng(seed)
+    k = inp.k_cache.clone()
+    v = inp.v_cache.clone()
+    sc = inp.kv_scales.clone()
+    bt = inp.block_tables.cpu().numpy().copy()
+    sl = inp.seq_lens.cpu().numpy()
+    BS = inp.wl.kv_block_size
+    for s, L in enumerate(sl):
+        L = int(L)
+        nb_used = -(-L // BS)
+        if L % BS:
+            b = int(bt[s, nb_used - 1])
+            k[b, L % BS:] = 0x7F
+            v[b, L % BS:] = 0x7F
+            sc[b, :, :, L % BS:] = float("nan")
+        tail = bt.shape[1] - nb_used
+        if tail > 0:
+            bt[s, nb_used:] = rng.integers(0, inp.num_blocks, size=tail)
+    return dataclasses.replace(inp, k_cache=k, v_cache=v, kv_scales=sc,
+                               block_tables=torch.from_numpy(bt).to(inp.block_tables.device))

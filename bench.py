@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark: paged GQA decode attention over an fp8 paged KV cache.
+
+A step is tq_decode (partition kernel) + tq_decode_reduce (merge) over the
+whole batch of the bandwidth workload (128 sequences x 8 kv heads x query
+group 8, head_dim 128, 8192 cached tokens each, block size 32, 32 partitions,
+1 tile group per partition), with inputs already resident in HBM.  Prints ONE
+JSON line on stdout; details go to stderr.
+
+  value      algorithmic KV bytes per step / step time (GB/s), KV bytes =
+             sum over sequences and kv heads of L * 264 (128 B K codes,
+             128 B V codes, 2 fp32 scales)
+  roofline   the partition kernel: the same bytes / its average duration,
+             measured with HIP events on the launch stream over the timed
+             region, against MI355X's 8 TB/s HBM peak
+  cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+KV_BYTES_PER_TOKEN_HEAD = 2 * 128 + 8
+METRIC = "KV-cache GB/s achieved (% of MI355X HBM peak); decode attn µs per step"
+KERNEL_SOURCE = os.path.join(ROOT, "paged_gqa_decode_amd", "csrc", "tq_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per partition-kernel launch from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_partition_kernel_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float):
+    """Time the fp64 oracle (as it stands) on whole (sequence, kv head) units of the workload."""
+    import oracle
+
+    c = inp.to("cpu")
+    wl = inp.wl
+    threads = max(1, min(16, os.cpu_count() or 1))
+    # calibrate on `threads` units, then size the sample to about budget_s
+    units = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_kv_heads)]
+    def run(n):
+        sel = units[:n]
+        t0 = time.perf_counter()
+        oracle.decode(c.q, c.k_cache, c.v_cache, c.kv_scales, c.block_tables, c.seq_lens,
+                      inp.softmax_scale, units=sel, nthreads=threads)
+        return time.perf_counter() - t0, sel
+    dt, sel = run(threads)
+    n = max(threads, min(len(units), int(threads * budget_s / max(dt, 1e-3))))
+    n = (n // threads) * threads or threads
+    dt, sel = run(n)
+    lens = c.seq_lens.numpy()
+    kv_bytes = sum(int(lens[s]) for s, _ in sel) * KV_BYTES_PER_TOKEN_HEAD
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{len(sel)} of {len(units)} (sequence, kv head) units of {wl.name} "
+                      f"({int(lens[sel[0][0]])} tokens each, all {wl.query_group_size} query rows), "
+                      f"fp64 C oracle, {dt:.1f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="w4_s128_ctx8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this library runs "
+              "its decode on a single MI355X; sharding across GPUs is not implemented",
+              file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import paged_gqa_decode_amd as tq
+    import workloads
+
+    wl = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] generating {wl.name} on {dev}")
+    inp = workloads.make_inputs(wl, device=dev)
+    torch.cuda.synchronize()
+    S, Hkv, QG, G = wl.num_seqs, wl.num_kv_heads, wl.query_group_size, wl.tile_groups_per_partition
+    P = inp.num_partitions
+    maxlen = int(inp.seq_lens.max().item())
+    kv_bytes = inp.kv_bytes()
+    part = tq.alloc_partials(S, Hkv, P, QG, dev)
+    out = torch.empty((S, Hkv * QG, 128), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        tq.tq_decode(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, inp.seq_lens,
+                     part, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale, num_partitions=P,
+                     max_seq_len=maxlen, num_blocks=inp.num_blocks, stream=stream)
+        tq.tq_decode_reduce(part, inp.seq_lens, out, Hkv, QG, G, num_partitions=P,
+                            max_seq_len=maxlen, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        tq.tq_decode(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, inp.seq_lens,
+                     part, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale, num_partitions=P,
+                     max_seq_len=maxlen, num_blocks=inp.num_blocks, stream=stream)
+        ev[i][1].record(stream)
+        tq.tq_decode_reduce(part, inp.seq_lens, out, Hkv, QG, G, num_partitions=P,
+                            max_seq_len=maxlen, stream=stream)
+        ev[i][2].record(stream)
+    t_stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
+    red_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
+    ms_per_step = total_ms / K
+    dec_avg = sum(dec_ms) / K
+    red_avg = sum(red_ms) / K
+    dec_sorted = sorted(dec_ms)
+    step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    dec_gbs = kv_bytes / (dec_avg * 1e-3) / 1e9
+    log(f"[bench] {wl.name}: KV bytes {kv_bytes / 1e6:.1f} MB, step {ms_per_step * 1e3:.1f} us "
+        f"(decode avg {dec_avg * 1e3:.1f} us, p10 {dec_sorted[K // 10] * 1e3:.1f}, "
+        f"p90 {dec_sorted[(9 * K) // 10] * 1e3:.1f}; reduce avg {red_avg * 1e3:.1f} us)")
+    log(f"[bench] step {step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of peak), "
+        f"partition kernel {dec_gbs:.0f} GB/s ({100 * dec_gbs / HBM_PEAK_GBS:.1f}% of peak)")
+
+    traffic = measured_traffic(wl.name)
+    res = {
+        "metric": METRIC,
+        "value": round(step_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_of_hbm_peak": round(100 * step_gbs / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "num_seqs": S, "num_kv_heads": Hkv, "query_group_size": QG,
+                   "head_dim": 128, "context_tokens": maxlen, "kv_block_size": wl.kv_block_size,
+                   "num_partitions": P, "tile_groups_per_partition": G,
+                   "kv_format": "e4m3fn codes + fp32 scale per (token, kv head) for K and V",
+                   "kv_bytes_per_step": kv_bytes},
+        "kernels_us": {"tq_decode": round(dec_avg * 1e3, 2), "tq_decode_reduce": round(red_avg * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "tq_decode (partition kernel)",
+                     "bytes_per_launch": kv_bytes},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the fp64 oracle on a sample (cpu_baseline)")
+        res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,155 @@
+/*
+ * tq_decode.h -- C ABI of the MI355X (gfx950) paged grouped-query decode
+ * attention library (libtqdecode.so).
+ *
+ * One decode step of attention for every sequence of a batch: each sequence
+ * has ONE new query token with Hq = Hkv * QG query heads (grouped-query
+ * attention: query heads h*QG .. h*QG+QG-1 share kv head h) and attends to
+ * its L cached tokens, which live in a paged KV cache addressed through a
+ * block table.  The context is split into partitions of E = 256 * G tokens
+ * (flash-decoding split-K); tq_decode computes one normalised partial result
+ * per live partition and tq_decode_reduce merges the partials by log-sum-exp.
+ * Page "vllm.v1.attention.ops.flydsl_kernels.tq_decode": the argument list,
+ * supported sizes and partition semantics are those of the docstring of
+ * build_tq_decode_module; the partial triple (out, exp_sums, max_logits) is
+ * that of STEP G of tq_decode_kernel.
+ *
+ * Cache format.  The page's 4-bit "TQ" contents are left open there; this
+ * library stores K and V as OCP fp8 e4m3fn codes with one fp32 scale per
+ * (token, kv head) for K and one for V, the scales kept as SoA metadata per
+ * cache block in the kv_head -> field -> slot order of the page's per-block
+ * metadata region:
+ *   k_cache, v_cache : uint8 [num_blocks][BS][Hkv][128]   (e4m3fn codes)
+ *   kv_scales        : fp32  [num_blocks][Hkv][2][BS]     (field 0 = K, 1 = V)
+ * The dequantized value is code * scale.
+ *
+ * Memory and threading.
+ *   - Every pointer argument is a DEVICE pointer (HIP device memory) owned
+ *     by the caller, except `ext` and `partials`, which point to HOST structs
+ *     read during the call only.  The library allocates nothing, keeps no
+ *     state other than a thread-local last HIP error, never synchronizes, and
+ *     enqueues its kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream).  All calls are asynchronous and reentrant.
+ *   - q, k_cache, v_cache, kv_scales, the partial buffers and out must be
+ *     16-byte aligned.
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     the call then returns the status and the device is not touched.  A
+ *     failed launch returns TQ_ERR_HIP (see tq_last_hip_error()).  Faults of
+ *     an enqueued kernel surface at the caller's next synchronization.
+ *   - Device-side values are clamped, never trusted for addressing: a
+ *     seq_lens entry is clamped to [0, min(max_seq_len_bound, P*E,
+ *     max_blocks_per_seq*BS)] where max_seq_len_bound = ext->max_seq_len, and
+ *     a block-table entry to [0, num_blocks-1].  A caller that breaks the
+ *     contract (a length above ext->max_seq_len, a block id outside the
+ *     pool) gets wrong numbers, never an out-of-bounds access.
+ */
+#ifndef TQ_DECODE_H
+#define TQ_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TQ_ABI_VERSION 1
+#define TQ_HEAD_DIM 128
+#define TQ_TOKENS_PER_TILE_GROUP 256 /* 16 tiles of 16 tokens */
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  TQ_ERR_MISALIGNED = 2,  /* a data pointer is not 16-byte aligned */
+  TQ_ERR_UNSUPPORTED = 3, /* QG not in {6, 8, 16}, BS not in {16, 32}, head_dim != 128 */
+  TQ_ERR_SHAPE = 4,       /* num_seqs, Hkv, num_blocks, max_blocks_per_seq, P or G < 1,
+                             or a size that overflows the index types */
+  TQ_ERR_COVERAGE = 5,    /* max_seq_len < 0, > P*G*256 or > max_blocks_per_seq*BS */
+  TQ_ERR_SCALE = 6,       /* softmax_scale not finite or <= 0 */
+  TQ_ERR_HIP = 7          /* a HIP launch failed; see tq_last_hip_error() */
+} tq_status;
+
+/* Sizes that a decode step needs besides the named arguments (host struct). */
+typedef struct {
+  int32_t num_seqs;           /* S: sequences in the batch (>= 1) */
+  int32_t num_blocks;         /* NB: physical blocks in k_cache / v_cache / kv_scales (>= 1) */
+  int32_t max_blocks_per_seq; /* row length (stride) of block_tables (>= 1) */
+  int32_t num_partitions;     /* P: partitions per (sequence, kv head) (>= 1) */
+  int32_t max_seq_len;        /* host-known upper bound of seq_lens[] (0 <= . <= P*E) */
+  int32_t head_dim;           /* must be 128 */
+} tq_extent;
+
+/* The split-K partial triple (host struct of device pointers), fp32:
+ *   out        [S][Hkv][P][QG][128]  partial output o_p, normalised by its own l_p
+ *   max_logits [S][Hkv][P][QG]       m_p = max over the partition's tokens of the
+ *                                    scaled logit x = softmax_scale * q.k (natural-log units)
+ *   exp_sums   [S][Hkv][P][QG]       l_p = sum over those tokens of exp(x - m_p)
+ * Entries are written only for live partitions (p*E < L); others are left untouched. */
+typedef struct {
+  float* out;
+  float* max_logits;
+  float* exp_sums;
+} tq_partials;
+
+/*
+ * tq_decode -- the partition kernel: for every (sequence s, kv head h,
+ * partition p) with p*E < L_s, where E = 256 * tile_groups_per_partition,
+ * attend the QG query rows q[s][h*QG + g] to the cached tokens
+ * [p*E, min((p+1)*E, L_s)) and write the partial triple.
+ *   q              bf16 [S][Hkv*QG][128]
+ *   k_cache        e4m3fn [NB][BS][Hkv][128]
+ *   v_cache        e4m3fn [NB][BS][Hkv][128]
+ *   kv_scales      fp32 [NB][Hkv][2][BS]
+ *   block_tables   int32 [S][max_blocks_per_seq]: token t of sequence s is slot
+ *                  t % BS of block block_tables[s][t / BS]; entries at or past
+ *                  ceil(L_s / BS) are never read
+ *   seq_lens       int32 [S]: L_s
+ *   partials       where the partial triple goes (see tq_partials)
+ *   num_kv_heads   Hkv >= 1
+ *   query_group_size  QG in {6, 8, 16}
+ *   kv_block_size  BS in {16, 32}
+ *   tile_groups_per_partition  G >= 1 (E = 256 * G tokens per partition)
+ *   softmax_scale  finite and > 0 (1/sqrt(128) is the usual value)
+ *   ext, stream    see above
+ * Cache slots at or past L_s may hold any bytes (NaN codes and scales
+ * included); they never change the result.
+ */
+tq_status tq_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                    const float* kv_scales, const int32_t* block_tables, const int32_t* seq_lens,
+                    const tq_partials* partials, int32_t num_kv_heads, int32_t query_group_size,
+                    int32_t kv_block_size, int32_t tile_groups_per_partition, float softmax_scale,
+                    const tq_extent* ext, void* stream);
+
+/*
+ * tq_decode_reduce -- the merge kernel: for every (s, h, g), over the live
+ * partitions p of sequence s, M = max m_p, w_p = l_p * exp(m_p - M) and
+ *   out[s][h*QG + g][:] = bf16_rne( sum_p (w_p / sum_p' w_p') * o_p )
+ * With a single live partition this is exactly bf16_rne(o_0); L_s = 0 gives
+ * zeros.  The merge itself is not on the page; it is the log-sum-exp
+ * combination that the partial triple of STEP G of tq_decode_kernel implies.
+ *   out  bf16 [S][Hkv*QG][128], fully overwritten.
+ * The other arguments mean what they mean for tq_decode and must be the same
+ * values that produced the partials.
+ */
+tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens, void* out,
+                           int32_t num_kv_heads, int32_t query_group_size,
+                           int32_t tile_groups_per_partition, const tq_extent* ext, void* stream);
+
+/* Bytes of the three partial arrays for these sizes (each rounded up to 256 B),
+ * laid out out | max_logits | exp_sums; 0 if the sizes are invalid. */
+size_t tq_partials_bytes(const tq_extent* ext, int32_t num_kv_heads, int32_t query_group_size);
+
+/* Static, human-readable text for a status code. */
+const char* tq_status_str(tq_status status);
+
+/* hipError_t of the last TQ_ERR_HIP returned on the calling thread (0 if none). */
+int32_t tq_last_hip_error(void);
+
+/* TQ_ABI_VERSION of the loaded library. */
+int32_t tq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_DECODE_H */

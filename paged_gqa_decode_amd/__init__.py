@@ -1,0 +1,215 @@
+"""Python binding of libtqdecode.so: paged grouped-query decode attention over an
+fp8 e4m3fn paged KV cache on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/tq_decode.h.  torch provides the
+device memory and the current stream.  If the built library is missing, or
+the arguments are not tensors on a GPU, the calls raise -- there is no other
+implementation to fall back to.
+
+Names follow the C ABI: ``tq_decode`` (partition kernel, writes the split-K
+partial triple), ``tq_decode_reduce`` (log-sum-exp merge into bf16), plus
+``decode`` (both, with the partials and output allocated here).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtqdecode.so")
+
+HEAD_DIM = 128
+TOKENS_PER_TILE_GROUP = 256
+SUPPORTED_QUERY_GROUP_SIZES = (6, 8, 16)
+SUPPORTED_KV_BLOCK_SIZES = (16, 32)
+
+TQ_OK, TQ_ERR_NULL, TQ_ERR_MISALIGNED, TQ_ERR_UNSUPPORTED, TQ_ERR_SHAPE, TQ_ERR_COVERAGE, \
+    TQ_ERR_SCALE, TQ_ERR_HIP = range(8)
+
+EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_partials_bytes", "tq_status_str",
+                    "tq_last_hip_error", "tq_abi_version")
+
+
+class TqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: status {status} ({status_str(status)})")
+        self.status = status
+
+
+class Extent(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
+                ("max_blocks_per_seq", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class PartialsStruct(ctypes.Structure):
+    _fields_ = [("out", ctypes.c_void_p), ("max_logits", ctypes.c_void_p),
+                ("exp_sums", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_gqa_decode_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32 = ctypes.c_int32
+    lib.tq_decode.argtypes = [P, P, P, P, P, P, ctypes.POINTER(PartialsStruct), i32, i32, i32, i32,
+                              ctypes.c_float, ctypes.POINTER(Extent), P]
+    lib.tq_decode.restype = ctypes.c_int
+    lib.tq_decode_reduce.argtypes = [ctypes.POINTER(PartialsStruct), P, P, i32, i32, i32,
+                                     ctypes.POINTER(Extent), P]
+    lib.tq_decode_reduce.restype = ctypes.c_int
+    lib.tq_partials_bytes.argtypes = [ctypes.POINTER(Extent), i32, i32]
+    lib.tq_partials_bytes.restype = ctypes.c_size_t
+    lib.tq_status_str.argtypes = [ctypes.c_int]
+    lib.tq_status_str.restype = ctypes.c_char_p
+    lib.tq_last_hip_error.argtypes = []
+    lib.tq_last_hip_error.restype = ctypes.c_int32
+    lib.tq_abi_version.argtypes = []
+    lib.tq_abi_version.restype = ctypes.c_int32
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load_library().tq_status_str(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(load_library().tq_abi_version())
+
+
+def last_hip_error() -> int:
+    return int(load_library().tq_last_hip_error())
+
+
+@dataclass
+class Partials:
+    """The split-K partial triple: out [S][Hkv][P][QG][128], max_logits / exp_sums [S][Hkv][P][QG] (fp32)."""
+    out: torch.Tensor
+    max_logits: torch.Tensor
+    exp_sums: torch.Tensor
+
+    def _struct(self) -> PartialsStruct:
+        return PartialsStruct(self.out.data_ptr(), self.max_logits.data_ptr(), self.exp_sums.data_ptr())
+
+
+def alloc_partials(num_seqs: int, num_kv_heads: int, num_partitions: int, query_group_size: int,
+                   device) -> Partials:
+    shape = (num_seqs, num_kv_heads, num_partitions, query_group_size)
+    return Partials(out=torch.empty(shape + (HEAD_DIM,), dtype=torch.float32, device=device),
+                    max_logits=torch.empty(shape, dtype=torch.float32, device=device),
+                    exp_sums=torch.empty(shape, dtype=torch.float32, device=device))
+
+
+def _extent(num_seqs, num_blocks, max_blocks_per_seq, num_partitions, max_seq_len) -> Extent:
+    return Extent(int(num_seqs), int(num_blocks), int(max_blocks_per_seq), int(num_partitions),
+                  int(max_seq_len), HEAD_DIM)
+
+
+def partials_bytes(num_seqs, num_kv_heads, num_partitions, query_group_size) -> int:
+    ext = _extent(num_seqs, 1, 1, num_partitions, 0)
+    return int(load_library().tq_partials_bytes(ctypes.byref(ext), int(num_kv_heads),
+                                                int(query_group_size)))
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a torch tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def tq_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, partials: Partials,
+              num_kv_heads: int, query_group_size: int, kv_block_size: int,
+              tile_groups_per_partition: int, softmax_scale: float, *, num_partitions: int,
+              max_seq_len: int, num_blocks: Optional[int] = None, stream=None) -> None:
+    """Enqueue the partition kernel (C ABI tq_decode); writes `partials` for live partitions."""
+    lib = load_library()
+    ptrs = [_dev(t, n) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                                    (kv_scales, "kv_scales"), (block_tables, "block_tables"),
+                                    (seq_lens, "seq_lens"))]
+    for t, n in ((partials.out, "partials.out"), (partials.max_logits, "partials.max_logits"),
+                 (partials.exp_sums, "partials.exp_sums")):
+        _dev(t, n)
+    nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ps = partials._struct()
+    st = lib.tq_decode(*ptrs, ctypes.byref(ps), int(num_kv_heads), int(query_group_size),
+                       int(kv_block_size), int(tile_groups_per_partition), float(softmax_scale),
+                       ctypes.byref(ext), _stream(stream))
+    if st != TQ_OK:
+        raise TqError(st, "tq_decode")
+
+
+def tq_decode_reduce(partials: Partials, seq_lens, out, num_kv_heads: int, query_group_size: int,
+                     tile_groups_per_partition: int, *, num_partitions: int, max_seq_len: int,
+                     stream=None) -> None:
+    """Enqueue the merge kernel (C ABI tq_decode_reduce) into bf16 `out` [S][Hkv*QG][128]."""
+    lib = load_library()
+    for t, n in ((partials.out, "partials.out"), (partials.max_logits, "partials.max_logits"),
+                 (partials.exp_sums, "partials.exp_sums")):
+        _dev(t, n)
+    ext = _extent(out.shape[0], 1, 1, num_partitions, max_seq_len)
+    ps = partials._struct()
+    st = lib.tq_decode_reduce(ctypes.byref(ps), _dev(seq_lens, "seq_lens"), _dev(out, "out"),
+                              int(num_kv_heads), int(query_group_size),
+                              int(tile_groups_per_partition), ctypes.byref(ext), _stream(stream))
+    if st != TQ_OK:
+        raise TqError(st, "tq_decode_reduce")
+
+
+def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partitions=None,
+           tile_groups_per_partition: int = 1, softmax_scale: Optional[float] = None,
+           max_seq_len: Optional[int] = None, partials: Optional[Partials] = None,
+           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Decode attention: tq_decode then tq_decode_reduce; returns bf16 [S][Hkv*QG][128].
+
+    q bf16 [S][Hq][128]; k_cache/v_cache uint8 (e4m3fn codes) [NB][BS][Hkv][128];
+    kv_scales fp32 [NB][Hkv][2][BS]; block_tables/seq_lens int32.
+    ``max_seq_len`` (an upper bound of seq_lens) is read from seq_lens when not
+    given, which synchronizes the stream; ``num_partitions`` defaults to
+    ceil(max_seq_len / (256 * G))."""
+    S, Hq, D = q.shape
+    NB, BS, Hkv, Dk = k_cache.shape
+    if D != HEAD_DIM or Dk != HEAD_DIM or Hq % Hkv:
+        raise ValueError("head_dim must be 128 and num_q_heads a multiple of num_kv_heads")
+    QG = Hq // Hkv
+    G = int(tile_groups_per_partition)
+    if max_seq_len is None:
+        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+    if num_partitions is None:
+        num_partitions = max(1, -(-int(max_seq_len) // (TOKENS_PER_TILE_GROUP * G)))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if partials is None:
+        partials = alloc_partials(S, Hkv, num_partitions, QG, q.device)
+    if out is None:
+        out = torch.empty((S, Hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    tq_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, partials, Hkv, QG, BS, G,
+              softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
+              num_blocks=NB, stream=stream)
+    tq_decode_reduce(partials, seq_lens, out, Hkv, QG, G, num_partitions=num_partitions,
+                     max_seq_len=max_seq_len, stream=stream)
+    return out

@@ -1,0 +1,150 @@
+// C ABI of libtqdecode.so (declared in include/tq_decode.h): host-side
+// argument checks, sizes and kernel dispatch.  Nothing here touches the
+// device before every check has passed.
+#include <math.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "tq_decode.h"
+#include "tq_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+bool supported_qg(int32_t qg) { return qg == 6 || qg == 8 || qg == 16; }
+bool supported_bs(int32_t bs) { return bs == 16 || bs == 32; }
+
+// Checks shared by both entry points.  On success fills partition_tokens and
+// len_cap (the device-side clamp of sequence lengths).
+tq_status check_common(const tq_extent* ext, int32_t num_kv_heads, int32_t query_group_size,
+                       int32_t tile_groups_per_partition, int32_t* partition_tokens) {
+  if (!ext) return TQ_ERR_NULL;
+  if (ext->head_dim != TQ_HEAD_DIM || !supported_qg(query_group_size)) return TQ_ERR_UNSUPPORTED;
+  if (ext->num_seqs < 1 || num_kv_heads < 1 || ext->num_blocks < 1 || ext->max_blocks_per_seq < 1 ||
+      ext->num_partitions < 1 || tile_groups_per_partition < 1)
+    return TQ_ERR_SHAPE;
+  const int64_t E = (int64_t)TQ_TOKENS_PER_TILE_GROUP * tile_groups_per_partition;
+  const int64_t units = (int64_t)ext->num_seqs * num_kv_heads * ext->num_partitions;
+  if (E > INT32_MAX / 2 || units > INT32_MAX || (int64_t)ext->num_seqs * num_kv_heads > INT32_MAX)
+    return TQ_ERR_SHAPE;
+  if ((int64_t)ext->num_partitions * E > INT32_MAX) return TQ_ERR_SHAPE;
+  if (ext->max_seq_len < 0 || (int64_t)ext->max_seq_len > (int64_t)ext->num_partitions * E)
+    return TQ_ERR_COVERAGE;
+  *partition_tokens = (int32_t)E;
+  return TQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                    const float* kv_scales, const int32_t* block_tables, const int32_t* seq_lens,
+                    const tq_partials* partials, int32_t num_kv_heads, int32_t query_group_size,
+                    int32_t kv_block_size, int32_t tile_groups_per_partition, float softmax_scale,
+                    const tq_extent* ext, void* stream) {
+  if (!q || !k_cache || !v_cache || !kv_scales || !block_tables || !seq_lens || !partials ||
+      !partials->out || !partials->max_logits || !partials->exp_sums || !ext)
+    return TQ_ERR_NULL;
+  if (!supported_bs(kv_block_size)) return TQ_ERR_UNSUPPORTED;
+  int32_t E = 0;
+  tq_status st = check_common(ext, num_kv_heads, query_group_size, tile_groups_per_partition, &E);
+  if (st != TQ_OK) return st;
+  if ((int64_t)ext->max_seq_len > (int64_t)ext->max_blocks_per_seq * kv_block_size)
+    return TQ_ERR_COVERAGE;
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return TQ_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kv_scales) ||
+      !aligned16(partials->out) || !aligned4(partials->max_logits) ||
+      !aligned4(partials->exp_sums) || !aligned4(block_tables) || !aligned4(seq_lens))
+    return TQ_ERR_MISALIGNED;
+
+  tq::PartitionArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = k_cache;
+  a.v = v_cache;
+  a.scales = kv_scales;
+  a.bt = block_tables;
+  a.seq_lens = seq_lens;
+  a.o = partials->out;
+  a.ml = partials->max_logits;
+  a.es = partials->exp_sums;
+  a.num_kv_heads = num_kv_heads;
+  a.num_partitions = ext->num_partitions;
+  a.partition_tokens = E;
+  a.max_blocks = ext->max_blocks_per_seq;
+  a.num_blocks = ext->num_blocks;
+  a.len_cap = ext->max_seq_len;
+  a.qk_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  const int units = ext->num_seqs * num_kv_heads * ext->num_partitions;
+  hipError_t e = tq::launch_partition(a, query_group_size, kv_block_size, units,
+                                      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return TQ_ERR_HIP;
+  }
+  return TQ_OK;
+}
+
+tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens, void* out,
+                           int32_t num_kv_heads, int32_t query_group_size,
+                           int32_t tile_groups_per_partition, const tq_extent* ext, void* stream) {
+  if (!partials || !partials->out || !partials->max_logits || !partials->exp_sums || !seq_lens ||
+      !out || !ext)
+    return TQ_ERR_NULL;
+  int32_t E = 0;
+  tq_status st = check_common(ext, num_kv_heads, query_group_size, tile_groups_per_partition, &E);
+  if (st != TQ_OK) return st;
+  if (!aligned16(partials->out) || !aligned4(partials->max_logits) ||
+      !aligned4(partials->exp_sums) || !aligned4(seq_lens) || !aligned16(out))
+    return TQ_ERR_MISALIGNED;
+  tq::ReduceArgs a;
+  a.o = partials->out;
+  a.ml = partials->max_logits;
+  a.es = partials->exp_sums;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.num_kv_heads = num_kv_heads;
+  a.query_group_size = query_group_size;
+  a.num_partitions = ext->num_partitions;
+  a.partition_tokens = E;
+  a.len_cap = ext->max_seq_len;
+  hipError_t e = tq::launch_reduce(a, ext->num_seqs * num_kv_heads, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return TQ_ERR_HIP;
+  }
+  return TQ_OK;
+}
+
+size_t tq_partials_bytes(const tq_extent* ext, int32_t num_kv_heads, int32_t query_group_size) {
+  if (!ext || ext->head_dim != TQ_HEAD_DIM || !supported_qg(query_group_size)) return 0;
+  if (ext->num_seqs < 1 || num_kv_heads < 1 || ext->num_partitions < 1) return 0;
+  const uint64_t rows = (uint64_t)ext->num_seqs * num_kv_heads * ext->num_partitions * query_group_size;
+  auto up = [](uint64_t x) { return (x + 255u) & ~(uint64_t)255u; };
+  return (size_t)(up(rows * TQ_HEAD_DIM * 4) + 2 * up(rows * 4));
+}
+
+const char* tq_status_str(tq_status status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_NULL: return "a required pointer is NULL";
+    case TQ_ERR_MISALIGNED: return "a data pointer is not 16-byte aligned";
+    case TQ_ERR_UNSUPPORTED: return "unsupported size (query_group_size in {6,8,16}, kv_block_size in {16,32}, head_dim 128)";
+    case TQ_ERR_SHAPE: return "invalid or overflowing shape (a count < 1 or too large)";
+    case TQ_ERR_COVERAGE: return "max_seq_len is negative or exceeds num_partitions*256*G or max_blocks_per_seq*kv_block_size";
+    case TQ_ERR_SCALE: return "softmax_scale must be finite and > 0";
+    case TQ_ERR_HIP: return "HIP launch failed (see tq_last_hip_error)";
+  }
+  return "unknown status";
+}
+
+int32_t tq_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t tq_abi_version(void) { return TQ_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal interface between the C ABI (tq_api.cpp) and the gfx950 kernels
+// (tq_kernels.hip).  Not installed; the public interface is include/tq_decode.h.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace tq {
+
+constexpr int kHeadDim = 128;
+constexpr int kTokensPerTileGroup = 256;
+
+// Everything the partition kernel reads; sizes already validated on the host.
+struct PartitionArgs {
+  const uint16_t* q;        // bf16 [S][Hkv*QG][128]
+  const uint8_t* k;         // e4m3fn [NB][BS][Hkv][128]
+  const uint8_t* v;         // e4m3fn [NB][BS][Hkv][128]
+  const float* scales;      // fp32 [NB][Hkv][2][BS]
+  const int32_t* bt;        // int32 [S][max_blocks]
+  const int32_t* seq_lens;  // int32 [S]
+  float* o;                 // fp32 [S][Hkv][P][QG][128]
+  float* ml;                // fp32 [S][Hkv][P][QG]
+  float* es;                // fp32 [S][Hkv][P][QG]
+  int32_t num_kv_heads;
+  int32_t num_partitions;
+  int32_t partition_tokens;  // E = 256 * G
+  int32_t max_blocks;        // block-table row stride
+  int32_t num_blocks;        // NB, for clamping block ids
+  int32_t len_cap;           // device lengths are clamped to [0, len_cap]
+  float qk_scale_log2;       // softmax_scale * log2(e)
+};
+
+struct ReduceArgs {
+  const float* o;
+  const float* ml;
+  const float* es;
+  const int32_t* seq_lens;
+  uint16_t* out;  // bf16 [S][Hkv*QG][128]
+  int32_t num_kv_heads;
+  int32_t query_group_size;
+  int32_t num_partitions;
+  int32_t partition_tokens;
+  int32_t len_cap;
+};
+
+// Enqueue the kernels; return the launch status (hipGetLastError after launch).
+hipError_t launch_partition(const PartitionArgs& a, int query_group_size, int kv_block_size,
+                            int num_units, hipStream_t stream);
+hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,393 @@
+// gfx950 (CDNA4) kernels of paged grouped-query decode attention over an fp8
+// e4m3fn KV cache: the split-K partition kernel and the log-sum-exp merge.
+//
+// What is computed follows the page "vllm.v1.attention.ops.flydsl_kernels.
+// tq_decode": the block-table walk (STEP F), the QK^T and PV products with
+// the query group on the MFMA's 16 columns, the online softmax with running
+// max and sum (STEP F, FA-2 state of STEP D), and the normalised partial
+// output with its max logit and exp sum (STEP G).  The kernel design here is
+// its own, made for gfx950:
+//
+//  * One 64-lane wave per live unit (sequence s, kv head h, partition p).
+//    The partition's tokens are walked in chunks of 32 (two 16-token MFMA
+//    tiles), with the next chunk's loads in flight while the current one is
+//    computed.
+//  * K never touches LDS.  QK^T contracts over head_dim, so any permutation
+//    of d applied to both q and K is allowed: lane (r = lane%16, b = lane/16)
+//    supplies K[token r][d = 32b .. 32b+31], one contiguous 32-byte piece of
+//    the token's 128-byte row (two 16-byte loads), and q is loaded with the
+//    same permutation.  fp8 e4m3fn -> bf16 is exact, so the MFMA sees the
+//    exact codes; the per-token K scale and softmax_scale*log2(e) multiply
+//    the fp32 logits afterwards.
+//  * V and the K/V scales go HBM -> LDS directly (global_load_lds_dwordx4 /
+//    _dword, no VGPRs), V rows stored with their 16-byte pieces XOR-swizzled.
+//    ds_read_b64_tr_b8 then returns, per lane, 8 tokens of one head_dim
+//    column: the A operand of a 16x16x32 f16 MFMA (O^T = V^T P), converted
+//    fp8 -> f16 exactly in registers.
+//  * The V scale is folded into P: the B operand is p_t * vs_t / sigma in
+//    f16, where sigma is the running maximum V scale of the partition, so the
+//    operand stays in [0, 1] whatever the data's magnitude; acc is rescaled
+//    when sigma grows, together with the softmax rescale.
+//  * Tokens past the sequence end inside the last chunk may hold any bytes
+//    (NaN codes or scales included): their logits are selected to -inf, their
+//    P and V operand bytes to zero, so they cannot reach the result.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(2))) int i32x2;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+constexpr int D = kHeadDim;
+constexpr int CHUNK = 32;  // tokens per pipeline step
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kLn2 = 0.693147180559945309417f;
+
+// s_waitcnt with vmcnt = 0 and the other counters left at their maxima
+// (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+
+__device__ __forceinline__ float wave_max_xor16_32(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum_xor16_32(float x) {
+  x += __shfl_xor(x, 16, 64);
+  x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
+// 8 fp8 e4m3fn codes (two dwords) -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(int w0, int w1) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// 8 fp8 e4m3fn codes (two dwords) -> 8 f16, exact.
+__device__ __forceinline__ f16x8 fp8x8_to_f16(int w0, int w1) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Cache row (token slot within its block, kv head) byte offset.
+__device__ __forceinline__ size_t row_offset(uint32_t blk, int slot, int BS, int Hkv, int h) {
+  return (((size_t)blk * BS + slot) * Hkv + h) * D;
+}
+
+// Byte offset in the V LDS tile of 16-byte piece `piece` of token row `tok`:
+// rows are 128 B, pieces XOR-swizzled by bits 1..3 of the row index so that
+// the 32 rows read by one transposing load spread over all banks.
+__device__ __forceinline__ int v_lds_offset(int tok, int piece) {
+  return tok * D + 16 * (piece ^ ((tok >> 1) & 7));
+}
+
+template <int QG, int BS>
+__global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
+  static_assert(BS == 16 || BS == 32, "kv block size");
+  static_assert(QG >= 1 && QG <= 16, "query group size");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][CHUNK * D];  // 2 x 4 KiB
+  __shared__ __attribute__((aligned(16))) float lds_sc[2][2 * CHUNK];   // [field][token]
+
+  const int lane = threadIdx.x;
+  const int r = lane & 15;  // MFMA row/column index within a 16-lane group
+  const int b = lane >> 4;  // 16-lane group
+  const int P = a.num_partitions;
+  const int Hkv = a.num_kv_heads;
+  const int unit = blockIdx.x;
+  const int p = unit % P;
+  const int sh = unit / P;
+  const int h = sh % Hkv;
+  const int s = sh / Hkv;
+
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int t_begin = p * a.partition_tokens;
+  if (t_begin >= L) return;  // dead partition: nothing is written
+  const int t_end = min(t_begin + a.partition_tokens, L);
+  const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
+  const int n_blocks = (t_end - t_begin + BS - 1) / BS;  // block-table entries this unit reads
+  const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks + t_begin / BS;
+  const uint32_t nb_max = (uint32_t)a.num_blocks - 1u;
+
+  // Block-table window: lane i holds entry 64*win + i of this partition.
+  int bt_win = 0;
+  int bt_reg = lane < n_blocks ? bt_row[lane] : 0;
+  auto block_id = [&](int j) -> uint32_t {  // j: block index within the partition, uniform
+    if ((j >> 6) != bt_win) {
+      bt_win = j >> 6;
+      const int e = 64 * bt_win + lane;
+      bt_reg = e < n_blocks ? bt_row[e] : 0;
+    }
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane(bt_reg, j & 63);
+    return id < nb_max ? id : nb_max;  // negative ids wrap high and clamp too
+  };
+
+  // q operand (B of QK^T): lane holds q[row r][32b + 8c .. +7] for c = 0..3.
+  bf16x8 qop[4];
+  if (r < QG) {
+    const uint16_t* qrow = a.q + ((size_t)(s * Hkv + h) * QG + r) * D + 32 * b;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qrow + 8 * c);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qop[c] = bf16x8{};
+  }
+
+  const uint8_t* kbase = a.k;
+  const uint8_t* vbase = a.v;
+  const float* sbase = a.scales;
+
+  // Issue the loads of chunk c: K pieces into registers, V rows and scales into LDS stage `st`.
+  i32x4 kraw[2][2];
+  auto issue = [&](int c, int st) {
+    const int jb = (c * CHUNK) / BS;
+    const uint32_t blkA = block_id(jb);
+    uint32_t blkB = blkA;
+    if (BS == 16) blkB = (jb + 1 < n_blocks) ? block_id(jb + 1) : blkA;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t blk = (BS == 32 || t == 0) ? blkA : blkB;
+      const int slot = BS == 32 ? 16 * t + r : r;
+      const uint8_t* src = kbase + row_offset(blk, slot, BS, Hkv, h) + 32 * b;
+      kraw[t][0] = *reinterpret_cast<const i32x4*>(src);
+      kraw[t][1] = *reinterpret_cast<const i32x4*>(src + 16);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = 8 * j + (lane >> 3);
+      const int piece = (lane & 7) ^ ((tok >> 1) & 7);
+      const uint32_t blk = (BS == 32 || tok < 16) ? blkA : blkB;
+      const int slot = BS == 32 ? tok : (tok & 15);
+      const uint8_t* src = vbase + row_offset(blk, slot, BS, Hkv, h) + 16 * piece;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)&lds_v[st][1024 * j], 16, 0, 0);
+    }
+    {
+      const int field = lane >> 5;
+      const int tok = lane & 31;
+      const uint32_t blk = (BS == 32 || tok < 16) ? blkA : blkB;
+      const int slot = BS == 32 ? tok : (tok & 15);
+      const float* src = sbase + (((size_t)blk * Hkv + h) * 2 + field) * BS + slot;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)&lds_sc[st][0], 4, 0, 0);
+    }
+  };
+
+  // Transposing-read address of this lane: MFMA k-slot e of group b is token
+  // 16*(e/4) + 4b + e%4 (the order of the QK^T C layout); source lane s of the
+  // group supplies k-slot s/2 and column half s%2.
+  const int tr_tok = 16 * (r >> 3) + 4 * b + ((r >> 1) & 3);
+  const int tr_half = 8 * (r & 1);
+
+  float m2 = kNegInf;  // running max of log2-scaled logits (row r)
+  float lsum = 0.f;    // this lane's share of the running exp sum
+  float sigma = 0.f;   // running max V scale (operand reference)
+  f32x4 acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  issue(0, 0);
+  for (int c = 0; c < n_chunks; ++c) {
+    const int st = c & 1;
+    // Chunk c's loads are the only ones outstanding: drain them (the LDS
+    // writes of global_load_lds complete under vmcnt) and take everything the
+    // chunk needs out of LDS before chunk c+1's LDS-direct loads are issued;
+    // from then on the chunk is computed from registers only, so no later LDS
+    // read has to wait for the in-flight loads.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 ks0 = *reinterpret_cast<const f32x4*>(&lds_sc[st][4 * b]);
+    f32x4 ks1 = *reinterpret_cast<const f32x4*>(&lds_sc[st][16 + 4 * b]);
+    f32x4 vs0 = *reinterpret_cast<const f32x4*>(&lds_sc[st][32 + 4 * b]);
+    f32x4 vs1 = *reinterpret_cast<const f32x4*>(&lds_sc[st][48 + 4 * b]);
+    i32x2 vraw[8];
+    const uint8_t* vt = &lds_v[st][0];
+#pragma unroll
+    for (int dblk = 0; dblk < 8; ++dblk)
+      vraw[dblk] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_i32x2*)(vt + v_lds_offset(tr_tok, dblk) + tr_half));
+    i32x4 kc[2][2] = {{kraw[0][0], kraw[0][1]}, {kraw[1][0], kraw[1][1]}};
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < n_chunks) issue(c + 1, st ^ 1);
+
+    const int nvalid = min(CHUNK, t_end - (t_begin + c * CHUNK));
+
+    // ---- QK^T: C[token 4b+i][query r] for tiles 0 and 1 ----
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int hi = cc >> 1, lo = 2 * (cc & 1);
+      const bf16x8 k0 = fp8x8_to_bf16(kc[0][hi][lo], kc[0][hi][lo + 1]);
+      const bf16x8 k1 = fp8x8_to_bf16(kc[1][hi][lo], kc[1][hi][lo + 1]);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0, qop[cc], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1, qop[cc], s1, 0, 0, 0);
+    }
+
+    // ---- scale, mask (this lane's tokens 4b..4b+3 and 16+4b..16+4b+3) ----
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = s0[i] * (ks0[i] * a.qk_scale_log2);
+      y[4 + i] = s1[i] * (ks1[i] * a.qk_scale_log2);
+    }
+    int vmask0 = -1, vmask1 = -1;
+    if (nvalid < CHUNK) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool v0 = 4 * b + i < nvalid, v1 = 16 + 4 * b + i < nvalid;
+        y[i] = v0 ? y[i] : kNegInf;
+        y[4 + i] = v1 ? y[4 + i] : kNegInf;
+        vs0[i] = v0 ? vs0[i] : 0.f;
+        vs1[i] = v1 ? vs1[i] : 0.f;
+        if (!v0) vmask0 &= ~(0xFF << (8 * i));
+        if (!v1) vmask1 &= ~(0xFF << (8 * i));
+      }
+    }
+
+    // ---- online softmax (base 2) ----
+    float mx = y[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
+    mx = wave_max_xor16_32(mx);
+    const float m2_new = fmaxf(m2, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m2 - m2_new);
+    float pr[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(y[i] - m2_new);
+      psum += pr[i];
+    }
+    lsum = lsum * alpha + psum;
+    m2 = m2_new;
+
+    // ---- V-scale reference and P operand ----
+    float vmax = fmaxf(fmaxf(fmaxf(vs0[0], vs0[1]), fmaxf(vs0[2], vs0[3])),
+                       fmaxf(fmaxf(vs1[0], vs1[1]), fmaxf(vs1[2], vs1[3])));
+    vmax = wave_max_xor16_32(vmax);
+    const float sigma_new = fmaxf(sigma, vmax);
+    const float inv_sigma = sigma_new > 0.f ? 1.0f / sigma_new : 0.f;
+    const float acc_scale = alpha * (sigma * inv_sigma);
+    sigma = sigma_new;
+    f16x8 pop;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pop[i] = (_Float16)(pr[i] * (vs0[i] * inv_sigma));
+      pop[4 + i] = (_Float16)(pr[4 + i] * (vs1[i] * inv_sigma));
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= acc_scale;
+
+    // ---- PV: acc[dblk] (O^T[d = 16 dblk + 4b + i][query r]) += V^T P ----
+#pragma unroll
+    for (int dblk = 0; dblk < 8; ++dblk) {
+      const f16x8 vop = fp8x8_to_f16(vraw[dblk][0] & vmask0, vraw[dblk][1] & vmask1);
+      acc[dblk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, acc[dblk], 0, 0, 0);
+    }
+  }
+
+  // ---- partial triple (STEP G): o_p = acc * sigma / l_p, m_p, l_p ----
+  const float l = wave_sum_xor16_32(lsum);
+  if (r < QG) {
+    const float f = sigma / l;
+    const size_t row = ((size_t)(s * Hkv + h) * P + p) * QG + r;
+    float* dst = a.o + row * D + 4 * b;
+#pragma unroll
+    for (int dblk = 0; dblk < 8; ++dblk) *reinterpret_cast<f32x4*>(dst + 16 * dblk) = acc[dblk] * f;
+    if (b == 0) {
+      a.ml[row] = m2 * kLn2;
+      a.es[row] = l;
+    }
+  }
+}
+
+// Merge: one 256-thread block per (sequence, kv head); thread -> (query row g,
+// 4 consecutive head_dim columns).
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+  const int sh = blockIdx.x;
+  const int QG = a.query_group_size;
+  const int P = a.num_partitions;
+  const int s = sh / a.num_kv_heads;
+  int L = a.seq_lens[s];
+  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int live = (L + a.partition_tokens - 1) / a.partition_tokens;  // <= P (host-validated)
+  for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x) {
+    const int g = idx / (D / 4);
+    const int col = 4 * (idx % (D / 4));
+    uint16_t* dst = a.out + ((size_t)sh * QG + g) * D + col;
+    const size_t row0 = (size_t)sh * P * QG + g;  // (s, h, p = 0, g)
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    if (live == 1) {
+      o = *reinterpret_cast<const f32x4*>(a.o + row0 * D + col);
+    } else if (live > 1) {
+      float M = kNegInf;
+      for (int p = 0; p < live; ++p) M = fmaxf(M, a.ml[row0 + (size_t)p * QG]);
+      float W = 0.f;
+      for (int p = 0; p < live; ++p) {
+        const size_t rp = row0 + (size_t)p * QG;
+        W += a.es[rp] * __expf(a.ml[rp] - M);
+      }
+      const float invW = 1.0f / W;
+      for (int p = 0; p < live; ++p) {
+        const size_t rp = row0 + (size_t)p * QG;
+        const float w = a.es[rp] * __expf(a.ml[rp] - M) * invW;
+        o += w * *reinterpret_cast<const f32x4*>(a.o + rp * D + col);
+      }
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_partition(const PartitionArgs& a, int query_group_size, int kv_block_size,
+                            int num_units, hipStream_t stream) {
+  const dim3 grid(num_units), block(64);
+#define TQ_LAUNCH(QGV, BSV)                                                            \
+  if (query_group_size == QGV && kv_block_size == BSV) {                              \
+    hipLaunchKernelGGL((partition_kernel<QGV, BSV>), grid, block, 0, stream, a);      \
+    return hipGetLastError();                                                          \
+  }
+  TQ_LAUNCH(6, 16)
+  TQ_LAUNCH(6, 32)
+  TQ_LAUNCH(8, 16)
+  TQ_LAUNCH(8, 32)
+  TQ_LAUNCH(16, 16)
+  TQ_LAUNCH(16, 32)
+#undef TQ_LAUNCH
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream) {
+  hipLaunchKernelGGL(reduce_kernel, dim3(num_seq_heads), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tq

@@ -1,0 +1,104 @@
+"""HIP path vs the fp64 oracle, element by element (bf16 out: max abs <= 1e-2,
+mean abs <= 1e-3).  Needs an MI355X."""
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import compare, gpu_decode, oracle_decode, say, units_rows
+
+pytestmark = pytest.mark.gpu
+
+# (workload, sampled (s, h) units or None for every unit)
+WORKLOAD_CASES = [
+    ("w1_tiny", None),
+    ("w2_s32_ctx4k", None),
+    ("w3_s64_ragged", None),
+    ("w4_s128_ctx8k", 64),
+    ("w5_s16_long", None),
+]
+
+
+@pytest.mark.parametrize("name,sample", WORKLOAD_CASES, ids=[c[0] for c in WORKLOAD_CASES])
+def test_workload_parity(name, sample):
+    wl = workloads.WORKLOADS[name]
+    say(f"[parity] {name}: generating on cuda:0")
+    inp = workloads.make_inputs(wl, device="cuda")
+    say(f"[parity] {name}: S={wl.num_seqs} Hkv={wl.num_kv_heads} QG={wl.query_group_size} "
+        f"BS={wl.kv_block_size} P={inp.num_partitions} G={wl.tile_groups_per_partition} "
+        f"NB={inp.num_blocks} maxL={int(inp.seq_lens.max())}")
+    out = gpu_decode(inp)
+    QG = wl.query_group_size
+    if sample is None:
+        ref = oracle_decode(inp)
+        compare(out, ref, name)
+    else:
+        rng = np.random.default_rng(wl.seed)
+        all_units = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_kv_heads)]
+        idx = rng.choice(len(all_units), size=sample, replace=False)
+        units = [all_units[i] for i in sorted(idx)]
+        ref = oracle_decode(inp, units=units)
+        compare(units_rows(out, units, QG), ref, f"{name} ({sample} sampled units)")
+        # at full size: every output finite and bounded by the largest |V| value
+        o = out.float()
+        assert torch.isfinite(o).all()
+
+
+SWEEP_LENS = (1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 300, 513, 1000)
+SWEEP = [(qg, bs) for qg in (6, 8, 16) for bs in (16, 32)]
+
+
+@pytest.mark.parametrize("qg,bs", SWEEP, ids=[f"qg{q}_bs{b}" for q, b in SWEEP])
+def test_small_sweep(qg, bs):
+    lens = SWEEP_LENS
+    wl = workloads.small_workload(name=f"sweep_qg{qg}_bs{bs}", num_seqs=len(lens), num_kv_heads=3,
+                                  query_group_size=qg, kv_block_size=bs, seq_lens=lens,
+                                  seed=100 + qg + bs)
+    for G, P in ((1, 4), (1, 7), (2, 2), (3, 2), (5, 1)):
+        say(f"[sweep] qg={qg} bs={bs} G={G} P={P} lens={lens}")
+        inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=P)
+        out = gpu_decode(inp, num_partitions=P, tile_groups=G)
+        compare(out, oracle_decode(inp), f"qg{qg} bs{bs} G{G} P{P}")
+
+
+def test_zero_lengths_and_outliers():
+    lens = (0, 1, 700, 0, 33)
+    wl = workloads.small_workload(name="zeros", num_seqs=len(lens), num_kv_heads=2,
+                                  query_group_size=16, kv_block_size=32, seq_lens=lens, seed=7,
+                                  outlier_frac=0.01)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=3)
+    say("[zeros] lens with zeros, outlier q channels")
+    out = gpu_decode(inp, num_partitions=3, tile_groups=1)
+    assert (out[0].float() == 0).all() and (out[3].float() == 0).all()
+    compare(out, oracle_decode(inp), "zero lengths + outliers")
+
+
+def test_partials_match_oracle():
+    """The partial triple itself (fp32) against the oracle's split-K partials."""
+    import oracle
+    import paged_gqa_decode_amd as tq
+
+    lens = (40, 256, 257, 600)
+    wl = workloads.small_workload(name="partials", num_seqs=4, num_kv_heads=2, query_group_size=8,
+                                  kv_block_size=16, seq_lens=lens, seed=11)
+    P, G = 3, 1
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=P)
+    part = tq.alloc_partials(4, 2, P, 8, "cuda")
+    for t in (part.out, part.max_logits, part.exp_sums):
+        t.fill_(float("nan"))
+    say("[partials] P=3 G=1")
+    gpu_decode(inp, num_partitions=P, tile_groups=G, partials=part)
+    c = inp.to("cpu")
+    o, m, l = oracle.partials(c.q, c.k_cache, c.v_cache, c.kv_scales, c.block_tables, c.seq_lens,
+                              inp.softmax_scale, P, 256 * G)
+    live = ~np.isnan(m)
+    gm = part.max_logits.cpu().numpy()
+    gl = part.exp_sums.cpu().numpy()
+    go = part.out.cpu().numpy()
+    assert np.array_equal(np.isnan(gm), ~live), "dead partitions must stay untouched"
+    assert np.max(np.abs(gm[live] - m[live])) < 1e-4 * max(1.0, np.abs(m[live]).max())
+    assert np.max(np.abs(gl[live] / l[live] - 1)) < 2e-3
+    err = np.abs(go[live] - o[live]).max()
+    say(f"  partial o max abs err {err:.3e}")
+    assert err < 5e-3

@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
 """Decode-step benchmark: paged GQA decode attention over an fp8 paged KV cache.
 
-A step is tq_decode (partition kernel) + tq_decode_reduce (merge) over the
-whole batch of the bandwidth workload (128 sequences x 8 kv heads x query
-group 8, head_dim 128, 8192 cached tokens each, block size 32, 32 partitions,
-1 tile group per partition), with inputs already resident in HBM.  Prints ONE
-JSON line on stdout; details go to stderr.
+A step is one decode of the whole batch of the bandwidth workload (128
+sequences x 8 kv heads x query group 8, head_dim 128, 8192 cached tokens each,
+block size 32, 32 partitions of 1 tile group), with inputs already resident in
+HBM, through either complete path of the library: tq_decode (partition kernel)
++ tq_decode_reduce (merge), or tq_decode_fused (one launch).  Both are timed;
+the faster is the headline step.  Prints ONE JSON line on stdout; details go to
+stderr.
 
-  value      algorithmic KV bytes per step / step time (GB/s), KV bytes =
-             sum over sequences and kv heads of L * 264 (128 B K codes,
-             128 B V codes, 2 fp32 scales)
-  roofline   the partition kernel: the same bytes / its average duration,
-             measured with HIP events on the launch stream over the timed
-             region, against MI355X's 8 TB/s HBM peak
+  value         algorithmic KV bytes per step / step time (GB/s); KV bytes =
+                sum over sequences and kv heads of L * 264 (128 B K codes,
+                128 B V codes, 2 fp32 scales)
+  roofline      the headline path's first kernel: the same bytes / its average
+                duration, from HIP events recorded on the launch stream around
+                every launch of the timed region, against MI355X's 8 TB/s
+  hbm_probe     best read and copy bandwidth of plain streaming kernels
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
 """
 
@@ -21,7 +24,6 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
-import math
 import os
 import sys
 import time
@@ -33,6 +35,7 @@ HBM_PEAK_GBS = 8000.0
 KV_BYTES_PER_TOKEN_HEAD = 2 * 128 + 8
 METRIC = "KV-cache GB/s achieved (% of MI355X HBM peak); decode attn µs per step"
 KERNEL_SOURCE = os.path.join(ROOT, "paged_gqa_decode_amd", "csrc", "tq_kernels.hip")
+KERNEL_NAMES = {"two_kernel": "tq_partition_kernel", "fused": "tq_fused_kernel"}
 
 
 def log(*a):
@@ -44,10 +47,10 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per partition-kernel launch from the committed rocprofv3 counter
-    summary, or None if there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"traffic_partition_kernel_{workload}.json")
+def measured_traffic(workload: str, path_name: str):
+    """HBM bytes per launch of the headline kernel from the committed rocprofv3
+    counter summary, or None if there is none or the kernel source changed since."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAMES[path_name]}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -64,14 +67,16 @@ def cpu_baseline(inp, budget_s: float):
     c = inp.to("cpu")
     wl = inp.wl
     threads = max(1, min(16, os.cpu_count() or 1))
-    # calibrate on `threads` units, then size the sample to about budget_s
     units = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_kv_heads)]
+
     def run(n):
         sel = units[:n]
         t0 = time.perf_counter()
         oracle.decode(c.q, c.k_cache, c.v_cache, c.kv_scales, c.block_tables, c.seq_lens,
                       inp.softmax_scale, units=sel, nthreads=threads)
         return time.perf_counter() - t0, sel
+
+    # calibrate on `threads` units, then size the sample to about budget_s
     dt, sel = run(threads)
     n = max(threads, min(len(units), int(threads * budget_s / max(dt, 1e-3))))
     n = (n // threads) * threads or threads
@@ -85,6 +90,42 @@ def cpu_baseline(inp, budget_s: float):
                       f"fp64 C oracle, {dt:.1f} s wall"}
 
 
+def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10):
+    """Best-of read and copy bandwidth of the streaming probes (GB/s, bytes moved / time)."""
+    import torch
+
+    from paged_gqa_decode_amd import probe
+
+    nread = int(read_gib * (1 << 30))
+    ncopy = int(copy_gib * (1 << 30))
+    src = torch.empty(nread, dtype=torch.uint8, device=dev)
+    src.random_(0, 256)
+    dst = torch.empty(ncopy, dtype=torch.uint8, device=dev)
+    sink = torch.empty(65536, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def best(fn, moved, wgs_list):
+        out = (0.0, 0)
+        for wgs in wgs_list:
+            fn(wgs)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn(wgs)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out = max(out, (moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, wgs))
+        return out
+
+    rd = best(lambda w: probe.read(src, sink, w), nread, (1024, 2048, 4096, 8192))
+    cp = best(lambda w: probe.copy(dst, src[:ncopy], w), 2 * ncopy, (2048, 4096, 8192))
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return {"read_bytes": nread, "copy_bytes": ncopy, "reps": reps,
+            "read_gbs": round(rd[0], 1), "read_workgroups": rd[1],
+            "copy_gbs": round(cp[0], 1), "copy_workgroups": cp[1]}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,6 +134,7 @@ def main() -> int:
     ap.add_argument("--workload", default="w4_s128_ctx8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-probe", action="store_true", help="skip the HBM read/copy probe")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this library runs "
@@ -111,6 +153,10 @@ def main() -> int:
     wl = workloads.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    probe_res = None
+    if not args.no_probe:
+        probe_res = hbm_probe(dev)
+        log(f"[bench] HBM probe: read {probe_res['read_gbs']} GB/s, copy {probe_res['copy_gbs']} GB/s")
     log(f"[bench] generating {wl.name} on {dev}")
     inp = workloads.make_inputs(wl, device=dev)
     torch.cuda.synchronize()
@@ -122,50 +168,69 @@ def main() -> int:
     out = torch.empty((S, Hkv * QG, 128), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
+    def two_kernel(events=None):
+        if events is not None:
+            events[0].record(stream)
         tq.tq_decode(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, inp.seq_lens,
                      part, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale, num_partitions=P,
                      max_seq_len=maxlen, num_blocks=inp.num_blocks, stream=stream)
+        if events is not None:
+            events[1].record(stream)
         tq.tq_decode_reduce(part, inp.seq_lens, out, Hkv, QG, G, num_partitions=P,
                             max_seq_len=maxlen, stream=stream)
+        if events is not None:
+            events[2].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def fused(events=None):
+        if events is not None:
+            events[0].record(stream)
+        tq.tq_decode_fused(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables,
+                           inp.seq_lens, out, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale,
+                           num_partitions=P, max_seq_len=maxlen, num_blocks=inp.num_blocks,
+                           stream=stream)
+        if events is not None:
+            events[1].record(stream)
+            events[2].record(stream)
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(K):
-        ev[i][0].record(stream)
-        tq.tq_decode(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, inp.seq_lens,
-                     part, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale, num_partitions=P,
-                     max_seq_len=maxlen, num_blocks=inp.num_blocks, stream=stream)
-        ev[i][1].record(stream)
-        tq.tq_decode_reduce(part, inp.seq_lens, out, Hkv, QG, G, num_partitions=P,
-                            max_seq_len=maxlen, stream=stream)
-        ev[i][2].record(stream)
-    t_stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_stop)
-    dec_ms = [ev[i][0].elapsed_time(ev[i][1]) for i in range(K)]
-    red_ms = [ev[i][1].elapsed_time(ev[i][2]) for i in range(K)]
-    ms_per_step = total_ms / K
-    dec_avg = sum(dec_ms) / K
-    red_avg = sum(red_ms) / K
-    dec_sorted = sorted(dec_ms)
-    step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    dec_gbs = kv_bytes / (dec_avg * 1e-3) / 1e9
-    log(f"[bench] {wl.name}: KV bytes {kv_bytes / 1e6:.1f} MB, step {ms_per_step * 1e3:.1f} us "
-        f"(decode avg {dec_avg * 1e3:.1f} us, p10 {dec_sorted[K // 10] * 1e3:.1f}, "
-        f"p90 {dec_sorted[(9 * K) // 10] * 1e3:.1f}; reduce avg {red_avg * 1e3:.1f} us)")
-    log(f"[bench] step {step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% of peak), "
-        f"partition kernel {dec_gbs:.0f} GB/s ({100 * dec_gbs / HBM_PEAK_GBS:.1f}% of peak)")
 
-    traffic = measured_traffic(wl.name)
+    def timed(step_fn):
+        """W warmup steps, then K steps between synchronizations, HIP events on the launch
+        stream around every kernel.  Returns (ms per step, [first-kernel ms], [second-kernel ms])."""
+        for _ in range(args.warmup):
+            step_fn()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_stop = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(K):
+            step_fn(ev[i])
+        t_stop.record(stream)
+        torch.cuda.synchronize()
+        return (t_start.elapsed_time(t_stop) / K, [e[0].elapsed_time(e[1]) for e in ev],
+                [e[1].elapsed_time(e[2]) for e in ev])
+
+    paths = {}
+    for name, fn in (("two_kernel", two_kernel), ("fused", fused)):
+        ms, k1, k2 = timed(fn)
+        k1s = sorted(k1)
+        paths[name] = {"ms_per_step": ms, "k1_avg": sum(k1) / K, "k2_avg": sum(k2) / K,
+                       "k1_p10": k1s[K // 10], "k1_p90": k1s[(9 * K) // 10]}
+        log(f"[bench] {wl.name} {name}: step {ms * 1e3:.1f} us "
+            f"({kv_bytes / (ms * 1e-3) / 1e9:.0f} GB/s); first kernel avg "
+            f"{paths[name]['k1_avg'] * 1e3:.1f} us (p10 {paths[name]['k1_p10'] * 1e3:.1f}, "
+            f"p90 {paths[name]['k1_p90'] * 1e3:.1f}), second kernel avg "
+            f"{paths[name]['k2_avg'] * 1e3:.1f} us")
+    head = min(paths, key=lambda n: paths[n]["ms_per_step"])
+    ms_per_step = paths[head]["ms_per_step"]
+    k1_avg = paths[head]["k1_avg"]
+    step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    k1_gbs = kv_bytes / (k1_avg * 1e-3) / 1e9
+    log(f"[bench] headline path {head}: step {step_gbs:.0f} GB/s ({100 * step_gbs / HBM_PEAK_GBS:.1f}% "
+        f"of peak); {KERNEL_NAMES[head]} {k1_gbs:.0f} GB/s ({100 * k1_gbs / HBM_PEAK_GBS:.1f}% of peak)")
+
     res = {
         "metric": METRIC,
         "value": round(step_gbs, 2),
@@ -183,15 +248,24 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": wl.name, "num_seqs": S, "num_kv_heads": Hkv, "query_group_size": QG,
                    "head_dim": 128, "context_tokens": maxlen, "kv_block_size": wl.kv_block_size,
-                   "num_partitions": P, "tile_groups_per_partition": G,
+                   "num_partitions": P, "tile_groups_per_partition": G, "path": head,
                    "kv_format": "e4m3fn codes + fp32 scale per (token, kv head) for K and V",
                    "kv_bytes_per_step": kv_bytes},
-        "kernels_us": {"tq_decode": round(dec_avg * 1e3, 2), "tq_decode_reduce": round(red_avg * 1e3, 2)},
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(dec_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "tq_decode (partition kernel)",
+        "paths_us": {
+            "two_kernel": {"step": round(paths["two_kernel"]["ms_per_step"] * 1e3, 2),
+                           "tq_decode": round(paths["two_kernel"]["k1_avg"] * 1e3, 2),
+                           "tq_decode_reduce": round(paths["two_kernel"]["k2_avg"] * 1e3, 2)},
+            "fused": {"step": round(paths["fused"]["ms_per_step"] * 1e3, 2),
+                      "tq_decode_fused": round(paths["fused"]["k1_avg"] * 1e3, 2)},
+        },
+        "roofline": {"bound": "hbm", "achieved": round(k1_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(wl.name, head), "kernel": KERNEL_NAMES[head],
                      "bytes_per_launch": kv_bytes},
     }
+    if probe_res is not None:
+        res["hbm_probe"] = probe_res
+        res["roofline"]["frac_of_probe_read"] = round(k1_gbs / probe_res["read_gbs"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a sample (cpu_baseline)")
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

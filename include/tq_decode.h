@@ -19,9 +19,11 @@
  * (token, kv head) for K and one for V, the scales kept as SoA metadata per
  * cache block in the kv_head -> field -> slot order of the page's per-block
  * metadata region:
- *   k_cache, v_cache : uint8 [num_blocks][BS][Hkv][128]   (e4m3fn codes)
+ *   k_cache, v_cache : uint8 [num_blocks][Hkv][BS][128]   (e4m3fn codes)
  *   kv_scales        : fp32  [num_blocks][Hkv][2][BS]     (field 0 = K, 1 = V)
- * The dequantized value is code * scale.
+ * Both are kv-head-major inside a block, like the page's per-block metadata
+ * region (kv head, then field, then slot): the BS rows of one (block, kv head)
+ * are one contiguous 2 or 4 KiB range.  The dequantized value is code * scale.
  *
  * Memory and threading.
  *   - Every pointer argument is a DEVICE pointer (HIP device memory) owned
@@ -97,8 +99,8 @@ typedef struct {
  * attend the QG query rows q[s][h*QG + g] to the cached tokens
  * [p*E, min((p+1)*E, L_s)) and write the partial triple.
  *   q              bf16 [S][Hkv*QG][128]
- *   k_cache        e4m3fn [NB][BS][Hkv][128]
- *   v_cache        e4m3fn [NB][BS][Hkv][128]
+ *   k_cache        e4m3fn [NB][Hkv][BS][128]
+ *   v_cache        e4m3fn [NB][Hkv][BS][128]
  *   kv_scales      fp32 [NB][Hkv][2][BS]
  *   block_tables   int32 [S][max_blocks_per_seq]: token t of sequence s is slot
  *                  t % BS of block block_tables[s][t / BS]; entries at or past
@@ -134,6 +136,29 @@ tq_status tq_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_cach
 tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens, void* out,
                            int32_t num_kv_heads, int32_t query_group_size,
                            int32_t tile_groups_per_partition, const tq_extent* ext, void* stream);
+
+/*
+ * tq_decode_fused -- the whole decode step in one launch, bf16 out directly.
+ * One workgroup per (sequence s, kv head h): the live partitions of s
+ * (partitions of E = 256 * tile_groups_per_partition tokens, as for tq_decode)
+ * are dealt in contiguous runs to the workgroup's waves; each wave keeps one
+ * online softmax over its run, and the waves' partial results (o, m, l, as in
+ * STEP G of tq_decode_kernel) are merged by log-sum-exp inside the workgroup,
+ * in wave order, with the formula of tq_decode_reduce.  No partial leaves the
+ * chip, so no partial buffer is needed; the merge across partitions is the
+ * in-launch merge that the page's partial triple implies.
+ *   out  bf16 [S][Hkv*QG][128], fully overwritten (L_s = 0 gives zeros).
+ * Other arguments, errors and guarantees are those of tq_decode.  With one
+ * live partition the output is bit-identical to tq_decode + tq_decode_reduce;
+ * otherwise the two differ only by rounding (they group the same partitions
+ * differently), and repeated calls are bit-identical.
+ */
+tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                          const float* kv_scales, const int32_t* block_tables,
+                          const int32_t* seq_lens, void* out, int32_t num_kv_heads,
+                          int32_t query_group_size, int32_t kv_block_size,
+                          int32_t tile_groups_per_partition, float softmax_scale,
+                          const tq_extent* ext, void* stream);
 
 /* Bytes of the three partial arrays for these sizes (each rounded up to 256 B),
  * laid out out | max_logits | exp_sums; 0 if the sizes are invalid. */

@@ -10,8 +10,8 @@ definition and the readings taken where that page is silent.
 
 Array conventions (numpy, C-contiguous):
   q_bits        uint16 [S][Hkv*QG][D]   bfloat16 bit patterns
-  k_codes       uint8  [NB][BS][Hkv][D] OCP e4m3fn codes
-  v_codes       uint8  [NB][BS][Hkv][D]
+  k_codes       uint8  [NB][Hkv][BS][D] OCP e4m3fn codes
+  v_codes       uint8  [NB][Hkv][BS][D]
   kv_scales     float32 [NB][Hkv][2][BS] (field 0 = K, field 1 = V)
   block_tables  int32  [S][max_blocks_per_seq]
   seq_lens      int32  [S]
@@ -196,7 +196,7 @@ def _problem(q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens):
     sc = _np(kv_scales, np.float32)
     bt = _np(block_tables, np.int32)
     sl = _np(seq_lens, np.int32)
-    NB, BS, Hkv, D = k.shape
+    NB, Hkv, BS, D = k.shape
     S, Hq, Dq = q.shape
     if v.shape != k.shape or sc.shape != (NB, Hkv, 2, BS) or Dq != D or Hq % Hkv:
         raise OracleError("inconsistent shapes")

@@ -19,11 +19,12 @@
  *   out   = sum_t exp(x_t - max x) v_t / sum_t exp(x_t - max x)
  *
  * Cache format (the pages leave the "TQ" contents open; this library fixes
- * fp8): K and V are OCP e4m3fn codes k_cache/v_cache[NB][BS][Hkv][D], each
+ * fp8): K and V are OCP e4m3fn codes k_cache/v_cache[NB][Hkv][BS][D], each
  * (token, kv head) row carrying one fp32 scale for K and one for V, stored as
  * SoA metadata per cache block: kv_scales[NB][Hkv][2][BS] (field 0 = K,
- * field 1 = V), the kv_head -> field -> slot order of the page's per-block
- * metadata region.  Dequantized k_t[d] = e4m3fn(code) * scale.
+ * field 1 = V).  Both follow the kv_head-major order of the page's per-block
+ * metadata region (kv head, then field, then slot).  Dequantized
+ * k_t[d] = e4m3fn(code) * scale.
  *
  * Everything is fp64: bf16 q and fp8 codes decode exactly, the fp32 scales and
  * the fp32 softmax_scale are widened, and exp() is libm's double exp().
@@ -93,7 +94,7 @@ static int orc_block(const orc_problem* pb, int s, int t, int* blk) {
 /* Dequantized element d of the K (field 0) or V (field 1) row of token t. */
 static double orc_kv(const orc_problem* pb, int field, int blk, int slot, int h, int d) {
   const uint8_t* cache = field == 0 ? pb->k_cache : pb->v_cache;
-  int64_t row = ((int64_t)blk * pb->BS + slot) * pb->Hkv + h;
+  int64_t row = ((int64_t)blk * pb->Hkv + h) * pb->BS + slot;
   double code = orc_dec_e4m3fn(cache[row * pb->D + d]);
   double sc = (double)pb->kv_scales[(((int64_t)blk * pb->Hkv + h) * 2 + field) * pb->BS + slot];
   return code * sc;

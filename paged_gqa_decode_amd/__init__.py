@@ -33,8 +33,8 @@ SUPPORTED_KV_BLOCK_SIZES = (16, 32)
 TQ_OK, TQ_ERR_NULL, TQ_ERR_MISALIGNED, TQ_ERR_UNSUPPORTED, TQ_ERR_SHAPE, TQ_ERR_COVERAGE, \
     TQ_ERR_SCALE, TQ_ERR_HIP = range(8)
 
-EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_partials_bytes", "tq_status_str",
-                    "tq_last_hip_error", "tq_abi_version")
+EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_decode_fused", "tq_partials_bytes",
+                    "tq_status_str", "tq_last_hip_error", "tq_abi_version")
 
 
 class TqError(RuntimeError):
@@ -73,6 +73,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq_decode_reduce.argtypes = [ctypes.POINTER(PartialsStruct), P, P, i32, i32, i32,
                                      ctypes.POINTER(Extent), P]
     lib.tq_decode_reduce.restype = ctypes.c_int
+    lib.tq_decode_fused.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float,
+                                    ctypes.POINTER(Extent), P]
+    lib.tq_decode_fused.restype = ctypes.c_int
     lib.tq_partials_bytes.argtypes = [ctypes.POINTER(Extent), i32, i32]
     lib.tq_partials_bytes.restype = ctypes.c_size_t
     lib.tq_status_str.argtypes = [ctypes.c_int]
@@ -180,19 +183,40 @@ def tq_decode_reduce(partials: Partials, seq_lens, out, num_kv_heads: int, query
         raise TqError(st, "tq_decode_reduce")
 
 
+def tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
+                    num_kv_heads: int, query_group_size: int, kv_block_size: int,
+                    tile_groups_per_partition: int, softmax_scale: float, *, num_partitions: int,
+                    max_seq_len: int, num_blocks: Optional[int] = None, stream=None) -> None:
+    """Enqueue the one-launch decode (C ABI tq_decode_fused) into bf16 `out` [S][Hkv*QG][128]."""
+    lib = load_library()
+    ptrs = [_dev(t, n) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                                    (kv_scales, "kv_scales"), (block_tables, "block_tables"),
+                                    (seq_lens, "seq_lens"), (out, "out"))]
+    nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    st = lib.tq_decode_fused(*ptrs, int(num_kv_heads), int(query_group_size), int(kv_block_size),
+                             int(tile_groups_per_partition), float(softmax_scale),
+                             ctypes.byref(ext), _stream(stream))
+    if st != TQ_OK:
+        raise TqError(st, "tq_decode_fused")
+
+
 def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partitions=None,
            tile_groups_per_partition: int = 1, softmax_scale: Optional[float] = None,
            max_seq_len: Optional[int] = None, partials: Optional[Partials] = None,
-           out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Decode attention: tq_decode then tq_decode_reduce; returns bf16 [S][Hkv*QG][128].
+           out: Optional[torch.Tensor] = None, fused: bool = False, stream=None) -> torch.Tensor:
+    """Decode attention; returns bf16 [S][Hkv*QG][128].
 
-    q bf16 [S][Hq][128]; k_cache/v_cache uint8 (e4m3fn codes) [NB][BS][Hkv][128];
+    fused=False: tq_decode then tq_decode_reduce (partials in `partials` or
+    allocated here); fused=True: tq_decode_fused (no partials).
+
+    q bf16 [S][Hq][128]; k_cache/v_cache uint8 (e4m3fn codes) [NB][Hkv][BS][128];
     kv_scales fp32 [NB][Hkv][2][BS]; block_tables/seq_lens int32.
     ``max_seq_len`` (an upper bound of seq_lens) is read from seq_lens when not
     given, which synchronizes the stream; ``num_partitions`` defaults to
     ceil(max_seq_len / (256 * G))."""
     S, Hq, D = q.shape
-    NB, BS, Hkv, Dk = k_cache.shape
+    NB, Hkv, BS, Dk = k_cache.shape
     if D != HEAD_DIM or Dk != HEAD_DIM or Hq % Hkv:
         raise ValueError("head_dim must be 128 and num_q_heads a multiple of num_kv_heads")
     QG = Hq // Hkv
@@ -203,10 +227,15 @@ def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partit
         num_partitions = max(1, -(-int(max_seq_len) // (TOKENS_PER_TILE_GROUP * G)))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
-    if partials is None:
-        partials = alloc_partials(S, Hkv, num_partitions, QG, q.device)
     if out is None:
         out = torch.empty((S, Hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
+    if fused:
+        tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out, Hkv, QG, BS, G,
+                        softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
+                        num_blocks=NB, stream=stream)
+        return out
+    if partials is None:
+        partials = alloc_partials(S, Hkv, num_partitions, QG, q.device)
     tq_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, partials, Hkv, QG, BS, G,
               softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
               num_blocks=NB, stream=stream)

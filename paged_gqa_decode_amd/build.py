@@ -11,6 +11,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtqdecode.so")
 SOURCES = [os.path.join(CSRC, "tq_kernels.hip"), os.path.join(CSRC, "tq_api.cpp")]
+PROBE_LIB = os.path.join(PKG, "libtqprobe.so")
+PROBE_SOURCES = [os.path.join(CSRC, "tq_probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops off: hipcc may otherwise pair fp32 arithmetic into packed
@@ -20,9 +22,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-Wal
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, "-o", tmp, *SOURCES]
+def _hipcc(out: str, sources, verbose: bool) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -32,8 +34,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Build libtqdecode.so (decode kernels + C ABI) and libtqprobe.so (HBM probes)."""
+    _hipcc(PROBE_LIB, PROBE_SOURCES, verbose)
+    return _hipcc(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -39,6 +39,45 @@ tq_status check_common(const tq_extent* ext, int32_t num_kv_heads, int32_t query
   return TQ_OK;
 }
 
+// Checks of the decode arguments shared by tq_decode and tq_decode_fused
+// (all but the output pointers); fills the stream arguments and E.
+tq_status check_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                       const float* kv_scales, const int32_t* block_tables,
+                       const int32_t* seq_lens, int32_t num_kv_heads, int32_t query_group_size,
+                       int32_t kv_block_size, int32_t tile_groups_per_partition,
+                       float softmax_scale, const tq_extent* ext, tq::StreamArgs* st,
+                       int32_t* E) {
+  if (!q || !k_cache || !v_cache || !kv_scales || !block_tables || !seq_lens || !ext)
+    return TQ_ERR_NULL;
+  if (!supported_bs(kv_block_size)) return TQ_ERR_UNSUPPORTED;
+  tq_status s = check_common(ext, num_kv_heads, query_group_size, tile_groups_per_partition, E);
+  if (s != TQ_OK) return s;
+  if ((int64_t)ext->max_seq_len > (int64_t)ext->max_blocks_per_seq * kv_block_size)
+    return TQ_ERR_COVERAGE;
+  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return TQ_ERR_SCALE;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kv_scales) ||
+      !aligned4(block_tables) || !aligned4(seq_lens))
+    return TQ_ERR_MISALIGNED;
+  st->q = static_cast<const uint16_t*>(q);
+  st->k = k_cache;
+  st->v = v_cache;
+  st->scales = kv_scales;
+  st->bt = block_tables;
+  st->num_kv_heads = num_kv_heads;
+  st->max_blocks = ext->max_blocks_per_seq;
+  st->num_blocks = ext->num_blocks;
+  st->qk_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  return TQ_OK;
+}
+
+tq_status hip_status(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_hip_error = (int32_t)e;
+    return TQ_ERR_HIP;
+  }
+  return TQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -48,46 +87,48 @@ tq_status tq_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_cach
                     const tq_partials* partials, int32_t num_kv_heads, int32_t query_group_size,
                     int32_t kv_block_size, int32_t tile_groups_per_partition, float softmax_scale,
                     const tq_extent* ext, void* stream) {
-  if (!q || !k_cache || !v_cache || !kv_scales || !block_tables || !seq_lens || !partials ||
-      !partials->out || !partials->max_logits || !partials->exp_sums || !ext)
+  if (!partials || !partials->out || !partials->max_logits || !partials->exp_sums)
     return TQ_ERR_NULL;
-  if (!supported_bs(kv_block_size)) return TQ_ERR_UNSUPPORTED;
-  int32_t E = 0;
-  tq_status st = check_common(ext, num_kv_heads, query_group_size, tile_groups_per_partition, &E);
-  if (st != TQ_OK) return st;
-  if ((int64_t)ext->max_seq_len > (int64_t)ext->max_blocks_per_seq * kv_block_size)
-    return TQ_ERR_COVERAGE;
-  if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return TQ_ERR_SCALE;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kv_scales) ||
-      !aligned16(partials->out) || !aligned4(partials->max_logits) ||
-      !aligned4(partials->exp_sums) || !aligned4(block_tables) || !aligned4(seq_lens))
-    return TQ_ERR_MISALIGNED;
-
   tq::PartitionArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = k_cache;
-  a.v = v_cache;
-  a.scales = kv_scales;
-  a.bt = block_tables;
+  int32_t E = 0;
+  tq_status st = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
+                              query_group_size, kv_block_size, tile_groups_per_partition,
+                              softmax_scale, ext, &a.st, &E);
+  if (st != TQ_OK) return st;
+  if (!aligned16(partials->out) || !aligned4(partials->max_logits) || !aligned4(partials->exp_sums))
+    return TQ_ERR_MISALIGNED;
   a.seq_lens = seq_lens;
   a.o = partials->out;
   a.ml = partials->max_logits;
   a.es = partials->exp_sums;
-  a.num_kv_heads = num_kv_heads;
   a.num_partitions = ext->num_partitions;
   a.partition_tokens = E;
-  a.max_blocks = ext->max_blocks_per_seq;
-  a.num_blocks = ext->num_blocks;
+  a.parts_per_wave = 1;  // chosen by the launcher
   a.len_cap = ext->max_seq_len;
-  a.qk_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
-  const int units = ext->num_seqs * num_kv_heads * ext->num_partitions;
-  hipError_t e = tq::launch_partition(a, query_group_size, kv_block_size, units,
-                                      static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    g_last_hip_error = (int32_t)e;
-    return TQ_ERR_HIP;
-  }
-  return TQ_OK;
+  return hip_status(tq::launch_partition(a, ext->num_seqs, query_group_size, kv_block_size,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                          const float* kv_scales, const int32_t* block_tables,
+                          const int32_t* seq_lens, void* out, int32_t num_kv_heads,
+                          int32_t query_group_size, int32_t kv_block_size,
+                          int32_t tile_groups_per_partition, float softmax_scale,
+                          const tq_extent* ext, void* stream) {
+  if (!out) return TQ_ERR_NULL;
+  tq::FusedArgs a;
+  int32_t E = 0;
+  tq_status st = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
+                              query_group_size, kv_block_size, tile_groups_per_partition,
+                              softmax_scale, ext, &a.st, &E);
+  if (st != TQ_OK) return st;
+  if (!aligned16(out)) return TQ_ERR_MISALIGNED;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.partition_tokens = E;
+  a.len_cap = ext->max_seq_len;
+  return hip_status(tq::launch_fused(a, ext->num_seqs, ext->num_partitions, query_group_size,
+                                     kv_block_size, static_cast<hipStream_t>(stream)));
 }
 
 tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens, void* out,
@@ -113,12 +154,8 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
   a.num_partitions = ext->num_partitions;
   a.partition_tokens = E;
   a.len_cap = ext->max_seq_len;
-  hipError_t e = tq::launch_reduce(a, ext->num_seqs * num_kv_heads, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    g_last_hip_error = (int32_t)e;
-    return TQ_ERR_HIP;
-  }
-  return TQ_OK;
+  return hip_status(
+      tq::launch_reduce(a, ext->num_seqs * num_kv_heads, static_cast<hipStream_t>(stream)));
 }
 
 size_t tq_partials_bytes(const tq_extent* ext, int32_t num_kv_heads, int32_t query_group_size) {

@@ -11,24 +11,37 @@ namespace tq {
 constexpr int kHeadDim = 128;
 constexpr int kTokensPerTileGroup = 256;
 
-// Everything the partition kernel reads; sizes already validated on the host.
-struct PartitionArgs {
+// What every decode kernel reads to stream one (sequence, kv head).
+struct StreamArgs {
   const uint16_t* q;        // bf16 [S][Hkv*QG][128]
-  const uint8_t* k;         // e4m3fn [NB][BS][Hkv][128]
-  const uint8_t* v;         // e4m3fn [NB][BS][Hkv][128]
+  const uint8_t* k;         // e4m3fn [NB][Hkv][BS][128]
+  const uint8_t* v;         // e4m3fn [NB][Hkv][BS][128]
   const float* scales;      // fp32 [NB][Hkv][2][BS]
   const int32_t* bt;        // int32 [S][max_blocks]
-  const int32_t* seq_lens;  // int32 [S]
-  float* o;                 // fp32 [S][Hkv][P][QG][128]
-  float* ml;                // fp32 [S][Hkv][P][QG]
-  float* es;                // fp32 [S][Hkv][P][QG]
   int32_t num_kv_heads;
+  int32_t max_blocks;       // block-table row stride
+  int32_t num_blocks;       // NB, for clamping block ids
+  float qk_scale_log2;      // softmax_scale * log2(e)
+};
+
+struct PartitionArgs {
+  StreamArgs st;
+  const int32_t* seq_lens;   // int32 [S]
+  float* o;                  // fp32 [S][Hkv][P][QG][128]
+  float* ml;                 // fp32 [S][Hkv][P][QG]
+  float* es;                 // fp32 [S][Hkv][P][QG]
   int32_t num_partitions;
   int32_t partition_tokens;  // E = 256 * G
-  int32_t max_blocks;        // block-table row stride
-  int32_t num_blocks;        // NB, for clamping block ids
+  int32_t parts_per_wave;    // consecutive partitions of one (s, h) walked by one wave
   int32_t len_cap;           // device lengths are clamped to [0, len_cap]
-  float qk_scale_log2;       // softmax_scale * log2(e)
+};
+
+struct FusedArgs {
+  StreamArgs st;
+  const int32_t* seq_lens;   // int32 [S]
+  uint16_t* out;             // bf16 [S][Hkv*QG][128]
+  int32_t partition_tokens;  // E = 256 * G
+  int32_t len_cap;
 };
 
 struct ReduceArgs {
@@ -44,9 +57,13 @@ struct ReduceArgs {
   int32_t len_cap;
 };
 
-// Enqueue the kernels; return the launch status (hipGetLastError after launch).
-hipError_t launch_partition(const PartitionArgs& a, int query_group_size, int kv_block_size,
-                            int num_units, hipStream_t stream);
+// Enqueue the kernels; each returns the launch status (hipGetLastError after
+// the launch).  launch_partition chooses parts_per_wave and launch_fused the
+// waves per workgroup from the sizes.
+hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
+                            int kv_block_size, hipStream_t stream);
+hipError_t launch_fused(const FusedArgs& a, int num_seqs, int num_partitions, int query_group_size,
+                        int kv_block_size, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream);
 
 }  // namespace tq

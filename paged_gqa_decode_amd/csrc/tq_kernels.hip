@@ -8,10 +8,12 @@
 // output with its max logit and exp sum (STEP G).  The kernel design here is
 // its own, made for gfx950:
 //
-//  * One 64-lane wave per live unit (sequence s, kv head h, partition p).
-//    The partition's tokens are walked in chunks of 32 (two 16-token MFMA
-//    tiles), with the next chunk's loads in flight while the current one is
-//    computed.
+//  * One 64-lane wave per group of `parts_per_wave` consecutive partitions of
+//    one (sequence s, kv head h).  Their tokens are walked as one stream of
+//    32-token chunks (two 16-token MFMA tiles), with the next chunk's loads in
+//    flight while the current one is computed; at every partition boundary
+//    the partial triple is written and the softmax state restarts, so the
+//    result of each partition does not depend on the grouping.
 //  * K never touches LDS.  QK^T contracts over head_dim, so any permutation
 //    of d applied to both q and K is allowed: lane (r = lane%16, b = lane/16)
 //    supplies K[token r][d = 32b .. 32b+31], one contiguous 32-byte piece of
@@ -95,9 +97,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Cache row (token slot within its block, kv head) byte offset.
+// Byte offset of the 128-byte row of (block, kv head, slot): each (block, kv
+// head) slice of BS rows is contiguous.
 __device__ __forceinline__ size_t row_offset(uint32_t blk, int slot, int BS, int Hkv, int h) {
-  return (((size_t)blk * BS + slot) * Hkv + h) * D;
+  return (((size_t)blk * Hkv + h) * BS + slot) * D;
 }
 
 // Byte offset in the V LDS tile of 16-byte piece `piece` of token row `tok`:
@@ -107,38 +110,58 @@ __device__ __forceinline__ int v_lds_offset(int tok, int piece) {
   return tok * D + 16 * (piece ^ ((tok >> 1) & 7));
 }
 
-template <int QG, int BS>
-__global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
+// Running state of one wave's online softmax over its tokens (row r = lane%16
+// of the query group): m2 = running max of the log2-scaled logits, lsum = this
+// lane's share of the running exp sum, sigma = running max V scale (the P
+// operand's reference), acc = O^T tile (d = 16 dblk + 4b + i, query r).
+struct WaveState {
+  float m2;
+  float lsum;
+  float sigma;
+  f32x4 acc[8];
+  __device__ __forceinline__ void reset() {
+    m2 = kNegInf;
+    lsum = 0.f;
+    sigma = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  // Partial output of the tokens seen so far, o = acc * sigma / l, for d =
+  // 16 dblk + 4b + i; returns l (the whole row's exp sum, all lanes).
+  __device__ __forceinline__ float finish(f32x4 o[8]) const {
+    const float l = wave_sum_xor16_32(lsum);
+    const float f = sigma / l;
+#pragma unroll
+    for (int dblk = 0; dblk < 8; ++dblk) o[dblk] = acc[dblk] * f;
+    return l;
+  }
+};
+
+// Walk tokens [t_begin, t_end) of (s, h) in 32-token chunks, accumulating into
+// `w`.  Every `chunks_per_part` chunks, on_boundary(k, w) is called with the
+// index k (from 0) of the partition that just ended; it must consume and reset
+// `w`.  The caller handles the last partition after the return.  lds_v (8 KiB,
+// two stages) and lds_sc (512 B) are this wave's LDS staging area.
+template <int QG, int BS, typename OnBoundary>
+__device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h, int t_begin,
+                                              int t_end, int chunks_per_part, uint8_t* lds_v,
+                                              float* lds_sc, WaveState& w,
+                                              OnBoundary on_boundary) {
   static_assert(BS == 16 || BS == 32, "kv block size");
   static_assert(QG >= 1 && QG <= 16, "query group size");
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2][CHUNK * D];  // 2 x 4 KiB
-  __shared__ __attribute__((aligned(16))) float lds_sc[2][2 * CHUNK];   // [field][token]
-
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int r = lane & 15;  // MFMA row/column index within a 16-lane group
   const int b = lane >> 4;  // 16-lane group
-  const int P = a.num_partitions;
   const int Hkv = a.num_kv_heads;
-  const int unit = blockIdx.x;
-  const int p = unit % P;
-  const int sh = unit / P;
-  const int h = sh % Hkv;
-  const int s = sh / Hkv;
-
-  int L = a.seq_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
-  const int t_begin = p * a.partition_tokens;
-  if (t_begin >= L) return;  // dead partition: nothing is written
-  const int t_end = min(t_begin + a.partition_tokens, L);
   const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
-  const int n_blocks = (t_end - t_begin + BS - 1) / BS;  // block-table entries this unit reads
+  const int n_blocks = (t_end - t_begin + BS - 1) / BS;  // block-table entries read
   const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks + t_begin / BS;
   const uint32_t nb_max = (uint32_t)a.num_blocks - 1u;
 
-  // Block-table window: lane i holds entry 64*win + i of this partition.
+  // Block-table window: lane i holds entry 64*win + i of this range.
   int bt_win = 0;
   int bt_reg = lane < n_blocks ? bt_row[lane] : 0;
-  auto block_id = [&](int j) -> uint32_t {  // j: block index within the partition, uniform
+  auto block_id = [&](int j) -> uint32_t {  // j: block index within the range, uniform
     if ((j >> 6) != bt_win) {
       bt_win = j >> 6;
       const int e = 64 * bt_win + lane;
@@ -159,11 +182,8 @@ __global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
     for (int c = 0; c < 4; ++c) qop[c] = bf16x8{};
   }
 
-  const uint8_t* kbase = a.k;
-  const uint8_t* vbase = a.v;
-  const float* sbase = a.scales;
-
-  // Issue the loads of chunk c: K pieces into registers, V rows and scales into LDS stage `st`.
+  // Issue the loads of chunk c: K pieces into registers, V rows and scales
+  // into LDS stage `st`.
   i32x4 kraw[2][2];
   auto issue = [&](int c, int st) {
     const int jb = (c * CHUNK) / BS;
@@ -174,26 +194,27 @@ __global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
     for (int t = 0; t < 2; ++t) {
       const uint32_t blk = (BS == 32 || t == 0) ? blkA : blkB;
       const int slot = BS == 32 ? 16 * t + r : r;
-      const uint8_t* src = kbase + row_offset(blk, slot, BS, Hkv, h) + 32 * b;
+      const uint8_t* src = a.k + row_offset(blk, slot, BS, Hkv, h) + 32 * b;
       kraw[t][0] = *reinterpret_cast<const i32x4*>(src);
       kraw[t][1] = *reinterpret_cast<const i32x4*>(src + 16);
     }
+    uint8_t* vdst = lds_v + st * (CHUNK * D);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int tok = 8 * j + (lane >> 3);
       const int piece = (lane & 7) ^ ((tok >> 1) & 7);
       const uint32_t blk = (BS == 32 || tok < 16) ? blkA : blkB;
       const int slot = BS == 32 ? tok : (tok & 15);
-      const uint8_t* src = vbase + row_offset(blk, slot, BS, Hkv, h) + 16 * piece;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)&lds_v[st][1024 * j], 16, 0, 0);
+      const uint8_t* src = a.v + row_offset(blk, slot, BS, Hkv, h) + 16 * piece;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(vdst + 1024 * j), 16, 0, 0);
     }
     {
       const int field = lane >> 5;
       const int tok = lane & 31;
       const uint32_t blk = (BS == 32 || tok < 16) ? blkA : blkB;
       const int slot = BS == 32 ? tok : (tok & 15);
-      const float* src = sbase + (((size_t)blk * Hkv + h) * 2 + field) * BS + slot;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)&lds_sc[st][0], 4, 0, 0);
+      const float* src = a.scales + (((size_t)blk * Hkv + h) * 2 + field) * BS + slot;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds_sc + st * (2 * CHUNK)), 4, 0, 0);
     }
   };
 
@@ -203,14 +224,9 @@ __global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
   const int tr_tok = 16 * (r >> 3) + 4 * b + ((r >> 1) & 3);
   const int tr_half = 8 * (r & 1);
 
-  float m2 = kNegInf;  // running max of log2-scaled logits (row r)
-  float lsum = 0.f;    // this lane's share of the running exp sum
-  float sigma = 0.f;   // running max V scale (operand reference)
-  f32x4 acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
   issue(0, 0);
+  int next_boundary = chunks_per_part;
+  int part_done = 0;
   for (int c = 0; c < n_chunks; ++c) {
     const int st = c & 1;
     // Chunk c's loads are the only ones outstanding: drain them (the LDS
@@ -221,12 +237,13 @@ __global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __builtin_amdgcn_sched_barrier(0);
-    f32x4 ks0 = *reinterpret_cast<const f32x4*>(&lds_sc[st][4 * b]);
-    f32x4 ks1 = *reinterpret_cast<const f32x4*>(&lds_sc[st][16 + 4 * b]);
-    f32x4 vs0 = *reinterpret_cast<const f32x4*>(&lds_sc[st][32 + 4 * b]);
-    f32x4 vs1 = *reinterpret_cast<const f32x4*>(&lds_sc[st][48 + 4 * b]);
+    const float* sc = lds_sc + st * (2 * CHUNK);
+    f32x4 ks0 = *reinterpret_cast<const f32x4*>(sc + 4 * b);
+    f32x4 ks1 = *reinterpret_cast<const f32x4*>(sc + 16 + 4 * b);
+    f32x4 vs0 = *reinterpret_cast<const f32x4*>(sc + 32 + 4 * b);
+    f32x4 vs1 = *reinterpret_cast<const f32x4*>(sc + 48 + 4 * b);
     i32x2 vraw[8];
-    const uint8_t* vt = &lds_v[st][0];
+    const uint8_t* vt = lds_v + st * (CHUNK * D);
 #pragma unroll
     for (int dblk = 0; dblk < 8; ++dblk)
       vraw[dblk] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
@@ -234,6 +251,12 @@ __global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
     i32x4 kc[2][2] = {{kraw[0][0], kraw[0][1]}, {kraw[1][0], kraw[1][1]}};
     __builtin_amdgcn_sched_barrier(0);
     if (c + 1 < n_chunks) issue(c + 1, st ^ 1);
+    // A partition boundary: its stores go out behind the next chunk's loads.
+    if (c == next_boundary) {
+      on_boundary(part_done, w);
+      ++part_done;
+      next_boundary += chunks_per_part;
+    }
 
     const int nvalid = min(CHUNK, t_end - (t_begin + c * CHUNK));
 
@@ -274,8 +297,8 @@ __global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
     mx = wave_max_xor16_32(mx);
-    const float m2_new = fmaxf(m2, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m2 - m2_new);
+    const float m2_new = fmaxf(w.m2, mx);
+    const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
     float pr[8];
     float psum = 0.f;
 #pragma unroll
@@ -283,17 +306,17 @@ __global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
       pr[i] = __builtin_amdgcn_exp2f(y[i] - m2_new);
       psum += pr[i];
     }
-    lsum = lsum * alpha + psum;
-    m2 = m2_new;
+    w.lsum = w.lsum * alpha + psum;
+    w.m2 = m2_new;
 
     // ---- V-scale reference and P operand ----
     float vmax = fmaxf(fmaxf(fmaxf(vs0[0], vs0[1]), fmaxf(vs0[2], vs0[3])),
                        fmaxf(fmaxf(vs1[0], vs1[1]), fmaxf(vs1[2], vs1[3])));
     vmax = wave_max_xor16_32(vmax);
-    const float sigma_new = fmaxf(sigma, vmax);
+    const float sigma_new = fmaxf(w.sigma, vmax);
     const float inv_sigma = sigma_new > 0.f ? 1.0f / sigma_new : 0.f;
-    const float acc_scale = alpha * (sigma * inv_sigma);
-    sigma = sigma_new;
+    const float acc_scale = alpha * (w.sigma * inv_sigma);
+    w.sigma = sigma_new;
     f16x8 pop;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -301,34 +324,165 @@ __global__ __launch_bounds__(64) void partition_kernel(PartitionArgs a) {
       pop[4 + i] = (_Float16)(pr[4 + i] * (vs1[i] * inv_sigma));
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= acc_scale;
+    for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
 
     // ---- PV: acc[dblk] (O^T[d = 16 dblk + 4b + i][query r]) += V^T P ----
 #pragma unroll
     for (int dblk = 0; dblk < 8; ++dblk) {
       const f16x8 vop = fp8x8_to_f16(vraw[dblk][0] & vmask0, vraw[dblk][1] & vmask1);
-      acc[dblk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, acc[dblk], 0, 0, 0);
+      w.acc[dblk] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vop, pop, w.acc[dblk], 0, 0, 0);
     }
   }
+}
 
-  // ---- partial triple (STEP G): o_p = acc * sigma / l_p, m_p, l_p ----
-  const float l = wave_sum_xor16_32(lsum);
-  if (r < QG) {
-    const float f = sigma / l;
-    const size_t row = ((size_t)(s * Hkv + h) * P + p) * QG + r;
-    float* dst = a.o + row * D + 4 * b;
+// Clamp a device-side sequence length into [0, cap].
+__device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
+
+// Split-K partition kernel: one wave per group of `parts_per_wave`
+// consecutive partitions of one (s, h); writes the partial triple of every
+// live partition in the group (STEP G).
+template <int QG, int BS>
+__global__ __launch_bounds__(64) void tq_partition_kernel(PartitionArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * CHUNK * D];
+  __shared__ __attribute__((aligned(16))) float lds_sc[2 * 2 * CHUNK];
+  const int lane = threadIdx.x;
+  const int r = lane & 15;
+  const int b = lane >> 4;
+  const int P = a.num_partitions;
+  const int Hkv = a.st.num_kv_heads;
+  const int E = a.partition_tokens;
+  const int ppw = a.parts_per_wave;
+  const int n_groups = (P + ppw - 1) / ppw;
+  const int pg = blockIdx.x % n_groups;
+  const int sh = blockIdx.x / n_groups;
+  const int h = sh % Hkv;
+  const int s = sh / Hkv;
+  const int p0 = pg * ppw;
+  const int L = clamp_len(a.seq_lens[s], a.len_cap);
+  const int t_begin = p0 * E;
+  if (t_begin >= L) return;  // dead partitions: nothing is written
+  const int t_end = min(t_begin + min(ppw, P - p0) * E, L);
+
+  // Partial triple of partition p: o_p = acc * sigma / l_p, m_p (natural
+  // log units), l_p; then the running state restarts.
+  auto store_partial = [&](int p, WaveState& w) {
+    f32x4 o[8];
+    const float l = w.finish(o);
+    if (r < QG) {
+      const size_t row = ((size_t)(s * Hkv + h) * P + p) * QG + r;
+      float* dst = a.o + row * D + 4 * b;
 #pragma unroll
-    for (int dblk = 0; dblk < 8; ++dblk) *reinterpret_cast<f32x4*>(dst + 16 * dblk) = acc[dblk] * f;
-    if (b == 0) {
-      a.ml[row] = m2 * kLn2;
-      a.es[row] = l;
+      for (int dblk = 0; dblk < 8; ++dblk) *reinterpret_cast<f32x4*>(dst + 16 * dblk) = o[dblk];
+      if (b == 0) {
+        a.ml[row] = w.m2 * kLn2;
+        a.es[row] = l;
+      }
     }
+    w.reset();
+  };
+
+  WaveState w;
+  w.reset();
+  const int chunks_per_part = E / CHUNK;
+  stream_tokens<QG, BS>(a.st, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_sc, w,
+                        [&](int k, WaveState& ws) { store_partial(p0 + k, ws); });
+  const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
+  store_partial(p0 + (n_chunks - 1) / chunks_per_part, w);
+}
+
+// Per-wave LDS: two 4 KiB V stages + two 256 B scale stages; after the stream
+// the same bytes hold the wave's normalised partial (up to 16 rows x 512 B)
+// and its max logits / exp sums (2 x 16 floats).
+constexpr int kWaveLds = 2 * CHUNK * D + 2 * 2 * CHUNK * 4;
+static_assert(16 * D * 4 + 2 * 16 * 4 <= kWaveLds, "merge area must fit the staging area");
+
+// Fused decode: one workgroup of W waves per (s, h).  The live partitions of
+// the sequence are dealt to the waves in contiguous runs; each wave runs one
+// online softmax over its run, and the W partial results are merged by
+// log-sum-exp through LDS, so no partial ever leaves the CU; bf16 out is
+// written directly.
+template <int QG, int BS>
+__global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int r = lane & 15;
+  const int b = lane >> 4;
+  const int Hkv = a.st.num_kv_heads;
+  const int E = a.partition_tokens;
+  const int sh = blockIdx.x;
+  const int h = sh % Hkv;
+  const int s = sh / Hkv;
+  const int L = clamp_len(a.seq_lens[s], a.len_cap);
+  uint16_t* out = a.out + (size_t)sh * QG * D;
+  if (L == 0) {  // uniform over the workgroup
+    for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x)
+      *reinterpret_cast<uint2*>(out + 4 * idx) = make_uint2(0u, 0u);
+    return;
+  }
+  const int n_live = (L + E - 1) / E;
+  const int per_wave = (n_live + W - 1) / W;       // partitions per wave
+  const int n_used = (n_live + per_wave - 1) / per_wave;
+  uint8_t* region = lds_dyn + wave * kWaveLds;
+  float* part_o = reinterpret_cast<float*>(region);                 // [QG][128]
+  float* part_m = reinterpret_cast<float*>(region + 16 * D * 4);    // [QG]
+  float* part_l = part_m + 16;                                      // [QG]
+  if (wave < n_used) {  // uniform over the wave
+    const int t_begin = wave * per_wave * E;
+    const int t_end = min(t_begin + per_wave * E, L);
+    WaveState w;
+    w.reset();
+    stream_tokens<QG, BS>(a.st, s, h, t_begin, t_end, 0x7fffffff, region,
+                          reinterpret_cast<float*>(region + 2 * CHUNK * D), w,
+                          [](int, WaveState&) {});
+    f32x4 o[8];
+    const float l = w.finish(o);
+    if (r < QG) {
+#pragma unroll
+      for (int dblk = 0; dblk < 8; ++dblk)
+        *reinterpret_cast<f32x4*>(part_o + r * D + 16 * dblk + 4 * b) = o[dblk];
+      if (b == 0) {
+        part_m[r] = w.m2 * kLn2;
+        part_l[r] = l;
+      }
+    }
+  }
+  __syncthreads();
+  // Log-sum-exp merge of the waves' partials, as tq_merge_kernel does for partitions.
+  for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x) {
+    const int g = idx / (D / 4);
+    const int col = 4 * (idx % (D / 4));
+    f32x4 o;
+    if (n_used == 1) {
+      o = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds_dyn) + g * D + col);
+    } else {
+      float M = kNegInf;
+      for (int v = 0; v < n_used; ++v)
+        M = fmaxf(M, reinterpret_cast<const float*>(lds_dyn + v * kWaveLds + 16 * D * 4)[g]);
+      float Wsum = 0.f;
+      for (int v = 0; v < n_used; ++v) {
+        const float* pm = reinterpret_cast<const float*>(lds_dyn + v * kWaveLds + 16 * D * 4);
+        Wsum += pm[16 + g] * __expf(pm[g] - M);
+      }
+      const float invW = 1.0f / Wsum;
+      o = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int v = 0; v < n_used; ++v) {
+        const float* po = reinterpret_cast<const float*>(lds_dyn + v * kWaveLds);
+        const float* pm = po + 16 * D;
+        const float wt = pm[16 + g] * __expf(pm[g] - M) * invW;
+        o += wt * *reinterpret_cast<const f32x4*>(po + g * D + col);
+      }
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+    *reinterpret_cast<uint2*>(out + g * D + col) = make_uint2(lo, hi);
   }
 }
 
 // Merge: one 256-thread block per (sequence, kv head); thread -> (query row g,
 // 4 consecutive head_dim columns).
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
+__global__ __launch_bounds__(256) void tq_merge_kernel(ReduceArgs a) {
   const int sh = blockIdx.x;
   const int QG = a.query_group_size;
   const int P = a.num_partitions;
@@ -367,12 +521,38 @@ __global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs a) {
 
 }  // namespace
 
-hipError_t launch_partition(const PartitionArgs& a, int query_group_size, int kv_block_size,
-                            int num_units, hipStream_t stream) {
-  const dim3 grid(num_units), block(64);
+int choose_parts_per_wave(int64_t units, int num_partitions) {
+  // Keep enough waves for many rounds over every SIMD; past that, longer
+  // per-wave streams amortize each wave's start-up (length, block-table and
+  // first-chunk loads, one after the other).
+  constexpr int64_t kMinWaves = 32768;
+  int64_t ppw = units / kMinWaves;
+  if (ppw < 1) ppw = 1;
+  if (ppw > num_partitions) ppw = num_partitions;
+  return (int)ppw;
+}
+
+int choose_fused_waves(int64_t seq_heads, int num_partitions) {
+  // One workgroup per (s, h): enough waves per workgroup to put ~4096 waves
+  // on the device, at most 8 (the register budget of __launch_bounds__(512)),
+  // and no more than there are partitions to deal out.
+  constexpr int64_t kTargetWaves = 4096;
+  int64_t w = (kTargetWaves + seq_heads - 1) / seq_heads;
+  if (w > 8) w = 8;
+  if (w > num_partitions) w = num_partitions;
+  if (w < 1) w = 1;
+  return (int)w;
+}
+
+hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
+                            int kv_block_size, hipStream_t stream) {
+  const int64_t units = (int64_t)num_seqs * a.st.num_kv_heads * a.num_partitions;
+  a.parts_per_wave = choose_parts_per_wave(units, a.num_partitions);
+  const int64_t groups = (a.num_partitions + a.parts_per_wave - 1) / a.parts_per_wave;
+  const dim3 grid((unsigned)(num_seqs * (int64_t)a.st.num_kv_heads * groups)), block(64);
 #define TQ_LAUNCH(QGV, BSV)                                                            \
   if (query_group_size == QGV && kv_block_size == BSV) {                              \
-    hipLaunchKernelGGL((partition_kernel<QGV, BSV>), grid, block, 0, stream, a);      \
+    hipLaunchKernelGGL((tq_partition_kernel<QGV, BSV>), grid, block, 0, stream, a);      \
     return hipGetLastError();                                                          \
   }
   TQ_LAUNCH(6, 16)
@@ -385,8 +565,38 @@ hipError_t launch_partition(const PartitionArgs& a, int query_group_size, int kv
   return hipErrorInvalidValue;
 }
 
+template <int QG, int BS>
+hipError_t launch_fused_t(const FusedArgs& a, unsigned grid, int waves, hipStream_t stream) {
+  // Allow dynamic LDS beyond 64 KiB for this kernel, once; an error here only
+  // means the runtime needs no opt-in, and must not leak into the launch status.
+  static const bool lds_opt_in = [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_fused_kernel<QG, BS>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, 8 * kWaveLds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)lds_opt_in;
+  hipLaunchKernelGGL((tq_fused_kernel<QG, BS>), dim3(grid), dim3(64 * waves),
+                     (size_t)waves * kWaveLds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused(const FusedArgs& a, int num_seqs, int num_partitions, int query_group_size,
+                        int kv_block_size, hipStream_t stream) {
+  const int64_t seq_heads = (int64_t)num_seqs * a.st.num_kv_heads;
+  const int waves = choose_fused_waves(seq_heads, num_partitions);
+  const unsigned grid = (unsigned)seq_heads;
+  if (query_group_size == 6 && kv_block_size == 16) return launch_fused_t<6, 16>(a, grid, waves, stream);
+  if (query_group_size == 6 && kv_block_size == 32) return launch_fused_t<6, 32>(a, grid, waves, stream);
+  if (query_group_size == 8 && kv_block_size == 16) return launch_fused_t<8, 16>(a, grid, waves, stream);
+  if (query_group_size == 8 && kv_block_size == 32) return launch_fused_t<8, 32>(a, grid, waves, stream);
+  if (query_group_size == 16 && kv_block_size == 16) return launch_fused_t<16, 16>(a, grid, waves, stream);
+  if (query_group_size == 16 && kv_block_size == 32) return launch_fused_t<16, 32>(a, grid, waves, stream);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream) {
-  hipLaunchKernelGGL(reduce_kernel, dim3(num_seq_heads), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(tq_merge_kernel, dim3(num_seq_heads), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -23,8 +23,11 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
+PATHS = ("two_kernel", "fused")
+
+
 def gpu_decode(inp: workloads.Inputs, num_partitions=None, tile_groups=None, partials=None,
-               out=None):
+               out=None, path="two_kernel"):
     wl = inp.wl
     G = wl.tile_groups_per_partition if tile_groups is None else tile_groups
     P = inp.num_partitions if num_partitions is None else num_partitions
@@ -32,7 +35,7 @@ def gpu_decode(inp: workloads.Inputs, num_partitions=None, tile_groups=None, par
     res = tq.decode(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, inp.seq_lens,
                     num_partitions=P, tile_groups_per_partition=G,
                     softmax_scale=inp.softmax_scale, max_seq_len=maxlen, partials=partials,
-                    out=out)
+                    out=out, fused=(path == "fused"))
     torch.cuda.synchronize()
     return res
 

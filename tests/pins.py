@@ -48,7 +48,7 @@ def tiny_problem(S=3, Hkv=2, QG=4, D=32, BS=4, lens=(1, 7, 13), extra_blocks=3, 
         pos += need[s]
     q = torch.from_numpy(rng.standard_normal((S, Hkv * QG, D)).astype(np.float32)).to(torch.bfloat16)
     def codes():
-        x = torch.from_numpy(rng.standard_normal((NB, BS, Hkv, D)).astype(np.float32) * 100)
+        x = torch.from_numpy(rng.standard_normal((NB, Hkv, BS, D)).astype(np.float32) * 100)
         return x.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
     k = codes()
     v = codes()
@@ -61,13 +61,13 @@ def tiny_problem(S=3, Hkv=2, QG=4, D=32, BS=4, lens=(1, 7, 13), extra_blocks=3, 
 def dense_rows(p, s, h, field):
     """Gathered, dequantized K (field 0) or V (field 1) rows of (s, h) as float64 [L][D]."""
     cache = p["k"] if field == 0 else p["v"]
-    BS = cache.shape[1]
+    BS = cache.shape[2]
     L = int(p["sl"][s])
     rows = []
     for t in range(L):
         b = int(p["bt"][s, t // BS])
         j = t % BS
-        vals = cache[b, j, h].view(torch.float8_e4m3fn).to(torch.float64)
+        vals = cache[b, h, j].view(torch.float8_e4m3fn).to(torch.float64)
         rows.append(vals * float(p["sc"][b, h, field, j]))
     D = cache.shape[3]
     return torch.stack(rows) if rows else torch.zeros((0, D), dtype=torch.float64)
@@ -136,7 +136,7 @@ def pin_bf16_library(orc):
 
 def _bruteforce(p):
     S, Hq, D = p["q"].shape
-    Hkv = p["k"].shape[2]
+    Hkv = p["k"].shape[1]
     QG = Hq // Hkv
     out = torch.zeros((S, Hq, D), dtype=torch.float64)
     for s in range(S):
@@ -212,11 +212,11 @@ def pin_two_token_golden(orc):
     q = torch.zeros((1, 1, D), dtype=torch.int16)
     q[0, 0, 0] = ex["q_d0_bf16_bits"]
     q = q.view(torch.bfloat16)
-    k = torch.zeros((1, BS, 1, D), dtype=torch.uint8)
-    k[0, 1, 0, 0] = ex["k_token1_d0_code"]
-    v = torch.zeros((1, BS, 1, D), dtype=torch.uint8)
+    k = torch.zeros((1, 1, BS, D), dtype=torch.uint8)
+    k[0, 0, 1, 0] = ex["k_token1_d0_code"]
+    v = torch.zeros((1, 1, BS, D), dtype=torch.uint8)
     v[0, 0, 0, :] = ex["v_token0_code"]
-    v[0, 1, 0, :] = ex["v_token1_code"]
+    v[0, 0, 1, :] = ex["v_token1_code"]
     sc = torch.ones((1, 1, 2, BS), dtype=torch.float32)
     sc[0, 0, 1, 0] = ex["v_token0_scale"]
     sc[0, 0, 1, 1] = ex["v_token1_scale"]
@@ -281,7 +281,7 @@ def pin_dominant_token(orc):
         p["q"] = q.to(torch.bfloat16)
         k = torch.zeros_like(p["k"])
         b = int(p["bt"][0, tstar // BS])
-        k[b, tstar % BS, :, :] = 0x48  # 4.0
+        k[b, :, tstar % BS, :] = 0x48  # 4.0
         p["k"] = k
         p["sc"][:, :, 0, :] = 1.0
         p["scale"] = 1.0  # logit of t* = 128, others 0

@@ -13,10 +13,11 @@ import paged_gqa_decode_amd as tq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tq_decode.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "tq_probe.h")
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(tq_\w+)\s*\(", text, flags=re.M)))
 
@@ -31,6 +32,24 @@ def test_exports_every_declared_function(lib):
     assert set(names) == set(tq.EXPORTED_SYMBOLS), names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported"
+
+
+def test_probe_library_exports_its_header():
+    from paged_gqa_decode_amd import probe
+
+    names = header_functions(PROBE_HEADER)
+    assert set(names) == set(probe.EXPORTED_SYMBOLS), names
+    plib = probe.load_library()
+    for n in names:
+        assert hasattr(plib, n), f"{n} not exported"
+    # argument errors are reported without touching the device
+    assert plib.tq_probe_read(0, 16, 0x10000, 1, None) != 0
+    assert plib.tq_probe_copy(0x10000, 0x10000, 17, 1, None) != 0
+
+
+def test_every_header_is_covered():
+    hdrs = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert hdrs == ["tq_decode.h", "tq_probe.h"], hdrs
 
 
 def test_abi_version_and_status_strings(lib):
@@ -110,6 +129,28 @@ def test_coverage_boundary_from_the_page_sizing_example(lib):
         tq.TQ_ERR_SCALE  # coverage passes; the scale check then fails before any launch
 
 
+def call_fused(lib, *, ptrs=None, out=A, QG=8, BS=16, G=1, Hkv=2, scale=0.088, S=2, NB=8, MB=4,
+               P=1, maxlen=64, head_dim=128):
+    ptrs = ptrs or [A] * 6
+    ext = tq.Extent(S, NB, MB, P, maxlen, head_dim)
+    return lib.tq_decode_fused(*ptrs, out, Hkv, QG, BS, G, scale, ctypes.byref(ext), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=0), tq.TQ_ERR_NULL),
+    (dict(ptrs=[A, A, 0, A, A, A]), tq.TQ_ERR_NULL),
+    (dict(QG=12), tq.TQ_ERR_UNSUPPORTED),
+    (dict(BS=48), tq.TQ_ERR_UNSUPPORTED),
+    (dict(P=0), tq.TQ_ERR_SHAPE),
+    (dict(maxlen=300, P=1, MB=64), tq.TQ_ERR_COVERAGE),
+    (dict(scale=float("nan")), tq.TQ_ERR_SCALE),
+    (dict(out=A + 8), tq.TQ_ERR_MISALIGNED),
+    (dict(ptrs=[A, A, A, A, A, A + 1]), tq.TQ_ERR_MISALIGNED),
+])
+def test_fused_rejects(lib, kw, status):
+    assert call_fused(lib, **kw) == status
+
+
 def call_reduce(lib, *, part=None, sl=A, out=A, QG=8, Hkv=2, G=1, S=2, P=1, maxlen=64):
     ps = tq.PartialsStruct(*(part or (A, A, A)))
     ext = tq.Extent(S, 1, 1, P, maxlen, 128)
@@ -135,7 +176,7 @@ def test_reduce_rejects(lib, kw, status):
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros((1, 8, 128), dtype=torch.bfloat16)
-    k = torch.zeros((1, 16, 1, 128), dtype=torch.uint8)
+    k = torch.zeros((1, 1, 16, 128), dtype=torch.uint8)
     sc = torch.zeros((1, 1, 2, 16))
     bt = torch.zeros((1, 1), dtype=torch.int32)
     sl = torch.ones((1,), dtype=torch.int32)

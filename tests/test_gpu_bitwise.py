@@ -11,7 +11,7 @@ import torch
 
 import paged_gqa_decode_amd as tq
 import workloads
-from gpu_util import gpu_decode, say
+from gpu_util import PATHS, gpu_decode, say
 
 pytestmark = pytest.mark.gpu
 
@@ -26,19 +26,21 @@ def small(lens, qg=8, bs=16, hkv=2, seed=5, P=None):
     return workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=P)
 
 
-def test_run_to_run_determinism():
+@pytest.mark.parametrize("path", PATHS)
+def test_run_to_run_determinism(path):
     inp = workloads.make_inputs(workloads.WORKLOADS["w2_s32_ctx4k"], device="cuda")
-    say("[bitwise] w2 twice")
-    a = gpu_decode(inp)
-    b = gpu_decode(inp)
+    say(f"[bitwise] w2 twice, {path}")
+    a = gpu_decode(inp, path=path)
+    b = gpu_decode(inp, path=path)
     assert np.array_equal(bits(a), bits(b))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("bs", [16, 32])
-def test_block_relabelling_is_invisible(bs):
+def test_block_relabelling_is_invisible(bs, path):
     inp = small((1, 40, 333, 1000), bs=bs, P=4, seed=21)
-    say(f"[bitwise] block relabelling bs={bs}")
-    ref = gpu_decode(inp)
+    say(f"[bitwise] block relabelling bs={bs} {path}")
+    ref = gpu_decode(inp, path=path)
     NB = inp.num_blocks
     perm = torch.from_numpy(np.random.default_rng(3).permutation(NB).astype(np.int64)).cuda()
     inv = torch.empty_like(perm)
@@ -47,40 +49,44 @@ def test_block_relabelling_is_invisible(bs):
         inp, k_cache=inp.k_cache[inv].contiguous(), v_cache=inp.v_cache[inv].contiguous(),
         kv_scales=inp.kv_scales[inv].contiguous(),
         block_tables=perm[inp.block_tables.long()].to(torch.int32))
-    assert np.array_equal(bits(gpu_decode(moved)), bits(ref))
+    assert np.array_equal(bits(gpu_decode(moved, path=path)), bits(ref))
 
 
 @pytest.mark.parametrize("qg,bs", [(8, 16), (16, 32), (6, 32)])
 def test_single_live_partition_identity(qg, bs):
-    """L <= 256: (P=1, G=1), (P=3, G=1), (P=1, G=5), (P=2, G=2) give the same bits."""
+    """L <= 256: (P=1, G=1), (P=3, G=1), (P=1, G=5), (P=2, G=2) give the same bits,
+    through the two-kernel path and the fused path alike."""
     lens = (1, 16, 31, 100, 255, 256)
     inp = small(lens, qg=qg, bs=bs, P=1, seed=30 + qg)
     outs = []
-    for P, G in ((1, 1), (3, 1), (1, 5), (2, 2)):
-        say(f"[bitwise] single live partition qg={qg} bs={bs} P={P} G={G}")
-        outs.append(bits(gpu_decode(inp, num_partitions=P, tile_groups=G)))
+    for path in PATHS:
+        for P, G in ((1, 1), (3, 1), (1, 5), (2, 2)):
+            say(f"[bitwise] single live partition qg={qg} bs={bs} P={P} G={G} {path}")
+            outs.append(bits(gpu_decode(inp, num_partitions=P, tile_groups=G, path=path)))
     for o in outs[1:]:
         assert np.array_equal(o, outs[0])
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("bs", [16, 32])
-def test_poison_invariance(bs):
+def test_poison_invariance(bs, path):
     """Garbage past each sequence end, in unused table entries and in the partial buffers."""
     lens = (1, 17, 250, 333, 769)
     inp = small(lens, bs=bs, P=4, seed=40)
-    say(f"[bitwise] poison bs={bs}")
-    clean = gpu_decode(inp)
+    say(f"[bitwise] poison bs={bs} {path}")
+    clean = gpu_decode(inp, path=path)
     dirty = workloads.poison(inp)
     part = tq.alloc_partials(len(lens), 2, 4, 8, "cuda")
     for t in (part.out, part.max_logits, part.exp_sums):
         t.fill_(float("nan"))
     out = torch.full_like(clean, float("nan"))
-    got = gpu_decode(dirty, partials=part, out=out)
+    got = gpu_decode(dirty, partials=part, out=out, path=path)
     assert np.array_equal(bits(got), bits(clean))
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("bs,P", [(16, 1), (32, 3)])
-def test_one_hot_gather_probe(bs, P):
+def test_one_hot_gather_probe(bs, P, path):
     """K is zero except at token t*, whose logit leads by ~724, so every other weight is exactly
     0 in fp32: out == bf16(V[t*]) bit for bit."""
     L = 200 if P == 1 else 700
@@ -94,35 +100,36 @@ def test_one_hot_gather_probe(bs, P):
     q = torch.ones_like(inp.q)
     bt = inp.block_tables.cpu().numpy()
     v64 = (inp.v_cache.view(torch.float8_e4m3fn).double() *
-           sc[:, :, 1, :].permute(0, 2, 1).unsqueeze(-1).double())  # [NB][BS][Hkv][D]
+           sc[:, :, 1, :].unsqueeze(-1).double())  # [NB][Hkv][BS][D]
     sweep = [0, 1, bs - 1, bs, bs + 1, 2 * bs - 1, 100, L - 1] + ([255, 256, 257, 511, 512] if P > 1 else [])
     for tstar in sweep:
         k = torch.zeros_like(inp.k_cache)
         sck = sc.clone()
         for s in range(2):
             blk, slot = int(bt[s, tstar // bs]), tstar % bs
-            k[blk, slot] = 0x38  # 1.0
+            k[blk, :, slot] = 0x38  # 1.0
             sck[blk, :, 0, slot] = 64.0  # logit 128 * 64 / sqrt(128) ~ 724
         probe = dataclasses.replace(inp, q=q, k_cache=k, kv_scales=sck)
-        say(f"[bitwise] one-hot probe bs={bs} P={P} t*={tstar}")
-        out = gpu_decode(probe)
+        say(f"[bitwise] one-hot probe bs={bs} P={P} t*={tstar} {path}")
+        out = gpu_decode(probe, path=path)
         for s in range(2):
             blk, slot = int(bt[s, tstar // bs]), tstar % bs
             for h in range(Hkv):
-                want = v64[blk, slot, h].float().to(torch.bfloat16)  # exact: code * 2^k
-                assert torch.equal(want.float(), v64[blk, slot, h].float())
+                want = v64[blk, h, slot].float().to(torch.bfloat16)  # exact: code * 2^k
+                assert torch.equal(want.float(), v64[blk, h, slot].float())
                 for g in range(QG):
                     # value equality: a zero component may come out as +0 where V holds -0
                     assert torch.equal(out[s, h * QG + g].float(), want.float()), (tstar, s, h, g)
 
 
-def test_v_magnitude_equivariance():
+@pytest.mark.parametrize("path", PATHS)
+def test_v_magnitude_equivariance(path):
     """Scaling every V scale by 2^20 (or 2^-20) scales the output by exactly that."""
     inp = small((5, 300, 1000), qg=16, bs=32, P=4, seed=60)
-    say("[bitwise] V magnitude equivariance")
-    ref = gpu_decode(inp).float()
+    say(f"[bitwise] V magnitude equivariance {path}")
+    ref = gpu_decode(inp, path=path).float()
     for e in (20, -20):
         sc = inp.kv_scales.clone()
         sc[:, :, 1, :] *= 2.0 ** e
-        got = gpu_decode(dataclasses.replace(inp, kv_scales=sc)).float()
+        got = gpu_decode(dataclasses.replace(inp, kv_scales=sc), path=path).float()
         assert torch.equal(got, ref * 2.0 ** e)

@@ -6,7 +6,7 @@ import pytest
 import torch
 
 import workloads
-from gpu_util import compare, gpu_decode, oracle_decode, say, units_rows
+from gpu_util import PATHS, compare, gpu_decode, oracle_decode, say, units_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -20,26 +20,32 @@ WORKLOAD_CASES = [
 ]
 
 
+_REF_CACHE = {}
+
+
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("name,sample", WORKLOAD_CASES, ids=[c[0] for c in WORKLOAD_CASES])
-def test_workload_parity(name, sample):
+def test_workload_parity(name, sample, path):
     wl = workloads.WORKLOADS[name]
-    say(f"[parity] {name}: generating on cuda:0")
+    say(f"[parity] {name} {path}: generating on cuda:0")
     inp = workloads.make_inputs(wl, device="cuda")
-    say(f"[parity] {name}: S={wl.num_seqs} Hkv={wl.num_kv_heads} QG={wl.query_group_size} "
+    say(f"[parity] {name} {path}: S={wl.num_seqs} Hkv={wl.num_kv_heads} QG={wl.query_group_size} "
         f"BS={wl.kv_block_size} P={inp.num_partitions} G={wl.tile_groups_per_partition} "
         f"NB={inp.num_blocks} maxL={int(inp.seq_lens.max())}")
-    out = gpu_decode(inp)
+    out = gpu_decode(inp, path=path)
     QG = wl.query_group_size
     if sample is None:
-        ref = oracle_decode(inp)
-        compare(out, ref, name)
+        if name not in _REF_CACHE:
+            _REF_CACHE.clear()
+            _REF_CACHE[name] = oracle_decode(inp)
+        compare(out, _REF_CACHE[name], f"{name} {path}")
     else:
         rng = np.random.default_rng(wl.seed)
         all_units = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_kv_heads)]
         idx = rng.choice(len(all_units), size=sample, replace=False)
         units = [all_units[i] for i in sorted(idx)]
         ref = oracle_decode(inp, units=units)
-        compare(units_rows(out, units, QG), ref, f"{name} ({sample} sampled units)")
+        compare(units_rows(out, units, QG), ref, f"{name} {path} ({sample} sampled units)")
         # at full size: every output finite and bounded by the largest |V| value
         o = out.float()
         assert torch.isfinite(o).all()
@@ -49,29 +55,31 @@ SWEEP_LENS = (1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 300, 513, 1000)
 SWEEP = [(qg, bs) for qg in (6, 8, 16) for bs in (16, 32)]
 
 
+@pytest.mark.parametrize("path", PATHS)
 @pytest.mark.parametrize("qg,bs", SWEEP, ids=[f"qg{q}_bs{b}" for q, b in SWEEP])
-def test_small_sweep(qg, bs):
+def test_small_sweep(qg, bs, path):
     lens = SWEEP_LENS
     wl = workloads.small_workload(name=f"sweep_qg{qg}_bs{bs}", num_seqs=len(lens), num_kv_heads=3,
                                   query_group_size=qg, kv_block_size=bs, seq_lens=lens,
                                   seed=100 + qg + bs)
     for G, P in ((1, 4), (1, 7), (2, 2), (3, 2), (5, 1)):
-        say(f"[sweep] qg={qg} bs={bs} G={G} P={P} lens={lens}")
+        say(f"[sweep] {path} qg={qg} bs={bs} G={G} P={P} lens={lens}")
         inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=P)
-        out = gpu_decode(inp, num_partitions=P, tile_groups=G)
-        compare(out, oracle_decode(inp), f"qg{qg} bs{bs} G{G} P{P}")
+        out = gpu_decode(inp, num_partitions=P, tile_groups=G, path=path)
+        compare(out, oracle_decode(inp), f"{path} qg{qg} bs{bs} G{G} P{P}")
 
 
-def test_zero_lengths_and_outliers():
+@pytest.mark.parametrize("path", PATHS)
+def test_zero_lengths_and_outliers(path):
     lens = (0, 1, 700, 0, 33)
     wl = workloads.small_workload(name="zeros", num_seqs=len(lens), num_kv_heads=2,
                                   query_group_size=16, kv_block_size=32, seq_lens=lens, seed=7,
                                   outlier_frac=0.01)
     inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=3)
-    say("[zeros] lens with zeros, outlier q channels")
-    out = gpu_decode(inp, num_partitions=3, tile_groups=1)
+    say(f"[zeros] {path}: lens with zeros, outlier q channels")
+    out = gpu_decode(inp, num_partitions=3, tile_groups=1, path=path)
     assert (out[0].float() == 0).all() and (out[3].float() == 0).all()
-    compare(out, oracle_decode(inp), "zero lengths + outliers")
+    compare(out, oracle_decode(inp), f"{path} zero lengths + outliers")
 
 
 def test_partials_match_oracle():

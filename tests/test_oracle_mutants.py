@@ -19,7 +19,8 @@ MUTANTS = [
     ("bf16_shift", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     ("block_index_wrong_divisor", "t / pb->BS]", "t / (pb->BS + 1)]"),
     ("slot_off_by_one", "orc_kv(pb, 0, blk, t % pb->BS, h, d)", "orc_kv(pb, 0, blk, (t + 1) % pb->BS, h, d)"),
-    ("cache_head_ignored", "* pb->Hkv + h;", "* pb->Hkv + 0;"),
+    ("cache_head_ignored", "((int64_t)blk * pb->Hkv + h) * pb->BS + slot;",
+     "((int64_t)blk * pb->Hkv + 0) * pb->BS + slot;"),
     ("scale_field_ignored", "* 2 + field) * pb->BS + slot]", "* 2 + 0) * pb->BS + slot]"),
     ("scale_slot_ignored", "* 2 + field) * pb->BS + slot]", "* 2 + field) * pb->BS + 0]"),
     ("q_row_group_ignored", "(int64_t)h * pb->QG + g) * pb->D", "(int64_t)h * pb->QG + 0) * pb->D"),

@@ -22,8 +22,8 @@ Recipe (the same for every workload):
 
 Layouts (all C-contiguous):
   q             bf16   [S][Hkv*QG][D]
-  k_cache       uint8  [NB][BS][Hkv][D]  (e4m3fn codes)
-  v_cache       uint8  [NB][BS][Hkv][D]
+  k_cache       uint8  [NB][Hkv][BS][D]  (e4m3fn codes; one (block, kv head) slice contiguous)
+  v_cache       uint8  [NB][Hkv][BS][D]
   kv_scales     fp32   [NB][Hkv][2][BS]  (field 0 = K, field 1 = V)
   block_tables  int32  [S][max_blocks_per_seq]
   seq_lens      int32  [S]
@@ -173,18 +173,18 @@ def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
         q = q * mult.view(1, Hkv * QG, D).to(dev)
     q = q.to(torch.bfloat16)
 
-    k_codes = torch.empty((NB, BS, Hkv, D), dtype=torch.uint8, device=dev)
-    v_codes = torch.empty((NB, BS, Hkv, D), dtype=torch.uint8, device=dev)
+    k_codes = torch.empty((NB, Hkv, BS, D), dtype=torch.uint8, device=dev)
+    v_codes = torch.empty((NB, Hkv, BS, D), dtype=torch.uint8, device=dev)
     scales = torch.empty((NB, Hkv, 2, BS), dtype=torch.float32, device=dev)
     gk = torch.Generator(device=dev).manual_seed(wl.seed + 2)
     gv = torch.Generator(device=dev).manual_seed(wl.seed + 3)
     for b0 in range(0, NB, SLAB_BLOCKS):
         b1 = min(NB, b0 + SLAB_BLOCKS)
         for field, (gen, dst) in enumerate(((gk, k_codes), (gv, v_codes))):
-            x = torch.randn((b1 - b0, BS, Hkv, D), generator=gen, device=dev, dtype=torch.float32)
+            x = torch.randn((b1 - b0, Hkv, BS, D), generator=gen, device=dev, dtype=torch.float32)
             codes, sc = quantize_rows(x)
             dst[b0:b1] = codes
-            scales[b0:b1, :, field, :] = sc.permute(0, 2, 1)
+            scales[b0:b1, :, field, :] = sc
             del x, codes, sc
     if softmax_scale is None:
         softmax_scale = float(np.float32(1.0 / math.sqrt(D)))
@@ -227,8 +227,8 @@ def poison(inp: Inputs, seed: int = 99) -> Inputs:
         nb_used = -(-L // BS)
         if L % BS:
             b = int(bt[s, nb_used - 1])
-            k[b, L % BS:] = 0x7F
-            v[b, L % BS:] = 0x7F
+            k[b, :, L % BS:] = 0x7F
+            v[b, :, L % BS:] = 0x7F
             sc[b, :, :, L % BS:] = float("nan")
         tail = bt.shape[1] - nb_used
         if tail > 0:

@@ -126,6 +126,77 @@ def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10)
             "copy_gbs": round(cp[0], 1), "copy_workgroups": cp[1]}
 
 
+PROFILE_KERNELS = ("tq_fused_kernel", "tq_partition_kernel", "tq_merge_kernel")
+PROFILE_CMD = ("rocprofv3 {what} -T -d <dir>/{sub} -o {sub} --output-format csv -- "
+               "python3 bench.py --workload {wl} --steps 20 --warmup 3 --no-cpu-baseline")
+
+
+def _csv_rows(path):
+    import csv
+
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_rocprof(prof_dir: str, workload: str) -> None:
+    """Turn the rocprofv3 output of three profiled bench runs under `prof_dir`
+    (trace/: --kernel-trace --stats; fetch/: --pmc FETCH_SIZE; write/: --pmc
+    WRITE_SIZE) into the summaries kept under profiles/: per-kernel duration
+    statistics, and HBM bytes per launch of each decode kernel, the counters
+    scaled by what they read for the copy probe, whose bytes are known."""
+    stats = {r["Name"]: r for r in _csv_rows(os.path.join(prof_dir, "trace", "trace_kernel_stats.csv"))}
+
+    def per_kernel(sub, counter):
+        vals = {}
+        for r in _csv_rows(os.path.join(prof_dir, sub, f"{sub}_counter_collection.csv")):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    fetch = per_kernel("fetch", "FETCH_SIZE")
+    write = per_kernel("write", "WRITE_SIZE")
+    copy_bytes = 1 << 30  # the probe copies 1 GiB: reads 1 GiB, writes 1 GiB
+    f_scale = copy_bytes / (fetch["probe_copy_kernel"] * 1024.0)
+    w_scale = copy_bytes / (write["probe_copy_kernel"] * 1024.0)
+    sha = kernel_sha()
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    lines = [f"# rocprofv3 kernel statistics, {workload} (bench.py, both decode paths)", "",
+             "Commands (run from the repository root; <dir> = an output directory):", "",
+             "    " + PROFILE_CMD.format(what="--kernel-trace --stats", sub="trace", wl=workload),
+             "    " + PROFILE_CMD.format(what="--pmc FETCH_SIZE", sub="fetch", wl=workload),
+             "    " + PROFILE_CMD.format(what="--pmc WRITE_SIZE", sub="write", wl=workload),
+             f"    python3 bench.py --summarize-rocprof <dir> --workload {workload}", "",
+             f"Kernel source sha256: {sha}", "",
+             "| kernel | calls | avg us | min us | max us | FETCH_SIZE KiB/launch | WRITE_SIZE KiB/launch |",
+             "|---|---|---|---|---|---|---|"]
+    for name in PROFILE_KERNELS + ("probe_read_kernel", "probe_copy_kernel"):
+        if name not in stats:
+            continue
+        st = stats[name]
+        lines.append(f"| {name} | {st['Calls']} | {float(st['AverageNs']) / 1e3:.1f} | "
+                     f"{float(st['MinNs']) / 1e3:.1f} | {float(st['MaxNs']) / 1e3:.1f} | "
+                     f"{fetch.get(name, float('nan')):.0f} | {write.get(name, float('nan')):.0f} |")
+    lines += ["", f"Counter calibration with the 1 GiB copy probe: bytes = FETCH_SIZE x 1024 x "
+              f"{f_scale:.4f}, WRITE_SIZE x 1024 x {w_scale:.4f}.", ""]
+    for name in ("tq_fused_kernel", "tq_partition_kernel"):
+        if name not in fetch or name not in write:
+            continue
+        fb = fetch[name] * 1024.0 * f_scale
+        wb = write[name] * 1024.0 * w_scale
+        rec = {"kernel": name, "workload": workload, "kernel_source_sha256": sha,
+               "fetch_bytes_per_launch": round(fb), "write_bytes_per_launch": round(wb),
+               "hbm_bytes_per_launch": round(fb + wb),
+               "avg_duration_us": round(float(stats[name]["AverageNs"]) / 1e3, 2),
+               "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
+               "source": f"profiles/rocprof_{workload}.md"}
+        with open(os.path.join(ROOT, "profiles", f"traffic_{name}_{workload}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+        lines.append(f"- {name}: {fb / 1e9:.4f} GB fetched + {wb / 1e9:.4f} GB written per launch")
+    with open(os.path.join(ROOT, "profiles", f"rocprof_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,7 +206,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read/copy probe")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="write profiles/ summaries from rocprofv3 output under DIR and exit")
     args = ap.parse_args()
+    if args.summarize_rocprof:
+        summarize_rocprof(args.summarize_rocprof, args.workload)
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this library runs "
               "its decode on a single MI355X; sharding across GPUs is not implemented",

@@ -14,7 +14,9 @@ stderr.
                 128 B V codes, 2 fp32 scales)
   roofline      the headline path's first kernel: the same bytes / its average
                 duration, from HIP events recorded on the launch stream around
-                every launch of the timed region, against MI355X's 8 TB/s
+                every launch of a second timed pass of K steps, against
+                MI355X's 8 TB/s (the step time comes from a first pass with no
+                events between the steps)
   hbm_probe     best read and copy bandwidth of plain streaming kernels
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
 """
@@ -242,6 +244,7 @@ def main() -> int:
     kv_bytes = inp.kv_bytes()
     part = tq.alloc_partials(S, Hkv, P, QG, dev)
     out = torch.empty((S, Hkv * QG, 128), dtype=torch.bfloat16, device=dev)
+    workspace = tq.alloc_fused_workspace(S, Hkv, QG, maxlen, dev)
     stream = torch.cuda.current_stream()
 
     def two_kernel(events=None):
@@ -263,7 +266,7 @@ def main() -> int:
         tq.tq_decode_fused(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables,
                            inp.seq_lens, out, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale,
                            num_partitions=P, max_seq_len=maxlen, num_blocks=inp.num_blocks,
-                           stream=stream)
+                           workspace=workspace, stream=stream)
         if events is not None:
             events[1].record(stream)
             events[2].record(stream)
@@ -271,19 +274,23 @@ def main() -> int:
     K = args.steps
 
     def timed(step_fn):
-        """W warmup steps, then K steps between synchronizations, HIP events on the launch
-        stream around every kernel.  Returns (ms per step, [first-kernel ms], [second-kernel ms])."""
+        """W warmup steps; then K steps between two events (the step time: nothing else is
+        enqueued between the steps); then K more steps with HIP events recorded on the launch
+        stream around every kernel (the kernel durations).  Returns (ms per step,
+        [first-kernel ms], [second-kernel ms])."""
         for _ in range(args.warmup):
             step_fn()
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
         t_start = torch.cuda.Event(enable_timing=True)
         t_stop = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
         t_start.record(stream)
+        for _ in range(K):
+            step_fn()
+        t_stop.record(stream)
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
         for i in range(K):
             step_fn(ev[i])
-        t_stop.record(stream)
         torch.cuda.synchronize()
         return (t_start.elapsed_time(t_stop) / K, [e[0].elapsed_time(e[1]) for e in ev],
                 [e[1].elapsed_time(e[2]) for e in ev])

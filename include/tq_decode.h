@@ -139,26 +139,44 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
 
 /*
  * tq_decode_fused -- the whole decode step in one launch, bf16 out directly.
- * One workgroup per (sequence s, kv head h): the live partitions of s
- * (partitions of E = 256 * tile_groups_per_partition tokens, as for tq_decode)
- * are dealt in contiguous runs to the workgroup's waves; each wave keeps one
- * online softmax over its run, and the waves' partial results (o, m, l, as in
- * STEP G of tq_decode_kernel) are merged by log-sum-exp inside the workgroup,
- * in wave order, with the formula of tq_decode_reduce.  No partial leaves the
- * chip, so no partial buffer is needed; the merge across partitions is the
- * in-launch merge that the page's partial triple implies.
- *   out  bf16 [S][Hkv*QG][128], fully overwritten (L_s = 0 gives zeros).
- * Other arguments, errors and guarantees are those of tq_decode.  With one
- * live partition the output is bit-identical to tq_decode + tq_decode_reduce;
- * otherwise the two differ only by rounding (they group the same partitions
- * differently), and repeated calls are bit-identical.
+ * Each (sequence s, kv head h) gets one or more workgroups; its cached
+ * tokens, in tile groups of 256, are dealt in contiguous runs to the
+ * workgroups and, inside a workgroup, to its waves.  Each wave keeps one
+ * online softmax over its run; a workgroup merges its waves' partial results
+ * (o, m, l, as in STEP G of tq_decode_kernel) by log-sum-exp in LDS with the
+ * formula of tq_decode_reduce.  When an (s, h) has work for several
+ * workgroups, each writes its merged partial to `workspace`, and the last one
+ * to finish merges them all in workgroup order and writes out: the in-launch
+ * merge across partitions that the page's partial triple implies, with no
+ * second launch and no partial round trip through a separate kernel.
+ *   out        bf16 [S][Hkv*QG][128], fully overwritten (L_s = 0 gives zeros)
+ *   workspace  NULL, or device memory of workspace_bytes bytes, 16-byte
+ *              aligned; its first tq_fused_workspace_bytes-sized use needs it
+ *              ZERO-FILLED once (it holds arrival counters that every call
+ *              leaves at zero again).  With NULL or too few bytes for the
+ *              preferred split, fewer workgroups per (s, h) are used (down to
+ *              one, which needs no workspace).  Calls that run concurrently
+ *              must not share a workspace.
+ * tile_groups_per_partition and ext->num_partitions bound the context as for
+ * tq_decode (coverage check); the split itself is the library's choice,
+ * deterministic for given sizes and workspace_bytes, so repeated calls are
+ * bit-identical.  With one tile group of context (L <= 256) the output is
+ * bit-identical to tq_decode + tq_decode_reduce; otherwise the two paths
+ * differ only by rounding.  Other arguments and errors are those of tq_decode.
  */
 tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
                           const float* kv_scales, const int32_t* block_tables,
                           const int32_t* seq_lens, void* out, int32_t num_kv_heads,
                           int32_t query_group_size, int32_t kv_block_size,
                           int32_t tile_groups_per_partition, float softmax_scale,
-                          const tq_extent* ext, void* stream);
+                          const tq_extent* ext, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/* Workspace bytes tq_decode_fused can use for these sizes (0: it would use
+ * one workgroup per (s, h) and needs none).  Depends on num_seqs,
+ * max_seq_len, num_kv_heads and query_group_size. */
+size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,
+                                int32_t query_group_size);
 
 /* Bytes of the three partial arrays for these sizes (each rounded up to 256 B),
  * laid out out | max_logits | exp_sums; 0 if the sizes are invalid. */

@@ -33,8 +33,8 @@ SUPPORTED_KV_BLOCK_SIZES = (16, 32)
 TQ_OK, TQ_ERR_NULL, TQ_ERR_MISALIGNED, TQ_ERR_UNSUPPORTED, TQ_ERR_SHAPE, TQ_ERR_COVERAGE, \
     TQ_ERR_SCALE, TQ_ERR_HIP = range(8)
 
-EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_decode_fused", "tq_partials_bytes",
-                    "tq_status_str", "tq_last_hip_error", "tq_abi_version")
+EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_decode_fused", "tq_fused_workspace_bytes",
+                    "tq_partials_bytes", "tq_status_str", "tq_last_hip_error", "tq_abi_version")
 
 
 class TqError(RuntimeError):
@@ -74,8 +74,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                      ctypes.POINTER(Extent), P]
     lib.tq_decode_reduce.restype = ctypes.c_int
     lib.tq_decode_fused.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float,
-                                    ctypes.POINTER(Extent), P]
+                                    ctypes.POINTER(Extent), P, ctypes.c_size_t, P]
     lib.tq_decode_fused.restype = ctypes.c_int
+    lib.tq_fused_workspace_bytes.argtypes = [ctypes.POINTER(Extent), i32, i32]
+    lib.tq_fused_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_partials_bytes.argtypes = [ctypes.POINTER(Extent), i32, i32]
     lib.tq_partials_bytes.restype = ctypes.c_size_t
     lib.tq_status_str.argtypes = [ctypes.c_int]
@@ -183,20 +185,39 @@ def tq_decode_reduce(partials: Partials, seq_lens, out, num_kv_heads: int, query
         raise TqError(st, "tq_decode_reduce")
 
 
+def fused_workspace_bytes(num_seqs, num_kv_heads, query_group_size, max_seq_len) -> int:
+    ext = _extent(num_seqs, 1, 1, 1, max_seq_len)
+    return int(load_library().tq_fused_workspace_bytes(ctypes.byref(ext), int(num_kv_heads),
+                                                       int(query_group_size)))
+
+
+def alloc_fused_workspace(num_seqs, num_kv_heads, query_group_size, max_seq_len,
+                          device) -> Optional[torch.Tensor]:
+    """Zero-filled workspace for tq_decode_fused (None when it needs none)."""
+    n = fused_workspace_bytes(num_seqs, num_kv_heads, query_group_size, max_seq_len)
+    return torch.zeros(n, dtype=torch.uint8, device=device) if n else None
+
+
 def tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
                     num_kv_heads: int, query_group_size: int, kv_block_size: int,
                     tile_groups_per_partition: int, softmax_scale: float, *, num_partitions: int,
-                    max_seq_len: int, num_blocks: Optional[int] = None, stream=None) -> None:
-    """Enqueue the one-launch decode (C ABI tq_decode_fused) into bf16 `out` [S][Hkv*QG][128]."""
+                    max_seq_len: int, num_blocks: Optional[int] = None,
+                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Enqueue the one-launch decode (C ABI tq_decode_fused) into bf16 `out` [S][Hkv*QG][128].
+    `workspace`: None or a zero-filled uint8 device tensor (see alloc_fused_workspace)."""
     lib = load_library()
     ptrs = [_dev(t, n) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                                     (kv_scales, "kv_scales"), (block_tables, "block_tables"),
                                     (seq_lens, "seq_lens"), (out, "out"))]
     nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
     ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
     st = lib.tq_decode_fused(*ptrs, int(num_kv_heads), int(query_group_size), int(kv_block_size),
                              int(tile_groups_per_partition), float(softmax_scale),
-                             ctypes.byref(ext), _stream(stream))
+                             ctypes.byref(ext), ws_ptr, ws_bytes, _stream(stream))
     if st != TQ_OK:
         raise TqError(st, "tq_decode_fused")
 
@@ -204,11 +225,13 @@ def tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
 def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partitions=None,
            tile_groups_per_partition: int = 1, softmax_scale: Optional[float] = None,
            max_seq_len: Optional[int] = None, partials: Optional[Partials] = None,
-           out: Optional[torch.Tensor] = None, fused: bool = False, stream=None) -> torch.Tensor:
+           out: Optional[torch.Tensor] = None, fused: bool = False,
+           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Decode attention; returns bf16 [S][Hkv*QG][128].
 
     fused=False: tq_decode then tq_decode_reduce (partials in `partials` or
-    allocated here); fused=True: tq_decode_fused (no partials).
+    allocated here); fused=True: tq_decode_fused with `workspace` (a zero-filled
+    one is allocated here when None).
 
     q bf16 [S][Hq][128]; k_cache/v_cache uint8 (e4m3fn codes) [NB][Hkv][BS][128];
     kv_scales fp32 [NB][Hkv][2][BS]; block_tables/seq_lens int32.
@@ -230,9 +253,11 @@ def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partit
     if out is None:
         out = torch.empty((S, Hq, HEAD_DIM), dtype=torch.bfloat16, device=q.device)
     if fused:
+        if workspace is None:
+            workspace = alloc_fused_workspace(S, Hkv, QG, max_seq_len, q.device)
         tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out, Hkv, QG, BS, G,
                         softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
-                        num_blocks=NB, stream=stream)
+                        num_blocks=NB, workspace=workspace, stream=stream)
         return out
     if partials is None:
         partials = alloc_partials(S, Hkv, num_partitions, QG, q.device)

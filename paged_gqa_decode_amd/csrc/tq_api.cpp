@@ -114,7 +114,8 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
                           const int32_t* seq_lens, void* out, int32_t num_kv_heads,
                           int32_t query_group_size, int32_t kv_block_size,
                           int32_t tile_groups_per_partition, float softmax_scale,
-                          const tq_extent* ext, void* stream) {
+                          const tq_extent* ext, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   if (!out) return TQ_ERR_NULL;
   tq::FusedArgs a;
   int32_t E = 0;
@@ -122,13 +123,29 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
                               query_group_size, kv_block_size, tile_groups_per_partition,
                               softmax_scale, ext, &a.st, &E);
   if (st != TQ_OK) return st;
-  if (!aligned16(out)) return TQ_ERR_MISALIGNED;
+  if (!aligned16(out) || (workspace && !aligned16(workspace))) return TQ_ERR_MISALIGNED;
+  const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
+  const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size,
+                                            workspace ? workspace_bytes : 0);
   a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);
-  a.partition_tokens = E;
   a.len_cap = ext->max_seq_len;
-  return hip_status(tq::launch_fused(a, ext->num_seqs, ext->num_partitions, query_group_size,
-                                     kv_block_size, static_cast<hipStream_t>(stream)));
+  a.splits = plan.splits;
+  a.counters = nullptr;
+  a.ws_o = a.ws_m = a.ws_l = nullptr;
+  if (plan.splits > 1) tq::bind_fused_workspace(&a, workspace, seq_heads, query_group_size);
+  return hip_status(tq::launch_fused(a, ext->num_seqs, plan.waves, query_group_size, kv_block_size,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,
+                                int32_t query_group_size) {
+  if (!ext || ext->num_seqs < 1 || num_kv_heads < 1 || !supported_qg(query_group_size) ||
+      ext->max_seq_len < 0)
+    return 0;
+  const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
+  const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size, SIZE_MAX);
+  return tq::fused_workspace_bytes(seq_heads, plan.splits, query_group_size);
 }
 
 tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens, void* out,

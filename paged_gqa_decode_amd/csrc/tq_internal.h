@@ -38,11 +38,29 @@ struct PartitionArgs {
 
 struct FusedArgs {
   StreamArgs st;
-  const int32_t* seq_lens;   // int32 [S]
-  uint16_t* out;             // bf16 [S][Hkv*QG][128]
-  int32_t partition_tokens;  // E = 256 * G
+  const int32_t* seq_lens;  // int32 [S]
+  uint16_t* out;            // bf16 [S][Hkv*QG][128]
   int32_t len_cap;
+  int32_t splits;           // workgroups per (s, h), >= 1
+  // Cross-workgroup merge workspace, used when splits > 1.
+  int32_t* counters;        // [S*Hkv] arrival counters: 0 on entry, re-armed to 0
+  float* ws_o;              // [S*Hkv][splits][QG][128] workgroup partials
+  float* ws_m;              // [S*Hkv][splits][QG]
+  float* ws_l;              // [S*Hkv][splits][QG]
 };
+
+// How the fused kernel is launched: waves per workgroup and workgroups per (s, h).
+struct FusedPlan {
+  int waves;
+  int splits;
+};
+
+// Plan for these sizes with `ws_bytes` of workspace (0: none), and the
+// workspace bytes a plan needs (counters first, at a fixed offset).
+FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes);
+size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size);
+// Carve the workspace for `splits` into the pointers of `a`.
+void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size);
 
 struct ReduceArgs {
   const float* o;
@@ -62,7 +80,7 @@ struct ReduceArgs {
 // waves per workgroup from the sizes.
 hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
                             int kv_block_size, hipStream_t stream);
-hipError_t launch_fused(const FusedArgs& a, int num_seqs, int num_partitions, int query_group_size,
+hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_group_size,
                         int kv_block_size, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream);
 

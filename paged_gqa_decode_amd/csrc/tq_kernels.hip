@@ -396,41 +396,100 @@ __global__ __launch_bounds__(64) void tq_partition_kernel(PartitionArgs a) {
 constexpr int kWaveLds = 2 * CHUNK * D + 2 * 2 * CHUNK * 4;
 static_assert(16 * D * 4 + 2 * 16 * 4 <= kWaveLds, "merge area must fit the staging area");
 
-// Fused decode: one workgroup of W waves per (s, h).  The live partitions of
-// the sequence are dealt to the waves in contiguous runs; each wave runs one
-// online softmax over its run, and the W partial results are merged by
-// log-sum-exp through LDS, so no partial ever leaves the CU; bf16 out is
-// written directly.
+// Log-sum-exp merge of n partials j = 0..n-1 for 4 columns, in j order:
+// o = sum_j (l_j e^{m_j - M} / sum_j' l_j' e^{m_j' - M}) o_j.  ld_o(j) returns
+// the 4 columns of o_j, ld_m(j) / ld_l(j) its max logit and exp sum.  Returns
+// the merged exp sum and max through *l_out, *m_out.  A single partial is
+// returned as is.
+template <typename LdO, typename LdM, typename LdL>
+__device__ __forceinline__ f32x4 lse_merge4(int n, LdO ld_o, LdM ld_m, LdL ld_l, float* m_out,
+                                            float* l_out) {
+  if (n == 1) {
+    *m_out = ld_m(0);
+    *l_out = ld_l(0);
+    return ld_o(0);
+  }
+  float M = kNegInf;
+  for (int j = 0; j < n; ++j) M = fmaxf(M, ld_m(j));
+  float Wsum = 0.f;
+  for (int j = 0; j < n; ++j) Wsum += ld_l(j) * __expf(ld_m(j) - M);
+  const float invW = 1.0f / Wsum;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < n; ++j) {
+    const float wt = ld_l(j) * __expf(ld_m(j) - M) * invW;
+    o += wt * ld_o(j);
+  }
+  *m_out = M;
+  *l_out = Wsum;
+  return o;
+}
+
+// Device-coherent (agent scope) loads and stores of the cross-workgroup
+// partials: relaxed atomics write through to, and read from, the point where
+// all XCDs see the same bytes, so no L2-wide write-back or invalidate is
+// needed around them.
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 o) {
+  const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+}
+
+// Fused decode.  Each (s, h) gets `splits` workgroups of W waves; its tile
+// groups (256 tokens) are dealt in contiguous runs to the workgroups, and
+// within a workgroup to its waves.  Each wave keeps one online softmax over
+// its run; the workgroup merges its waves' partials by log-sum-exp through
+// LDS.  With one workgroup of work for the (s, h), that merge writes bf16 out.
+// Otherwise each workgroup writes its merged partial (o, m, l) to the
+// workspace, releases it at device scope and counts itself in; the last to
+// arrive acquires all partials, merges them in workgroup order (so the result
+// does not depend on arrival order), writes out and re-arms the counter to 0.
 template <int QG, int BS>
 __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  __shared__ int last_arrival;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int W = blockDim.x >> 6;
   const int r = lane & 15;
   const int b = lane >> 4;
   const int Hkv = a.st.num_kv_heads;
-  const int E = a.partition_tokens;
-  const int sh = blockIdx.x;
+  const int splits = a.splits;
+  const int sh = blockIdx.x / splits;
+  const int split = blockIdx.x % splits;
   const int h = sh % Hkv;
   const int s = sh / Hkv;
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
   uint16_t* out = a.out + (size_t)sh * QG * D;
   if (L == 0) {  // uniform over the workgroup
-    for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x)
-      *reinterpret_cast<uint2*>(out + 4 * idx) = make_uint2(0u, 0u);
+    if (split == 0)
+      for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x)
+        *reinterpret_cast<uint2*>(out + 4 * idx) = make_uint2(0u, 0u);
     return;
   }
-  const int n_live = (L + E - 1) / E;
-  const int per_wave = (n_live + W - 1) / W;       // partitions per wave
-  const int n_used = (n_live + per_wave - 1) / per_wave;
+  constexpr int TG = kTokensPerTileGroup;
+  const int n_tg = (L + TG - 1) / TG;
+  const int per_wg = (n_tg + splits - 1) / splits;
+  const int n_wg = (n_tg + per_wg - 1) / per_wg;  // workgroups of this (s, h) with work
+  if (split >= n_wg) return;                        // no work, does not count itself in
+  const int tg0 = split * per_wg;
+  const int cnt = min(per_wg, n_tg - tg0);
+  const int per_wave = (cnt + W - 1) / W;
+  const int n_used = (cnt + per_wave - 1) / per_wave;
+
   uint8_t* region = lds_dyn + wave * kWaveLds;
-  float* part_o = reinterpret_cast<float*>(region);                 // [QG][128]
-  float* part_m = reinterpret_cast<float*>(region + 16 * D * 4);    // [QG]
-  float* part_l = part_m + 16;                                      // [QG]
+  float* part_o = reinterpret_cast<float*>(region);               // [QG][128]
+  float* part_m = reinterpret_cast<float*>(region + 16 * D * 4);  // [QG]
+  float* part_l = part_m + 16;                                    // [QG]
   if (wave < n_used) {  // uniform over the wave
-    const int t_begin = wave * per_wave * E;
-    const int t_end = min(t_begin + per_wave * E, L);
+    const int t_begin = (tg0 + wave * per_wave) * TG;
+    const int t_end = min(t_begin + per_wave * TG, min((tg0 + cnt) * TG, L));
     WaveState w;
     w.reset();
     stream_tokens<QG, BS>(a.st, s, h, t_begin, t_end, 0x7fffffff, region,
@@ -449,34 +508,62 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
     }
   }
   __syncthreads();
-  // Log-sum-exp merge of the waves' partials, as tq_merge_kernel does for partitions.
+
+  // Merge this workgroup's waves.
+  const float* lds_f = reinterpret_cast<const float*>(lds_dyn);
+  constexpr int kWaveF = kWaveLds / 4;
+  const size_t wsrow0 = ((size_t)sh * splits + split) * QG;
   for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x) {
     const int g = idx / (D / 4);
     const int col = 4 * (idx % (D / 4));
-    f32x4 o;
-    if (n_used == 1) {
-      o = *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(lds_dyn) + g * D + col);
+    float m, l;
+    const f32x4 o = lse_merge4(
+        n_used,
+        [&](int v) { return *reinterpret_cast<const f32x4*>(lds_f + v * kWaveF + g * D + col); },
+        [&](int v) { return lds_f[v * kWaveF + 16 * D + g]; },
+        [&](int v) { return lds_f[v * kWaveF + 16 * D + 16 + g]; }, &m, &l);
+    if (n_wg == 1) {
+      store_bf16x4(out + g * D + col, o);
     } else {
-      float M = kNegInf;
-      for (int v = 0; v < n_used; ++v)
-        M = fmaxf(M, reinterpret_cast<const float*>(lds_dyn + v * kWaveLds + 16 * D * 4)[g]);
-      float Wsum = 0.f;
-      for (int v = 0; v < n_used; ++v) {
-        const float* pm = reinterpret_cast<const float*>(lds_dyn + v * kWaveLds + 16 * D * 4);
-        Wsum += pm[16 + g] * __expf(pm[g] - M);
-      }
-      const float invW = 1.0f / Wsum;
-      o = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int v = 0; v < n_used; ++v) {
-        const float* po = reinterpret_cast<const float*>(lds_dyn + v * kWaveLds);
-        const float* pm = po + 16 * D;
-        const float wt = pm[16 + g] * __expf(pm[g] - M) * invW;
-        o += wt * *reinterpret_cast<const f32x4*>(po + g * D + col);
+      float* dst = a.ws_o + (wsrow0 + g) * D + col;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_coherent(dst + i, o[i]);
+      if (col == 0) {
+        st_coherent(a.ws_m + wsrow0 + g, m);
+        st_coherent(a.ws_l + wsrow0 + g, l);
       }
     }
-    const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-    *reinterpret_cast<uint2*>(out + g * D + col) = make_uint2(lo, hi);
+  }
+  if (n_wg == 1) return;
+
+  // Cross-workgroup merge.  Release: every thread's coherent stores complete
+  // (vmcnt drained) before the barrier, and only then is the arrival counted.
+  // Acquire: the last arrival reads the partials with coherent loads issued
+  // after its count returned.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (threadIdx.x == 0)
+    last_arrival = __hip_atomic_fetch_add(a.counters + sh, 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT) == n_wg - 1;
+  __syncthreads();
+  if (!last_arrival) return;
+  if (threadIdx.x == 0)  // re-arm for the next call; every arrival of this launch is in
+    __hip_atomic_store(a.counters + sh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const size_t row_sh = (size_t)sh * splits * QG;
+  for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x) {
+    const int g = idx / (D / 4);
+    const int col = 4 * (idx % (D / 4));
+    float m, l;
+    const f32x4 o = lse_merge4(
+        n_wg,
+        [&](int j) {
+          const float* src = a.ws_o + (row_sh + (size_t)j * QG + g) * D + col;
+          return f32x4{ld_coherent(src), ld_coherent(src + 1), ld_coherent(src + 2),
+                       ld_coherent(src + 3)};
+        },
+        [&](int j) { return ld_coherent(a.ws_m + row_sh + (size_t)j * QG + g); },
+        [&](int j) { return ld_coherent(a.ws_l + row_sh + (size_t)j * QG + g); }, &m, &l);
+    store_bf16x4(out + g * D + col, o);
   }
 }
 
@@ -496,26 +583,15 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(ReduceArgs a) {
     uint16_t* dst = a.out + ((size_t)sh * QG + g) * D + col;
     const size_t row0 = (size_t)sh * P * QG + g;  // (s, h, p = 0, g)
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (live == 1) {
-      o = *reinterpret_cast<const f32x4*>(a.o + row0 * D + col);
-    } else if (live > 1) {
-      float M = kNegInf;
-      for (int p = 0; p < live; ++p) M = fmaxf(M, a.ml[row0 + (size_t)p * QG]);
-      float W = 0.f;
-      for (int p = 0; p < live; ++p) {
-        const size_t rp = row0 + (size_t)p * QG;
-        W += a.es[rp] * __expf(a.ml[rp] - M);
-      }
-      const float invW = 1.0f / W;
-      for (int p = 0; p < live; ++p) {
-        const size_t rp = row0 + (size_t)p * QG;
-        const float w = a.es[rp] * __expf(a.ml[rp] - M) * invW;
-        o += w * *reinterpret_cast<const f32x4*>(a.o + rp * D + col);
-      }
+    if (live > 0) {
+      float m, l;
+      o = lse_merge4(
+          live,
+          [&](int p) { return *reinterpret_cast<const f32x4*>(a.o + (row0 + (size_t)p * QG) * D + col); },
+          [&](int p) { return a.ml[row0 + (size_t)p * QG]; },
+          [&](int p) { return a.es[row0 + (size_t)p * QG]; }, &m, &l);
     }
-    const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-    const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
-    *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    store_bf16x4(dst, o);
   }
 }
 
@@ -532,16 +608,46 @@ int choose_parts_per_wave(int64_t units, int num_partitions) {
   return (int)ppw;
 }
 
-int choose_fused_waves(int64_t seq_heads, int num_partitions) {
-  // One workgroup per (s, h): enough waves per workgroup to put ~4096 waves
-  // on the device, at most 8 (the register budget of __launch_bounds__(512)),
-  // and no more than there are partitions to deal out.
-  constexpr int64_t kTargetWaves = 4096;
-  int64_t w = (kTargetWaves + seq_heads - 1) / seq_heads;
-  if (w > 8) w = 8;
-  if (w > num_partitions) w = num_partitions;
-  if (w < 1) w = 1;
-  return (int)w;
+constexpr int kMaxSplits = 16;
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)seq_heads * splits * query_group_size;
+  return round256((size_t)seq_heads * 4) + round256(rows * D * 4) + 2 * round256(rows * 4);
+}
+
+void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size) {
+  const size_t rows = (size_t)seq_heads * a->splits * query_group_size;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  a->counters = reinterpret_cast<int32_t*>(p);
+  p += round256((size_t)seq_heads * 4);
+  a->ws_o = reinterpret_cast<float*>(p);
+  p += round256(rows * D * 4);
+  a->ws_m = reinterpret_cast<float*>(p);
+  p += round256(rows * 4);
+  a->ws_l = reinterpret_cast<float*>(p);
+}
+
+FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes) {
+  // About kTargetWaves waves on the device (one resident round at two waves
+  // per SIMD; measured best across the workloads), each with at least one tile
+  // group of work; at most 8 waves per workgroup (the register budget of
+  // __launch_bounds__(512)), then more workgroups per (s, h) if the workspace
+  // can hold their partials.
+  constexpr int64_t kTargetWaves = 2048;
+  const int64_t n_tg = max_seq_len > 0 ? (max_seq_len + kTokensPerTileGroup - 1) / kTokensPerTileGroup : 1;
+  int64_t waves_per_sh = (kTargetWaves + seq_heads - 1) / seq_heads;
+  if (waves_per_sh > n_tg) waves_per_sh = n_tg;
+  if (waves_per_sh < 1) waves_per_sh = 1;
+  FusedPlan plan;
+  plan.waves = (int)(waves_per_sh < 8 ? waves_per_sh : 8);
+  int64_t splits = (waves_per_sh + plan.waves - 1) / plan.waves;
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  while (splits > 1 && fused_workspace_bytes(seq_heads, (int)splits, query_group_size) > ws_bytes) --splits;
+  plan.splits = (int)splits;
+  return plan;
 }
 
 hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
@@ -581,11 +687,9 @@ hipError_t launch_fused_t(const FusedArgs& a, unsigned grid, int waves, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_fused(const FusedArgs& a, int num_seqs, int num_partitions, int query_group_size,
+hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_group_size,
                         int kv_block_size, hipStream_t stream) {
-  const int64_t seq_heads = (int64_t)num_seqs * a.st.num_kv_heads;
-  const int waves = choose_fused_waves(seq_heads, num_partitions);
-  const unsigned grid = (unsigned)seq_heads;
+  const unsigned grid = (unsigned)((int64_t)num_seqs * a.st.num_kv_heads * a.splits);
   if (query_group_size == 6 && kv_block_size == 16) return launch_fused_t<6, 16>(a, grid, waves, stream);
   if (query_group_size == 6 && kv_block_size == 32) return launch_fused_t<6, 32>(a, grid, waves, stream);
   if (query_group_size == 8 && kv_block_size == 16) return launch_fused_t<8, 16>(a, grid, waves, stream);

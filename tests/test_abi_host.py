@@ -130,10 +130,11 @@ def test_coverage_boundary_from_the_page_sizing_example(lib):
 
 
 def call_fused(lib, *, ptrs=None, out=A, QG=8, BS=16, G=1, Hkv=2, scale=0.088, S=2, NB=8, MB=4,
-               P=1, maxlen=64, head_dim=128):
+               P=1, maxlen=64, head_dim=128, ws=None, ws_bytes=0):
     ptrs = ptrs or [A] * 6
     ext = tq.Extent(S, NB, MB, P, maxlen, head_dim)
-    return lib.tq_decode_fused(*ptrs, out, Hkv, QG, BS, G, scale, ctypes.byref(ext), None)
+    return lib.tq_decode_fused(*ptrs, out, Hkv, QG, BS, G, scale, ctypes.byref(ext), ws, ws_bytes,
+                               None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -146,9 +147,20 @@ def call_fused(lib, *, ptrs=None, out=A, QG=8, BS=16, G=1, Hkv=2, scale=0.088, S
     (dict(scale=float("nan")), tq.TQ_ERR_SCALE),
     (dict(out=A + 8), tq.TQ_ERR_MISALIGNED),
     (dict(ptrs=[A, A, A, A, A, A + 1]), tq.TQ_ERR_MISALIGNED),
+    (dict(ws=A + 8, ws_bytes=1 << 20), tq.TQ_ERR_MISALIGNED),
 ])
 def test_fused_rejects(lib, kw, status):
     assert call_fused(lib, **kw) == status
+
+
+def test_fused_workspace_bytes():
+    # one workgroup per (s, h) suffices when there are many (s, h): no workspace
+    assert tq.fused_workspace_bytes(128, 8, 8, 8192) == 0
+    # 64 (s, h) with 160 tile groups: 32 waves each, as 8 waves x 4 workgroups
+    rows = 64 * 4 * 16
+    assert tq.fused_workspace_bytes(16, 4, 16, 40960) == 256 + rows * 512 + 2 * rows * 4
+    assert tq.fused_workspace_bytes(16, 4, 7, 40960) == 0  # unsupported QG
+    assert tq.fused_workspace_bytes(4, 1, 16, 200) == 0    # a single tile group
 
 
 def call_reduce(lib, *, part=None, sl=A, out=A, QG=8, Hkv=2, G=1, S=2, P=1, maxlen=64):

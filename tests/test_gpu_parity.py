@@ -110,3 +110,48 @@ def test_partials_match_oracle():
     err = np.abs(go[live] - o[live]).max()
     say(f"  partial o max abs err {err:.3e}")
     assert err < 5e-3
+
+
+def test_fused_split_modes():
+    """tq_decode_fused with no workspace (one workgroup per (s, h)), the full workspace (the
+    tokens of an (s, h) split over several workgroups, last arrival merges) and a workspace
+    that fits only two workgroups per (s, h): all match the oracle; repeated calls give the
+    same bits; the arrival counters are left at zero; garbage in the partial area is harmless."""
+    import paged_gqa_decode_amd as tq
+
+    lens = (5000, 37, 3000, 8191)
+    wl = workloads.small_workload(name="splits", num_seqs=4, num_kv_heads=1, query_group_size=16,
+                                  kv_block_size=32, seq_lens=lens, seed=17)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=32)
+    ref = oracle_decode(inp)
+    S, Hkv, QG, maxlen = 4, 1, 16, max(lens)
+    full = tq.fused_workspace_bytes(S, Hkv, QG, maxlen)
+    assert full > 0, "these sizes should split each (s, h) over several workgroups"
+
+    def run(ws):
+        out = torch.empty((S, Hkv * QG, 128), dtype=torch.bfloat16, device="cuda")
+        tq.tq_decode_fused(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables,
+                           inp.seq_lens, out, Hkv, QG, 32, 1, inp.softmax_scale, num_partitions=32,
+                           max_seq_len=maxlen, workspace=ws)
+        torch.cuda.synchronize()
+        return out
+
+    say("[splits] no workspace")
+    a = run(None)
+    compare(a, ref, "fused, one workgroup per (s, h)")
+    ws = torch.zeros(full, dtype=torch.uint8, device="cuda")
+    ws[256:] = 0xFF  # NaN garbage in the partial area; the counters (first 256 B) stay zero
+    say(f"[splits] full workspace ({full} B)")
+    b1 = run(ws)
+    compare(b1, ref, "fused, split over workgroups")
+    assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "counters must be re-armed to 0"
+    b2 = run(ws)
+    assert torch.equal(b1.view(torch.int16), b2.view(torch.int16))
+    # a workspace with room for exactly two workgroups per (s, h)
+    rows = S * Hkv * 2 * QG
+    two = 256 + ((rows * 512 + 255) // 256) * 256 + 2 * ((rows * 4 + 255) // 256) * 256
+    ws2 = torch.zeros(two, dtype=torch.uint8, device="cuda")
+    say(f"[splits] two-split workspace ({two} B)")
+    c = run(ws2)
+    compare(c, ref, "fused, two workgroups per (s, h)")
+    assert int(ws2[:256].view(torch.int32).abs().sum()) == 0

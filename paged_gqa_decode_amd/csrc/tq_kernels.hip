@@ -567,29 +567,77 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   }
 }
 
-// Merge: one 256-thread block per (sequence, kv head); thread -> (query row g,
-// 4 consecutive head_dim columns).
+// Merge of the split-K partials: one 256-thread block per (sequence, kv
+// head).  Each wave takes query rows g = wave, wave + 4, ...; its lanes read
+// the live partitions' max logits and exp sums, reduce M = max m_p and
+// W = sum l_p e^{m_p - M} across the wave, and store the coefficients
+// c[g][p] = l_p e^{m_p - M} / W in LDS.  Then every thread accumulates
+// sum_p c[g][p] o_p for 4 columns of one row with independent 16-byte loads.
+// One live partition is copied (c = 1).  More than kMergeMaxParts live
+// partitions fall back to recomputing the coefficients per thread.
+constexpr int kMergeMaxParts = 256;
+
 __global__ __launch_bounds__(256) void tq_merge_kernel(ReduceArgs a) {
+  __shared__ float coef[16 * kMergeMaxParts];
   const int sh = blockIdx.x;
   const int QG = a.query_group_size;
   const int P = a.num_partitions;
   const int s = sh / a.num_kv_heads;
-  int L = a.seq_lens[s];
-  L = L < 0 ? 0 : (L > a.len_cap ? a.len_cap : L);
+  const int L = clamp_len(a.seq_lens[s], a.len_cap);
   const int live = (L + a.partition_tokens - 1) / a.partition_tokens;  // <= P (host-validated)
+  const size_t row_sh = (size_t)sh * P * QG;  // (s, h, p = 0, g = 0)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const bool staged = live > 1 && live <= kMergeMaxParts;
+  if (staged) {
+    for (int g = wave; g < QG; g += 4) {
+      float mx = kNegInf;
+      for (int p = lane; p < live; p += 64) mx = fmaxf(mx, a.ml[row_sh + (size_t)p * QG + g]);
+      for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+      float wsum = 0.f;
+      for (int p = lane; p < live; p += 64) {
+        const size_t rp = row_sh + (size_t)p * QG + g;
+        const float w = a.es[rp] * __expf(a.ml[rp] - mx);
+        coef[g * kMergeMaxParts + p] = w;
+        wsum += w;
+      }
+      for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
+      const float inv = 1.0f / wsum;
+      for (int p = lane; p < live; p += 64) coef[g * kMergeMaxParts + p] *= inv;
+    }
+    __syncthreads();
+  }
   for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x) {
     const int g = idx / (D / 4);
     const int col = 4 * (idx % (D / 4));
     uint16_t* dst = a.out + ((size_t)sh * QG + g) * D + col;
-    const size_t row0 = (size_t)sh * P * QG + g;  // (s, h, p = 0, g)
+    const float* src = a.o + (row_sh + g) * D + col;  // partition p at + p * QG * D
+    const size_t pstride = (size_t)QG * D;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    if (live > 0) {
+    if (live == 1) {
+      o = *reinterpret_cast<const f32x4*>(src);
+    } else if (staged) {
+      // 8 independent loads in flight per thread, summed in a fixed order.
+      const float* c = coef + g * kMergeMaxParts;
+      f32x4 acc[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      int p = 0;
+      for (; p + 8 <= live; p += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const f32x4*>(src + (p + u) * pstride);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc[u] += c[p + u] * v[u];
+      }
+      for (int u = 0; p < live; ++p, ++u) acc[u] += c[p] * *reinterpret_cast<const f32x4*>(src + p * pstride);
+      o = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    } else if (live > 1) {
       float m, l;
       o = lse_merge4(
-          live,
-          [&](int p) { return *reinterpret_cast<const f32x4*>(a.o + (row0 + (size_t)p * QG) * D + col); },
-          [&](int p) { return a.ml[row0 + (size_t)p * QG]; },
-          [&](int p) { return a.es[row0 + (size_t)p * QG]; }, &m, &l);
+          live, [&](int p) { return *reinterpret_cast<const f32x4*>(src + p * pstride); },
+          [&](int p) { return a.ml[row_sh + (size_t)p * QG + g]; },
+          [&](int p) { return a.es[row_sh + (size_t)p * QG + g]; }, &m, &l);
     }
     store_bf16x4(dst, o);
   }

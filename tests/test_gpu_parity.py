@@ -155,3 +155,24 @@ def test_fused_split_modes():
     c = run(ws2)
     compare(c, ref, "fused, two workgroups per (s, h)")
     assert int(ws2[:256].view(torch.int32).abs().sum()) == 0
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_long_ranges_and_many_partitions(path):
+    """A partition (or wave range) of more than 64 cache blocks, so the block-table window is
+    reloaded mid-stream (G=8, BS=16: 128 blocks per partition), and a merge over more than
+    256 live partitions (G=1, 280 partitions), which takes the merge kernel's unstaged path."""
+    lens = (1500, 2048, 700, 4096)
+    wl = workloads.small_workload(name="longrange", num_seqs=4, num_kv_heads=2, query_group_size=8,
+                                  kv_block_size=16, seq_lens=lens, seed=23)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=2)
+    say(f"[longrange] {path} G=8 P=2 BS=16")
+    out = gpu_decode(inp, num_partitions=2, tile_groups=8, path=path)
+    compare(out, oracle_decode(inp), f"{path} G8 BS16 (window reload)")
+    lens = (280 * 256 - 5, 3000)
+    wl = workloads.small_workload(name="manyparts", num_seqs=2, num_kv_heads=1, query_group_size=6,
+                                  kv_block_size=32, seq_lens=lens, seed=29)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=280)
+    say(f"[manyparts] {path} G=1 P=280 L={lens}")
+    out = gpu_decode(inp, num_partitions=280, tile_groups=1, path=path)
+    compare(out, oracle_decode(inp), f"{path} 280 partitions")

@@ -14,8 +14,8 @@ stderr.
                 128 B V codes, 2 fp32 scales)
   roofline      the headline path's first kernel: the same bytes / its average
                 duration, from HIP events recorded on the launch stream around
-                every launch of a second timed pass of K steps, against
-                MI355X's 8 TB/s (the step time comes from a first pass with no
+                every launch of a first timed pass of K steps, against
+                MI355X's 8 TB/s (the step time comes from a second pass with no
                 events between the steps)
   hbm_probe     best read and copy bandwidth of plain streaming kernels
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
@@ -274,12 +274,16 @@ def main() -> int:
     K = args.steps
 
     def timed(step_fn):
-        """W warmup steps; then K steps between two events (the step time: nothing else is
-        enqueued between the steps); then K more steps with HIP events recorded on the launch
-        stream around every kernel (the kernel durations).  Returns (ms per step,
+        """W warmup steps; then K steps with HIP events recorded on the launch stream around
+        every kernel (the kernel durations); then K steps between two events only, nothing
+        else enqueued between the steps (the step time).  Returns (ms per step,
         [first-kernel ms], [second-kernel ms])."""
         for _ in range(args.warmup):
             step_fn()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+        for i in range(K):
+            step_fn(ev[i])
         torch.cuda.synchronize()
         t_start = torch.cuda.Event(enable_timing=True)
         t_stop = torch.cuda.Event(enable_timing=True)
@@ -287,10 +291,6 @@ def main() -> int:
         for _ in range(K):
             step_fn()
         t_stop.record(stream)
-        torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-        for i in range(K):
-            step_fn(ev[i])
         torch.cuda.synchronize()
         return (t_start.elapsed_time(t_stop) / K, [e[0].elapsed_time(e[1]) for e in ev],
                 [e[1].elapsed_time(e[2]) for e in ev])

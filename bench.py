@@ -13,10 +13,9 @@ stderr.
                 sum over sequences and kv heads of L * 264 (128 B K codes,
                 128 B V codes, 2 fp32 scales)
   roofline      the headline path's first kernel: the same bytes / its average
-                duration, from HIP events recorded on the launch stream around
-                every launch of a first timed pass of K steps, against
-                MI355X's 8 TB/s (the step time comes from a second pass with no
-                events between the steps)
+                duration over K back-to-back launches between two HIP events on
+                the launch stream, against MI355X's 8 TB/s (the step time is
+                measured the same way over K whole steps)
   hbm_probe     best read and copy bandwidth of plain streaming kernels
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
 """
@@ -119,8 +118,8 @@ def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10)
             out = max(out, (moved * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, wgs))
         return out
 
-    rd = best(lambda w: probe.read(src, sink, w), nread, (1024, 2048, 4096, 8192))
-    cp = best(lambda w: probe.copy(dst, src[:ncopy], w), 2 * ncopy, (2048, 4096, 8192))
+    rd = best(lambda w: probe.read(src, sink, w), nread, (2048, 4096, 8192, 16384, 32768))
+    cp = best(lambda w: probe.copy(dst, src[:ncopy], w), 2 * ncopy, (2048, 4096, 8192, 16384))
     del src, dst, sink
     torch.cuda.empty_cache()
     return {"read_bytes": nread, "copy_bytes": ncopy, "reps": reps,
@@ -247,65 +246,49 @@ def main() -> int:
     workspace = tq.alloc_fused_workspace(S, Hkv, QG, maxlen, dev)
     stream = torch.cuda.current_stream()
 
-    def two_kernel(events=None):
-        if events is not None:
-            events[0].record(stream)
+    def dec():
         tq.tq_decode(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, inp.seq_lens,
                      part, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale, num_partitions=P,
                      max_seq_len=maxlen, num_blocks=inp.num_blocks, stream=stream)
-        if events is not None:
-            events[1].record(stream)
+
+    def red():
         tq.tq_decode_reduce(part, inp.seq_lens, out, Hkv, QG, G, num_partitions=P,
                             max_seq_len=maxlen, stream=stream)
-        if events is not None:
-            events[2].record(stream)
 
-    def fused(events=None):
-        if events is not None:
-            events[0].record(stream)
+    def fused():
         tq.tq_decode_fused(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables,
                            inp.seq_lens, out, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale,
                            num_partitions=P, max_seq_len=maxlen, num_blocks=inp.num_blocks,
                            workspace=workspace, stream=stream)
-        if events is not None:
-            events[1].record(stream)
-            events[2].record(stream)
 
     K = args.steps
 
-    def timed(step_fn):
-        """W warmup steps; then K steps with HIP events recorded on the launch stream around
-        every kernel (the kernel durations); then K steps between two events only, nothing
-        else enqueued between the steps (the step time).  Returns (ms per step,
-        [first-kernel ms], [second-kernel ms])."""
+    def timed(*kernels):
+        """Average ms of K back-to-back runs of `kernels` (one step), between two HIP events
+        on the launch stream with nothing else enqueued in between."""
         for _ in range(args.warmup):
-            step_fn()
+            for k in kernels:
+                k()
         torch.cuda.synchronize()
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
-        for i in range(K):
-            step_fn(ev[i])
-        torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_stop = torch.cuda.Event(enable_timing=True)
-        t_start.record(stream)
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
         for _ in range(K):
-            step_fn()
-        t_stop.record(stream)
+            for k in kernels:
+                k()
+        t1.record(stream)
         torch.cuda.synchronize()
-        return (t_start.elapsed_time(t_stop) / K, [e[0].elapsed_time(e[1]) for e in ev],
-                [e[1].elapsed_time(e[2]) for e in ev])
+        return t0.elapsed_time(t1) / K
 
-    paths = {}
-    for name, fn in (("two_kernel", two_kernel), ("fused", fused)):
-        ms, k1, k2 = timed(fn)
-        k1s = sorted(k1)
-        paths[name] = {"ms_per_step": ms, "k1_avg": sum(k1) / K, "k2_avg": sum(k2) / K,
-                       "k1_p10": k1s[K // 10], "k1_p90": k1s[(9 * K) // 10]}
-        log(f"[bench] {wl.name} {name}: step {ms * 1e3:.1f} us "
-            f"({kv_bytes / (ms * 1e-3) / 1e9:.0f} GB/s); first kernel avg "
-            f"{paths[name]['k1_avg'] * 1e3:.1f} us (p10 {paths[name]['k1_p10'] * 1e3:.1f}, "
-            f"p90 {paths[name]['k1_p90'] * 1e3:.1f}), second kernel avg "
-            f"{paths[name]['k2_avg'] * 1e3:.1f} us")
+    # Per-kernel averages: each kernel alone, K launches; then the step itself.
+    paths = {
+        "two_kernel": {"k1_avg": timed(dec), "k2_avg": timed(red), "ms_per_step": timed(dec, red)},
+        "fused": {"k1_avg": timed(fused), "k2_avg": 0.0, "ms_per_step": timed(fused)},
+    }
+    for name, pth in paths.items():
+        log(f"[bench] {wl.name} {name}: step {pth['ms_per_step'] * 1e3:.1f} us "
+            f"({kv_bytes / (pth['ms_per_step'] * 1e-3) / 1e9:.0f} GB/s); first kernel "
+            f"{pth['k1_avg'] * 1e3:.1f} us, second kernel {pth['k2_avg'] * 1e3:.1f} us")
     head = min(paths, key=lambda n: paths[n]["ms_per_step"])
     ms_per_step = paths[head]["ms_per_step"]
     k1_avg = paths[head]["k1_avg"]

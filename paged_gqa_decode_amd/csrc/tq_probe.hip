@@ -14,13 +14,13 @@ __global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
   size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  // 4 independent loads in flight per thread per iteration
-  for (; i + 3 * stride < n; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(src + i);
-    const u32x4 b = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(src + i + 3 * stride);
-    acc ^= a ^ b ^ c ^ d;
+  // 8 independent non-temporal loads in flight per thread per iteration
+  for (; i + 7 * stride < n; i += 8 * stride) {
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
   }
   for (; i < n; i += stride) acc ^= src[i];
   uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];

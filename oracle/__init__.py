@@ -66,6 +66,10 @@ class Oracle:
         lib.orc_partials.restype = ctypes.c_int
         lib.orc_merge.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
         lib.orc_merge.restype = ctypes.c_int
+        lib.orc_enc_e4m3fn.argtypes = [ctypes.c_float]
+        lib.orc_enc_e4m3fn.restype = ctypes.c_uint8
+        lib.orc_kv_write.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P]
+        lib.orc_kv_write.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
 
@@ -133,6 +137,32 @@ class Oracle:
         b = _np(bits, np.uint16)
         flat = np.array([self.lib.orc_dec_bf16(int(x)) for x in b.reshape(-1)], dtype=np.float64)
         return flat.reshape(b.shape)
+
+    def enc_e4m3fn(self, values) -> np.ndarray:
+        """Nearest e4m3fn codes (ties to even, saturating) of fp32 values."""
+        v = np.asarray(values, dtype=np.float32)
+        flat = np.array([self.lib.orc_enc_e4m3fn(float(x)) for x in v.reshape(-1)], dtype=np.uint8)
+        return flat.reshape(v.shape)
+
+    def kv_write(self, k_new_bits, v_new_bits, slot_mapping, k_cache, v_cache, kv_scales):
+        """Quantize and scatter new K/V rows into copies of the cache arrays; returns them.
+        k_new/v_new: bf16 bits [T][Hkv][D]; slot_mapping int32 [T] (-1: skip)."""
+        kn = _np(k_new_bits, np.uint16)
+        vn = _np(v_new_bits, np.uint16)
+        sm = _np(slot_mapping, np.int32)
+        kc = _np(k_cache, np.uint8).copy()
+        vc = _np(v_cache, np.uint8).copy()
+        sc = _np(kv_scales, np.float32).copy()
+        T, Hkv, D = kn.shape
+        NB, Hkv2, BS, D2 = kc.shape
+        if vn.shape != kn.shape or Hkv2 != Hkv or D2 != D or sm.shape != (T,) or vc.shape != kc.shape \
+                or sc.shape != (NB, Hkv, 2, BS):
+            raise OracleError("inconsistent shapes")
+        rc = self.lib.orc_kv_write(_ptr(kn), _ptr(vn), _ptr(sm), T, Hkv, D, BS, NB, _ptr(kc), _ptr(vc),
+                                   _ptr(sc))
+        if rc:
+            raise OracleError("orc_kv_write failed with code %d" % rc)
+        return kc, vc, sc
 
 
 _default = None
@@ -223,3 +253,11 @@ def dec_e4m3fn(codes):
 
 def dec_bf16(bits):
     return default().dec_bf16(bits)
+
+
+def enc_e4m3fn(values):
+    return default().enc_e4m3fn(values)
+
+
+def kv_write(*a, **k):
+    return default().kv_write(*a, **k)

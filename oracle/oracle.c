@@ -323,3 +323,67 @@ int orc_merge(const double* o, const double* m, const double* l, const int32_t* 
   }
   return ORC_OK;
 }
+
+/*
+ * KV-cache writer (the step upstream of decode that fills the cache this
+ * oracle reads; the per-block scale region follows the fp8 record writer of
+ * page "vllm.models.deepseek_v41.amd.mono.attention.front", stage_qkv, with
+ * this library's scale rule).  For each new token t with slot_mapping[t] >= 0
+ * (slot = block * BS + offset) and each kv head h, the K row and the V row
+ * (bf16, 128 values each) are quantized on their own:
+ *   s = absmax / 448        (fp32 division: the quantizer's integer decisions
+ *   q_d = x_d / s            are taken in fp32, as the GPU writer takes them)
+ *   code_d = e4m3fn(q_d), round to nearest, ties to even, saturating at 448;
+ *   absmax = 0 gives s = 0 and codes 0.
+ * Codes go to k_cache / v_cache[block][h][offset][:], s to
+ * kv_scales[block][h][field][offset]; nothing else is touched.
+ */
+
+/* Nearest e4m3fn code of a finite fp32 value, ties to the code with an even
+ * mantissa: a plain search over the 127 non-negative finite codes, using the
+ * closed-form decoder above.  The search only sees finite codes, so a
+ * magnitude above 448 saturates to +-448 by construction. */
+uint8_t orc_enc_e4m3fn(float x) {
+  double ax = fabs((double)x);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {
+    double err = fabs(orc_dec_e4m3fn((uint8_t)c) - ax);
+    if (err < best_err || (err == best_err && (c & 1) == 0)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)((signbit(x) ? 0x80 : 0x00) | best);
+}
+
+int orc_kv_write(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slot_mapping,
+                 int32_t T, int32_t Hkv, int32_t D, int32_t BS, int32_t NB, uint8_t* k_cache,
+                 uint8_t* v_cache, float* kv_scales) {
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !kv_scales || T < 0 ||
+      Hkv < 1 || D < 1 || BS < 1 || NB < 1)
+    return ORC_ERR_ARGS;
+  for (int t = 0; t < T; ++t) {
+    int32_t slot = slot_mapping[t];
+    if (slot < 0) continue;
+    if ((int64_t)slot >= (int64_t)NB * BS) return ORC_ERR_BLOCK;
+    int blk = slot / BS, off = slot % BS;
+    for (int h = 0; h < Hkv; ++h)
+      for (int field = 0; field < 2; ++field) {
+        const uint16_t* src = (field == 0 ? k_new : v_new) + ((int64_t)t * Hkv + h) * D;
+        uint8_t* dst = (field == 0 ? k_cache : v_cache) + (((int64_t)blk * Hkv + h) * BS + off) * D;
+        float absmax = 0.0f;
+        for (int d = 0; d < D; ++d) {
+          float x = (float)orc_dec_bf16(src[d]);
+          if (fabsf(x) > absmax) absmax = fabsf(x);
+        }
+        float s = absmax / 448.0f;
+        for (int d = 0; d < D; ++d) {
+          float x = (float)orc_dec_bf16(src[d]);
+          dst[d] = s > 0.0f ? orc_enc_e4m3fn(x / s) : 0;
+        }
+        kv_scales[(((int64_t)blk * Hkv + h) * 2 + field) * BS + off] = s;
+      }
+  }
+  return ORC_OK;
+}

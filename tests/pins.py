@@ -299,7 +299,114 @@ def pin_zero_length(orc):
     assert np.any(got[1] != 0)
 
 
+# ----------------------------------------------------------------------------
+# KV-cache writer pins (quantize + scatter)
+# ----------------------------------------------------------------------------
+
+def pin_e4m3fn_encode_roundtrip(orc):
+    """Every finite code encodes back to itself from its own value."""
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    vals = orc.dec_e4m3fn(codes).astype(np.float32)
+    assert np.array_equal(orc.enc_e4m3fn(vals), codes)
+
+
+def pin_e4m3fn_encode_ties_and_saturation(orc):
+    """Midpoints between neighbouring codes go to the even code; just off a midpoint goes to the
+    nearer code; magnitudes above 448 saturate to 448 (0x7E / 0xFE)."""
+    pos = orc.dec_e4m3fn(np.arange(0, 0x7F, dtype=np.uint8))
+    for c in range(0, 0x7E):
+        mid = np.float32((pos[c] + pos[c + 1]) / 2)  # exact in fp32
+        want_even = c if c % 2 == 0 else c + 1
+        assert orc.enc_e4m3fn([mid])[0] == want_even, f"tie between {c:#x} and {c + 1:#x}"
+        lo = np.nextafter(mid, np.float32(0))
+        hi = np.nextafter(mid, np.float32(1000))
+        assert orc.enc_e4m3fn([lo])[0] == c and orc.enc_e4m3fn([hi])[0] == c + 1
+    sat = orc.enc_e4m3fn(np.array([448.0, 449.0, 464.0, 480.0, 1e30, -500.0, -1e30], np.float32))
+    assert list(sat) == [0x7E] * 5 + [0xFE] * 2
+    assert orc.enc_e4m3fn([np.float32(-0.0)])[0] == 0x80
+
+
+def pin_e4m3fn_encode_library(orc):
+    """Random fp32 values within +-448 (subnormal fp8 range included) against torch's
+    round-to-nearest-even float8_e4m3fn cast."""
+    rng = np.random.default_rng(3)
+    v = np.concatenate([rng.uniform(-448, 448, 3000), rng.uniform(-0.02, 0.02, 2000),
+                        rng.standard_normal(2000) * 10]).astype(np.float32)
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(orc.enc_e4m3fn(v), ref)
+
+
+def _kv_write_problem(seed=0, T=5, Hkv=3, D=128, BS=16, NB=4):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((2, T, Hkv, D)).astype(np.float32)
+    x[0, 1, 0] *= 1e-6      # a tiny row: codes land in the fp8 subnormal range after scaling
+    x[1, 2, 1] = 0.0        # an all-zero row: scale 0, codes 0
+    x[0, 3, 2, 5] = 300.0   # an outlier
+    bits = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    slots = rng.permutation(NB * BS)[:T].astype(np.int32)
+    slots[4] = -1           # padding token: skipped
+    kc = rng.integers(0, 256, size=(NB, Hkv, BS, D), dtype=np.uint8)
+    vc = rng.integers(0, 256, size=(NB, Hkv, BS, D), dtype=np.uint8)
+    sc = rng.uniform(1, 2, size=(NB, Hkv, 2, BS)).astype(np.float32)
+    return bits[0], bits[1], slots, kc, vc, sc
+
+
+def pin_kv_write_quantizer(orc):
+    """Written rows: scale = fp32(absmax / 448); the max element maps to +-448; every value is
+    within half a code step (RNE); zero rows give scale 0, codes 0; skipped tokens and other
+    slots are untouched."""
+    kn, vn, slots, kc, vc, sc = _kv_write_problem()
+    kc2, vc2, sc2 = orc.kv_write(kn, vn, slots, kc, vc, sc)
+    NB, Hkv, BS, D = kc.shape
+    written = np.zeros((NB, Hkv, BS), dtype=bool)
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = divmod(int(slot), BS)
+        for h in range(Hkv):
+            written[blk, h, off] = True
+            for field, (bits, cache) in enumerate(((kn, kc2), (vn, vc2))):
+                x = torch.from_numpy(bits[t, h].view(np.int16)).view(torch.bfloat16).float().numpy()
+                s = sc2[blk, h, field, off]
+                assert s == np.float32(np.abs(x).max()) / np.float32(448.0)
+                codes = cache[blk, h, off]
+                if s == 0:
+                    assert not codes.any()
+                    continue
+                deq = orc.dec_e4m3fn(codes) * np.float64(s)
+                q = np.abs(x.astype(np.float64) / s)
+                step = np.where(q >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(q, 1e-300))) - 3),
+                                2.0 ** -9)
+                assert np.all(np.abs(deq - x) <= 0.5 * step * s * (1 + 1e-6) + 1e-30)
+                assert np.abs(orc.dec_e4m3fn(codes)).max() == 448.0
+    keep = ~written
+    assert np.array_equal(kc2[keep], kc[keep]) and np.array_equal(vc2[keep], vc[keep])
+    assert np.array_equal(sc2[:, :, 0][keep], sc[:, :, 0][keep])
+    assert np.array_equal(sc2[:, :, 1][keep], sc[:, :, 1][keep])
+
+
+def pin_kv_write_matches_library_quantizer(orc):
+    """The same rows quantized with torch ops (fp32 division, clamp, torch's RNE fp8 cast) give
+    the same codes and scales."""
+    kn, vn, slots, kc, vc, sc = _kv_write_problem(seed=4)
+    kc2, vc2, sc2 = orc.kv_write(kn, vn, slots, kc, vc, sc)
+    BS = kc.shape[2]
+    for t, slot in enumerate(slots):
+        if slot < 0:
+            continue
+        blk, off = divmod(int(slot), BS)
+        for field, (bits, cache) in enumerate(((kn, kc2), (vn, vc2))):
+            x = torch.from_numpy(bits[t].view(np.int16)).view(torch.bfloat16).float()  # [Hkv][D]
+            s = x.abs().amax(dim=-1) / 448.0
+            div = torch.where(s > 0, s, torch.ones_like(s))
+            codes = (x / div[:, None]).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8)
+            codes = torch.where(s[:, None] > 0, codes, torch.zeros_like(codes))
+            assert np.array_equal(cache[blk, :, off], codes.numpy())
+            assert np.array_equal(sc2[blk, :, field, off], s.numpy())
+
+
 ALL_PINS = [pin_e4m3fn_points, pin_e4m3fn_library, pin_bf16_library, pin_dense_bruteforce, pin_sdpa,
             pin_single_token, pin_zero_query, pin_constant_v, pin_two_token_golden,
             pin_block_permutation, pin_split_merge, pin_v_scale_linearity, pin_dominant_token,
-            pin_zero_length]
+            pin_zero_length, pin_e4m3fn_encode_roundtrip, pin_e4m3fn_encode_ties_and_saturation,
+            pin_e4m3fn_encode_library, pin_kv_write_quantizer, pin_kv_write_matches_library_quantizer]

@@ -1,0 +1,71 @@
+"""Both decode paths captured in a HIP graph (through torch's graph capture) and
+replayed: between replays the inputs change in place (new queries, new sequence
+lengths up to the captured max_seq_len) and eager work runs; every replay must
+give the same bits as an eager call on the same inputs.  Needs an MI355X."""
+
+import pytest
+import torch
+
+import paged_gqa_decode_amd as tq
+import workloads
+from gpu_util import say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("path", ["two_kernel", "fused"])
+def test_graph_replay_matches_eager(path):
+    lens0 = (3000, 700, 4096, 1)
+    wl = workloads.small_workload(name="graph", num_seqs=4, num_kv_heads=2, query_group_size=8,
+                                  kv_block_size=32, seq_lens=lens0, seed=31)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens0, num_partitions=16)
+    S, Hkv, QG, BS, G, P = 4, 2, 8, 32, 1, 16
+    maxlen = 4096
+    out = torch.empty((S, Hkv * QG, 128), dtype=torch.bfloat16, device="cuda")
+    part = tq.alloc_partials(S, Hkv, P, QG, "cuda")
+    # a workspace that makes the fused path split every (s, h) over several workgroups
+    ws = torch.zeros(max(tq.fused_workspace_bytes(S, Hkv, QG, maxlen), 256), dtype=torch.uint8,
+                     device="cuda")
+    q = inp.q.clone()
+    seq_lens = inp.seq_lens.clone()
+
+    def step(stream=None):
+        if path == "fused":
+            tq.tq_decode_fused(q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables,
+                               seq_lens, out, Hkv, QG, BS, G, inp.softmax_scale, num_partitions=P,
+                               max_seq_len=maxlen, workspace=ws, stream=stream)
+        else:
+            tq.tq_decode(q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, seq_lens,
+                         part, Hkv, QG, BS, G, inp.softmax_scale, num_partitions=P,
+                         max_seq_len=maxlen, stream=stream)
+            tq.tq_decode_reduce(part, seq_lens, out, Hkv, QG, G, num_partitions=P,
+                                max_seq_len=maxlen, stream=stream)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm up outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say(f"[graph] capture {path}")
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    for rep, lens in enumerate(((3000, 700, 4096, 1), (1, 4096, 17, 2500), (4096, 0, 333, 4000))):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+        torch.cuda.synchronize()
+        say(f"[graph] replay {rep} {path} lens={lens}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        out.fill_(float("nan"))  # eager work between replays
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), out.view(torch.int16)), f"replay {rep} differs"
+        assert torch.isfinite(got.float()).all()
+    if path == "fused":
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "counters must stay re-armed"

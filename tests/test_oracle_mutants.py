@@ -35,6 +35,14 @@ MUTANTS = [
     ("merge_first_partition_only", "for (int p = 0; p < live; ++p) {\n          int64_t r",
      "for (int p = 0; p < 1; ++p) {\n          int64_t r"),
     ("merge_no_division", "for (int d = 0; d < D; ++d) dst[d] /= W;", ""),
+    ("enc_ties_to_odd", "(err == best_err && (c & 1) == 0)", "(err == best_err && (c & 1) == 1)"),
+    ("enc_search_range_short", "for (int c = 0; c <= 0x7E; ++c) {", "for (int c = 0; c < 0x7E; ++c) {"),
+    ("enc_sign_dropped", "(signbit(x) ? 0x80 : 0x00) | best", "best"),
+    ("writer_fnuz_max", "float s = absmax / 448.0f;", "float s = absmax / 240.0f;"),
+    ("writer_offset_wrong", "int blk = slot / BS, off = slot % BS;", "int blk = slot / BS, off = 0;"),
+    ("writer_scale_field_swapped", "kv_scales[(((int64_t)blk * Hkv + h) * 2 + field) * BS + off] = s;",
+     "kv_scales[(((int64_t)blk * Hkv + h) * 2 + (1 - field)) * BS + off] = s;"),
+    ("writer_ignores_skip", "if (slot < 0) continue;", "if (slot < 0) slot = 0;"),
 ]
 
 

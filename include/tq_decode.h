@@ -178,6 +178,30 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
 size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,
                                 int32_t query_group_size);
 
+/*
+ * tq_kv_write -- the KV-cache writer, the step that fills the cache the
+ * decode reads: for each new token t with 0 <= slot_mapping[t] < NB*BS
+ * (slot = block * BS + offset) and each kv head h, the K row and the V row are
+ * quantized on their own,
+ *   s = fp32(absmax / 448),  code_d = e4m3fn(x_d / s)
+ * (fp32 division, round to nearest even, saturating at +-448; an all-zero row
+ * gives s = 0 and codes 0), and stored at k_cache / v_cache[block][h][offset]
+ * with s at kv_scales[block][h][0 or 1][offset].  Other slots are untouched;
+ * a negative slot (padding) or one at or past NB*BS is skipped.  The
+ * per-block scale region follows the fp8 record writer of page
+ * "vllm.models.deepseek_v41.amd.mono.attention.front" (stage_qkv), with this
+ * library's scale rule instead of its power-of-two scale codes.
+ *   k_new, v_new   bf16 [T][Hkv][128], finite values
+ *   slot_mapping   int32 [T]
+ *   k_cache, v_cache, kv_scales   as for tq_decode (written in place)
+ * Tokens that map to the same slot race: the caller must not do that.
+ * Errors as for tq_decode; num_tokens = 0 is a no-op.
+ */
+tq_status tq_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                      uint8_t* k_cache, uint8_t* v_cache, float* kv_scales, int32_t num_tokens,
+                      int32_t num_kv_heads, int32_t kv_block_size, int32_t num_blocks,
+                      int32_t head_dim, void* stream);
+
 /* Bytes of the three partial arrays for these sizes (each rounded up to 256 B),
  * laid out out | max_logits | exp_sums; 0 if the sizes are invalid. */
 size_t tq_partials_bytes(const tq_extent* ext, int32_t num_kv_heads, int32_t query_group_size);

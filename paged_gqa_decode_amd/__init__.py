@@ -34,7 +34,8 @@ TQ_OK, TQ_ERR_NULL, TQ_ERR_MISALIGNED, TQ_ERR_UNSUPPORTED, TQ_ERR_SHAPE, TQ_ERR_
     TQ_ERR_SCALE, TQ_ERR_HIP = range(8)
 
 EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_decode_fused", "tq_fused_workspace_bytes",
-                    "tq_partials_bytes", "tq_status_str", "tq_last_hip_error", "tq_abi_version")
+                    "tq_kv_write", "tq_partials_bytes", "tq_status_str", "tq_last_hip_error",
+                    "tq_abi_version")
 
 
 class TqError(RuntimeError):
@@ -76,6 +77,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq_decode_fused.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float,
                                     ctypes.POINTER(Extent), P, ctypes.c_size_t, P]
     lib.tq_decode_fused.restype = ctypes.c_int
+    lib.tq_kv_write.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
+    lib.tq_kv_write.restype = ctypes.c_int
     lib.tq_fused_workspace_bytes.argtypes = [ctypes.POINTER(Extent), i32, i32]
     lib.tq_fused_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_partials_bytes.argtypes = [ctypes.POINTER(Extent), i32, i32]
@@ -220,6 +223,24 @@ def tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
                              ctypes.byref(ext), ws_ptr, ws_bytes, _stream(stream))
     if st != TQ_OK:
         raise TqError(st, "tq_decode_fused")
+
+
+def tq_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, kv_scales, *, stream=None) -> None:
+    """Enqueue the KV-cache writer (C ABI tq_kv_write): quantize the new bf16 K/V rows
+    [T][Hkv][128] and store them at slot_mapping (int32 [T], negative = skip)."""
+    lib = load_library()
+    T, Hkv, D = k_new.shape
+    NB, Hkv2, BS, D2 = k_cache.shape
+    if v_new.shape != k_new.shape or Hkv2 != Hkv or D2 != D or tuple(slot_mapping.shape) != (T,):
+        raise ValueError("inconsistent shapes")
+    if T == 0:
+        return
+    ptrs = [_dev(t, n) for t, n in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"),
+                                    (k_cache, "k_cache"), (v_cache, "v_cache"),
+                                    (kv_scales, "kv_scales"))]
+    st = lib.tq_kv_write(*ptrs, int(T), int(Hkv), int(BS), int(NB), int(D), _stream(stream))
+    if st != TQ_OK:
+        raise TqError(st, "tq_kv_write")
 
 
 def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partitions=None,

@@ -175,6 +175,34 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
       tq::launch_reduce(a, ext->num_seqs * num_kv_heads, static_cast<hipStream_t>(stream)));
 }
 
+tq_status tq_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                      uint8_t* k_cache, uint8_t* v_cache, float* kv_scales, int32_t num_tokens,
+                      int32_t num_kv_heads, int32_t kv_block_size, int32_t num_blocks,
+                      int32_t head_dim, void* stream) {
+  if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 1) return TQ_ERR_SHAPE;
+  if (head_dim != TQ_HEAD_DIM || !supported_bs(kv_block_size)) return TQ_ERR_UNSUPPORTED;
+  if ((int64_t)num_blocks * kv_block_size > INT32_MAX ||
+      (int64_t)num_tokens * num_kv_heads > INT32_MAX / 2)
+    return TQ_ERR_SHAPE;
+  if (num_tokens == 0) return TQ_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !kv_scales) return TQ_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      !aligned16(kv_scales) || !aligned4(slot_mapping))
+    return TQ_ERR_MISALIGNED;
+  tq::KvWriteArgs a;
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.slot_mapping = slot_mapping;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.scales = kv_scales;
+  a.num_tokens = num_tokens;
+  a.num_kv_heads = num_kv_heads;
+  a.kv_block_size = kv_block_size;
+  a.num_slots = num_blocks * kv_block_size;
+  return hip_status(tq::launch_kv_write(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t tq_partials_bytes(const tq_extent* ext, int32_t num_kv_heads, int32_t query_group_size) {
   if (!ext || ext->head_dim != TQ_HEAD_DIM || !supported_qg(query_group_size)) return 0;
   if (ext->num_seqs < 1 || num_kv_heads < 1 || ext->num_partitions < 1) return 0;

@@ -75,6 +75,19 @@ struct ReduceArgs {
   int32_t len_cap;
 };
 
+struct KvWriteArgs {
+  const uint16_t* k_new;        // bf16 [T][Hkv][128]
+  const uint16_t* v_new;        // bf16 [T][Hkv][128]
+  const int32_t* slot_mapping;  // [T]: block * BS + offset, negative = skip
+  uint8_t* k;                   // e4m3fn [NB][Hkv][BS][128]
+  uint8_t* v;
+  float* scales;                // fp32 [NB][Hkv][2][BS]
+  int32_t num_tokens;
+  int32_t num_kv_heads;
+  int32_t kv_block_size;
+  int32_t num_slots;            // NB * BS: slots at or past it are skipped
+};
+
 // Enqueue the kernels; each returns the launch status (hipGetLastError after
 // the launch).  launch_partition chooses parts_per_wave and launch_fused the
 // waves per workgroup from the sizes.
@@ -83,5 +96,6 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
 hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_group_size,
                         int kv_block_size, hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream);
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 
 }  // namespace tq

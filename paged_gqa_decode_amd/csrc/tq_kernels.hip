@@ -650,6 +650,48 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(ReduceArgs a) {
   }
 }
 
+// KV-cache writer: one wave per (new token t, kv head h).  Lane l holds
+// dims 2l, 2l+1 of the K row and of the V row; each row is quantized on its
+// own: s = absmax / 448, codes = e4m3fn(x / s) (IEEE fp32 division, round to
+// nearest even, clamped to +-448 so the convert never overflows), all-zero
+// rows get s = 0 and codes 0.  The 128 codes of a row go out as one 128-byte
+// store across the wave; lanes 0 and 1 write the K and V scales.  A slot
+// outside [0, NB*BS) is skipped (negative: padding by convention).
+__global__ __launch_bounds__(256) void tq_kv_write_kernel(KvWriteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (t, h)
+  if (row >= (int64_t)a.num_tokens * a.num_kv_heads) return;
+  const int Hkv = a.num_kv_heads;
+  const int t = (int)(row / Hkv);
+  const int h = (int)(row % Hkv);
+  const int slot = a.slot_mapping[t];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int BS = a.kv_block_size;
+  const int blk = slot / BS;
+  const int off = slot % BS;
+  const size_t src = (size_t)row * D + 2 * lane;
+  const size_t dst = (((size_t)blk * Hkv + h) * BS + off) * D + 2 * lane;
+#pragma unroll
+  for (int field = 0; field < 2; ++field) {
+    const uint32_t pair = *reinterpret_cast<const uint32_t*>((field == 0 ? a.k_new : a.v_new) + src);
+    const float x0 = __uint_as_float(pair << 16);
+    const float x1 = __uint_as_float(pair & 0xffff0000u);
+    float amax = fmaxf(fabsf(x0), fabsf(x1));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float scale = amax / 448.0f;
+    uint32_t codes = 0;
+    if (scale > 0.f) {
+      const float q0 = fminf(fmaxf(x0 / scale, -448.0f), 448.0f);
+      const float q1 = fminf(fmaxf(x1 / scale, -448.0f), 448.0f);
+      codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xffffu;
+    }
+    *reinterpret_cast<uint16_t*>((field == 0 ? a.k : a.v) + dst) = (uint16_t)codes;
+    if (lane == 0)
+      a.scales[(((size_t)blk * Hkv + h) * 2 + field) * BS + off] = scale;
+  }
+}
+
 }  // namespace
 
 int choose_parts_per_wave(int64_t units, int num_partitions) {
@@ -752,6 +794,13 @@ hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_g
   if (query_group_size == 16 && kv_block_size == 16) return launch_fused_t<16, 16>(a, grid, waves, stream);
   if (query_group_size == 16 && kv_block_size == 32) return launch_fused_t<16, 32>(a, grid, waves, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
+  const int64_t rows = (int64_t)a.num_tokens * a.num_kv_heads;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(tq_kv_write_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream) {

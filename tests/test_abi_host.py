@@ -205,3 +205,28 @@ def test_product_path_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "oracle.c" not in text and "liboracle" not in text, f
+
+
+def call_kv_write(lib, *, ptrs=None, T=4, Hkv=2, BS=16, NB=8, D=128):
+    ptrs = ptrs or [A] * 6
+    return lib.tq_kv_write(*ptrs, T, Hkv, BS, NB, D, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(T=-1), tq.TQ_ERR_SHAPE),
+    (dict(Hkv=0), tq.TQ_ERR_SHAPE),
+    (dict(NB=0), tq.TQ_ERR_SHAPE),
+    (dict(NB=1 << 30, BS=32), tq.TQ_ERR_SHAPE),
+    (dict(BS=8), tq.TQ_ERR_UNSUPPORTED),
+    (dict(D=64), tq.TQ_ERR_UNSUPPORTED),
+    (dict(ptrs=[A, A, 0, A, A, A]), tq.TQ_ERR_NULL),
+    (dict(ptrs=[A + 4, A, A, A, A, A]), tq.TQ_ERR_MISALIGNED),
+    (dict(ptrs=[A, A, A, A, A, A + 8]), tq.TQ_ERR_MISALIGNED),
+    (dict(ptrs=[A, A, A + 2, A, A, A]), tq.TQ_ERR_MISALIGNED),
+])
+def test_kv_write_rejects(lib, kw, status):
+    assert call_kv_write(lib, **kw) == status
+
+
+def test_kv_write_zero_tokens_is_a_noop(lib):
+    assert call_kv_write(lib, ptrs=[0] * 6, T=0) == tq.TQ_OK

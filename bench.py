@@ -18,6 +18,7 @@ stderr.
                 measured the same way over K whole steps)
   hbm_probe     best read and copy bandwidth of plain streaming kernels
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
+  kv_writer     tq_kv_write on 16384 new tokens scattered into the same pool
 """
 
 from __future__ import annotations
@@ -337,6 +338,24 @@ def main() -> int:
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     else:
         res["cpu_baseline"] = None
+
+    # The KV-cache writer (the step that fills the cache): a prefill-sized batch of new
+    # tokens scattered into random slots of the same pool; bytes per (token, kv head) row =
+    # 512 read (bf16 K and V) + 264 written (fp8 codes and two fp32 scales).
+    T = 16384
+    gen = torch.Generator(device=dev).manual_seed(wl.seed + 7)
+    k_new = torch.randn((T, Hkv, 128), generator=gen, device=dev).to(torch.bfloat16)
+    v_new = torch.randn((T, Hkv, 128), generator=gen, device=dev).to(torch.bfloat16)
+    slots = torch.randperm(inp.num_blocks * wl.kv_block_size, generator=gen, device=dev)[:T]
+    slots = slots.to(torch.int32)
+    write = lambda: tq.tq_kv_write(k_new, v_new, slots, inp.k_cache, inp.v_cache,  # noqa: E731
+                                   inp.kv_scales, stream=stream)
+    w_ms = timed(write)
+    w_bytes = T * Hkv * (512 + 264)
+    res["kv_writer"] = {"tokens": T, "num_kv_heads": Hkv, "us": round(w_ms * 1e3, 2),
+                        "GBps": round(w_bytes / (w_ms * 1e-3) / 1e9, 1), "bytes_per_launch": w_bytes}
+    log(f"[bench] kv writer: {T} tokens x {Hkv} heads in {w_ms * 1e3:.1f} us "
+        f"({res['kv_writer']['GBps']} GB/s)")
     print(json.dumps(res), flush=True)
     return 0
 

@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 KV_BYTES_PER_TOKEN_HEAD = 2 * 128 + 8
 METRIC = "KV-cache GB/s achieved (% of MI355X HBM peak); decode attn µs per step"
 KERNEL_SOURCE = os.path.join(ROOT, "paged_gqa_decode_amd", "csrc", "tq_kernels.hip")
-KERNEL_NAMES = {"two_kernel": "tq_partition_kernel", "fused": "tq_fused_kernel"}
+KERNEL_NAMES = {"two_kernel": "tq_partition_kernel", "fused": "tq_flat_kernel"}
 
 
 def log(*a):
@@ -128,7 +128,8 @@ def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10)
             "copy_gbs": round(cp[0], 1), "copy_workgroups": cp[1]}
 
 
-PROFILE_KERNELS = ("tq_fused_kernel", "tq_partition_kernel", "tq_merge_kernel")
+PROFILE_KERNELS = ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel", "tq_merge_kernel",
+                   "tq_kv_write_kernel")
 PROFILE_CMD = ("rocprofv3 {what} -T -d <dir>/{sub} -o {sub} --output-format csv -- "
                "python3 bench.py --workload {wl} --steps 20 --warmup 3 --no-cpu-baseline")
 
@@ -180,7 +181,7 @@ def summarize_rocprof(prof_dir: str, workload: str) -> None:
                      f"{fetch.get(name, float('nan')):.0f} | {write.get(name, float('nan')):.0f} |")
     lines += ["", f"Counter calibration with the 1 GiB copy probe: bytes = FETCH_SIZE x 1024 x "
               f"{f_scale:.4f}, WRITE_SIZE x 1024 x {w_scale:.4f}.", ""]
-    for name in ("tq_fused_kernel", "tq_partition_kernel"):
+    for name in ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel"):
         if name not in fetch or name not in write:
             continue
         fb = fetch[name] * 1024.0 * f_scale

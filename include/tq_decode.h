@@ -139,30 +139,36 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
 
 /*
  * tq_decode_fused -- the whole decode step in one launch, bf16 out directly.
- * Each (sequence s, kv head h) gets one or more workgroups; its cached
- * tokens, in tile groups of 256, are dealt in contiguous runs to the
- * workgroups and, inside a workgroup, to its waves.  Each wave keeps one
- * online softmax over its run; a workgroup merges its waves' partial results
- * (o, m, l, as in STEP G of tq_decode_kernel) by log-sum-exp in LDS with the
- * formula of tq_decode_reduce.  When an (s, h) has work for several
- * workgroups, each writes its merged partial to `workspace`, and the last one
- * to finish merges them all in workgroup order and writes out: the in-launch
- * merge across partitions that the page's partial triple implies, with no
- * second launch and no partial round trip through a separate kernel.
+ * Work is split into tile groups of 256 tokens, the unit of work of the page's
+ * kernel.  With a large enough workspace (tq_fused_workspace_bytes) and at
+ * most 256 sequences, the live tile groups of all (sequence s, kv head h)
+ * pairs form one list in (s, h, tile group) order, dealt evenly to the waves
+ * of one resident round of workgroups (8 waves each): every wave streams the
+ * same number of tile groups to within one, however ragged the lengths.  Each
+ * wave keeps one online softmax per (s, h) it touches; the partial results (o,
+ * m, l, as in STEP G of tq_decode_kernel) of an (s, h) split across waves are
+ * merged by log-sum-exp with the formula of tq_decode_reduce, first in LDS
+ * among the waves of a workgroup, then, for an (s, h) split across
+ * workgroups, through `workspace`: the last workgroup to finish merges them in
+ * workgroup order and writes out.  This is the in-launch merge across
+ * partitions that the page's partial triple implies, with no second launch.
+ * Without a workspace (or with more than 256 sequences, or too few bytes)
+ * each (s, h) gets its own workgroups instead, its tile groups dealt in
+ * contiguous runs to them, with the same merges.
  *   out        bf16 [S][Hkv*QG][128], fully overwritten (L_s = 0 gives zeros)
  *   workspace  NULL, or device memory of workspace_bytes bytes, 16-byte
- *              aligned; its first tq_fused_workspace_bytes-sized use needs it
- *              ZERO-FILLED once (it holds arrival counters that every call
- *              leaves at zero again).  With NULL or too few bytes for the
- *              preferred split, fewer workgroups per (s, h) are used (down to
- *              one, which needs no workspace).  Calls that run concurrently
- *              must not share a workspace.
+ *              aligned; ZERO-FILLED before its first use (it holds arrival
+ *              counters that every call leaves at zero again).  Calls that run
+ *              concurrently must not share a workspace.
  * tile_groups_per_partition and ext->num_partitions bound the context as for
- * tq_decode (coverage check); the split itself is the library's choice,
- * deterministic for given sizes and workspace_bytes, so repeated calls are
- * bit-identical.  With one tile group of context (L <= 256) the output is
- * bit-identical to tq_decode + tq_decode_reduce; otherwise the two paths
- * differ only by rounding.  Other arguments and errors are those of tq_decode.
+ * tq_decode (coverage check); the split itself is the library's choice: a
+ * function of the sizes, ext->max_seq_len, workspace_bytes and the device-side
+ * lengths, so repeated calls are bit-identical, and one launch serves any
+ * lengths up to ext->max_seq_len (a captured graph may be replayed with new
+ * lengths).  An (s, h) with one tile group of context (L <= 256) is computed
+ * by one wave, bit-identical to tq_decode + tq_decode_reduce; otherwise the
+ * two paths differ only by rounding.  Other arguments and errors are those of
+ * tq_decode.
  */
 tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
                           const float* kv_scales, const int32_t* block_tables,
@@ -172,9 +178,10 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
                           const tq_extent* ext, void* workspace, size_t workspace_bytes,
                           void* stream);
 
-/* Workspace bytes tq_decode_fused can use for these sizes (0: it would use
- * one workgroup per (s, h) and needs none).  Depends on num_seqs,
- * max_seq_len, num_kv_heads and query_group_size. */
+/* Workspace bytes for the fastest split of tq_decode_fused at these sizes (0:
+ * it needs none).  Depends on num_seqs, max_seq_len, num_kv_heads and
+ * query_group_size: with the even split, 256 B-rounded arrival counters (4 B per
+ * (s, h)) and two partial slots per workgroup (QG*520 B each). */
 size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,
                                 int32_t query_group_size);
 

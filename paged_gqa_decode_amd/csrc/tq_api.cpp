@@ -125,6 +125,20 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
   if (st != TQ_OK) return st;
   if (!aligned16(out) || (workspace && !aligned16(workspace))) return TQ_ERR_MISALIGNED;
   const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
+  const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
+  if (flat_groups > 0 && workspace &&
+      workspace_bytes >= tq::flat_workspace_bytes(seq_heads, flat_groups, query_group_size)) {
+    tq::FlatArgs f;
+    f.st = a.st;
+    f.seq_lens = seq_lens;
+    f.out = static_cast<uint16_t*>(out);
+    f.len_cap = ext->max_seq_len;
+    f.num_seqs = ext->num_seqs;
+    f.n_groups = flat_groups;
+    tq::bind_flat_workspace(&f, workspace, seq_heads, query_group_size);
+    return hip_status(tq::launch_flat(f, query_group_size, kv_block_size,
+                                      static_cast<hipStream_t>(stream)));
+  }
   const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size,
                                             workspace ? workspace_bytes : 0);
   a.seq_lens = seq_lens;
@@ -144,6 +158,8 @@ size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,
       ext->max_seq_len < 0)
     return 0;
   const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
+  const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
+  if (flat_groups > 0) return tq::flat_workspace_bytes(seq_heads, flat_groups, query_group_size);
   const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size, SIZE_MAX);
   return tq::fused_workspace_bytes(seq_heads, plan.splits, query_group_size);
 }

@@ -62,6 +62,29 @@ size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size
 // Carve the workspace for `splits` into the pointers of `a`.
 void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size);
 
+// Fused decode over one flat work list (the live tile groups of every (s, h)
+// in (s, h, tile group) order) dealt evenly to the waves of n_groups
+// workgroups of 8 waves.
+struct FlatArgs {
+  StreamArgs st;
+  const int32_t* seq_lens;  // int32 [S]
+  uint16_t* out;            // bf16 [S][Hkv*QG][128]
+  int32_t len_cap;
+  int32_t num_seqs;
+  int32_t n_groups;         // the grid
+  int32_t* counters;        // [S*Hkv] arrival counters: 0 on entry, re-armed to 0
+  float* ws_o;              // [2*n_groups][QG][128] workgroup partials: slot 2g = workgroup
+                            // g's first (s, h), 2g+1 = its last
+  float* ws_m;              // [2*n_groups][QG]
+  float* ws_l;              // [2*n_groups][QG]
+};
+
+// Workgroups of the flat plan for these sizes (0: the flat kernel does not
+// apply), the workspace bytes it needs, and the carving of that workspace.
+int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len);
+size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size);
+void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size);
+
 struct ReduceArgs {
   const float* o;
   const float* ml;
@@ -95,6 +118,8 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
                             int kv_block_size, hipStream_t stream);
 hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_group_size,
                         int kv_block_size, hipStream_t stream);
+hipError_t launch_flat(const FlatArgs& a, int query_group_size, int kv_block_size,
+                       hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
 

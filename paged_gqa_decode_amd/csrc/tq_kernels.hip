@@ -574,6 +574,386 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   }
 }
 
+// Fused decode over a flat work list, dealt evenly.  The live tile groups (256
+// tokens) of all (s, h) form one list in (s, h, tile group) order, T entries
+// long.  The grid's G workgroups of W waves hold N = G*W waves, of which the
+// first Nu = min(N, T) take consecutive ranges of q = T / Nu entries, the
+// first T % Nu of them one more: every wave streams the same number of tile
+// groups, to within one, however ragged the lengths are.  Workgroup g holds
+// the waves g*W .. g*W+W-1.
+// A wave's range is cut into segments at (s, h) boundaries; each segment gets
+// one online softmax.  A segment that holds a whole (s, h) is finished by its
+// wave, which writes bf16 out.  Any other segment is a piece: only a wave's
+// first or last segment can be one.  The wave stores a piece's partial (o, m,
+// l) in its LDS area (first piece: a slot of its own; last piece: its staging
+// area, free once the stream is done).  After a barrier the workgroup merges
+// the pieces of each (s, h) it holds, in wave order.  If the (s, h) lies
+// inside the workgroup's range, that merge writes out.  Otherwise (only the
+// workgroup's first or last (s, h) can reach outside) the merged partial goes
+// to workspace slot 2g (the workgroup's first (s, h)) or 2g+1 (its last),
+// released at device scope, and the workgroup counts itself in on the (s, h)'s
+// counter; the last arrival merges the partials of workgroups g_first ..
+// g_last in workgroup order (so the result does not depend on arrival order),
+// writes out and re-arms the counter to 0.  The list and all its indices
+// follow from the device-side lengths and the grid alone.  Zero-length
+// sequences are not in the list: workgroup g zeroes the rows of sequences g,
+// g+G, ... that have none.
+constexpr int kFlatSlices = 4;                 // sequences per lane in the length scan
+constexpr int kFlatMaxSeqs = 64 * kFlatSlices;
+constexpr int kFlatWaves = 8;       // waves per workgroup
+
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: shifts by 1, 2, 4, 8
+// within each 16-lane row, then row 0's and row 2's last lane added to rows 1
+// and 3 (row_bcast:15) and lane 31 added to rows 2 and 3 (row_bcast:31).
+// Lanes whose source is outside the row, or whose row is masked off, add 0.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
+// Log-sum-exp merge of n <= NMAX partials (the formula of lse_merge4) with
+// every load issued up front, so the loads take one round trip.
+constexpr int kFlatMergeRegs = 16;
+template <int NMAX, typename LdO, typename LdM, typename LdL>
+__device__ __forceinline__ f32x4 lse_merge4_regs(int n, LdO ld_o, LdM ld_m, LdL ld_l,
+                                                 float* m_out = nullptr, float* l_out = nullptr) {
+  if (n == 1) {  // a single partial is returned as is
+    if (m_out) *m_out = ld_m(0);
+    if (l_out) *l_out = ld_l(0);
+    return ld_o(0);
+  }
+  float mj[NMAX], lj[NMAX];
+  f32x4 oj[NMAX];
+#pragma unroll
+  for (int j = 0; j < NMAX; ++j) {
+    if (j < n) {
+      mj[j] = ld_m(j);
+      lj[j] = ld_l(j);
+      oj[j] = ld_o(j);
+    }
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int j = 0; j < NMAX; ++j)
+    if (j < n) M = fmaxf(M, mj[j]);
+  float Wsum = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NMAX; ++j) {
+    if (j < n) {
+      const float wt = lj[j] * __expf(mj[j] - M);
+      Wsum += wt;
+      o += wt * oj[j];
+    }
+  }
+  if (m_out) *m_out = M;
+  if (l_out) *l_out = Wsum;
+  return o * (1.0f / Wsum);
+}
+
+template <int QG>
+struct FlatLayout {
+  // A partial in LDS or the workspace: o [QG][128], then m [16] and l [16].
+  static constexpr int kPieceFloats = QG * D + 32;
+  // Per-wave LDS: the staging area (which also holds the last piece), then the
+  // first piece.
+  static constexpr int kArea = kWaveLds + kPieceFloats * 4;
+  static_assert(kPieceFloats * 4 <= kWaveLds, "the last piece must fit the staging area");
+};
+
+// Store the wave's finished partial (rows r < QG) at piece P.
+template <int QG>
+__device__ __forceinline__ void store_piece(float* P, const f32x4 o[8], float m, float l) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, b = lane >> 4;
+  if (r < QG) {
+#pragma unroll
+    for (int dblk = 0; dblk < 8; ++dblk)
+      *reinterpret_cast<f32x4*>(P + r * D + 16 * dblk + 4 * b) = o[dblk];
+    if (b == 0) {
+      P[QG * D + r] = m;
+      P[QG * D + 16 + r] = l;
+    }
+  }
+}
+
+template <int QG, int BS>
+__global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
+  using Lay = FlatLayout<QG>;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  __shared__ int piece_sh[2 * kFlatWaves];        // s*Hkv+h of wave v's first (2v) / last
+                                                  // (2v+1) piece, -1: none
+  __shared__ int piece_ea[2 * kFlatWaves];        // list offset of that (s, h)'s first entry
+  __shared__ int piece_n[2 * kFlatWaves];         // its tile groups
+  __shared__ int arrived_last[2];
+  constexpr int TG = kTokensPerTileGroup;
+  constexpr int kItems = QG * (D / 4);  // (row, 4 columns) items of one merge, <= blockDim
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int W = blockDim.x >> 6;
+  const int S = a.num_seqs;
+  const int Hkv = a.st.num_kv_heads;
+  const int G = gridDim.x;
+  const int g = blockIdx.x;
+  auto len_of = [&](int s) { return clamp_len(a.seq_lens[s], a.len_cap); };
+
+  // Tile groups per kv head, per wave in registers: lane l holds the clamped
+  // lengths of sequences s = l + 64 i (i < k <= 4); per slice i an inclusive
+  // scan over the lanes gives the list offsets within the slice.
+  const int k = (S + 63) >> 6;
+  int len_r[kFlatSlices], incl_r[kFlatSlices], slice_total[kFlatSlices];
+  int total = 0;
+  // All loads first (in bounds, unconditional), so they share one wait.
+#pragma unroll
+  for (int i = 0; i < kFlatSlices; ++i) len_r[i] = a.seq_lens[min(lane + 64 * i, S - 1)];
+#pragma unroll
+  for (int i = 0; i < kFlatSlices; ++i) {
+    len_r[i] = (i < k && lane + 64 * i < S) ? clamp_len(len_r[i], a.len_cap) : 0;
+    incl_r[i] = 0;
+    slice_total[i] = 0;
+    if (i < k) {
+      incl_r[i] = wave_inclusive_scan((len_r[i] + TG - 1) / TG);
+      slice_total[i] = __builtin_amdgcn_readlane(incl_r[i], 63);
+      total += slice_total[i];
+    }
+  }
+  const int T = total * Hkv;
+
+  // Zero the rows of empty sequences g, g + G, ...
+  for (int s = g; s < S; s += G) {
+    int Ls = 0;
+#pragma unroll
+    for (int i = 0; i < kFlatSlices; ++i)
+      if (i == (s >> 6)) Ls = __builtin_amdgcn_readlane(len_r[i], s & 63);
+    if (Ls == 0) {
+      uint16_t* o = a.out + (size_t)s * Hkv * QG * D;
+      for (int idx = threadIdx.x; idx < Hkv * QG * (D / 4); idx += blockDim.x)
+        *reinterpret_cast<uint2*>(o + 4 * idx) = make_uint2(0u, 0u);
+    }
+  }
+
+  // Nu = min(N, T) waves in use; wave x takes q or q + 1 entries: the first
+  // `rem` waves one more.
+  const int Nw = G * W;
+  const int Nu = T < Nw ? T : Nw;
+  const int gw0 = g * W;
+  if (gw0 >= Nu) return;  // uniform over the workgroup (T = 0 included)
+  const int Wu = Nu - gw0 < W ? Nu - gw0 : W;
+  const int q = T / Nu, rem = T - q * Nu;
+  auto entry_of = [&](int x) { return x * q + (x < rem ? x : rem); };  // first entry of wave x
+  auto wave_of = [&](int e) {                                           // wave holding entry e
+    const int big = rem * (q + 1);
+    return e < big ? e / (q + 1) : rem + (e - big) / q;
+  };
+  const int wg_begin = entry_of(gw0);
+  const int wg_end = entry_of(gw0 + Wu);
+  const int gw = gw0 + (wave < Wu ? wave : Wu - 1);
+  const int A = entry_of(gw);
+  const int B = entry_of(gw + 1);
+  // Locate entry A: its slice, then the first lane of the slice whose
+  // sequences reach past it.  base = list offset of (s, h = 0).
+  int s = S - 1, L = 0, n = 0, base = 0;
+  {
+    int sb = 0;
+#pragma unroll
+    for (int i = 0; i < kFlatSlices; ++i) {
+      if (i < k && A >= sb * Hkv && A < (sb + slice_total[i]) * Hkv) {
+        const int ln = __builtin_ctzll(__ballot((sb + incl_r[i]) * Hkv > A));
+        L = __builtin_amdgcn_readlane(len_r[i], ln);
+        n = (L + TG - 1) / TG;
+        s = 64 * i + ln;
+        base = (sb + __builtin_amdgcn_readlane(incl_r[i], ln) - n) * Hkv;
+      }
+      sb += slice_total[i];
+    }
+  }
+
+  uint8_t* area = lds_dyn + wave * Lay::kArea;
+  float* last_piece = reinterpret_cast<float*>(area);
+  float* first_piece = reinterpret_cast<float*>(area + kWaveLds);
+  int f_sh = -1, l_sh = -1, f_n = 0, l_n = 0;
+  int f_ea = 0, l_ea = 0;
+  if (wave < Wu) {  // uniform over the wave
+    int h = n > 0 ? (A - base) / n : Hkv;
+    int k0 = n > 0 ? (A - base) - h * n : 0;
+    int pos = A;
+    bool first_seg = true;
+    while (h < Hkv) {  // h >= Hkv only if the lengths changed under the kernel
+      const int k1 = min(n, k0 + (B - pos));
+      const int sh = s * Hkv + h;
+      WaveState st;
+      st.reset();
+      stream_tokens<QG, BS>(a.st, s, h, k0 * TG, min(k1 * TG, L), 0x7fffffff, area,
+                            reinterpret_cast<float*>(area + 2 * CHUNK * D), st,
+                            [](int, WaveState&) {});
+      f32x4 o[8];
+      const float l = st.finish(o);
+      if (k0 == 0 && k1 == n) {  // the whole (s, h)
+        const int r = lane & 15, b = lane >> 4;
+        if (r < QG) {
+          uint16_t* dst = a.out + ((size_t)sh * QG + r) * D + 4 * b;
+#pragma unroll
+          for (int dblk = 0; dblk < 8; ++dblk) store_bf16x4(dst + 16 * dblk, o[dblk]);
+        }
+      } else if (first_seg) {
+        store_piece<QG>(first_piece, o, st.m2 * kLn2, l);
+        f_sh = sh;
+        f_ea = base + h * n;
+        f_n = n;
+      } else {  // a piece that is not the first is the wave's last segment
+        store_piece<QG>(last_piece, o, st.m2 * kLn2, l);
+        l_sh = sh;
+        l_ea = base + h * n;
+        l_n = n;
+      }
+      pos += k1 - k0;
+      if (pos >= B) break;
+      // Next (s, h) of the list: the next kv head, or the next non-empty sequence.
+      first_seg = false;
+      k0 = 0;
+      if (++h == Hkv) {
+        h = 0;
+        base += n * Hkv;
+        do {
+          if (++s >= S) {
+            h = Hkv;
+            break;
+          }
+          L = len_of(s);
+          n = (L + TG - 1) / TG;
+        } while (n == 0);
+      }
+    }
+  }
+  if (lane == 0) {
+    piece_sh[2 * wave] = f_sh;
+    piece_ea[2 * wave] = f_ea;
+    piece_n[2 * wave] = f_n;
+    piece_sh[2 * wave + 1] = l_sh;
+    piece_ea[2 * wave + 1] = l_ea;
+    piece_n[2 * wave + 1] = l_n;
+  }
+  __syncthreads();
+
+  // Merge the pieces of each (s, h) this workgroup holds.  Piece p = 2v + which
+  // is wave v's first (which = 0) or last piece.  The pieces of one (s, h) are
+  // consecutive: piece p0 = 2v0 + w0, then the first pieces of waves v0+1 ..
+  // v1.  Every wave finds the runs alike, lane p reading piece p.  At most two
+  // of these (s, h) reach outside the workgroup.
+  auto piece = [&](int v, int which) -> const float* {
+    return reinterpret_cast<const float*>(lds_dyn + v * Lay::kArea + (which == 0 ? kWaveLds : 0));
+  };
+  const int t = threadIdx.x;
+  const int item_g = t / (D / 4);
+  const int item_col = 4 * (t % (D / 4));
+  int ext_sh[2] = {-1, -1};
+  int ext_ea[2] = {0, 0};
+  int ext_n[2] = {0, 0};
+  // A wave's last piece always begins a run; its first piece continues the
+  // previous wave's last one exactly when the (s, h) began before the wave's
+  // range (piece_ea < the wave's first entry), except in the first wave.
+  const int my_sh = lane < 2 * Wu ? piece_sh[lane] : -1;
+  const int my_ea = lane < 2 * Wu ? piece_ea[lane] : 0;
+  const int my_n = lane < 2 * Wu ? piece_n[lane] : 0;
+  const bool cont = (lane & 1) == 0 && lane > 0 && my_ea < entry_of(gw0 + (lane >> 1));
+  const uint64_t have = __ballot(my_sh >= 0);
+  uint64_t starts = __ballot(my_sh >= 0 && !cont);
+  while (starts) {
+    const int p0 = __builtin_ctzll(starts);
+    starts &= starts - 1;
+    const uint64_t before_next = starts ? (1ull << __builtin_ctzll(starts)) - 1 : ~0ull;
+    const int p1 = 63 - __builtin_clzll(have & before_next);
+    const int v = p0 >> 1, which = p0 & 1, v1 = p1 >> 1;
+    const int sh = __builtin_amdgcn_readlane(my_sh, p0);
+    const int ea = __builtin_amdgcn_readlane(my_ea, p0);
+    const int n = __builtin_amdgcn_readlane(my_n, p0);
+    const bool inside = ea >= wg_begin && ea + n <= wg_end;
+    const int slot = ea <= wg_begin ? 0 : 1;
+    if (t < kItems) {
+      // Piece j of the run: p0's area for j = 0, else wave v + j's first piece.
+      const float* first = piece(v, which);
+      const float* rest = piece(v, 0);
+      auto at = [&](int j) { return j == 0 ? first : rest + j * (Lay::kArea / 4); };
+      float m, l;
+      const f32x4 o = lse_merge4_regs<kFlatWaves>(
+          v1 - v + 1,
+          [&](int j) { return *reinterpret_cast<const f32x4*>(at(j) + item_g * D + item_col); },
+          [&](int j) { return at(j)[QG * D + item_g]; },
+          [&](int j) { return at(j)[QG * D + 16 + item_g]; }, &m, &l);
+      if (inside) {
+        store_bf16x4(a.out + ((size_t)sh * QG + item_g) * D + item_col, o);
+      } else {
+        const size_t rec = 2 * (size_t)g + slot;
+        float* dst = a.ws_o + (rec * QG + item_g) * D + item_col;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) st_coherent(dst + i, o[i]);
+        if (item_col == 0) {
+          st_coherent(a.ws_m + rec * QG + item_g, m);
+          st_coherent(a.ws_l + rec * QG + item_g, l);
+        }
+      }
+    }
+    if (!inside) {
+      ext_sh[slot] = sh;
+      ext_ea[slot] = ea;
+      ext_n[slot] = n;
+    }
+  }
+  if (ext_sh[0] < 0 && ext_sh[1] < 0) return;
+
+  // Release: every thread's coherent stores complete before the barrier, and
+  // only then does the workgroup count itself in.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  int count[2] = {0, 0}, g_first[2] = {0, 0}, first_slot[2] = {0, 0};
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if (ext_sh[x] < 0) continue;
+    const int ea = ext_ea[x], eb = ea + ext_n[x];
+    // The waves holding its first and last entries, clamped into the grid so
+    // that lengths changed under the kernel cannot index past the workspace.
+    const int wf = min(max(wave_of(ea), 0), Nu - 1);
+    const int wl = min(max(wave_of(eb - 1), 0), Nu - 1);
+    g_first[x] = wf / W;
+    count[x] = max(wl / W - g_first[x] + 1, 0);
+    first_slot[x] = entry_of(g_first[x] * W) == ea ? 0 : 1;
+    if (t == 0)
+      arrived_last[x] = __hip_atomic_fetch_add(a.counters + ext_sh[x], 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT) == count[x] - 1;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    if (ext_sh[x] < 0 || !arrived_last[x]) continue;
+    if (t == 0)  // re-arm for the next call; every workgroup of this launch is in
+      __hip_atomic_store(a.counters + ext_sh[x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t < kItems) {
+      const int gf = g_first[x], fs = first_slot[x];
+      auto rec = [&](int j) -> size_t { return 2 * (size_t)(gf + j) + (j == 0 ? fs : 0); };
+      auto ld_o = [&](int j) {
+        const float* src = a.ws_o + (rec(j) * QG + item_g) * D + item_col;
+        return f32x4{ld_coherent(src), ld_coherent(src + 1), ld_coherent(src + 2),
+                     ld_coherent(src + 3)};
+      };
+      auto ld_m = [&](int j) { return ld_coherent(a.ws_m + rec(j) * QG + item_g); };
+      auto ld_l = [&](int j) { return ld_coherent(a.ws_l + rec(j) * QG + item_g); };
+      f32x4 o;
+      if (count[x] <= kFlatMergeRegs) {
+        o = lse_merge4_regs<kFlatMergeRegs>(count[x], ld_o, ld_m, ld_l);
+      } else {
+        float m, l;
+        o = lse_merge4(count[x], ld_o, ld_m, ld_l, &m, &l);
+      }
+      store_bf16x4(a.out + ((size_t)ext_sh[x] * QG + item_g) * D + item_col, o);
+    }
+  }
+}
+
 // Merge of the split-K partials: one 256-thread block per (sequence, kv
 // head).  Each wave takes query rows g = wave, wave + 4, ...; its lanes read
 // the live partitions' max logits and exp sums, reduce M = max m_p and
@@ -745,6 +1125,65 @@ FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, s
   while (splits > 1 && fused_workspace_bytes(seq_heads, (int)splits, query_group_size) > ws_bytes) --splits;
   plan.splits = (int)splits;
   return plan;
+}
+
+int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len) {
+  // One resident round at two waves per SIMD (256 workgroups of 8 waves, one
+  // per CU), or fewer when the list cannot fill them: at most one wave per tile
+  // group.
+  constexpr int64_t kFlatGroups = 256;
+  static_assert(kFlatGroups * kFlatWaves <= 65536, "waves per launch");
+  if (num_seqs < 1 || num_seqs > kFlatMaxSeqs || num_kv_heads < 1 || max_seq_len <= 0) return 0;
+  const int64_t n_tg = (max_seq_len + kTokensPerTileGroup - 1) / kTokensPerTileGroup;
+  const int64_t t_max = num_seqs * num_kv_heads * n_tg;
+  if (t_max > (int64_t(1) << 30)) return 0;
+  const int64_t groups = (t_max + kFlatWaves - 1) / kFlatWaves;
+  return (int)(groups < kFlatGroups ? groups : kFlatGroups);
+}
+
+size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size) {
+  const size_t rows = (size_t)2 * n_groups * query_group_size;
+  return round256((size_t)seq_heads * 4) + round256(rows * D * 4) + 2 * round256(rows * 4);
+}
+
+void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size) {
+  const size_t rows = (size_t)2 * a->n_groups * query_group_size;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  a->counters = reinterpret_cast<int32_t*>(p);
+  p += round256((size_t)seq_heads * 4);
+  a->ws_o = reinterpret_cast<float*>(p);
+  p += round256(rows * D * 4);
+  a->ws_m = reinterpret_cast<float*>(p);
+  p += round256(rows * 4);
+  a->ws_l = reinterpret_cast<float*>(p);
+}
+
+template <int QG, int BS>
+hipError_t launch_flat_t(const FlatArgs& a, hipStream_t stream) {
+  constexpr size_t lds = (size_t)kFlatWaves * FlatLayout<QG>::kArea;
+  // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
+  // the runtime needs none, and must not leak into the launch status.
+  static const bool lds_opt_in = [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_flat_kernel<QG, BS>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)lds_opt_in;
+  hipLaunchKernelGGL((tq_flat_kernel<QG, BS>), dim3((unsigned)a.n_groups), dim3(64 * kFlatWaves),
+                     lds, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_flat(const FlatArgs& a, int query_group_size, int kv_block_size,
+                       hipStream_t stream) {
+  if (query_group_size == 6 && kv_block_size == 16) return launch_flat_t<6, 16>(a, stream);
+  if (query_group_size == 6 && kv_block_size == 32) return launch_flat_t<6, 32>(a, stream);
+  if (query_group_size == 8 && kv_block_size == 16) return launch_flat_t<8, 16>(a, stream);
+  if (query_group_size == 8 && kv_block_size == 32) return launch_flat_t<8, 32>(a, stream);
+  if (query_group_size == 16 && kv_block_size == 16) return launch_flat_t<16, 16>(a, stream);
+  if (query_group_size == 16 && kv_block_size == 32) return launch_flat_t<16, 32>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,

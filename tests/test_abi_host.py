@@ -153,14 +153,26 @@ def test_fused_rejects(lib, kw, status):
     assert call_fused(lib, **kw) == status
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def _flat_bytes(seq_heads, groups, QG):
+    rows = 2 * groups * QG  # two partial slots per workgroup
+    return _r256(seq_heads * 4) + _r256(rows * 512) + 2 * _r256(rows * 4)
+
+
 def test_fused_workspace_bytes():
-    # one workgroup per (s, h) suffices when there are many (s, h): no workspace
-    assert tq.fused_workspace_bytes(128, 8, 8, 8192) == 0
-    # 64 (s, h) with 160 tile groups: 32 waves each, as 8 waves x 4 workgroups
-    rows = 64 * 4 * 16
-    assert tq.fused_workspace_bytes(16, 4, 16, 40960) == 256 + rows * 512 + 2 * rows * 4
+    # the flat work list: 256 workgroups of 8 waves once the list has 2048 tile groups
+    assert tq.fused_workspace_bytes(128, 8, 8, 8192) == _flat_bytes(1024, 256, 8)
+    assert tq.fused_workspace_bytes(16, 4, 16, 40960) == _flat_bytes(64, 256, 16)
+    # a shorter list: at most one wave per tile group (4 tile groups: one workgroup)
+    assert tq.fused_workspace_bytes(4, 1, 16, 200) == _flat_bytes(4, 1, 16)
+    assert tq.fused_workspace_bytes(256, 1, 6, 256) == _flat_bytes(256, 32, 6)
     assert tq.fused_workspace_bytes(16, 4, 7, 40960) == 0  # unsupported QG
-    assert tq.fused_workspace_bytes(4, 1, 16, 200) == 0    # a single tile group
+    # more than 256 sequences: workgroups per (s, h) instead, split by the per-(s, h) plan
+    assert tq.fused_workspace_bytes(257, 8, 8, 8192) == 0   # 2056 (s, h): one workgroup each
+    assert tq.fused_workspace_bytes(257, 1, 8, 40960) == 0  # 257 (s, h): one workgroup of 8 waves
 
 
 def call_reduce(lib, *, part=None, sl=A, out=A, QG=8, Hkv=2, G=1, S=2, P=1, maxlen=64):

@@ -27,9 +27,10 @@ def small(lens, qg=8, bs=16, hkv=2, seed=5, P=None):
 
 
 @pytest.mark.parametrize("path", PATHS)
-def test_run_to_run_determinism(path):
-    inp = workloads.make_inputs(workloads.WORKLOADS["w2_s32_ctx4k"], device="cuda")
-    say(f"[bitwise] w2 twice, {path}")
+@pytest.mark.parametrize("name", ["w2_s32_ctx4k", "w3_s64_ragged"])
+def test_run_to_run_determinism(path, name):
+    inp = workloads.make_inputs(workloads.WORKLOADS[name], device="cuda")
+    say(f"[bitwise] {name} twice, {path}")
     a = gpu_decode(inp, path=path)
     b = gpu_decode(inp, path=path)
     assert np.array_equal(bits(a), bits(b))

@@ -176,3 +176,61 @@ def test_long_ranges_and_many_partitions(path):
     say(f"[manyparts] {path} G=1 P=280 L={lens}")
     out = gpu_decode(inp, num_partitions=280, tile_groups=1, path=path)
     compare(out, oracle_decode(inp), f"{path} 280 partitions")
+
+
+def _fused_vs_oracle(inp, S, Hkv, QG, BS, maxlen, P, ws_bytes=None, what=""):
+    import paged_gqa_decode_amd as tq
+
+    nbytes = tq.fused_workspace_bytes(S, Hkv, QG, maxlen) if ws_bytes is None else ws_bytes
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device="cuda") if nbytes else None
+    out = torch.full((S, Hkv * QG, 128), float("nan"), dtype=torch.bfloat16, device="cuda")
+    tq.tq_decode_fused(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables,
+                       inp.seq_lens, out, Hkv, QG, BS, 1, inp.softmax_scale, num_partitions=P,
+                       max_seq_len=maxlen, workspace=ws)
+    torch.cuda.synchronize()
+    compare(out, oracle_decode(inp), what)
+    if ws is not None:
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "counters must be re-armed"
+    return out
+
+
+def test_even_split_one_long_sequence():
+    """One (s, h) of 160 tile groups: one wave per tile group, 20 workgroups, and a merge of
+    20 workgroup partials (more than the merge keeps in registers)."""
+    lens = (40960,)
+    wl = workloads.small_workload(name="onelong", num_seqs=1, num_kv_heads=1, query_group_size=16,
+                                  kv_block_size=32, seq_lens=lens, seed=41)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=160)
+    say("[even] one sequence of 40960 tokens, QG 16")
+    _fused_vs_oracle(inp, 1, 1, 16, 32, 40960, 160, what="fused, one long sequence")
+
+
+def test_even_split_ragged_with_empty_sequences():
+    """Lengths around tile-group edges, empty sequences between live ones, three kv heads: the
+    even split cuts (s, h) ranges at every kind of boundary."""
+    rng = np.random.default_rng(43)
+    base = [0, 1, 255, 256, 257, 511, 1000, 5000, 0, 3000]
+    lens = tuple(int(x) for x in rng.permutation(base * 4))
+    wl = workloads.small_workload(name="evenrag", num_seqs=len(lens), num_kv_heads=3,
+                                  query_group_size=6, kv_block_size=16, seq_lens=lens, seed=44)
+    maxlen = max(lens)
+    P = (maxlen + 255) // 256
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=P)
+    say(f"[even] ragged with empty sequences: S={len(lens)} Hkv=3 QG=6 BS=16")
+    out = _fused_vs_oracle(inp, len(lens), 3, 6, 16, maxlen, P, what="fused, ragged + empty")
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert (out[s].float() == 0).all()
+
+
+@pytest.mark.parametrize("S", [256, 257])
+def test_even_split_sequence_limit(S):
+    """256 sequences take the even split, 257 the per-(s, h) workgroups; both match the oracle."""
+    rng = np.random.default_rng(45 + S)
+    lens = tuple(int(x) for x in rng.integers(1, 700, size=S))
+    wl = workloads.small_workload(name=f"lim{S}", num_seqs=S, num_kv_heads=1, query_group_size=8,
+                                  kv_block_size=32, seq_lens=lens, seed=46)
+    maxlen = max(lens)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=3)
+    say(f"[even] S={S}")
+    _fused_vs_oracle(inp, S, 1, 8, 32, maxlen, 3, what=f"fused, S={S}")

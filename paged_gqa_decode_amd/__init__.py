@@ -257,8 +257,10 @@ def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partit
     q bf16 [S][Hq][128]; k_cache/v_cache uint8 (e4m3fn codes) [NB][Hkv][BS][128];
     kv_scales fp32 [NB][Hkv][2][BS]; block_tables/seq_lens int32.
     ``max_seq_len`` (an upper bound of seq_lens) is read from seq_lens when not
-    given, which synchronizes the stream; ``num_partitions`` defaults to
-    ceil(max_seq_len / (256 * G))."""
+    given, which synchronizes the stream; under graph capture it is the block
+    table's capacity (max_blocks_per_seq * BS) instead, so that nothing is read
+    back and the captured launches serve any lengths up to it.
+    ``num_partitions`` defaults to ceil(max_seq_len / (256 * G))."""
     S, Hq, D = q.shape
     NB, Hkv, BS, Dk = k_cache.shape
     if D != HEAD_DIM or Dk != HEAD_DIM or Hq % Hkv:
@@ -266,7 +268,10 @@ def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partit
     QG = Hq // Hkv
     G = int(tile_groups_per_partition)
     if max_seq_len is None:
-        max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+        if torch.cuda.is_current_stream_capturing():
+            max_seq_len = int(block_tables.shape[1]) * BS
+        else:
+            max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
     if num_partitions is None:
         num_partitions = max(1, -(-int(max_seq_len) // (TOKENS_PER_TILE_GROUP * G)))
     if softmax_scale is None:

@@ -69,3 +69,44 @@ def test_graph_replay_matches_eager(path):
         assert torch.isfinite(got.float()).all()
     if path == "fused":
         assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "counters must stay re-armed"
+
+
+@pytest.mark.parametrize("path", ["two_kernel", "fused"])
+def test_capture_at_length_one_without_host_lengths(path):
+    """decode() captured while every sequence has one token, with no host-side lengths: the
+    binding takes the block table's capacity as the bound, sizes the grid for it and reads
+    nothing back.  Replays with longer lengths (up to the capacity, zero included) equal eager
+    calls on the same inputs."""
+    S, Hkv, QG, BS = 3, 2, 16, 16
+    cap_lens = (2048, 2048, 2048)
+    wl = workloads.small_workload(name="graph1", num_seqs=S, num_kv_heads=Hkv, query_group_size=QG,
+                                  kv_block_size=BS, seq_lens=cap_lens, seed=37)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=cap_lens)
+    capacity = int(inp.block_tables.shape[1]) * BS  # the table has room for 2048 tokens or more
+    assert capacity >= 2048
+    q = inp.q.clone()
+    seq_lens = torch.ones(S, dtype=torch.int32, device="cuda")
+    fused = path == "fused"
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say(f"[graph] capture {path} at length 1")
+    with torch.cuda.graph(graph):
+        out = tq.decode(q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, seq_lens,
+                        softmax_scale=inp.softmax_scale, fused=fused)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    for rep, lens in enumerate(((1, 1, 1), (2048, 17, 0), (300, 2048, 1999), (256, 257, 2048))):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+        torch.cuda.synchronize()
+        say(f"[graph] replay {rep} {path} lens={lens}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = tq.decode(q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, seq_lens,
+                        softmax_scale=inp.softmax_scale, fused=fused, max_seq_len=capacity)
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), ref.view(torch.int16)), f"replay {rep} differs"
+        for s_, L in enumerate(lens):
+            if L == 0:
+                assert (got[s_].float() == 0).all()

@@ -15,6 +15,12 @@ Array conventions (numpy, C-contiguous):
   kv_scales     float32 [NB][Hkv][2][BS] (field 0 = K, field 1 = V)
   block_tables  int32  [S][max_blocks_per_seq]
   seq_lens      int32  [S]
+
+4-bit record format (decode_tq4):
+  tq4_cache     uint8  [NB][Hkv*BS*D + Hkv*3*BS*2] data rows [Hkv][BS][D] (K indices in
+                the first D/2 bytes, V indices in the last D/2; dim d = byte d/2, low
+                nibble for even d), then fp16 meta [Hkv][3][BS] (K norm, V scale, V zero)
+  centroids     float32 [16]
 """
 
 from __future__ import annotations
@@ -70,6 +76,13 @@ class Oracle:
         lib.orc_enc_e4m3fn.restype = ctypes.c_uint8
         lib.orc_kv_write.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P]
         lib.orc_kv_write.restype = ctypes.c_int
+        lib.orc_dec_f16.argtypes = [ctypes.c_uint16]
+        lib.orc_dec_f16.restype = ctypes.c_double
+        lib.orc_decode_tq4.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
+                                       ctypes.c_float, P, i32, P, i32]
+        lib.orc_decode_tq4.restype = ctypes.c_int
+        lib.orc_dequant_tq4.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P]
+        lib.orc_dequant_tq4.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
 
@@ -126,6 +139,56 @@ class Oracle:
         if rc:
             raise OracleError("orc_merge failed with code %d" % rc)
         return out
+
+    def decode_tq4(self, q_bits, tq4_cache, centroids, block_tables, seq_lens, softmax_scale,
+                   num_kv_heads: int, kv_block_size: int, units=None, nthreads: int = 1) -> np.ndarray:
+        """Unsplit decode attention over the 4-bit record format, in fp64.  Returns
+        [S][Hkv*QG][D], or [len(units)][QG][D] for the listed (s, h) pairs."""
+        q = _np(q_bits, np.uint16)
+        cache = _np(tq4_cache, np.uint8)
+        cent = _np(centroids, np.float32)
+        bt = _np(block_tables, np.int32)
+        sl = _np(seq_lens, np.int32)
+        S, Hq, D = q.shape
+        Hkv, BS = int(num_kv_heads), int(kv_block_size)
+        QG = Hq // Hkv
+        NB = cache.shape[0]
+        if Hq % Hkv or cache.reshape(NB, -1).shape[1] != Hkv * BS * D + Hkv * 3 * BS * 2 \
+                or cent.shape != (16,) or bt.shape[0] != S or sl.shape != (S,):
+            raise OracleError("inconsistent shapes")
+        if units is None:
+            u = None
+            n = S * Hkv
+        else:
+            u = np.ascontiguousarray(np.asarray(units, dtype=np.int32).reshape(-1, 2))
+            n = u.shape[0]
+        out = np.empty((n, QG, D), dtype=np.float64)
+        rc = self.lib.orc_decode_tq4(_ptr(q), _ptr(cache), _ptr(cent), _ptr(bt), _ptr(sl), S, Hkv, QG,
+                                     D, BS, NB, bt.shape[1], float(softmax_scale),
+                                     None if u is None else _ptr(u), n, _ptr(out), int(nthreads))
+        if rc:
+            raise OracleError("orc_decode_tq4 failed with code %d" % rc)
+        return out.reshape(S, Hkv * QG, D) if units is None else out
+
+    def dequant_tq4(self, tq4_cache, centroids, num_kv_heads: int, head_dim: int,
+                    kv_block_size: int, block: int, head: int, slot: int):
+        """The dequantized K and V rows (fp64 [D] each) of one (block, head, slot)."""
+        cache = _np(tq4_cache, np.uint8)
+        cent = _np(centroids, np.float32)
+        k = np.empty(head_dim, dtype=np.float64)
+        v = np.empty(head_dim, dtype=np.float64)
+        rc = self.lib.orc_dequant_tq4(_ptr(cache), _ptr(cent), int(num_kv_heads), int(head_dim),
+                                      int(kv_block_size), int(block), int(head), int(slot), _ptr(k),
+                                      _ptr(v))
+        if rc:
+            raise OracleError("orc_dequant_tq4 failed with code %d" % rc)
+        return k, v
+
+    def dec_f16(self, bits) -> np.ndarray:
+        """Decode IEEE fp16 bit patterns to float64 (closed form in oracle.c)."""
+        b = _np(bits, np.uint16)
+        flat = np.array([self.lib.orc_dec_f16(int(x)) for x in b.reshape(-1)], dtype=np.float64)
+        return flat.reshape(b.shape)
 
     def dec_e4m3fn(self, codes) -> np.ndarray:
         """Decode OCP e4m3fn codes to float64 (closed form in oracle.c)."""
@@ -261,3 +324,15 @@ def enc_e4m3fn(values):
 
 def kv_write(*a, **k):
     return default().kv_write(*a, **k)
+
+
+def decode_tq4(*a, **k):
+    return default().decode_tq4(*a, **k)
+
+
+def dequant_tq4(*a, **k):
+    return default().dequant_tq4(*a, **k)
+
+
+def dec_f16(bits):
+    return default().dec_f16(bits)

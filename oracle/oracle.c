@@ -29,6 +29,21 @@
  * Everything is fp64: bf16 q and fp8 codes decode exactly, the fp32 scales and
  * the fp32 softmax_scale are widened, and exp() is libm's double exp().
  *
+ * Second cache format, the page's 4-bit "TQ" record (STEP F: K dequantized as
+ * centroids[index] * K norm, V as index * V scale + V zero point, the query
+ * already rotated by the caller), in the reading this library takes where the
+ * page leaves the constants open.  Cache block b is block_bytes =
+ * Hkv*BS*D + Hkv*3*BS*2 bytes:
+ *   data region  [Hkv][BS][D] bytes: the (head, slot) row holds the K indices
+ *                in bytes 0..D/2-1 and the V indices in bytes D/2..D-1; dim d
+ *                is byte d/2, low nibble for even d, high nibble for odd d
+ *                (the page's word w, nibble n order, little-endian words);
+ *   meta region  [Hkv][3][BS] IEEE fp16: field 0 = K norm, 1 = V scale,
+ *                2 = V zero point;
+ *   k_t[d] = centroids[kidx] * knorm,  v_t[d] = vidx * vscale + vzero,
+ * with 16 fp32 centroids given by the caller.  The attention itself is the
+ * one above.
+ *
  * Split-K form (STEP E/F partition base and trip count, STEP G partial
  * stores): partition p of extent E tokens covers [p*E, min((p+1)*E, L)) and
  * yields m_p = max x, l_p = sum exp(x - m_p), o_p = sum exp(x - m_p) v / l_p
@@ -72,6 +87,20 @@ double orc_dec_bf16(uint16_t bits) {
   return (double)f;
 }
 
+/* IEEE binary16: 1 sign, 5 exponent bits (bias 15), 10 mantissa bits. */
+double orc_dec_f16(uint16_t bits) {
+  int sign = bits >> 15;
+  int e = (bits >> 10) & 0x1F;
+  int m = bits & 0x3FF;
+  double mag;
+  if (e == 31) return m ? NAN : (sign ? -INFINITY : INFINITY);
+  if (e == 0)
+    mag = ldexp((double)m, -24); /* subnormal: m/1024 * 2^(1-15) */
+  else
+    mag = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  return sign ? -mag : mag;
+}
+
 typedef struct {
   const uint16_t* q;
   const uint8_t* k_cache;
@@ -81,7 +110,29 @@ typedef struct {
   const int32_t* seq_lens;
   int32_t S, Hkv, QG, D, BS, NB, max_blocks_per_seq;
   double scale;
+  /* 4-bit record format when tq4_cache is set (k_cache, v_cache, kv_scales unused) */
+  const uint8_t* tq4_cache;
+  const float* centroids;
 } orc_problem;
+
+/* Bytes of one 4-bit cache block. */
+static int64_t orc_tq4_block_bytes(const orc_problem* pb) {
+  return (int64_t)pb->Hkv * pb->BS * pb->D + (int64_t)pb->Hkv * 3 * pb->BS * 2;
+}
+
+/* Dequantized element d of the K (field 0) or V (field 1) row of (blk, h, slot)
+ * in the 4-bit record format. */
+static double orc_tq4_kv(const orc_problem* pb, int field, int blk, int slot, int h, int d) {
+  const uint8_t* block = pb->tq4_cache + (int64_t)blk * orc_tq4_block_bytes(pb);
+  const uint8_t* row = block + ((int64_t)h * pb->BS + slot) * pb->D;
+  const uint8_t* meta = block + (int64_t)pb->Hkv * pb->BS * pb->D + (int64_t)h * 3 * pb->BS * 2;
+  int byte = row[(field == 0 ? 0 : pb->D / 2) + d / 2];
+  int idx = (d & 1) ? byte >> 4 : byte & 0xF;
+  uint16_t f[3];
+  for (int i = 0; i < 3; ++i) memcpy(&f[i], meta + ((int64_t)i * pb->BS + slot) * 2, 2);
+  if (field == 0) return (double)pb->centroids[idx] * orc_dec_f16(f[0]);
+  return (double)idx * orc_dec_f16(f[1]) + orc_dec_f16(f[2]);
+}
 
 /* Physical block of token t of sequence s (STEP F block-table walk). */
 static int orc_block(const orc_problem* pb, int s, int t, int* blk) {
@@ -93,6 +144,7 @@ static int orc_block(const orc_problem* pb, int s, int t, int* blk) {
 
 /* Dequantized element d of the K (field 0) or V (field 1) row of token t. */
 static double orc_kv(const orc_problem* pb, int field, int blk, int slot, int h, int d) {
+  if (pb->tq4_cache) return orc_tq4_kv(pb, field, blk, slot, h, d);
   const uint8_t* cache = field == 0 ? pb->k_cache : pb->v_cache;
   int64_t row = ((int64_t)blk * pb->Hkv + h) * pb->BS + slot;
   double code = orc_dec_e4m3fn(cache[row * pb->D + d]);
@@ -191,7 +243,9 @@ static void* orc_worker(void* arg) {
 }
 
 static int orc_check(const orc_problem* pb) {
-  if (!pb->q || !pb->k_cache || !pb->v_cache || !pb->kv_scales || !pb->block_tables || !pb->seq_lens)
+  if (!pb->q || !pb->block_tables || !pb->seq_lens) return ORC_ERR_ARGS;
+  if (pb->tq4_cache ? (!pb->centroids || (pb->D & 1))
+                    : (!pb->k_cache || !pb->v_cache || !pb->kv_scales))
     return ORC_ERR_ARGS;
   if (pb->S < 1 || pb->Hkv < 1 || pb->QG < 1 || pb->D < 1 || pb->BS < 1 || pb->NB < 1 ||
       pb->max_blocks_per_seq < 1)
@@ -210,13 +264,58 @@ static int orc_check(const orc_problem* pb) {
  * units; each unit's arithmetic is the same whatever the thread count.
  * q is bf16 bits [S][Hkv*QG][D]; softmax_scale is widened from fp32.
  */
+static int orc_run(orc_problem pb, const int32_t* units, int32_t n_units, double* out,
+                   int32_t nthreads);
+
 int orc_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
                const float* kv_scales, const int32_t* block_tables, const int32_t* seq_lens,
                int32_t S, int32_t Hkv, int32_t QG, int32_t D, int32_t BS, int32_t NB,
                int32_t max_blocks_per_seq, float softmax_scale, const int32_t* units,
                int32_t n_units, double* out, int32_t nthreads) {
   orc_problem pb = {q, k_cache, v_cache, kv_scales, block_tables, seq_lens, S, Hkv, QG, D, BS,
-                    NB, max_blocks_per_seq, (double)softmax_scale};
+                    NB, max_blocks_per_seq, (double)softmax_scale, NULL, NULL};
+  return orc_run(pb, units, n_units, out, nthreads);
+}
+
+/*
+ * The same decode over the 4-bit record format: cache is [NB][block_bytes]
+ * (block_bytes = Hkv*BS*D + Hkv*3*BS*2), centroids 16 fp32 values, q the
+ * (already rotated) bf16 query.
+ */
+int orc_decode_tq4(const uint16_t* q, const uint8_t* cache, const float* centroids,
+                   const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t Hkv,
+                   int32_t QG, int32_t D, int32_t BS, int32_t NB, int32_t max_blocks_per_seq,
+                   float softmax_scale, const int32_t* units, int32_t n_units, double* out,
+                   int32_t nthreads) {
+  orc_problem pb = {q, NULL, NULL, NULL, block_tables, seq_lens, S, Hkv, QG, D, BS,
+                    NB, max_blocks_per_seq, (double)softmax_scale, cache, centroids};
+  if (!cache) return ORC_ERR_ARGS;
+  return orc_run(pb, units, n_units, out, nthreads);
+}
+
+/* Dequantized K and V rows (D values each) of (blk, h, slot) in the 4-bit record format. */
+int orc_dequant_tq4(const uint8_t* cache, const float* centroids, int32_t Hkv, int32_t D,
+                    int32_t BS, int32_t blk, int32_t h, int32_t slot, double* k, double* v) {
+  if (!cache || !centroids || !k || !v || Hkv < 1 || D < 2 || (D & 1) || BS < 1 || blk < 0 ||
+      h < 0 || h >= Hkv || slot < 0 || slot >= BS)
+    return ORC_ERR_ARGS;
+  orc_problem pb;
+  memset(&pb, 0, sizeof pb);
+  pb.Hkv = Hkv;
+  pb.D = D;
+  pb.BS = BS;
+  pb.tq4_cache = cache;
+  pb.centroids = centroids;
+  for (int d = 0; d < D; ++d) {
+    k[d] = orc_tq4_kv(&pb, 0, blk, slot, h, d);
+    v[d] = orc_tq4_kv(&pb, 1, blk, slot, h, d);
+  }
+  return ORC_OK;
+}
+
+static int orc_run(orc_problem pb, const int32_t* units, int32_t n_units, double* out,
+                   int32_t nthreads) {
+  int32_t S = pb.S, Hkv = pb.Hkv;
   int rc = orc_check(&pb);
   if (rc) return rc;
   if (!out) return ORC_ERR_ARGS;
@@ -262,7 +361,7 @@ int orc_partials(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cac
                  int32_t max_blocks_per_seq, float softmax_scale, int32_t P, int32_t E,
                  double* o, double* m, double* l) {
   orc_problem pb = {q, k_cache, v_cache, kv_scales, block_tables, seq_lens, S, Hkv, QG, D, BS,
-                    NB, max_blocks_per_seq, (double)softmax_scale};
+                    NB, max_blocks_per_seq, (double)softmax_scale, NULL, NULL};
   int rc = orc_check(&pb);
   if (rc) return rc;
   if (P < 1 || E < 1 || !o || !m || !l) return ORC_ERR_ARGS;

@@ -405,8 +405,128 @@ def pin_kv_write_matches_library_quantizer(orc):
             assert np.array_equal(sc2[blk, :, field, off], s.numpy())
 
 
+# ----------------------------------------------------------------------------
+# The 4-bit record format
+# ----------------------------------------------------------------------------
+
+def pin_f16_library(orc):
+    """All 65536 fp16 bit patterns against numpy's float16 (NaN patterns decode to NaN)."""
+    bits = np.arange(65536, dtype=np.uint16)
+    got = orc.dec_f16(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    live = ~np.isnan(ref)
+    assert np.array_equal(got[live], ref[live])
+
+
+def pin_tq4_golden_record(orc):
+    """The hand-written record of tests/golden/tq4_record.json: its bytes sit at offsets
+    derived by hand from the layout, and its dequantized K and V rows are derived by hand.
+    Then a 4-token sequence whose other records are zero: with q = 0 the output is the mean
+    of the V rows; with q = e_0 a 4-token softmax in closed form."""
+    with open(os.path.join(GOLDEN, "tq4_record.json")) as f:
+        g = json.load(f)
+    sz = g["sizes"]
+    NB, Hkv, BS, D = sz["num_blocks"], sz["num_kv_heads"], sz["kv_block_size"], sz["head_dim"]
+    cache = np.zeros(NB * sz["block_bytes"], dtype=np.uint8)
+    for off, val in g["bytes"].items():
+        cache[int(off)] = val
+    cache = cache.reshape(NB, sz["block_bytes"])
+    cent = np.asarray(g["centroids"], dtype=np.float32)
+    rec = g["record"]
+    k, v = orc.dequant_tq4(cache, cent, Hkv, D, BS, rec["block"], rec["head"], rec["slot"])
+    assert np.array_equal(k, np.asarray(g["expected_k"])), k
+    assert np.array_equal(v, np.asarray(g["expected_v"])), v
+    # every other record of the cache is zero bytes: index 0 with zero norm, scale and zero point
+    for (b, h, slot) in ((0, 0, 0), (1, 1, 2), (1, 0, 3)):
+        k0, v0 = orc.dequant_tq4(cache, cent, Hkv, D, BS, b, h, slot)
+        assert not k0.any() and not v0.any()
+    # sequence of 4 tokens in block 1: slots 0..3, the record is token 3 of kv head 1
+    bt = np.array([[1]], dtype=np.int32)
+    sl = np.array([4], dtype=np.int32)
+    q = np.zeros((1, Hkv, D), dtype=np.uint16)  # QG = 1
+    out = orc.decode_tq4(q, cache, cent, bt, sl, 1.0, Hkv, BS)
+    assert np.array_equal(out[0, 1], np.asarray(g["expected_v"]) / 4)
+    assert not out[0, 0].any()
+    q[0, 1, 0] = 0x3F80  # bf16 1.0 at dim 0: x_3 = k[0] = -14, the other logits 0
+    out = orc.decode_tq4(q, cache, cent, bt, sl, 1.0, Hkv, BS)
+    w = math.exp(-14.0)
+    want = np.asarray(g["expected_v"]) * w / (w + 3.0)
+    assert np.max(np.abs(out[0, 1] - want)) < 1e-15
+
+
+_E4M3_EXACT_CENTROIDS = [-6.0, -4.0, -3.0, -2.0, -1.5, -1.0, -0.5, -0.25, 0.25, 0.5, 1.0, 1.5, 2.0,
+                         3.0, 4.0, 6.0]
+
+
+def _tq4_problem(seed, v_const=None, v_scale=None, v_zero=None):
+    """A small random problem in the 4-bit format, with the arrays of an equivalent fp8
+    cache when every dequantized value is e4m3-exact (centroids e4m3-exact, norms and V
+    scales powers of two, zero point 0)."""
+    import workloads
+
+    rng = np.random.default_rng(seed)
+    S, Hkv, QG, D, BS = 3, 2, 4, 128, 16
+    lens = np.array([5, 16, 40], dtype=np.int32)
+    need = [-(-int(L) // BS) for L in lens]
+    NB = sum(need) + 2
+    perm = rng.permutation(NB).astype(np.int32)
+    bt = np.zeros((S, max(need) + 1), dtype=np.int32)
+    pos = 0
+    for s_, n in enumerate(need):
+        bt[s_, :n] = perm[pos:pos + n]
+        pos += n
+    k_idx = rng.integers(0, 16, size=(NB, Hkv, BS, D), dtype=np.uint8)
+    v_idx = rng.integers(0, 16, size=(NB, Hkv, BS, D), dtype=np.uint8)
+    if v_const is not None:
+        v_idx[:] = v_const
+    knorm = np.ldexp(1.0, rng.integers(-3, 4, size=(NB, Hkv, BS))).astype(np.float16)
+    if v_scale is None:
+        vscale = np.ldexp(1.0, rng.integers(-3, 4, size=(NB, Hkv, BS))).astype(np.float16)
+    else:
+        vscale = np.full((NB, Hkv, BS), v_scale, dtype=np.float16)
+    vzero = np.full((NB, Hkv, BS), 0.0 if v_zero is None else v_zero, dtype=np.float16)
+    meta = np.stack([knorm, vscale, vzero], axis=2).view(np.int16)  # [NB][Hkv][3][BS]
+    cache = workloads.pack_tq4(torch.from_numpy(k_idx), torch.from_numpy(v_idx),
+                               torch.from_numpy(meta)).numpy()
+    cent = np.asarray(_E4M3_EXACT_CENTROIDS, dtype=np.float32)
+    q = torch.randn((S, Hkv * QG, D), generator=torch.Generator().manual_seed(seed)).to(torch.bfloat16)
+    q_bits = q.view(torch.int16).numpy().view(np.uint16)
+    # the equivalent fp8 form: codes of the exact values, scales = norms / V scales
+    k_codes = torch.from_numpy(cent[k_idx]).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    v_codes = torch.from_numpy(v_idx.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    scales = np.stack([knorm.astype(np.float32), vscale.astype(np.float32)], axis=2)  # [NB][Hkv][2][BS]
+    return dict(q=q_bits, cache=cache, cent=cent, bt=bt, sl=lens, Hkv=Hkv, BS=BS,
+                k_codes=k_codes, v_codes=v_codes, scales=np.ascontiguousarray(scales))
+
+
+def pin_tq4_matches_fp8_form(orc):
+    """A 4-bit cache whose dequantized values are all e4m3-exact gives the same bits as the
+    fp8 oracle on the fp8 cache holding those values (K codes of centroids[index] with the
+    norm as scale, V codes of the index with the V scale as scale): the 4-bit addressing,
+    nibble order and field order against the separately pinned fp8 path."""
+    for seed in (3, 4):
+        p = _tq4_problem(seed)
+        a = orc.decode_tq4(p["q"], p["cache"], p["cent"], p["bt"], p["sl"], 0.0883883461356163,
+                           p["Hkv"], p["BS"])
+        b = orc.decode(p["q"], p["k_codes"], p["v_codes"], p["scales"], p["bt"], p["sl"],
+                       0.0883883461356163)
+        assert np.array_equal(a, b)
+        assert np.abs(a).max() > 0.5
+
+
+def pin_tq4_constant_v(orc):
+    """Every V index 9 with V scale 0.375 and zero point -1.25: every value is 2.125 and so is
+    every output row, whatever the K side."""
+    p = _tq4_problem(5, v_const=9, v_scale=0.375, v_zero=-1.25)
+    out = orc.decode_tq4(p["q"], p["cache"], p["cent"], p["bt"], p["sl"], 0.0883883461356163,
+                         p["Hkv"], p["BS"])
+    assert np.max(np.abs(out - 2.125)) < 1e-13
+
+
 ALL_PINS = [pin_e4m3fn_points, pin_e4m3fn_library, pin_bf16_library, pin_dense_bruteforce, pin_sdpa,
             pin_single_token, pin_zero_query, pin_constant_v, pin_two_token_golden,
             pin_block_permutation, pin_split_merge, pin_v_scale_linearity, pin_dominant_token,
             pin_zero_length, pin_e4m3fn_encode_roundtrip, pin_e4m3fn_encode_ties_and_saturation,
-            pin_e4m3fn_encode_library, pin_kv_write_quantizer, pin_kv_write_matches_library_quantizer]
+            pin_e4m3fn_encode_library, pin_kv_write_quantizer, pin_kv_write_matches_library_quantizer,
+            pin_f16_library, pin_tq4_golden_record, pin_tq4_matches_fp8_form, pin_tq4_constant_v]

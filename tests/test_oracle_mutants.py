@@ -43,6 +43,20 @@ MUTANTS = [
     ("writer_scale_field_swapped", "kv_scales[(((int64_t)blk * Hkv + h) * 2 + field) * BS + off] = s;",
      "kv_scales[(((int64_t)blk * Hkv + h) * 2 + (1 - field)) * BS + off] = s;"),
     ("writer_ignores_skip", "if (slot < 0) continue;", "if (slot < 0) slot = 0;"),
+    ("f16_exponent_bias", "ldexp((double)(1024 + m), e - 25)", "ldexp((double)(1024 + m), e - 24)"),
+    ("f16_subnormal_scale", "ldexp((double)m, -24)", "ldexp((double)m, -25)"),
+    ("tq4_nibble_order", "int idx = (d & 1) ? byte >> 4 : byte & 0xF;",
+     "int idx = (d & 1) ? byte & 0xF : byte >> 4;"),
+    ("tq4_kv_regions_swapped", "row[(field == 0 ? 0 : pb->D / 2) + d / 2]",
+     "row[(field == 0 ? pb->D / 2 : 0) + d / 2]"),
+    ("tq4_norm_field", "return (double)pb->centroids[idx] * orc_dec_f16(f[0]);",
+     "return (double)pb->centroids[idx] * orc_dec_f16(f[1]);"),
+    ("tq4_zero_point_dropped", "return (double)idx * orc_dec_f16(f[1]) + orc_dec_f16(f[2]);",
+     "return (double)idx * orc_dec_f16(f[1]);"),
+    ("tq4_centroid_off_by_one", "pb->centroids[idx]", "pb->centroids[(idx + 1) & 15]"),
+    ("tq4_meta_head_stride", "(int64_t)h * 3 * pb->BS * 2;", "(int64_t)h * 2 * pb->BS * 2;"),
+    ("tq4_rows_slot_major", "((int64_t)h * pb->BS + slot) * pb->D", "((int64_t)slot * pb->Hkv + h) * pb->D"),
+    ("tq4_block_stride", "(int64_t)pb->Hkv * 3 * pb->BS * 2;\n}", "(int64_t)pb->Hkv * 2 * pb->BS * 2;\n}"),
 ]
 
 

@@ -141,8 +141,9 @@ def quantize_rows(x: torch.Tensor):
 
 
 def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
-                softmax_scale: Optional[float] = None) -> Inputs:
-    """Draw the inputs of workload `wl` on `device` (deterministic per device)."""
+                softmax_scale: Optional[float] = None, _skip_cache: bool = False) -> Inputs:
+    """Draw the inputs of workload `wl` on `device` (deterministic per device).
+    _skip_cache: leave the fp8 cache empty (for the 4-bit format's generator)."""
     dev = torch.device(device)
     rng = np.random.default_rng(wl.seed)
     sl = draw_seq_lens(wl, rng) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
@@ -173,6 +174,13 @@ def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
         q = q * mult.view(1, Hkv * QG, D).to(dev)
     q = q.to(torch.bfloat16)
 
+    if _skip_cache:
+        if softmax_scale is None:
+            softmax_scale = float(np.float32(1.0 / math.sqrt(D)))
+        empty = torch.empty(0, dtype=torch.uint8, device=dev)
+        return Inputs(wl=wl, q=q, k_cache=empty, v_cache=empty, kv_scales=empty,
+                      block_tables=torch.from_numpy(bt).to(dev), seq_lens=torch.from_numpy(sl).to(dev),
+                      num_partitions=int(num_partitions), num_blocks=NB, softmax_scale=softmax_scale)
     k_codes = torch.empty((NB, Hkv, BS, D), dtype=torch.uint8, device=dev)
     v_codes = torch.empty((NB, Hkv, BS, D), dtype=torch.uint8, device=dev)
     scales = torch.empty((NB, Hkv, 2, BS), dtype=torch.float32, device=dev)
@@ -234,4 +242,152 @@ def poison(inp: Inputs, seed: int = 99) -> Inputs:
         if tail > 0:
             bt[s, nb_used:] = rng.integers(0, inp.num_blocks, size=tail)
     return dataclasses.replace(inp, k_cache=k, v_cache=v, kv_scales=sc,
+                               block_tables=torch.from_numpy(bt).to(inp.block_tables.device))
+
+
+# ----------------------------------------------------------------------------
+# The 4-bit record format (the "TQ" cache of page "vllm.v1.attention.ops.
+# flydsl_kernels.tq_decode").  Layout of one cache block (uint8):
+#   data rows [Hkv][BS][D]: per (kv head, slot) D bytes, the K indices in the
+#     first D/2 (dim d in byte d/2, low nibble for even d), the V indices in
+#     the last D/2;
+#   meta [Hkv][3][BS] fp16: K norm, V scale, V zero point.
+# Recipe: q as above (the query arrives already rotated: a rotation of an
+# isotropic Gaussian is one); K rows x ~ N(0, 1): knorm = fp16(|x| / sqrt(D)),
+# indices = nearest of the 16 centroids to x / knorm; V rows y ~ N(0, 1): zero
+# = fp16(min y), scale = fp16((max y - min y) / 15), indices = round((y - zero)
+# / scale) clamped to [0, 15].  The centroids are those of the 16-level
+# Lloyd-Max quantizer of N(0, 1) (a plain fixed-point iteration, no RNG).
+# ----------------------------------------------------------------------------
+
+TQ4_META_FIELDS = 3
+
+
+def tq4_block_bytes(num_kv_heads: int, kv_block_size: int, head_dim: int = 128) -> int:
+    return num_kv_heads * kv_block_size * head_dim + num_kv_heads * TQ4_META_FIELDS * kv_block_size * 2
+
+
+def lloyd_max_normal_16(iters: int = 200) -> np.ndarray:
+    """Centroids (float32, ascending) of the 16-level Lloyd-Max quantizer of N(0, 1)."""
+    phi = lambda x: math.exp(-0.5 * x * x) / math.sqrt(2 * math.pi)  # noqa: E731
+    Phi = lambda x: 0.5 * (1.0 + math.erf(x / math.sqrt(2.0)))  # noqa: E731
+    c = [-2.5 + 5.0 * j / 15 for j in range(16)]
+    for _ in range(iters):
+        b = [-math.inf] + [(c[j] + c[j + 1]) / 2 for j in range(15)] + [math.inf]
+        c = []
+        for j in range(16):
+            lo, hi = b[j], b[j + 1]
+            pl = 0.0 if lo == -math.inf else phi(lo)
+            ph = 0.0 if hi == math.inf else phi(hi)
+            mass = (1.0 if hi == math.inf else Phi(hi)) - (0.0 if lo == -math.inf else Phi(lo))
+            c.append((pl - ph) / mass)
+    return np.asarray(c, dtype=np.float32)
+
+
+def pack_tq4(k_idx: torch.Tensor, v_idx: torch.Tensor, meta_bits: torch.Tensor) -> torch.Tensor:
+    """Indices uint8 [NB][Hkv][BS][D] (values 0..15) and fp16 meta bits int16
+    [NB][Hkv][3][BS] -> cache uint8 [NB][block_bytes]."""
+    NB, Hkv, BS, D = k_idx.shape
+    data = torch.empty((NB, Hkv, BS, D), dtype=torch.uint8, device=k_idx.device)
+    data[..., :D // 2] = k_idx[..., 0::2] | (k_idx[..., 1::2] << 4)
+    data[..., D // 2:] = v_idx[..., 0::2] | (v_idx[..., 1::2] << 4)
+    meta = meta_bits.contiguous().view(torch.uint8).reshape(NB, -1)
+    return torch.cat([data.reshape(NB, -1), meta], dim=1).contiguous()
+
+
+def quantize_tq4_rows(x: torch.Tensor, y: torch.Tensor, centroids: torch.Tensor):
+    """K rows x and V rows y, fp32 [..., D] -> (K indices, V indices, fp16 meta [..., 3])."""
+    D = x.shape[-1]
+    knorm = (x.norm(dim=-1) / math.sqrt(D)).to(torch.float16)
+    kn = knorm.float()
+    u = x / torch.where(kn > 0, kn, torch.ones_like(kn)).unsqueeze(-1)
+    mids = (centroids[:-1] + centroids[1:]) / 2
+    k_idx = torch.bucketize(u.contiguous(), mids.contiguous()).to(torch.uint8)
+    lo = y.amin(dim=-1)
+    hi = y.amax(dim=-1)
+    zero = lo.to(torch.float16)
+    scale = ((hi - lo) / 15).to(torch.float16)
+    sc = scale.float()
+    div = torch.where(sc > 0, sc, torch.ones_like(sc)).unsqueeze(-1)
+    v_idx = torch.round((y - zero.float().unsqueeze(-1)) / div).clamp_(0, 15).to(torch.uint8)
+    v_idx = torch.where(sc.unsqueeze(-1) > 0, v_idx, torch.zeros_like(v_idx))
+    meta = torch.stack([knorm, scale, zero], dim=-1)
+    return k_idx, v_idx, meta
+
+
+@dataclasses.dataclass
+class InputsTq4:
+    wl: Workload
+    q: torch.Tensor            # bf16 [S][Hkv*QG][D], the rotated query
+    cache: torch.Tensor        # uint8 [NB][block_bytes]
+    centroids: torch.Tensor    # fp32 [16]
+    block_tables: torch.Tensor
+    seq_lens: torch.Tensor
+    num_partitions: int
+    num_blocks: int
+    softmax_scale: float
+
+    def to(self, device) -> "InputsTq4":
+        f = lambda t: t.to(device)  # noqa: E731
+        return dataclasses.replace(self, q=f(self.q), cache=f(self.cache), centroids=f(self.centroids),
+                                   block_tables=f(self.block_tables), seq_lens=f(self.seq_lens))
+
+    def kv_bytes(self) -> int:
+        """Bytes of live records: sum over sequences and kv heads of L * (D + 6)."""
+        D = self.wl.head_dim
+        return int(self.seq_lens.to(torch.int64).sum().item()) * self.wl.num_kv_heads * (D + 2 * TQ4_META_FIELDS)
+
+
+def make_inputs_tq4(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
+                    softmax_scale: Optional[float] = None) -> InputsTq4:
+    """Draw the 4-bit-format inputs of workload `wl` on `device` (same lengths, tables and q
+    as make_inputs; the cache from the same K/V draws, quantized to the 4-bit record)."""
+    dev = torch.device(device)
+    base = make_inputs(wl, device=dev, seq_lens=seq_lens, num_partitions=num_partitions,
+                       softmax_scale=softmax_scale, _skip_cache=True)
+    S, Hkv, D, BS = wl.num_seqs, wl.num_kv_heads, wl.head_dim, wl.kv_block_size
+    NB = base.num_blocks
+    cent = torch.from_numpy(lloyd_max_normal_16()).to(dev)
+    cache = torch.empty((NB, tq4_block_bytes(Hkv, BS, D)), dtype=torch.uint8, device=dev)
+    gk = torch.Generator(device=dev).manual_seed(wl.seed + 2)
+    gv = torch.Generator(device=dev).manual_seed(wl.seed + 3)
+    for b0 in range(0, NB, SLAB_BLOCKS):
+        b1 = min(NB, b0 + SLAB_BLOCKS)
+        x = torch.randn((b1 - b0, Hkv, BS, D), generator=gk, device=dev, dtype=torch.float32)
+        y = torch.randn((b1 - b0, Hkv, BS, D), generator=gv, device=dev, dtype=torch.float32)
+        k_idx, v_idx, meta = quantize_tq4_rows(x, y, cent)
+        meta_bits = meta.view(torch.int16).permute(0, 1, 3, 2).contiguous()  # [b][Hkv][3][BS]
+        cache[b0:b1] = pack_tq4(k_idx, v_idx, meta_bits)
+        del x, y, k_idx, v_idx, meta, meta_bits
+    return InputsTq4(wl=wl, q=base.q, cache=cache, centroids=cent, block_tables=base.block_tables,
+                     seq_lens=base.seq_lens, num_partitions=base.num_partitions, num_blocks=NB,
+                     softmax_scale=base.softmax_scale)
+
+
+def poison_tq4(inp: InputsTq4, seed: int = 99) -> InputsTq4:
+    """Copy of `inp` with garbage wherever a correct reader must not look: the records of
+    slots past each sequence's length in its last block get random index bytes and NaN
+    meta (fp16 0x7E00); block-table entries past ceil(L / BS) get other valid block ids."""
+    rng = np.random.default_rng(seed)
+    cache = inp.cache.clone()
+    bt = inp.block_tables.cpu().numpy().copy()
+    sl = inp.seq_lens.cpu().numpy()
+    wl = inp.wl
+    Hkv, BS, D = wl.num_kv_heads, wl.kv_block_size, wl.head_dim
+    data_bytes = Hkv * BS * D
+    for s, L in enumerate(sl):
+        L = int(L)
+        nb_used = -(-L // BS)
+        if L % BS:
+            b = int(bt[s, nb_used - 1])
+            blk = cache[b]
+            rows = blk[:data_bytes].view(Hkv, BS, D)
+            rows[:, L % BS:] = torch.from_numpy(
+                rng.integers(0, 256, size=(Hkv, BS - L % BS, D), dtype=np.uint8)).to(cache.device)
+            meta = blk[data_bytes:].view(torch.int16).view(Hkv, TQ4_META_FIELDS, BS)
+            meta[:, :, L % BS:] = 0x7E00
+        tail = bt.shape[1] - nb_used
+        if tail > 0:
+            bt[s, nb_used:] = rng.integers(0, inp.num_blocks, size=tail)
+    return dataclasses.replace(inp, cache=cache,
                                block_tables=torch.from_numpy(bt).to(inp.block_tables.device))

@@ -186,6 +186,43 @@ size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,
                                 int32_t query_group_size);
 
 /*
+ * The 4-bit record format -- the "TQ" cache of page "vllm.v1.attention.ops.
+ * flydsl_kernels.tq_decode" (STEP F: K dequantized as centroids[index] * K
+ * norm, V as index * V scale + V zero point; the query rotated by the caller).
+ * The page leaves the record's constants open; this library reads them as:
+ *   kv_cache   uint8 [NB][tq4_block_bytes(Hkv, BS)], one cache block =
+ *              data rows [Hkv][BS][128] bytes: per (kv head, slot) the K
+ *              indices in bytes 0..63 and the V indices in bytes 64..127, dim
+ *              d in byte d/2, low nibble for even d, high nibble for odd d;
+ *              then metadata [Hkv][3][BS] IEEE fp16: field 0 = K norm, 1 = V
+ *              scale, 2 = V zero point.  16-byte aligned.
+ *   centroids  fp32 [16], the K codebook.  4-byte aligned.
+ *   q_rot      bf16 [S][Hkv*QG][128], the query in the rotated basis of K.
+ * k_t[d] = centroids[kidx] * knorm_t, v_t[d] = vidx * vscale_t + vzero_t, and
+ * the attention is the one of tq_decode.  Records past a sequence's length may
+ * hold any bytes (NaN metadata included).
+ *
+ * tq4_decode writes the same partial triple as tq_decode (merge it with
+ * tq_decode_reduce); tq4_decode_fused is tq_decode_fused for this format (the
+ * workspace size is tq_fused_workspace_bytes).  Arguments, checks and errors
+ * are those of tq_decode / tq_decode_fused, with kv_cache and centroids in
+ * place of k_cache, v_cache and kv_scales.
+ */
+tq_status tq4_decode(const void* q_rot, const uint8_t* kv_cache, const float* centroids,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     const tq_partials* out, int32_t num_kv_heads, int32_t query_group_size,
+                     int32_t kv_block_size, int32_t tile_groups_per_partition, float softmax_scale,
+                     const tq_extent* ext, void* stream);
+tq_status tq4_decode_fused(const void* q_rot, const uint8_t* kv_cache, const float* centroids,
+                           const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                           int32_t num_kv_heads, int32_t query_group_size, int32_t kv_block_size,
+                           int32_t tile_groups_per_partition, float softmax_scale,
+                           const tq_extent* ext, void* workspace, size_t workspace_bytes,
+                           void* stream);
+/* Bytes of one 4-bit cache block: Hkv*BS*128 + Hkv*3*BS*2 (0 if BS is unsupported). */
+size_t tq4_block_bytes(int32_t num_kv_heads, int32_t kv_block_size);
+
+/*
  * tq_kv_write -- the KV-cache writer, the step that fills the cache the
  * decode reads: for each new token t with 0 <= slot_mapping[t] < NB*BS
  * (slot = block * BS + offset) and each kv head h, the K row and the V row are

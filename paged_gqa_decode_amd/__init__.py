@@ -34,8 +34,8 @@ TQ_OK, TQ_ERR_NULL, TQ_ERR_MISALIGNED, TQ_ERR_UNSUPPORTED, TQ_ERR_SHAPE, TQ_ERR_
     TQ_ERR_SCALE, TQ_ERR_HIP = range(8)
 
 EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_decode_fused", "tq_fused_workspace_bytes",
-                    "tq_kv_write", "tq_partials_bytes", "tq_status_str", "tq_last_hip_error",
-                    "tq_abi_version")
+                    "tq4_decode", "tq4_decode_fused", "tq4_block_bytes", "tq_kv_write",
+                    "tq_partials_bytes", "tq_status_str", "tq_last_hip_error", "tq_abi_version")
 
 
 class TqError(RuntimeError):
@@ -77,6 +77,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq_decode_fused.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float,
                                     ctypes.POINTER(Extent), P, ctypes.c_size_t, P]
     lib.tq_decode_fused.restype = ctypes.c_int
+    lib.tq4_decode.argtypes = [P, P, P, P, P, ctypes.POINTER(PartialsStruct), i32, i32, i32, i32,
+                               ctypes.c_float, ctypes.POINTER(Extent), P]
+    lib.tq4_decode.restype = ctypes.c_int
+    lib.tq4_decode_fused.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float,
+                                     ctypes.POINTER(Extent), P, ctypes.c_size_t, P]
+    lib.tq4_decode_fused.restype = ctypes.c_int
+    lib.tq4_block_bytes.argtypes = [i32, i32]
+    lib.tq4_block_bytes.restype = ctypes.c_size_t
     lib.tq_kv_write.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
     lib.tq_kv_write.restype = ctypes.c_int
     lib.tq_fused_workspace_bytes.argtypes = [ctypes.POINTER(Extent), i32, i32]
@@ -223,6 +231,97 @@ def tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
                              ctypes.byref(ext), ws_ptr, ws_bytes, _stream(stream))
     if st != TQ_OK:
         raise TqError(st, "tq_decode_fused")
+
+
+def tq4_block_bytes(num_kv_heads: int, kv_block_size: int) -> int:
+    """Bytes of one cache block of the 4-bit record format (C ABI tq4_block_bytes)."""
+    return int(load_library().tq4_block_bytes(int(num_kv_heads), int(kv_block_size)))
+
+
+def tq4_decode(q_rot, kv_cache, centroids, block_tables, seq_lens, partials: Partials,
+               num_kv_heads: int, query_group_size: int, kv_block_size: int,
+               tile_groups_per_partition: int, softmax_scale: float, *, num_partitions: int,
+               max_seq_len: int, num_blocks: Optional[int] = None, stream=None) -> None:
+    """Enqueue the partition kernel over the 4-bit record format (C ABI tq4_decode)."""
+    lib = load_library()
+    ptrs = [_dev(t, n) for t, n in ((q_rot, "q_rot"), (kv_cache, "kv_cache"),
+                                    (centroids, "centroids"), (block_tables, "block_tables"),
+                                    (seq_lens, "seq_lens"))]
+    for t, n in ((partials.out, "partials.out"), (partials.max_logits, "partials.max_logits"),
+                 (partials.exp_sums, "partials.exp_sums")):
+        _dev(t, n)
+    nb = int(kv_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    ext = _extent(q_rot.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ps = partials._struct()
+    st = lib.tq4_decode(*ptrs, ctypes.byref(ps), int(num_kv_heads), int(query_group_size),
+                        int(kv_block_size), int(tile_groups_per_partition), float(softmax_scale),
+                        ctypes.byref(ext), _stream(stream))
+    if st != TQ_OK:
+        raise TqError(st, "tq4_decode")
+
+
+def tq4_decode_fused(q_rot, kv_cache, centroids, block_tables, seq_lens, out, num_kv_heads: int,
+                     query_group_size: int, kv_block_size: int, tile_groups_per_partition: int,
+                     softmax_scale: float, *, num_partitions: int, max_seq_len: int,
+                     num_blocks: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> None:
+    """Enqueue the one-launch decode over the 4-bit record format (C ABI tq4_decode_fused)."""
+    lib = load_library()
+    ptrs = [_dev(t, n) for t, n in ((q_rot, "q_rot"), (kv_cache, "kv_cache"),
+                                    (centroids, "centroids"), (block_tables, "block_tables"),
+                                    (seq_lens, "seq_lens"), (out, "out"))]
+    nb = int(kv_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    ext = _extent(q_rot.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr = _dev(workspace, "workspace")
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.tq4_decode_fused(*ptrs, int(num_kv_heads), int(query_group_size), int(kv_block_size),
+                              int(tile_groups_per_partition), float(softmax_scale),
+                              ctypes.byref(ext), ws_ptr, ws_bytes, _stream(stream))
+    if st != TQ_OK:
+        raise TqError(st, "tq4_decode_fused")
+
+
+def decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, *, num_kv_heads: int,
+               kv_block_size: int, num_partitions=None, tile_groups_per_partition: int = 1,
+               softmax_scale: Optional[float] = None, max_seq_len: Optional[int] = None,
+               partials: Optional[Partials] = None, out: Optional[torch.Tensor] = None,
+               fused: bool = False, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """decode() for the 4-bit record format: kv_cache uint8 [NB][tq4_block_bytes],
+    centroids fp32 [16], q_rot bf16 [S][Hq][128].  Returns bf16 [S][Hq][128]."""
+    S, Hq, D = q_rot.shape
+    Hkv, BS = int(num_kv_heads), int(kv_block_size)
+    if D != HEAD_DIM or Hq % Hkv:
+        raise ValueError("head_dim must be 128 and num_q_heads a multiple of num_kv_heads")
+    QG = Hq // Hkv
+    G = int(tile_groups_per_partition)
+    if max_seq_len is None:
+        if torch.cuda.is_current_stream_capturing():
+            max_seq_len = int(block_tables.shape[1]) * BS
+        else:
+            max_seq_len = int(seq_lens.max().item()) if seq_lens.numel() else 0
+    if num_partitions is None:
+        num_partitions = max(1, -(-int(max_seq_len) // (TOKENS_PER_TILE_GROUP * G)))
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(HEAD_DIM)
+    if out is None:
+        out = torch.empty((S, Hq, HEAD_DIM), dtype=torch.bfloat16, device=q_rot.device)
+    if fused:
+        if workspace is None:
+            workspace = alloc_fused_workspace(S, Hkv, QG, max_seq_len, q_rot.device)
+        tq4_decode_fused(q_rot, kv_cache, centroids, block_tables, seq_lens, out, Hkv, QG, BS, G,
+                         softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
+                         workspace=workspace, stream=stream)
+        return out
+    if partials is None:
+        partials = alloc_partials(S, Hkv, num_partitions, QG, q_rot.device)
+    tq4_decode(q_rot, kv_cache, centroids, block_tables, seq_lens, partials, Hkv, QG, BS, G,
+               softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len, stream=stream)
+    tq_decode_reduce(partials, seq_lens, out, Hkv, QG, G, num_partitions=num_partitions,
+                     max_seq_len=max_seq_len, stream=stream)
+    return out
 
 
 def tq_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, kv_scales, *, stream=None) -> None:

@@ -62,11 +62,38 @@ tq_status check_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_c
   st->k = k_cache;
   st->v = v_cache;
   st->scales = kv_scales;
+  st->tq4 = nullptr;
+  st->centroids = nullptr;
+  st->tq4_block_bytes = 0;
   st->bt = block_tables;
   st->num_kv_heads = num_kv_heads;
   st->max_blocks = ext->max_blocks_per_seq;
   st->num_blocks = ext->num_blocks;
   st->qk_scale_log2 = (float)((double)softmax_scale * 1.4426950408889634074);
+  return TQ_OK;
+}
+
+// The same checks for the 4-bit record format (cache and centroids instead of
+// k_cache, v_cache and kv_scales).
+tq_status check_decode_tq4(const void* q_rot, const uint8_t* kv_cache, const float* centroids,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           int32_t num_kv_heads, int32_t query_group_size, int32_t kv_block_size,
+                           int32_t tile_groups_per_partition, float softmax_scale,
+                           const tq_extent* ext, tq::StreamArgs* st, int32_t* E) {
+  if (!kv_cache || !centroids) return TQ_ERR_NULL;
+  // kv_cache stands in for the fp8 pointers: alignment and null checks alike.
+  tq_status s = check_decode(q_rot, kv_cache, kv_cache, reinterpret_cast<const float*>(kv_cache),
+                             block_tables, seq_lens, num_kv_heads, query_group_size, kv_block_size,
+                             tile_groups_per_partition, softmax_scale, ext, st, E);
+  if (s != TQ_OK) return s;
+  if (!aligned4(centroids)) return TQ_ERR_MISALIGNED;
+  const int64_t block_bytes = (int64_t)num_kv_heads * kv_block_size * (TQ_HEAD_DIM + 3 * 2);
+  if (block_bytes > INT32_MAX) return TQ_ERR_SHAPE;
+  st->k = st->v = nullptr;
+  st->scales = nullptr;
+  st->tq4 = kv_cache;
+  st->centroids = centroids;
+  st->tq4_block_bytes = (int32_t)block_bytes;
   return TQ_OK;
 }
 
@@ -76,6 +103,64 @@ tq_status hip_status(hipError_t e) {
     return TQ_ERR_HIP;
   }
   return TQ_OK;
+}
+
+// The partition kernel of either format, after the checks.
+tq_status run_partition(const tq::StreamArgs& st, const int32_t* seq_lens,
+                        const tq_partials* partials, int32_t query_group_size,
+                        int32_t kv_block_size, int32_t E, const tq_extent* ext, bool tq4,
+                        void* stream) {
+  if (!aligned16(partials->out) || !aligned4(partials->max_logits) || !aligned4(partials->exp_sums))
+    return TQ_ERR_MISALIGNED;
+  tq::PartitionArgs a;
+  a.st = st;
+  a.seq_lens = seq_lens;
+  a.o = partials->out;
+  a.ml = partials->max_logits;
+  a.es = partials->exp_sums;
+  a.num_partitions = ext->num_partitions;
+  a.partition_tokens = E;
+  a.parts_per_wave = 1;  // chosen by the launcher
+  a.len_cap = ext->max_seq_len;
+  return hip_status(tq::launch_partition(a, ext->num_seqs, query_group_size, kv_block_size, tq4,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+// The fused decode of either format, after the checks: the even split when
+// it applies and the workspace holds it, else workgroups per (s, h).
+tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out,
+                    int32_t num_kv_heads, int32_t query_group_size, int32_t kv_block_size,
+                    const tq_extent* ext, void* workspace, size_t workspace_bytes, bool tq4,
+                    void* stream) {
+  if (!aligned16(out) || (workspace && !aligned16(workspace))) return TQ_ERR_MISALIGNED;
+  const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
+  const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
+  if (flat_groups > 0 && workspace &&
+      workspace_bytes >= tq::flat_workspace_bytes(seq_heads, flat_groups, query_group_size)) {
+    tq::FlatArgs f;
+    f.st = st;
+    f.seq_lens = seq_lens;
+    f.out = static_cast<uint16_t*>(out);
+    f.len_cap = ext->max_seq_len;
+    f.num_seqs = ext->num_seqs;
+    f.n_groups = flat_groups;
+    tq::bind_flat_workspace(&f, workspace, seq_heads, query_group_size);
+    return hip_status(tq::launch_flat(f, query_group_size, kv_block_size, tq4,
+                                      static_cast<hipStream_t>(stream)));
+  }
+  const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size,
+                                            workspace ? workspace_bytes : 0);
+  tq::FusedArgs a;
+  a.st = st;
+  a.seq_lens = seq_lens;
+  a.out = static_cast<uint16_t*>(out);
+  a.len_cap = ext->max_seq_len;
+  a.splits = plan.splits;
+  a.counters = nullptr;
+  a.ws_o = a.ws_m = a.ws_l = nullptr;
+  if (plan.splits > 1) tq::bind_fused_workspace(&a, workspace, seq_heads, query_group_size);
+  return hip_status(tq::launch_fused(a, ext->num_seqs, plan.waves, query_group_size, kv_block_size,
+                                     tq4, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -89,24 +174,14 @@ tq_status tq_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_cach
                     const tq_extent* ext, void* stream) {
   if (!partials || !partials->out || !partials->max_logits || !partials->exp_sums)
     return TQ_ERR_NULL;
-  tq::PartitionArgs a;
+  tq::StreamArgs st;
   int32_t E = 0;
-  tq_status st = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
+  tq_status rc = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
                               query_group_size, kv_block_size, tile_groups_per_partition,
-                              softmax_scale, ext, &a.st, &E);
-  if (st != TQ_OK) return st;
-  if (!aligned16(partials->out) || !aligned4(partials->max_logits) || !aligned4(partials->exp_sums))
-    return TQ_ERR_MISALIGNED;
-  a.seq_lens = seq_lens;
-  a.o = partials->out;
-  a.ml = partials->max_logits;
-  a.es = partials->exp_sums;
-  a.num_partitions = ext->num_partitions;
-  a.partition_tokens = E;
-  a.parts_per_wave = 1;  // chosen by the launcher
-  a.len_cap = ext->max_seq_len;
-  return hip_status(tq::launch_partition(a, ext->num_seqs, query_group_size, kv_block_size,
-                                         static_cast<hipStream_t>(stream)));
+                              softmax_scale, ext, &st, &E);
+  if (rc != TQ_OK) return rc;
+  return run_partition(st, seq_lens, partials, query_group_size, kv_block_size, E, ext, false,
+                       stream);
 }
 
 tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
@@ -117,39 +192,53 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
                           const tq_extent* ext, void* workspace, size_t workspace_bytes,
                           void* stream) {
   if (!out) return TQ_ERR_NULL;
-  tq::FusedArgs a;
+  tq::StreamArgs st;
   int32_t E = 0;
-  tq_status st = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
+  tq_status rc = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
                               query_group_size, kv_block_size, tile_groups_per_partition,
-                              softmax_scale, ext, &a.st, &E);
-  if (st != TQ_OK) return st;
-  if (!aligned16(out) || (workspace && !aligned16(workspace))) return TQ_ERR_MISALIGNED;
-  const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
-  const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
-  if (flat_groups > 0 && workspace &&
-      workspace_bytes >= tq::flat_workspace_bytes(seq_heads, flat_groups, query_group_size)) {
-    tq::FlatArgs f;
-    f.st = a.st;
-    f.seq_lens = seq_lens;
-    f.out = static_cast<uint16_t*>(out);
-    f.len_cap = ext->max_seq_len;
-    f.num_seqs = ext->num_seqs;
-    f.n_groups = flat_groups;
-    tq::bind_flat_workspace(&f, workspace, seq_heads, query_group_size);
-    return hip_status(tq::launch_flat(f, query_group_size, kv_block_size,
-                                      static_cast<hipStream_t>(stream)));
-  }
-  const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size,
-                                            workspace ? workspace_bytes : 0);
-  a.seq_lens = seq_lens;
-  a.out = static_cast<uint16_t*>(out);
-  a.len_cap = ext->max_seq_len;
-  a.splits = plan.splits;
-  a.counters = nullptr;
-  a.ws_o = a.ws_m = a.ws_l = nullptr;
-  if (plan.splits > 1) tq::bind_fused_workspace(&a, workspace, seq_heads, query_group_size);
-  return hip_status(tq::launch_fused(a, ext->num_seqs, plan.waves, query_group_size, kv_block_size,
-                                     static_cast<hipStream_t>(stream)));
+                              softmax_scale, ext, &st, &E);
+  if (rc != TQ_OK) return rc;
+  return run_fused(st, seq_lens, out, num_kv_heads, query_group_size, kv_block_size, ext,
+                   workspace, workspace_bytes, false, stream);
+}
+
+tq_status tq4_decode(const void* q_rot, const uint8_t* kv_cache, const float* centroids,
+                     const int32_t* block_tables, const int32_t* seq_lens,
+                     const tq_partials* partials, int32_t num_kv_heads, int32_t query_group_size,
+                     int32_t kv_block_size, int32_t tile_groups_per_partition, float softmax_scale,
+                     const tq_extent* ext, void* stream) {
+  if (!partials || !partials->out || !partials->max_logits || !partials->exp_sums)
+    return TQ_ERR_NULL;
+  tq::StreamArgs st;
+  int32_t E = 0;
+  tq_status rc = check_decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads,
+                                  query_group_size, kv_block_size, tile_groups_per_partition,
+                                  softmax_scale, ext, &st, &E);
+  if (rc != TQ_OK) return rc;
+  return run_partition(st, seq_lens, partials, query_group_size, kv_block_size, E, ext, true,
+                       stream);
+}
+
+tq_status tq4_decode_fused(const void* q_rot, const uint8_t* kv_cache, const float* centroids,
+                           const int32_t* block_tables, const int32_t* seq_lens, void* out,
+                           int32_t num_kv_heads, int32_t query_group_size, int32_t kv_block_size,
+                           int32_t tile_groups_per_partition, float softmax_scale,
+                           const tq_extent* ext, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (!out) return TQ_ERR_NULL;
+  tq::StreamArgs st;
+  int32_t E = 0;
+  tq_status rc = check_decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads,
+                                  query_group_size, kv_block_size, tile_groups_per_partition,
+                                  softmax_scale, ext, &st, &E);
+  if (rc != TQ_OK) return rc;
+  return run_fused(st, seq_lens, out, num_kv_heads, query_group_size, kv_block_size, ext,
+                   workspace, workspace_bytes, true, stream);
+}
+
+size_t tq4_block_bytes(int32_t num_kv_heads, int32_t kv_block_size) {
+  if (num_kv_heads < 1 || !supported_bs(kv_block_size)) return 0;
+  return (size_t)num_kv_heads * kv_block_size * (TQ_HEAD_DIM + 3 * 2);
 }
 
 size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,

@@ -11,12 +11,16 @@ namespace tq {
 constexpr int kHeadDim = 128;
 constexpr int kTokensPerTileGroup = 256;
 
-// What every decode kernel reads to stream one (sequence, kv head).
+// What every decode kernel reads to stream one (sequence, kv head).  The fp8
+// format uses k, v and scales; the 4-bit record format tq4 and centroids.
 struct StreamArgs {
   const uint16_t* q;        // bf16 [S][Hkv*QG][128]
   const uint8_t* k;         // e4m3fn [NB][Hkv][BS][128]
   const uint8_t* v;         // e4m3fn [NB][Hkv][BS][128]
   const float* scales;      // fp32 [NB][Hkv][2][BS]
+  const uint8_t* tq4;       // 4-bit records [NB][tq4_block_bytes]
+  const float* centroids;   // fp32 [16]
+  int32_t tq4_block_bytes;  // Hkv*BS*128 + Hkv*3*BS*2
   const int32_t* bt;        // int32 [S][max_blocks]
   int32_t num_kv_heads;
   int32_t max_blocks;       // block-table row stride
@@ -114,11 +118,12 @@ struct KvWriteArgs {
 // Enqueue the kernels; each returns the launch status (hipGetLastError after
 // the launch).  launch_partition chooses parts_per_wave and launch_fused the
 // waves per workgroup from the sizes.
+// tq4 selects the 4-bit record format.
 hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
-                            int kv_block_size, hipStream_t stream);
+                            int kv_block_size, bool tq4, hipStream_t stream);
 hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_group_size,
-                        int kv_block_size, hipStream_t stream);
-hipError_t launch_flat(const FlatArgs& a, int query_group_size, int kv_block_size,
+                        int kv_block_size, bool tq4, hipStream_t stream);
+hipError_t launch_flat(const FlatArgs& a, int query_group_size, int kv_block_size, bool tq4,
                        hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);

@@ -123,11 +123,13 @@ struct WaveState {
   float m2;
   float lsum;
   float sigma;
+  float zsum;  // 4-bit format: this lane's share of sum_t p_t * vzero_t
   f32x4 acc[8];
   __device__ __forceinline__ void reset() {
     m2 = kNegInf;
     lsum = 0.f;
     sigma = 0.f;
+    zsum = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -140,7 +142,40 @@ struct WaveState {
     for (int dblk = 0; dblk < 8; ++dblk) o[dblk] = acc[dblk] * f;
     return l;
   }
+  // The same for the 4-bit format, o = (acc * sigma + zsum) / l: acc[2pc + par]
+  // holds d = 32 pc + 8b + 2i + par (par 0: even dims; par 1: odd dims, carried
+  // at 16x); o is returned interleaved, o[2pc + half] = d = 32 pc + 8b + 4 half
+  // + 0..3.
+  __device__ __forceinline__ float finish_tq4(f32x4 o[8]) const {
+    const float l = wave_sum_xor16_32(lsum);
+    const float z = wave_sum_xor16_32(zsum);
+    const float f = sigma / l;
+    const float f16th = f * 0.0625f;
+    const float zl = z / l;
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc) {
+      const f32x4 e = acc[2 * pc] * f + zl;
+      const f32x4 od = acc[2 * pc + 1] * f16th + zl;
+      o[2 * pc] = f32x4{e[0], od[0], e[1], od[1]};
+      o[2 * pc + 1] = f32x4{e[2], od[2], e[3], od[3]};
+    }
+    return l;
+  }
+  template <bool TQ4>
+  __device__ __forceinline__ float finish_as(f32x4 o[8]) const {
+    if constexpr (TQ4)
+      return finish_tq4(o);
+    else
+      return finish(o);
+  }
 };
+
+// Column of the first of the 4 consecutive dims o[dblk] holds in lane group b,
+// as returned by finish (fp8) or finish_tq4 (4-bit format).
+template <bool TQ4>
+__device__ __forceinline__ int out_col(int dblk, int b) {
+  return TQ4 ? 32 * (dblk >> 1) + 8 * b + 4 * (dblk & 1) : 16 * dblk + 4 * b;
+}
 
 // Walk tokens [t_begin, t_end) of (s, h) in 32-token chunks, accumulating into
 // `w`.  Every `chunks_per_part` chunks, on_boundary(k, w) is called with the
@@ -330,8 +365,10 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
       pop[i] = (_Float16)(pr[i] * (vs0[i] * inv_sigma));
       pop[4 + i] = (_Float16)(pr[4 + i] * (vs1[i] * inv_sigma));
     }
+    if (__ballot(acc_scale != 1.0f)) {  // a factor of exactly 1 changes no bits
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
+      for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
+    }
 
     // ---- PV: acc[dblk] (O^T[d = 16 dblk + 4b + i][query r]) += V^T P ----
 #pragma unroll
@@ -342,14 +379,314 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
   }
 }
 
+// ---------------------------------------------------------------------------
+// The 4-bit record format ("TQ" record of the tq_decode page).  A cache block
+// is [Hkv][BS][128] bytes of rows (K indices in bytes 0..63, V indices in
+// 64..127; dim d in byte d/2, low nibble for even d), then fp16 metadata
+// [Hkv][3][BS]: K norm, V scale, V zero point.  k = centroids[index] * norm,
+// v = index * scale + zero.
+//
+// Per-wave LDS of the 4-bit stream (inside the same 8.5 KiB staging area):
+// two 2 KiB V stages (32 rows of 64 B, 16-byte pieces XOR-swizzled by bits 1..2
+// of the row), two 256 B metadata stages ([3][32] fp16) and a 256-entry table
+// that maps an index byte to the centroids c of its two nibbles as two bf16
+// pairs, hi = bf16(c) then lo = bf16(c - hi): about 16 significant bits
+// together, so the QK product does not round the codebook to bf16's 8.  The
+// lo parts enter the contraction as extra dims against a duplicated q: one
+// MFMA operand = (hi, lo) of two index bytes = dims (d0, d1, d0, d1, d2, d3,
+// d2, d3), q = (q0, q1, q0, q1, q2, q3, q2, q3).
+constexpr int kTq4VStage = CHUNK * 64;
+constexpr int kTq4MetaStage = 256;
+constexpr int kTq4MetaOff = 2 * kTq4VStage;
+constexpr int kTq4TableOff = kTq4MetaOff + 2 * kTq4MetaStage;
+static_assert(kTq4TableOff + 256 * 8 <= 2 * CHUNK * D + 2 * 2 * CHUNK * 4, "4-bit staging area");
+
+__device__ __forceinline__ int tq4_v_lds_offset(int tok, int piece) {
+  return tok * 64 + 16 * (piece ^ ((tok >> 1) & 3));
+}
+
+// 8 index bytes (one per token) -> f16 operands of the 8 low nibbles (n) and of
+// the 8 high nibbles (16 n): a byte permute puts each masked byte under the f16
+// exponent byte 0x64, giving 1024 + n (or 1024 + 16 n), and subtracting 1024 is
+// exact.  The odd dims are thus carried at 16x and scaled back at the end.
+__device__ __forceinline__ void tq4_nibbles_f16(i32x2 raw, f16x8& lo, f16x8& hi) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  constexpr uint32_t kExp = 0x64646464u;
+  u32x4 l, h;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    const uint32_t ml = (uint32_t)raw[w] & 0x0F0F0F0Fu;
+    const uint32_t mh = (uint32_t)raw[w] & 0xF0F0F0F0u;
+    // result bytes: (m.b0, 0x64, m.b1, 0x64) and (m.b2, 0x64, m.b3, 0x64)
+    l[2 * w] = __builtin_amdgcn_perm(kExp, ml, 0x04010400u);
+    l[2 * w + 1] = __builtin_amdgcn_perm(kExp, ml, 0x04030402u);
+    h[2 * w] = __builtin_amdgcn_perm(kExp, mh, 0x04010400u);
+    h[2 * w + 1] = __builtin_amdgcn_perm(kExp, mh, 0x04030402u);
+  }
+  const f16x8 k1024 = {(_Float16)1024, (_Float16)1024, (_Float16)1024, (_Float16)1024,
+                       (_Float16)1024, (_Float16)1024, (_Float16)1024, (_Float16)1024};
+  lo = __builtin_bit_cast(f16x8, l) - k1024;
+  hi = __builtin_bit_cast(f16x8, h) - k1024;
+}
+
+// The 4-bit counterpart of stream_tokens: same contract, same chunk pipeline.
+template <int QG, int BS, typename OnBoundary>
+__device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, int h, int t_begin,
+                                                  int t_end, int chunks_per_part, uint8_t* lds,
+                                                  WaveState& w, OnBoundary on_boundary) {
+  static_assert(BS == 16 || BS == 32, "kv block size");
+  static_assert(QG >= 1 && QG <= 16, "query group size");
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15;
+  const int b = lane >> 4;
+  const int Hkv = a.num_kv_heads;
+  const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
+  const int n_blocks = (t_end - t_begin + BS - 1) / BS;
+  const int32_t* bt_row = a.bt + (size_t)s * a.max_blocks + t_begin / BS;
+  const uint32_t nb_max = (uint32_t)a.num_blocks - 1u;
+  const size_t block_bytes = (size_t)a.tq4_block_bytes;
+  const size_t meta_base = (size_t)Hkv * BS * D + (size_t)h * 3 * BS * 2;
+
+  int bt_win = 0;
+  int bt_reg = lane < n_blocks ? bt_row[lane] : 0;
+  auto block_id = [&](int j) -> uint32_t {
+    if ((j >> 6) != bt_win) {
+      bt_win = j >> 6;
+      const int e = 64 * bt_win + lane;
+      bt_reg = e < n_blocks ? bt_row[e] : 0;
+    }
+    const uint32_t id = (uint32_t)__builtin_amdgcn_readlane(bt_reg, j & 63);
+    return id < nb_max ? id : nb_max;
+  };
+
+  // Centroid table: entry x = {hi pair, lo pair} of (c[x & 15], c[x >> 4]),
+  // the first value of each pair in the low half.
+  i32x2* tab = reinterpret_cast<i32x2*>(lds + kTq4TableOff);
+  {
+    const float cl = a.centroids[lane & 15];
+    const uint16_t chi = f32_to_bf16_rne(cl);
+    const uint16_t clo = f32_to_bf16_rne(cl - __uint_as_float((uint32_t)chi << 16));
+    const int pair_hl = (int)((uint32_t)chi | ((uint32_t)clo << 16));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int x = lane + 64 * i;
+      const uint32_t e0 = (uint32_t)__shfl(pair_hl, x & 15, 64);  // c[x & 15]: hi | lo << 16
+      const uint32_t e1 = (uint32_t)__shfl(pair_hl, x >> 4, 64);  // c[x >> 4]
+      tab[x] = i32x2{(int)((e0 & 0xFFFFu) | (e1 << 16)), (int)((e0 >> 16) | (e1 & 0xFFFF0000u))};
+    }
+  }
+
+  // q operands, duplicated pairs: qdup[2c + half] = dims 8c + 4 half + (0, 1, 0,
+  // 1, 2, 3, 2, 3) of this lane's 32 (the d-permutation of stream_tokens).
+  bf16x8 qdup[8];
+  {
+    bf16x8 qop[4];
+    if (r < QG) {
+      const uint16_t* qrow = a.q + ((size_t)(s * Hkv + h) * QG + r) * D + 32 * b;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qrow + 8 * c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) qop[c] = bf16x8{};
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int o = 4 * hf;
+        qdup[2 * c + hf] = bf16x8{qop[c][o], qop[c][o + 1], qop[c][o], qop[c][o + 1],
+                                  qop[c][o + 2], qop[c][o + 3], qop[c][o + 2], qop[c][o + 3]};
+      }
+  }
+
+  // Issue chunk c: K index rows (16 B per lane and tile) into registers, V
+  // index rows and the metadata into LDS stage `st`.
+  i32x4 kraw[2];
+  auto issue = [&](int c, int st) {
+    const int jb = (c * CHUNK) / BS;
+    const uint32_t blkA = block_id(jb);
+    uint32_t blkB = blkA;
+    if (BS == 16) blkB = (jb + 1 < n_blocks) ? block_id(jb + 1) : blkA;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t blk = (BS == 32 || t == 0) ? blkA : blkB;
+      const int slot = BS == 32 ? 16 * t + r : r;
+      const uint8_t* src = a.tq4 + blk * block_bytes + ((size_t)h * BS + slot) * D + 16 * b;
+      kraw[t] = *reinterpret_cast<const i32x4*>(src);
+    }
+    uint8_t* vdst = lds + st * kTq4VStage;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int tok = 16 * j + (lane >> 2);
+      const int piece = (lane & 3) ^ ((tok >> 1) & 3);
+      const uint32_t blk = (BS == 32 || tok < 16) ? blkA : blkB;
+      const int slot = BS == 32 ? tok : (tok & 15);
+      const uint8_t* src = a.tq4 + blk * block_bytes + ((size_t)h * BS + slot) * D + 64 + 16 * piece;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(vdst + 1024 * j), 16, 0,
+                                       kCachePolicyStreaming);
+    }
+    {
+      // LDS dword l (l < 48) = field l / 16, tokens 2 (l % 16) and +1.
+      const int l = lane < 48 ? lane : 0;
+      const int field = l >> 4, pair = l & 15;
+      const uint32_t blk = (BS == 32 || pair < 8) ? blkA : blkB;
+      const int dword = BS == 32 ? l : field * 8 + (pair & 7);
+      const uint8_t* src = a.tq4 + blk * block_bytes + meta_base + 4 * dword;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + kTq4MetaOff + st * kTq4MetaStage), 4,
+                                       0, kCachePolicyStreaming);
+    }
+  };
+
+  const int tr_tok = 16 * (r >> 3) + 4 * b + ((r >> 1) & 3);
+  const int tr_half = 8 * (r & 1);
+
+  issue(0, 0);
+  int next_boundary = chunks_per_part;
+  int part_done = 0;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int st = c & 1;
+    // Drain chunk c and take everything it needs out of LDS (metadata, V index
+    // rows, and the centroids of its K indices) before chunk c+1's LDS-direct
+    // loads are issued.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* meta = lds + kTq4MetaOff + st * kTq4MetaStage;
+    typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+    const f16x4 kn0 = *reinterpret_cast<const f16x4*>(meta + 2 * (4 * b));
+    const f16x4 kn1 = *reinterpret_cast<const f16x4*>(meta + 2 * (16 + 4 * b));
+    const f16x4 vs0h = *reinterpret_cast<const f16x4*>(meta + 64 + 2 * (4 * b));
+    const f16x4 vs1h = *reinterpret_cast<const f16x4*>(meta + 64 + 2 * (16 + 4 * b));
+    const f16x4 vz0h = *reinterpret_cast<const f16x4*>(meta + 128 + 2 * (4 * b));
+    const f16x4 vz1h = *reinterpret_cast<const f16x4*>(meta + 128 + 2 * (16 + 4 * b));
+    i32x2 vraw[4];
+    const uint8_t* vt = lds + st * kTq4VStage;
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc)
+      vraw[pc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_i32x2*)(vt + tq4_v_lds_offset(tr_tok, pc) + tr_half));
+    // K operands: kop[t][2cc + hf] = (hi, lo) of index bytes 2hf and 2hf + 1 of
+    // dword cc, i.e. dims 8cc + 4hf + (0, 1, 0, 1, 2, 3, 2, 3).
+    bf16x8 kop[2][8];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const uint32_t x = (uint32_t)kraw[t][cc];
+        const i32x2 e0 = tab[x & 0xFF], e1 = tab[(x >> 8) & 0xFF], e2 = tab[(x >> 16) & 0xFF],
+                    e3 = tab[x >> 24];
+        kop[t][2 * cc] = __builtin_bit_cast(bf16x8, i32x4{e0[0], e0[1], e1[0], e1[1]});
+        kop[t][2 * cc + 1] = __builtin_bit_cast(bf16x8, i32x4{e2[0], e2[1], e3[0], e3[1]});
+      }
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < n_chunks) issue(c + 1, st ^ 1);
+    if (c == next_boundary) {
+      on_boundary(part_done, w);
+      ++part_done;
+      next_boundary += chunks_per_part;
+    }
+
+    const int nvalid = min(CHUNK, t_end - (t_begin + c * CHUNK));
+
+    // ---- QK^T: C[token 4b+i][query r] for tiles 0 and 1 ----
+    f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][k], qdup[k], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][k], qdup[k], s1, 0, 0, 0);
+    }
+
+    // ---- scale by the K norm, mask ----
+    float y[8], vs[8], vz[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      y[i] = s0[i] * ((float)kn0[i] * a.qk_scale_log2);
+      y[4 + i] = s1[i] * ((float)kn1[i] * a.qk_scale_log2);
+      vs[i] = (float)vs0h[i];
+      vs[4 + i] = (float)vs1h[i];
+      vz[i] = (float)vz0h[i];
+      vz[4 + i] = (float)vz1h[i];
+    }
+    if (nvalid < CHUNK) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const bool v0 = 4 * b + i < nvalid, v1 = 16 + 4 * b + i < nvalid;
+        y[i] = v0 ? y[i] : kNegInf;
+        y[4 + i] = v1 ? y[4 + i] : kNegInf;
+        vs[i] = v0 ? vs[i] : 0.f;
+        vs[4 + i] = v1 ? vs[4 + i] : 0.f;
+        vz[i] = v0 ? vz[i] : 0.f;
+        vz[4 + i] = v1 ? vz[4 + i] : 0.f;
+      }
+    }
+
+    // ---- online softmax (base 2) ----
+    float mx = y[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
+    mx = wave_max_xor16_32(mx);
+    const float m2_new = fmaxf(w.m2, mx);
+    const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
+    float pr[8];
+    float psum = 0.f, zs = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pr[i] = __builtin_amdgcn_exp2f(y[i] - m2_new);
+      psum += pr[i];
+      zs += pr[i] * vz[i];
+    }
+    w.lsum = w.lsum * alpha + psum;
+    w.zsum = w.zsum * alpha + zs;
+    w.m2 = m2_new;
+
+    // ---- V-scale reference and P operand ----
+    float vmax = vs[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) vmax = fmaxf(vmax, vs[i]);
+    vmax = wave_max_xor16_32(vmax);
+    const float sigma_new = fmaxf(w.sigma, vmax);
+    const float inv_sigma = sigma_new > 0.f ? 1.0f / sigma_new : 0.f;
+    const float acc_scale = alpha * (w.sigma * inv_sigma);
+    w.sigma = sigma_new;
+    f16x8 pop;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pop[i] = (_Float16)(pr[i] * (vs[i] * inv_sigma));
+    if (__ballot(acc_scale != 1.0f)) {  // a factor of exactly 1 changes no bits
+#pragma unroll
+      for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
+    }
+
+    // ---- PV: acc[2pc + par] (dims 32 pc + 2m + par, m = 4b + i) += V^T P ----
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc) {
+      f16x8 vlo, vhi;
+      tq4_nibbles_f16(vraw[pc], vlo, vhi);
+      w.acc[2 * pc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, pop, w.acc[2 * pc], 0, 0, 0);
+      w.acc[2 * pc + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, pop, w.acc[2 * pc + 1], 0, 0, 0);
+    }
+  }
+}
+
+// One stream call for either format (lds_v: the wave's staging area, lds_sc:
+// the fp8 scale stages inside it).
+template <int QG, int BS, bool TQ4, typename OnBoundary>
+__device__ __forceinline__ void stream_any(const StreamArgs& a, int s, int h, int t_begin, int t_end,
+                                           int chunks_per_part, uint8_t* lds_v, float* lds_sc,
+                                           WaveState& w, OnBoundary on_boundary) {
+  if constexpr (TQ4)
+    stream_tokens_tq4<QG, BS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, w, on_boundary);
+  else
+    stream_tokens<QG, BS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_sc, w, on_boundary);
+}
+
 // Clamp a device-side sequence length into [0, cap].
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
 // Split-K partition kernel: one wave per group of `parts_per_wave`
 // consecutive partitions of one (s, h); writes the partial triple of every
 // live partition in the group (STEP G).
-template <int QG, int BS>
-__global__ __launch_bounds__(64) void tq_partition_kernel(PartitionArgs a) {
+template <int QG, int BS, bool TQ4>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq_partition_kernel(PartitionArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * CHUNK * D];
   __shared__ __attribute__((aligned(16))) float lds_sc[2 * 2 * CHUNK];
   const int lane = threadIdx.x;
@@ -374,12 +711,13 @@ __global__ __launch_bounds__(64) void tq_partition_kernel(PartitionArgs a) {
   // log units), l_p; then the running state restarts.
   auto store_partial = [&](int p, WaveState& w) {
     f32x4 o[8];
-    const float l = w.finish(o);
+    const float l = w.template finish_as<TQ4>(o);
     if (r < QG) {
       const size_t row = ((size_t)(s * Hkv + h) * P + p) * QG + r;
-      float* dst = a.o + row * D + 4 * b;
+      float* dst = a.o + row * D;
 #pragma unroll
-      for (int dblk = 0; dblk < 8; ++dblk) *reinterpret_cast<f32x4*>(dst + 16 * dblk) = o[dblk];
+      for (int dblk = 0; dblk < 8; ++dblk)
+        *reinterpret_cast<f32x4*>(dst + out_col<TQ4>(dblk, b)) = o[dblk];
       if (b == 0) {
         a.ml[row] = w.m2 * kLn2;
         a.es[row] = l;
@@ -391,8 +729,8 @@ __global__ __launch_bounds__(64) void tq_partition_kernel(PartitionArgs a) {
   WaveState w;
   w.reset();
   const int chunks_per_part = E / CHUNK;
-  stream_tokens<QG, BS>(a.st, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_sc, w,
-                        [&](int k, WaveState& ws) { store_partial(p0 + k, ws); });
+  stream_any<QG, BS, TQ4>(a.st, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_sc, w,
+                          [&](int k, WaveState& ws) { store_partial(p0 + k, ws); });
   const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
   store_partial(p0 + (n_chunks - 1) / chunks_per_part, w);
 }
@@ -457,7 +795,7 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 o) {
 // workspace, releases it at device scope and counts itself in; the last to
 // arrive acquires all partials, merges them in workgroup order (so the result
 // does not depend on arrival order), writes out and re-arms the counter to 0.
-template <int QG, int BS>
+template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   __shared__ int last_arrival;
@@ -499,15 +837,15 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
     const int t_end = min(t_begin + per_wave * TG, min((tg0 + cnt) * TG, L));
     WaveState w;
     w.reset();
-    stream_tokens<QG, BS>(a.st, s, h, t_begin, t_end, 0x7fffffff, region,
-                          reinterpret_cast<float*>(region + 2 * CHUNK * D), w,
-                          [](int, WaveState&) {});
+    stream_any<QG, BS, TQ4>(a.st, s, h, t_begin, t_end, 0x7fffffff, region,
+                            reinterpret_cast<float*>(region + 2 * CHUNK * D), w,
+                            [](int, WaveState&) {});
     f32x4 o[8];
-    const float l = w.finish(o);
+    const float l = w.template finish_as<TQ4>(o);
     if (r < QG) {
 #pragma unroll
       for (int dblk = 0; dblk < 8; ++dblk)
-        *reinterpret_cast<f32x4*>(part_o + r * D + 16 * dblk + 4 * b) = o[dblk];
+        *reinterpret_cast<f32x4*>(part_o + r * D + out_col<TQ4>(dblk, b)) = o[dblk];
       if (b == 0) {
         part_m[r] = w.m2 * kLn2;
         part_l[r] = l;
@@ -667,14 +1005,14 @@ struct FlatLayout {
 };
 
 // Store the wave's finished partial (rows r < QG) at piece P.
-template <int QG>
+template <int QG, bool TQ4>
 __device__ __forceinline__ void store_piece(float* P, const f32x4 o[8], float m, float l) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, b = lane >> 4;
   if (r < QG) {
 #pragma unroll
     for (int dblk = 0; dblk < 8; ++dblk)
-      *reinterpret_cast<f32x4*>(P + r * D + 16 * dblk + 4 * b) = o[dblk];
+      *reinterpret_cast<f32x4*>(P + r * D + out_col<TQ4>(dblk, b)) = o[dblk];
     if (b == 0) {
       P[QG * D + r] = m;
       P[QG * D + 16 + r] = l;
@@ -682,7 +1020,7 @@ __device__ __forceinline__ void store_piece(float* P, const f32x4 o[8], float m,
   }
 }
 
-template <int QG, int BS>
+template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   using Lay = FlatLayout<QG>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
@@ -788,25 +1126,25 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
       const int sh = s * Hkv + h;
       WaveState st;
       st.reset();
-      stream_tokens<QG, BS>(a.st, s, h, k0 * TG, min(k1 * TG, L), 0x7fffffff, area,
-                            reinterpret_cast<float*>(area + 2 * CHUNK * D), st,
-                            [](int, WaveState&) {});
+      stream_any<QG, BS, TQ4>(a.st, s, h, k0 * TG, min(k1 * TG, L), 0x7fffffff, area,
+                              reinterpret_cast<float*>(area + 2 * CHUNK * D), st,
+                              [](int, WaveState&) {});
       f32x4 o[8];
-      const float l = st.finish(o);
+      const float l = st.template finish_as<TQ4>(o);
       if (k0 == 0 && k1 == n) {  // the whole (s, h)
         const int r = lane & 15, b = lane >> 4;
         if (r < QG) {
-          uint16_t* dst = a.out + ((size_t)sh * QG + r) * D + 4 * b;
+          uint16_t* dst = a.out + ((size_t)sh * QG + r) * D;
 #pragma unroll
-          for (int dblk = 0; dblk < 8; ++dblk) store_bf16x4(dst + 16 * dblk, o[dblk]);
+          for (int dblk = 0; dblk < 8; ++dblk) store_bf16x4(dst + out_col<TQ4>(dblk, b), o[dblk]);
         }
       } else if (first_seg) {
-        store_piece<QG>(first_piece, o, st.m2 * kLn2, l);
+        store_piece<QG, TQ4>(first_piece, o, st.m2 * kLn2, l);
         f_sh = sh;
         f_ea = base + h * n;
         f_n = n;
       } else {  // a piece that is not the first is the wave's last segment
-        store_piece<QG>(last_piece, o, st.m2 * kLn2, l);
+        store_piece<QG, TQ4>(last_piece, o, st.m2 * kLn2, l);
         l_sh = sh;
         l_ea = base + h * n;
         l_n = n;
@@ -1158,82 +1496,84 @@ void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_gro
   a->ws_l = reinterpret_cast<float*>(p);
 }
 
-template <int QG, int BS>
+// Run LAUNCH_T<QG, BS, TQ4>(args...) for the runtime sizes and format.
+#define TQ_DISPATCH(LAUNCH_T, qg, bs, tq4, ...)                                              \
+  do {                                                                                      \
+    if ((qg) == 6 && (bs) == 16) return (tq4) ? LAUNCH_T<6, 16, true>(__VA_ARGS__)           \
+                                              : LAUNCH_T<6, 16, false>(__VA_ARGS__);        \
+    if ((qg) == 6 && (bs) == 32) return (tq4) ? LAUNCH_T<6, 32, true>(__VA_ARGS__)           \
+                                              : LAUNCH_T<6, 32, false>(__VA_ARGS__);        \
+    if ((qg) == 8 && (bs) == 16) return (tq4) ? LAUNCH_T<8, 16, true>(__VA_ARGS__)           \
+                                              : LAUNCH_T<8, 16, false>(__VA_ARGS__);        \
+    if ((qg) == 8 && (bs) == 32) return (tq4) ? LAUNCH_T<8, 32, true>(__VA_ARGS__)           \
+                                              : LAUNCH_T<8, 32, false>(__VA_ARGS__);        \
+    if ((qg) == 16 && (bs) == 16) return (tq4) ? LAUNCH_T<16, 16, true>(__VA_ARGS__)         \
+                                               : LAUNCH_T<16, 16, false>(__VA_ARGS__);      \
+    if ((qg) == 16 && (bs) == 32) return (tq4) ? LAUNCH_T<16, 32, true>(__VA_ARGS__)         \
+                                               : LAUNCH_T<16, 32, false>(__VA_ARGS__);      \
+    return hipErrorInvalidValue;                                                            \
+  } while (0)
+
+template <int QG, int BS, bool TQ4>
 hipError_t launch_flat_t(const FlatArgs& a, hipStream_t stream) {
   constexpr size_t lds = (size_t)kFlatWaves * FlatLayout<QG>::kArea;
   // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
   // the runtime needs none, and must not leak into the launch status.
   static const bool lds_opt_in = [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_flat_kernel<QG, BS>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_flat_kernel<QG, BS, TQ4>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     (void)hipGetLastError();
     return true;
   }();
   (void)lds_opt_in;
-  hipLaunchKernelGGL((tq_flat_kernel<QG, BS>), dim3((unsigned)a.n_groups), dim3(64 * kFlatWaves),
-                     lds, stream, a);
+  hipLaunchKernelGGL((tq_flat_kernel<QG, BS, TQ4>), dim3((unsigned)a.n_groups),
+                     dim3(64 * kFlatWaves), lds, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_flat(const FlatArgs& a, int query_group_size, int kv_block_size,
+hipError_t launch_flat(const FlatArgs& a, int query_group_size, int kv_block_size, bool tq4,
                        hipStream_t stream) {
-  if (query_group_size == 6 && kv_block_size == 16) return launch_flat_t<6, 16>(a, stream);
-  if (query_group_size == 6 && kv_block_size == 32) return launch_flat_t<6, 32>(a, stream);
-  if (query_group_size == 8 && kv_block_size == 16) return launch_flat_t<8, 16>(a, stream);
-  if (query_group_size == 8 && kv_block_size == 32) return launch_flat_t<8, 32>(a, stream);
-  if (query_group_size == 16 && kv_block_size == 16) return launch_flat_t<16, 16>(a, stream);
-  if (query_group_size == 16 && kv_block_size == 32) return launch_flat_t<16, 32>(a, stream);
-  return hipErrorInvalidValue;
+  TQ_DISPATCH(launch_flat_t, query_group_size, kv_block_size, tq4, a, stream);
+}
+
+template <int QG, int BS, bool TQ4>
+hipError_t launch_partition_t(const PartitionArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((tq_partition_kernel<QG, BS, TQ4>), grid, dim3(64), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
-                            int kv_block_size, hipStream_t stream) {
+                            int kv_block_size, bool tq4, hipStream_t stream) {
   const int64_t units = (int64_t)num_seqs * a.st.num_kv_heads * a.num_partitions;
   a.parts_per_wave = choose_parts_per_wave(units, a.num_partitions);
   const int64_t groups = (a.num_partitions + a.parts_per_wave - 1) / a.parts_per_wave;
-  const dim3 grid((unsigned)(num_seqs * (int64_t)a.st.num_kv_heads * groups)), block(64);
-#define TQ_LAUNCH(QGV, BSV)                                                            \
-  if (query_group_size == QGV && kv_block_size == BSV) {                              \
-    hipLaunchKernelGGL((tq_partition_kernel<QGV, BSV>), grid, block, 0, stream, a);      \
-    return hipGetLastError();                                                          \
-  }
-  TQ_LAUNCH(6, 16)
-  TQ_LAUNCH(6, 32)
-  TQ_LAUNCH(8, 16)
-  TQ_LAUNCH(8, 32)
-  TQ_LAUNCH(16, 16)
-  TQ_LAUNCH(16, 32)
-#undef TQ_LAUNCH
-  return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(num_seqs * (int64_t)a.st.num_kv_heads * groups));
+  TQ_DISPATCH(launch_partition_t, query_group_size, kv_block_size, tq4, a, grid, stream);
 }
 
-template <int QG, int BS>
+template <int QG, int BS, bool TQ4>
 hipError_t launch_fused_t(const FusedArgs& a, unsigned grid, int waves, hipStream_t stream) {
   // Allow dynamic LDS beyond 64 KiB for this kernel, once; an error here only
   // means the runtime needs no opt-in, and must not leak into the launch status.
   static const bool lds_opt_in = [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_fused_kernel<QG, BS>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_fused_kernel<QG, BS, TQ4>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, 8 * kWaveLds);
     (void)hipGetLastError();
     return true;
   }();
   (void)lds_opt_in;
-  hipLaunchKernelGGL((tq_fused_kernel<QG, BS>), dim3(grid), dim3(64 * waves),
+  hipLaunchKernelGGL((tq_fused_kernel<QG, BS, TQ4>), dim3(grid), dim3(64 * waves),
                      (size_t)waves * kWaveLds, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_group_size,
-                        int kv_block_size, hipStream_t stream) {
+                        int kv_block_size, bool tq4, hipStream_t stream) {
   const unsigned grid = (unsigned)((int64_t)num_seqs * a.st.num_kv_heads * a.splits);
-  if (query_group_size == 6 && kv_block_size == 16) return launch_fused_t<6, 16>(a, grid, waves, stream);
-  if (query_group_size == 6 && kv_block_size == 32) return launch_fused_t<6, 32>(a, grid, waves, stream);
-  if (query_group_size == 8 && kv_block_size == 16) return launch_fused_t<8, 16>(a, grid, waves, stream);
-  if (query_group_size == 8 && kv_block_size == 32) return launch_fused_t<8, 32>(a, grid, waves, stream);
-  if (query_group_size == 16 && kv_block_size == 16) return launch_fused_t<16, 16>(a, grid, waves, stream);
-  if (query_group_size == 16 && kv_block_size == 32) return launch_fused_t<16, 32>(a, grid, waves, stream);
-  return hipErrorInvalidValue;
+  TQ_DISPATCH(launch_fused_t, query_group_size, kv_block_size, tq4, a, grid, waves, stream);
 }
+
+#undef TQ_DISPATCH
 
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_tokens * a.num_kv_heads;

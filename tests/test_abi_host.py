@@ -19,7 +19,7 @@ PROBE_HEADER = os.path.join(ROOT, "include", "tq_probe.h")
 def header_functions(path=HEADER):
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(tq_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(tq4?_\w+)\s*\(", text, flags=re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -173,6 +173,45 @@ def test_fused_workspace_bytes():
     # more than 256 sequences: workgroups per (s, h) instead, split by the per-(s, h) plan
     assert tq.fused_workspace_bytes(257, 8, 8, 8192) == 0   # 2056 (s, h): one workgroup each
     assert tq.fused_workspace_bytes(257, 1, 8, 40960) == 0  # 257 (s, h): one workgroup of 8 waves
+
+
+def call_tq4(lib, *, fused=False, q=A, cache=A, cent=A, bt=A, sl=A, out=A, QG=8, BS=16, G=1, Hkv=2,
+             scale=0.088, S=2, NB=8, MB=4, P=1, maxlen=64, head_dim=128):
+    ext = tq.Extent(S, NB, MB, P, maxlen, head_dim)
+    if fused:
+        return lib.tq4_decode_fused(q, cache, cent, bt, sl, out, Hkv, QG, BS, G, scale,
+                                    ctypes.byref(ext), None, 0, None)
+    ps = tq.PartialsStruct(out, A, A) if out else tq.PartialsStruct(0, A, A)
+    return lib.tq4_decode(q, cache, cent, bt, sl, ctypes.byref(ps), Hkv, QG, BS, G, scale,
+                          ctypes.byref(ext), None)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+@pytest.mark.parametrize("kw,status", [
+    (dict(cache=0), tq.TQ_ERR_NULL),
+    (dict(cent=0), tq.TQ_ERR_NULL),
+    (dict(q=0), tq.TQ_ERR_NULL),
+    (dict(out=0), tq.TQ_ERR_NULL),
+    (dict(QG=7), tq.TQ_ERR_UNSUPPORTED),
+    (dict(BS=8), tq.TQ_ERR_UNSUPPORTED),
+    (dict(head_dim=64), tq.TQ_ERR_UNSUPPORTED),
+    (dict(S=0), tq.TQ_ERR_SHAPE),
+    (dict(maxlen=257), tq.TQ_ERR_COVERAGE),
+    (dict(MB=1, maxlen=17, P=1), tq.TQ_ERR_COVERAGE),
+    (dict(scale=0.0), tq.TQ_ERR_SCALE),
+    (dict(cache=A + 8), tq.TQ_ERR_MISALIGNED),
+    (dict(cent=A + 2), tq.TQ_ERR_MISALIGNED),
+])
+def test_tq4_rejects(lib, fused, kw, status):
+    """The 4-bit entry points check their arguments on the host before any launch."""
+    assert call_tq4(lib, fused=fused, **kw) == status
+
+
+def test_tq4_block_bytes():
+    assert tq.tq4_block_bytes(8, 32) == 8 * 32 * 128 + 8 * 3 * 32 * 2
+    assert tq.tq4_block_bytes(1, 16) == 16 * 134
+    assert tq.tq4_block_bytes(2, 8) == 0
+    assert tq.tq4_block_bytes(0, 16) == 0
 
 
 def call_reduce(lib, *, part=None, sl=A, out=A, QG=8, Hkv=2, G=1, S=2, P=1, maxlen=64):

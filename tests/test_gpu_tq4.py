@@ -1,0 +1,123 @@
+"""The 4-bit record format on the GPU against the fp64 oracle (bf16 out: max abs <= 1e-2, mean
+abs <= 1e-3), both paths (tq4_decode + tq_decode_reduce, and tq4_decode_fused), and its
+bit-exact properties.  Needs an MI355X."""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_gqa_decode_amd as tq
+import workloads
+from gpu_util import ORACLE_THREADS, PATHS, compare, say, units_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_tq4(inp, path, num_partitions=None, tile_groups=None):
+    wl = inp.wl
+    G = wl.tile_groups_per_partition if tile_groups is None else tile_groups
+    P = inp.num_partitions if num_partitions is None else num_partitions
+    out = tq.decode_tq4(inp.q, inp.cache, inp.centroids, inp.block_tables, inp.seq_lens,
+                        num_kv_heads=wl.num_kv_heads, kv_block_size=wl.kv_block_size,
+                        num_partitions=P, tile_groups_per_partition=G,
+                        softmax_scale=inp.softmax_scale,
+                        max_seq_len=int(inp.seq_lens.max().item()), fused=(path == "fused"))
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_tq4(inp, units=None):
+    c = inp.to("cpu")
+    return oracle.decode_tq4(c.q, c.cache, c.centroids, c.block_tables, c.seq_lens,
+                             inp.softmax_scale, inp.wl.num_kv_heads, inp.wl.kv_block_size,
+                             units=units, nthreads=ORACLE_THREADS)
+
+
+def bits(t):
+    return t.detach().contiguous().view(torch.int16).cpu().numpy()
+
+
+SWEEP_LENS = (1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 300, 513, 1000)
+SWEEP = [(qg, bs) for qg in (6, 8, 16) for bs in (16, 32)]
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("qg,bs", SWEEP, ids=[f"qg{q}_bs{b}" for q, b in SWEEP])
+def test_tq4_small_sweep(qg, bs, path):
+    lens = SWEEP_LENS
+    wl = workloads.small_workload(name=f"tq4_qg{qg}_bs{bs}", num_seqs=len(lens), num_kv_heads=3,
+                                  query_group_size=qg, kv_block_size=bs, seq_lens=lens,
+                                  seed=200 + qg + bs)
+    for G, P in ((1, 4), (2, 2), (5, 1)):
+        say(f"[tq4 sweep] {path} qg={qg} bs={bs} G={G} P={P}")
+        inp = workloads.make_inputs_tq4(wl, device="cuda", seq_lens=lens, num_partitions=P)
+        out = gpu_tq4(inp, path, num_partitions=P, tile_groups=G)
+        compare(out, oracle_tq4(inp), f"tq4 {path} qg{qg} bs{bs} G{G} P{P}")
+
+
+WORKLOAD_CASES = [("w2_s32_ctx4k", None), ("w3_s64_ragged", None), ("w4_s128_ctx8k", 64),
+                  ("w5_s16_long", None)]
+_REF = {}
+
+
+@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("name,sample", WORKLOAD_CASES, ids=[c[0] for c in WORKLOAD_CASES])
+def test_tq4_workload_parity(name, sample, path):
+    wl = workloads.WORKLOADS[name]
+    say(f"[tq4 parity] {name} {path}: generating")
+    inp = workloads.make_inputs_tq4(wl, device="cuda")
+    out = gpu_tq4(inp, path)
+    if sample is None:
+        if name not in _REF:
+            _REF.clear()
+            _REF[name] = oracle_tq4(inp)
+        compare(out, _REF[name], f"tq4 {name} {path}")
+    else:
+        rng = np.random.default_rng(wl.seed)
+        all_units = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_kv_heads)]
+        idx = rng.choice(len(all_units), size=sample, replace=False)
+        units = [all_units[i] for i in sorted(idx)]
+        compare(units_rows(out, units, wl.query_group_size), oracle_tq4(inp, units=units),
+                f"tq4 {name} {path} ({sample} sampled units)")
+        assert torch.isfinite(out.float()).all()
+
+
+def _small(lens, qg=8, bs=16, hkv=2, seed=5, P=None):
+    wl = workloads.small_workload(name="tq4bit", num_seqs=len(lens), num_kv_heads=hkv,
+                                  query_group_size=qg, kv_block_size=bs, seq_lens=lens, seed=seed)
+    return workloads.make_inputs_tq4(wl, device="cuda", seq_lens=lens, num_partitions=P)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_tq4_determinism_relabelling_and_poison(path):
+    """Same bits run to run; relabelling physical blocks (with a consistent table) and
+    garbage past the lengths (random index bytes, NaN metadata, garbage table tails) change
+    nothing."""
+    inp = _small((1, 40, 333, 1000), bs=32, P=4, seed=21)
+    say(f"[tq4 bitwise] {path}")
+    ref = gpu_tq4(inp, path)
+    assert np.array_equal(bits(gpu_tq4(inp, path)), bits(ref))
+    NB = inp.num_blocks
+    perm = torch.from_numpy(np.random.default_rng(3).permutation(NB).astype(np.int64)).cuda()
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(NB, device="cuda")
+    moved = dataclasses.replace(inp, cache=inp.cache[inv].contiguous(),
+                                block_tables=perm[inp.block_tables.long()].to(torch.int32))
+    assert np.array_equal(bits(gpu_tq4(moved, path)), bits(ref))
+    assert np.array_equal(bits(gpu_tq4(workloads.poison_tq4(inp), path)), bits(ref))
+
+
+@pytest.mark.parametrize("qg,bs", [(8, 16), (16, 32), (6, 32)])
+def test_tq4_single_tile_group_identity(qg, bs):
+    """L <= 256: every (P, G) choice and both paths give the same bits."""
+    lens = (1, 16, 31, 100, 255, 256)
+    inp = _small(lens, qg=qg, bs=bs, P=1, seed=30 + qg)
+    say(f"[tq4 identity] qg={qg} bs={bs}")
+    ref = gpu_tq4(inp, "two_kernel", num_partitions=1, tile_groups=1)
+    for path in PATHS:
+        for P, G in ((1, 1), (3, 1), (1, 5), (2, 2)):
+            assert np.array_equal(bits(gpu_tq4(inp, path, num_partitions=P, tile_groups=G)),
+                                  bits(ref)), (path, P, G)

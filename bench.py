@@ -20,6 +20,8 @@ stderr.
   hbm_probe     best read and copy bandwidth of plain streaming kernels
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
   kv_writer     tq_kv_write on 16384 new tokens scattered into the same pool
+  tq4           the same step over the 4-bit record format (tq4_decode + reduce,
+                and tq4_decode_fused): time, GB/s and token-heads/s against fp8
 """
 
 from __future__ import annotations
@@ -130,8 +132,8 @@ def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10)
 
 
 PROFILE_KERNELS = ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel", "tq_merge_kernel",
-                   "tq_kv_write_kernel")
-PROFILE_CMD = ("rocprofv3 {what} -T -d <dir>/{sub} -o {sub} --output-format csv -- "
+                   "tq_kv_write_kernel", "tq_flat_kernel[tq4]", "tq_partition_kernel[tq4]")
+PROFILE_CMD = ("rocprofv3 {what} -d <dir>/{sub} -o {sub} --output-format csv -- "
                "python3 bench.py --workload {wl} --steps 20 --warmup 3 --no-cpu-baseline")
 
 
@@ -142,19 +144,42 @@ def _csv_rows(path):
         return list(csv.DictReader(f))
 
 
+def _kernel_key(name: str) -> str:
+    """Short kernel name from a full one: the function name, with "[tq4]" for the
+    4-bit-format instantiation (last template argument true)."""
+    import re
+
+    m = re.search(r"\b((?:tq|probe)_\w+)(?:<([^>]*)>)?", name)
+    if not m:
+        return name
+    key = m.group(1)
+    if (m.group(2) or "").replace(" ", "").endswith("true"):
+        key += "[tq4]"
+    return key
+
+
 def summarize_rocprof(prof_dir: str, workload: str) -> None:
     """Turn the rocprofv3 output of three profiled bench runs under `prof_dir`
     (trace/: --kernel-trace --stats; fetch/: --pmc FETCH_SIZE; write/: --pmc
     WRITE_SIZE) into the summaries kept under profiles/: per-kernel duration
     statistics, and HBM bytes per launch of each decode kernel, the counters
     scaled by what they read for the copy probe, whose bytes are known."""
-    stats = {r["Name"]: r for r in _csv_rows(os.path.join(prof_dir, "trace", "trace_kernel_stats.csv"))}
+    stats = {}
+    for r in _csv_rows(os.path.join(prof_dir, "trace", "trace_kernel_stats.csv")):
+        k = _kernel_key(r["Name"])
+        st = stats.setdefault(k, {"Calls": 0, "TotalNs": 0.0, "MinNs": float("inf"), "MaxNs": 0.0})
+        st["Calls"] += int(r["Calls"])
+        st["TotalNs"] += float(r["TotalDurationNs"])
+        st["MinNs"] = min(st["MinNs"], float(r["MinNs"]))
+        st["MaxNs"] = max(st["MaxNs"], float(r["MaxNs"]))
+    for st in stats.values():
+        st["AverageNs"] = st["TotalNs"] / st["Calls"]
 
     def per_kernel(sub, counter):
         vals = {}
         for r in _csv_rows(os.path.join(prof_dir, sub, f"{sub}_counter_collection.csv")):
             if r["Counter_Name"] == counter:
-                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+                vals.setdefault(_kernel_key(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in vals.items()}
 
     fetch = per_kernel("fetch", "FETCH_SIZE")
@@ -182,7 +207,8 @@ def summarize_rocprof(prof_dir: str, workload: str) -> None:
                      f"{fetch.get(name, float('nan')):.0f} | {write.get(name, float('nan')):.0f} |")
     lines += ["", f"Counter calibration with the 1 GiB copy probe: bytes = FETCH_SIZE x 1024 x "
               f"{f_scale:.4f}, WRITE_SIZE x 1024 x {w_scale:.4f}.", ""]
-    for name in ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel"):
+    for name in ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel", "tq_flat_kernel[tq4]",
+                 "tq_partition_kernel[tq4]"):
         if name not in fetch or name not in write:
             continue
         fb = fetch[name] * 1024.0 * f_scale
@@ -193,7 +219,8 @@ def summarize_rocprof(prof_dir: str, workload: str) -> None:
                "avg_duration_us": round(float(stats[name]["AverageNs"]) / 1e3, 2),
                "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
                "source": f"profiles/rocprof_{workload}.md"}
-        with open(os.path.join(ROOT, "profiles", f"traffic_{name}_{workload}.json"), "w") as f:
+        fname = name.replace("[tq4]", "_tq4")
+        with open(os.path.join(ROOT, "profiles", f"traffic_{fname}_{workload}.json"), "w") as f:
             json.dump(rec, f, indent=1)
         lines.append(f"- {name}: {fb / 1e9:.4f} GB fetched + {wb / 1e9:.4f} GB written per launch")
     with open(os.path.join(ROOT, "profiles", f"rocprof_{workload}.md"), "w") as f:
@@ -359,6 +386,50 @@ def main() -> int:
                         "GBps": round(w_bytes / (w_ms * 1e-3) / 1e9, 1), "bytes_per_launch": w_bytes}
     log(f"[bench] kv writer: {T} tokens x {Hkv} heads in {w_ms * 1e3:.1f} us "
         f"({res['kv_writer']['GBps']} GB/s)")
+
+    # The 4-bit record format on the same workload shape (same lengths and tables): its
+    # bytes per (token, kv head) are 128 + 6, so the comparison that matters is tokens/s.
+    del k_new, v_new, slots, part, workspace
+    inp_fp8_tokens = int(inp.seq_lens.to(torch.int64).sum().item()) * Hkv
+    del inp
+    torch.cuda.empty_cache()
+    log(f"[bench] generating {wl.name} in the 4-bit record format")
+    t4 = workloads.make_inputs_tq4(wl, device=dev)
+    part4 = tq.alloc_partials(S, Hkv, P, QG, dev)
+    ws4 = tq.alloc_fused_workspace(S, Hkv, QG, maxlen, dev)
+    bytes4 = t4.kv_bytes()
+
+    def dec4():
+        tq.tq4_decode(t4.q, t4.cache, t4.centroids, t4.block_tables, t4.seq_lens, part4, Hkv, QG,
+                      wl.kv_block_size, G, t4.softmax_scale, num_partitions=P, max_seq_len=maxlen,
+                      stream=stream)
+
+    def fused4():
+        tq.tq4_decode_fused(t4.q, t4.cache, t4.centroids, t4.block_tables, t4.seq_lens, out, Hkv,
+                            QG, wl.kv_block_size, G, t4.softmax_scale, num_partitions=P,
+                            max_seq_len=maxlen, workspace=ws4, stream=stream)
+
+    def red4():
+        tq.tq_decode_reduce(part4, t4.seq_lens, out, Hkv, QG, G, num_partitions=P,
+                            max_seq_len=maxlen, stream=stream)
+
+    t_two4 = timed(dec4, red4)
+    t_fused4 = timed(fused4)
+    best4 = min(t_two4, t_fused4)
+    tok_s = inp_fp8_tokens / (best4 * 1e-3)
+    tok_s_fp8 = inp_fp8_tokens / (ms_per_step * 1e-3)
+    res["tq4"] = {"format": "4-bit record: 16-centroid K indices + fp16 K norm, 4-bit V + fp16 "
+                            "scale and zero point (134 B per token and kv head)",
+                  "us_per_step": round(best4 * 1e3, 2),
+                  "paths_us": {"two_kernel": round(t_two4 * 1e3, 2), "fused": round(t_fused4 * 1e3, 2)},
+                  "GBps": round(bytes4 / (best4 * 1e-3) / 1e9, 1),
+                  "pct_of_hbm_peak": round(100 * bytes4 / (best4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+                  "bytes_per_step": bytes4,
+                  "token_heads_per_s": round(tok_s, 1),
+                  "vs_fp8_token_heads_per_s": round(tok_s / tok_s_fp8, 3)}
+    log(f"[bench] 4-bit format: step {best4 * 1e3:.1f} us ({res['tq4']['GBps']} GB/s, "
+        f"{res['tq4']['pct_of_hbm_peak']}% of peak), {tok_s / 1e9:.1f} G token-heads/s = "
+        f"{res['tq4']['vs_fp8_token_heads_per_s']}x the fp8 step")
     print(json.dumps(res), flush=True)
     return 0
 

@@ -65,16 +65,23 @@ constexpr int kCachePolicyStreaming = 2;
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
+// Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane groups) by
+// the gfx950 lane swaps, no LDS round trip: v_permlane16_swap of a value with
+// itself leaves {own, partner l^16} in the two results (in some order), and
+// v_permlane32_swap {own, partner l^32}.  Max and sum are commutative, so
+// every lane gets the same bits, as with a pair of xor shuffles.
 __device__ __forceinline__ float wave_max_xor16_32(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16, 64));
-  x = fmaxf(x, __shfl_xor(x, 32, 64));
-  return x;
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 __device__ __forceinline__ float wave_sum_xor16_32(float x) {
-  x += __shfl_xor(x, 16, 64);
-  x += __shfl_xor(x, 32, 64);
-  return x;
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
 // 8 fp8 e4m3fn codes (two dwords) -> 8 bf16, exact.
@@ -124,12 +131,14 @@ struct WaveState {
   float lsum;
   float sigma;
   float zsum;  // 4-bit format: this lane's share of sum_t p_t * vzero_t
+  float corr;  // 4-bit format: this lane's share of sum_t P'_t (the f16 P operand)
   f32x4 acc[8];
   __device__ __forceinline__ void reset() {
     m2 = kNegInf;
     lsum = 0.f;
     sigma = 0.f;
     zsum = 0.f;
+    corr = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -142,20 +151,21 @@ struct WaveState {
     for (int dblk = 0; dblk < 8; ++dblk) o[dblk] = acc[dblk] * f;
     return l;
   }
-  // The same for the 4-bit format, o = (acc * sigma + zsum) / l: acc[2pc + par]
-  // holds d = 32 pc + 8b + 2i + par (par 0: even dims; par 1: odd dims, carried
-  // at 16x); o is returned interleaved, o[2pc + half] = d = 32 pc + 8b + 4 half
-  // + 0..3.
+  // The same for the 4-bit format.  acc[2pc + par] holds sum_t P'_t (1024 + n)
+  // for d = 32 pc + 8b + 2i + par (par 0: even dims, n the index; par 1: odd
+  // dims, 16 n), so o = ((acc - 1024 corr) * sigma [/ 16] + zsum) / l; o is
+  // returned interleaved, o[2pc + half] = d = 32 pc + 8b + 4 half + 0..3.
   __device__ __forceinline__ float finish_tq4(f32x4 o[8]) const {
     const float l = wave_sum_xor16_32(lsum);
     const float z = wave_sum_xor16_32(zsum);
+    const float c1024 = 1024.0f * wave_sum_xor16_32(corr);
     const float f = sigma / l;
     const float f16th = f * 0.0625f;
     const float zl = z / l;
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc) {
-      const f32x4 e = acc[2 * pc] * f + zl;
-      const f32x4 od = acc[2 * pc + 1] * f16th + zl;
+      const f32x4 e = (acc[2 * pc] - c1024) * f + zl;
+      const f32x4 od = (acc[2 * pc + 1] - c1024) * f16th + zl;
       o[2 * pc] = f32x4{e[0], od[0], e[1], od[1]};
       o[2 * pc + 1] = f32x4{e[2], od[2], e[3], od[3]};
     }
@@ -405,10 +415,10 @@ __device__ __forceinline__ int tq4_v_lds_offset(int tok, int piece) {
   return tok * 64 + 16 * (piece ^ ((tok >> 1) & 3));
 }
 
-// 8 index bytes (one per token) -> f16 operands of the 8 low nibbles (n) and of
-// the 8 high nibbles (16 n): a byte permute puts each masked byte under the f16
-// exponent byte 0x64, giving 1024 + n (or 1024 + 16 n), and subtracting 1024 is
-// exact.  The odd dims are thus carried at 16x and scaled back at the end.
+// 8 index bytes (one per token) -> f16 operands 1024 + n of the 8 low nibbles and
+// 1024 + 16 n of the 8 high nibbles: a byte permute puts each masked byte under
+// the f16 exponent byte 0x64.  The 1024 is taken out at the end through the sum
+// of the P operand (WaveState::corr); the odd dims are carried at 16x.
 __device__ __forceinline__ void tq4_nibbles_f16(i32x2 raw, f16x8& lo, f16x8& hi) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   constexpr uint32_t kExp = 0x64646464u;
@@ -423,10 +433,8 @@ __device__ __forceinline__ void tq4_nibbles_f16(i32x2 raw, f16x8& lo, f16x8& hi)
     h[2 * w] = __builtin_amdgcn_perm(kExp, mh, 0x04010400u);
     h[2 * w + 1] = __builtin_amdgcn_perm(kExp, mh, 0x04030402u);
   }
-  const f16x8 k1024 = {(_Float16)1024, (_Float16)1024, (_Float16)1024, (_Float16)1024,
-                       (_Float16)1024, (_Float16)1024, (_Float16)1024, (_Float16)1024};
-  lo = __builtin_bit_cast(f16x8, l) - k1024;
-  hi = __builtin_bit_cast(f16x8, h) - k1024;
+  lo = __builtin_bit_cast(f16x8, l);
+  hi = __builtin_bit_cast(f16x8, h);
 }
 
 // The 4-bit counterpart of stream_tokens: same contract, same chunk pipeline.
@@ -654,6 +662,14 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     if (__ballot(acc_scale != 1.0f)) {  // a factor of exactly 1 changes no bits
 #pragma unroll
       for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
+      w.corr *= acc_scale;
+    }
+    {  // corr += sum of this lane's 8 P' values, exactly as the MFMA sees them
+      const f16x2 one = {(_Float16)1, (_Float16)1};
+      float c = w.corr;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_fdot2(f16x2{pop[2 * i], pop[2 * i + 1]}, one, c, false);
+      w.corr = c;
     }
 
     // ---- PV: acc[2pc + par] (dims 32 pc + 2m + par, m = 4b + i) += V^T P ----

@@ -17,7 +17,8 @@ stderr.
                 the launch stream, against MI355X's 8 TB/s (the step time is
                 measured the same way over K whole steps; for the one-launch
                 fused path the step and the kernel are the same timed region)
-  hbm_probe     best read and copy bandwidth of plain streaming kernels
+  hbm_probe     best read and copy bandwidth of plain streaming kernels, and the
+                bandwidth of the decode's own byte pattern with no arithmetic
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload
   kv_writer     tq_kv_write on 16384 new tokens scattered into the same pool
   tq4           the same step over the 4-bit record format (tq4_decode + reduce,
@@ -124,15 +125,25 @@ def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10)
 
     rd = best(lambda w: probe.read(src, sink, w), nread, (2048, 4096, 8192, 16384, 32768))
     cp = best(lambda w: probe.copy(dst, src[:ncopy], w), 2 * ncopy, (2048, 4096, 8192, 16384))
-    del src, dst, sink
+    # The decode's own byte pattern with no arithmetic: 2048 waves x 128 chunks of 4 KiB K,
+    # 4 KiB V and 256 B scales = 2.2146 GB, the bandwidth workload's bytes.
+    chunks, groups = 128, 256
+    kvb = groups * 8 * chunks * 4096
+    pk, pv = src[:kvb], src[kvb:2 * kvb]
+    ps = src[2 * kvb:2 * kvb + groups * 8 * chunks * 256]
+    pat_bytes = 2 * kvb + ps.numel()
+    pt = best(lambda w: probe.pattern(pk, pv, ps, chunks, w, sink), pat_bytes, (groups,))
+    del src, dst, sink, pk, pv, ps
     torch.cuda.empty_cache()
     return {"read_bytes": nread, "copy_bytes": ncopy, "reps": reps,
             "read_gbs": round(rd[0], 1), "read_workgroups": rd[1],
+            "pattern_bytes": pat_bytes, "pattern_gbs": round(pt[0], 1),
             "copy_gbs": round(cp[0], 1), "copy_workgroups": cp[1]}
 
 
 PROFILE_KERNELS = ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel", "tq_merge_kernel",
-                   "tq_kv_write_kernel", "tq_flat_kernel[tq4]", "tq_partition_kernel[tq4]")
+                   "tq_kv_write_kernel", "tq_flat_kernel[tq4]", "tq_partition_kernel[tq4]",
+                   "probe_pattern_kernel")
 PROFILE_CMD = ("rocprofv3 {what} -d <dir>/{sub} -o {sub} --output-format csv -- "
                "python3 bench.py --workload {wl} --steps 20 --warmup 3 --no-cpu-baseline")
 
@@ -263,7 +274,8 @@ def main() -> int:
     probe_res = None
     if not args.no_probe:
         probe_res = hbm_probe(dev)
-        log(f"[bench] HBM probe: read {probe_res['read_gbs']} GB/s, copy {probe_res['copy_gbs']} GB/s")
+        log(f"[bench] HBM probe: read {probe_res['read_gbs']} GB/s, copy {probe_res['copy_gbs']} GB/s, "
+            f"decode byte pattern without arithmetic {probe_res['pattern_gbs']} GB/s")
     log(f"[bench] generating {wl.name} on {dev}")
     inp = workloads.make_inputs(wl, device=dev)
     torch.cuda.synchronize()
@@ -363,6 +375,7 @@ def main() -> int:
     if probe_res is not None:
         res["hbm_probe"] = probe_res
         res["roofline"]["frac_of_probe_read"] = round(k1_gbs / probe_res["read_gbs"], 4)
+        res["roofline"]["frac_of_decode_pattern"] = round(k1_gbs / probe_res["pattern_gbs"], 4)
     if not args.no_cpu_baseline:
         log("[bench] timing the fp64 oracle on a sample (cpu_baseline)")
         res["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)

@@ -11,6 +11,14 @@
  *   elided.  num_workgroups <= 65536.
  * tq_probe_copy: dst[i] = src[i] for the 16-byte words of [0, n_bytes):
  *   a plain copy of known size, for scaling hardware byte counters.
+ * tq_probe_pattern: the byte pattern of the fp8 decode stream with no
+ *   arithmetic, as a ceiling for kernels that move those bytes that way.
+ *   num_workgroups workgroups of 8 waves; wave w reads chunks_per_wave chunks,
+ *   each 4096 bytes of k (into registers) and 4096 bytes of v plus 256 bytes of
+ *   scales (into LDS by LDS-direct loads), from k/v + (w * chunks_per_wave + c)
+ *   * 4096 and scales + (w * chunks_per_wave + c) * 256, one chunk in flight
+ *   ahead, and writes one digest per workgroup to sink.  kv_bytes and
+ *   scale_bytes are the buffer sizes (checked); all 16-byte aligned.
  */
 #ifndef TQ_PROBE_H
 #define TQ_PROBE_H
@@ -26,6 +34,9 @@ int32_t tq_probe_read(const void* src, size_t n_bytes, uint32_t* sink, int32_t n
                       void* stream);
 int32_t tq_probe_copy(void* dst, const void* src, size_t n_bytes, int32_t num_workgroups,
                       void* stream);
+int32_t tq_probe_pattern(const void* k, const void* v, const void* scales, size_t kv_bytes,
+                         size_t scale_bytes, int32_t chunks_per_wave, int32_t num_workgroups,
+                         uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

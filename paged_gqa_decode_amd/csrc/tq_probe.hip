@@ -1,5 +1,6 @@
-// HBM streaming probes (read-only and copy) for measuring achievable bandwidth
-// and calibrating byte counters; see include/tq_probe.h.
+// HBM streaming probes (read-only, copy, and the decode's byte pattern) for
+// measuring achievable bandwidth and calibrating byte counters; see
+// include/tq_probe.h.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -37,7 +38,93 @@ __global__ __launch_bounds__(256) void probe_copy_kernel(u32x4* __restrict__ dst
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = src[i];
 }
 
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kPatChunk = 4096;  // bytes of K and of V per chunk (32 tokens x 128)
+
+// The byte pattern of the decode's stream with no arithmetic: each wave walks
+// `chunks` chunks; per chunk 4 KiB of K into registers (two 16-byte loads per
+// lane per 16-token tile), 4 KiB of V and 256 B of scales into LDS by
+// LDS-direct loads (16 and 4 bytes per lane, non-temporal), the next chunk
+// issued once the current one is drained and read.  Workgroups of 8 waves.
+__global__ __launch_bounds__(512) void probe_pattern_kernel(const uint8_t* __restrict__ k,
+                                                            const uint8_t* __restrict__ v,
+                                                            const float* __restrict__ sc,
+                                                            int chunks, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t sa[8][kPatChunk + 256];
+  __shared__ __attribute__((aligned(16))) uint8_t sb[8][kPatChunk + 256];
+  constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t gw = (size_t)blockIdx.x * 8 + wave;
+  const uint8_t* kw = k + gw * (size_t)chunks * kPatChunk;
+  const uint8_t* vw = v + gw * (size_t)chunks * kPatChunk;
+  const float* sw = sc + gw * (size_t)chunks * 64;
+  i32x4 acc = {0, 0, 0, 0};
+  int lacc = 0;
+  auto issue = [&](int c, uint8_t* st, i32x4* r) {
+    const uint8_t* kc = kw + (size_t)c * kPatChunk;
+    r[0] = *reinterpret_cast<const i32x4*>(kc + 32 * lane);
+    r[1] = *reinterpret_cast<const i32x4*>(kc + 32 * lane + 16);
+    r[2] = *reinterpret_cast<const i32x4*>(kc + 2048 + 32 * lane);
+    r[3] = *reinterpret_cast<const i32x4*>(kc + 2048 + 32 * lane + 16);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(vw + (size_t)c * kPatChunk + 1024 * j + 16 * lane,
+                                       (lds_void*)(st + 1024 * j), 16, 0, 2);
+    __builtin_amdgcn_global_load_lds(sw + (size_t)c * 64 + lane, (lds_void*)(st + kPatChunk), 4, 0, 2);
+  };
+  i32x4 ra[4], rb[4];
+  if (chunks > 0) issue(0, sa[wave], ra);
+  for (int c = 0; c < chunks; c += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    lacc += *reinterpret_cast<const int*>(sa[wave] + 64 * lane) +
+            *reinterpret_cast<const int*>(sa[wave] + kPatChunk + 4 * (lane & 31));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc ^= ra[i];
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 >= chunks) break;
+    issue(c + 1, sb[wave], rb);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    lacc += *reinterpret_cast<const int*>(sb[wave] + 64 * lane) +
+            *reinterpret_cast<const int*>(sb[wave] + kPatChunk + 4 * (lane & 31));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc ^= rb[i];
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 2 < chunks) issue(c + 2, sa[wave], ra);
+  }
+  uint32_t x = (uint32_t)(acc[0] ^ acc[1] ^ acc[2] ^ acc[3] ^ lacc);
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
+  __shared__ uint32_t red[8];
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t y = 0;
+    for (int w = 0; w < 8; ++w) y ^= red[w];
+    sink[blockIdx.x] = y;
+  }
+}
+
 }  // namespace
+
+extern "C" int32_t tq_probe_pattern(const void* k, const void* v, const void* scales,
+                                    size_t kv_bytes, size_t scale_bytes, int32_t chunks_per_wave,
+                                    int32_t num_workgroups, uint32_t* sink, void* stream) {
+  const size_t waves = (size_t)num_workgroups * 8;
+  if (!k || !v || !scales || !sink || ((uintptr_t)k & 15) || ((uintptr_t)v & 15) ||
+      ((uintptr_t)scales & 15) || num_workgroups < 1 || num_workgroups > 65536 ||
+      chunks_per_wave < 1 || waves * (size_t)chunks_per_wave * kPatChunk > kv_bytes ||
+      waves * (size_t)chunks_per_wave * 256 > scale_bytes)
+    return (int32_t)hipErrorInvalidValue;
+  hipLaunchKernelGGL(probe_pattern_kernel, dim3(num_workgroups), dim3(512), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(k),
+                     static_cast<const uint8_t*>(v), static_cast<const float*>(scales),
+                     chunks_per_wave, sink);
+  return (int32_t)hipGetLastError();
+}
 
 extern "C" int32_t tq_probe_read(const void* src, size_t n_bytes, uint32_t* sink,
                                  int32_t num_workgroups, void* stream) {

@@ -1,4 +1,4 @@
-"""Binding of libtqprobe.so (include/tq_probe.h): HBM read and copy probes."""
+"""Binding of libtqprobe.so (include/tq_probe.h): HBM read, copy and decode-pattern probes."""
 
 from __future__ import annotations
 
@@ -9,7 +9,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtqprobe.so")
-EXPORTED_SYMBOLS = ("tq_probe_read", "tq_probe_copy")
+EXPORTED_SYMBOLS = ("tq_probe_read", "tq_probe_copy", "tq_probe_pattern")
 _lib = None
 
 
@@ -25,6 +25,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.tq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32,
                                       ctypes.c_void_p]
         lib.tq_probe_copy.restype = ctypes.c_int32
+        lib.tq_probe_pattern.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+        lib.tq_probe_pattern.restype = ctypes.c_int32
         _lib = lib
     return _lib
 
@@ -45,3 +49,16 @@ def copy(dst: torch.Tensor, src: torch.Tensor, num_workgroups: int, stream=None)
     rc = load_library().tq_probe_copy(dst.data_ptr(), src.data_ptr(), nbytes, int(num_workgroups), s)
     if rc:
         raise RuntimeError(f"tq_probe_copy failed: hipError {rc}")
+
+
+def pattern(k: torch.Tensor, v: torch.Tensor, scales: torch.Tensor, chunks_per_wave: int,
+            num_workgroups: int, sink: torch.Tensor, stream=None) -> None:
+    """The decode's byte pattern with no arithmetic (tq_probe_pattern)."""
+    assert k.is_cuda and v.is_cuda and scales.is_cuda and sink.is_cuda and sink.numel() >= num_workgroups
+    kvb = min(k.numel() * k.element_size(), v.numel() * v.element_size())
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    rc = load_library().tq_probe_pattern(k.data_ptr(), v.data_ptr(), scales.data_ptr(), kvb,
+                                         scales.numel() * scales.element_size(), int(chunks_per_wave),
+                                         int(num_workgroups), sink.data_ptr(), s)
+    if rc:
+        raise RuntimeError(f"tq_probe_pattern failed: hipError {rc}")

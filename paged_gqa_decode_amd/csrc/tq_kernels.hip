@@ -1,19 +1,26 @@
-// gfx950 (CDNA4) kernels of paged grouped-query decode attention over an fp8
-// e4m3fn KV cache: the split-K partition kernel and the log-sum-exp merge.
+// gfx950 (CDNA4) kernels of paged grouped-query decode attention over a
+// quantized KV cache (fp8 e4m3fn codes with per-row fp32 scales, or the 4-bit
+// record of centroid-coded K and affine V), and the writer that fills the fp8
+// cache.  The file holds, in order: the fp8 token stream and the 4-bit token
+// stream (the per-wave cores every decode kernel runs), the split-K partition
+// kernel, the per-(s, h) fused kernel, the flat even-split fused kernel, the
+// log-sum-exp merge of the partition kernel's partials, the KV-cache writer,
+// and the host launchers.
 //
 // What is computed follows the page "vllm.v1.attention.ops.flydsl_kernels.
 // tq_decode": the block-table walk (STEP F), the QK^T and PV products with
 // the query group on the MFMA's 16 columns, the online softmax with running
 // max and sum (STEP F, FA-2 state of STEP D), and the normalised partial
 // output with its max logit and exp sum (STEP G).  The kernel design here is
-// its own, made for gfx950:
+// its own, made for gfx950 (for the fp8 stream; the 4-bit stream is
+// described where it is defined):
 //
-//  * One 64-lane wave per group of `parts_per_wave` consecutive partitions of
-//    one (sequence s, kv head h).  Their tokens are walked as one stream of
-//    32-token chunks (two 16-token MFMA tiles), with the next chunk's loads in
-//    flight while the current one is computed; at every partition boundary
-//    the partial triple is written and the softmax state restarts, so the
-//    result of each partition does not depend on the grouping.
+//  * One 64-lane wave walks a run of tokens of one (sequence s, kv head h) as
+//    one stream of 32-token chunks (two 16-token MFMA tiles), with the next
+//    chunk's loads in flight while the current one is computed.  At every
+//    boundary its caller asks for (a split-K partition, a tile group), the
+//    finished partial goes to the caller and the softmax state restarts, so a
+//    partial does not depend on how runs are dealt to waves.
 //  * K never touches LDS.  QK^T contracts over head_dim, so any permutation
 //    of d applied to both q and K is allowed: lane (r = lane%16, b = lane/16)
 //    supplies K[token r][d = 32b .. 32b+31], one contiguous 32-byte piece of
@@ -27,9 +34,9 @@
 //    column: the A operand of a 16x16x32 f16 MFMA (O^T = V^T P), converted
 //    fp8 -> f16 exactly in registers.
 //  * The V scale is folded into P: the B operand is p_t * vs_t / sigma in
-//    f16, where sigma is the running maximum V scale of the partition, so the
-//    operand stays in [0, 1] whatever the data's magnitude; acc is rescaled
-//    when sigma grows, together with the softmax rescale.
+//    f16, where sigma is the running maximum V scale since the last restart,
+//    so the operand stays in [0, 1] whatever the data's magnitude; acc is
+//    rescaled when sigma grows, together with the softmax rescale.
 //  * Tokens past the sequence end inside the last chunk may hold any bytes
 //    (NaN codes or scales included): their logits are selected to -inf, their
 //    P and V operand bytes to zero, so they cannot reach the result.

@@ -158,10 +158,12 @@ struct WaveState {
     for (int dblk = 0; dblk < 8; ++dblk) o[dblk] = acc[dblk] * f;
     return l;
   }
-  // The same for the 4-bit format.  acc[2pc + par] holds sum_t P'_t (1024 + n)
-  // for d = 32 pc + 8b + 2i + par (par 0: even dims, n the index; par 1: odd
-  // dims, 16 n), so o = ((acc - 1024 corr) * sigma [/ 16] + zsum) / l; o is
-  // returned interleaved, o[2pc + half] = d = 32 pc + 8b + 4 half + 0..3.
+  // The same for the 4-bit format.  For the dim pair d = 32 pc + 8b + 2i + (0,
+  // 1), with index byte x = n_even + 16 n_odd, acc[2pc] holds sum_t P'_t (1024
+  // + x) and acc[2pc + 1] sum_t P'_t (1024 + 16 n_odd).  So o_even = ((acc[2pc]
+  // - acc[2pc + 1]) sigma + zsum) / l and o_odd = ((acc[2pc + 1] - 1024 corr)
+  // sigma / 16 + zsum) / l; o is returned interleaved, o[2pc + half] = d = 32 pc
+  // + 8b + 4 half + 0..3.
   __device__ __forceinline__ float finish_tq4(f32x4 o[8]) const {
     const float l = wave_sum_xor16_32(lsum);
     const float z = wave_sum_xor16_32(zsum);
@@ -171,7 +173,7 @@ struct WaveState {
     const float zl = z / l;
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc) {
-      const f32x4 e = (acc[2 * pc] - c1024) * f + zl;
+      const f32x4 e = (acc[2 * pc] - acc[2 * pc + 1]) * f + zl;
       const f32x4 od = (acc[2 * pc + 1] - c1024) * f16th + zl;
       o[2 * pc] = f32x4{e[0], od[0], e[1], od[1]};
       o[2 * pc + 1] = f32x4{e[2], od[2], e[3], od[3]};
@@ -403,52 +405,89 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
 // [Hkv][3][BS]: K norm, V scale, V zero point.  k = centroids[index] * norm,
 // v = index * scale + zero.
 //
-// Per-wave LDS of the 4-bit stream (inside the same 8.5 KiB staging area):
-// two 2 KiB V stages (32 rows of 64 B, 16-byte pieces XOR-swizzled by bits 1..2
-// of the row), two 256 B metadata stages ([3][32] fp16) and a 256-entry table
-// that maps an index byte to the centroids c of its two nibbles as two bf16
-// pairs, hi = bf16(c) then lo = bf16(c - hi): about 16 significant bits
-// together, so the QK product does not round the codebook to bf16's 8.  The
-// lo parts enter the contraction as extra dims against a duplicated q: one
-// MFMA operand = (hi, lo) of two index bytes = dims (d0, d1, d0, d1, d2, d3,
-// d2, d3), q = (q0, q1, q0, q1, q2, q3, q2, q3).
-constexpr int kTq4VStage = CHUNK * 64;
+// Per-wave LDS of the 4-bit stream: two 4 KiB row stages and two 256 B
+// metadata stages ([3][32] fp16), in the same 8.5 KiB staging area as the fp8
+// stream's; the 2 KiB centroid table is a workgroup's LDS array of its own.
+//  * A chunk's 32 rows of 128 B (a whole block's slots of one kv head when
+//    BS = 32, two 2 KiB runs when BS = 16) arrive whole, by LDS-direct loads
+//    of 1 KiB each, and K is read back from LDS.  Splitting each row between a
+//    K register load and a V LDS load instead (two requests per 128-byte line)
+//    streams about 13 % slower on this GPU.
+//  * Row R's 16-byte pieces p = 0..7 (K: 0..3, V: 4..7) sit at slot
+//    p ^ tq4_row_swz(R).  The swizzle keeps the K reads (rows 16t + r, piece
+//    b) and the transposed V reads (tokens 4b + i and 16 + 4b + i) on distinct
+//    16-byte bank groups within every 8 and 16 lanes.
+//  * The table is a separate LDS object, one per workgroup, so that the
+//    compiler can see that reading it never waits for the row stages'
+//    LDS-direct loads.  It maps an index byte to the centroids c of its two nibbles as two
+//    bf16 pairs, hi = bf16(c) then lo = bf16(c - hi): about 16 significant bits
+//    together, so the QK product does not round the codebook to bf16's 8.  The
+//    lo parts enter the contraction as extra dims against a duplicated q: one
+//    MFMA operand = (hi, lo) of two index bytes = dims (d0, d1, d0, d1, d2, d3,
+//    d2, d3), q = (q0, q1, q0, q1, q2, q3, q2, q3).
+constexpr int kTq4RowStage = CHUNK * D;
 constexpr int kTq4MetaStage = 256;
-constexpr int kTq4MetaOff = 2 * kTq4VStage;
-constexpr int kTq4TableOff = kTq4MetaOff + 2 * kTq4MetaStage;
-static_assert(kTq4TableOff + 256 * 8 <= 2 * CHUNK * D + 2 * 2 * CHUNK * 4, "4-bit staging area");
+constexpr int kTq4MetaOff = 2 * kTq4RowStage;
+constexpr int kTq4WaveLds = kTq4MetaOff + 2 * kTq4MetaStage;
+constexpr int kTq4TableEntries = 256;
 
-__device__ __forceinline__ int tq4_v_lds_offset(int tok, int piece) {
-  return tok * 64 + 16 * (piece ^ ((tok >> 1) & 3));
+__device__ __forceinline__ int tq4_row_swz(int row) {
+  return (row & 7) ^ ((row >> 3) & 1) ^ ((row >> 2) & 4);
 }
 
-// 8 index bytes (one per token) -> f16 operands 1024 + n of the 8 low nibbles and
-// 1024 + 16 n of the 8 high nibbles: a byte permute puts each masked byte under
-// the f16 exponent byte 0x64.  The 1024 is taken out at the end through the sum
-// of the P operand (WaveState::corr); the odd dims are carried at 16x.
-__device__ __forceinline__ void tq4_nibbles_f16(i32x2 raw, f16x8& lo, f16x8& hi) {
+// bf16(c) in the low half, bf16(c - bf16(c)) in the high half.
+__device__ __forceinline__ uint32_t bf16_hi_lo(float c) {
+  const uint16_t hi = f32_to_bf16_rne(c);
+  const uint16_t lo = f32_to_bf16_rne(c - __uint_as_float((uint32_t)hi << 16));
+  return (uint32_t)hi | ((uint32_t)lo << 16);
+}
+
+// The centroid table, written by threads tid, tid + nthreads, ...: entry x =
+// {hi pair, lo pair} of (c[x & 15], c[x >> 4]), the first value of each pair
+// in the low half.  One table serves every wave of a workgroup, at a fixed
+// LDS address, so a lookup's address is the index byte times 8 (one shift)
+// plus a constant offset.
+__device__ __forceinline__ void build_tq4_table(i32x2* tab, const float* centroids, int tid,
+                                                int nthreads) {
+  for (int x = tid; x < kTq4TableEntries; x += nthreads) {
+    const uint32_t e0 = bf16_hi_lo(centroids[x & 15]), e1 = bf16_hi_lo(centroids[x >> 4]);
+    tab[x] = i32x2{(int)((e0 & 0xFFFFu) | (e1 << 16)), (int)((e0 >> 16) | (e1 & 0xFFFF0000u))};
+  }
+}
+
+// 8 index bytes x = n_lo + 16 n_hi (one per token) -> f16 operands 1024 + x of
+// the whole bytes and 1024 + 16 n_hi of their high nibbles: a byte permute puts
+// each byte under the f16 exponent byte 0x64, and a mask clears the low nibble.
+// The even dims (low nibbles) follow from the difference of the two
+// accumulators; the odd dims from the second less 1024 times the sum of the P
+// operand (WaveState::corr), carried at 16x.
+__device__ __forceinline__ void tq4_nibbles_f16(i32x2 raw, f16x8& whole, f16x8& hi) {
   typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   constexpr uint32_t kExp = 0x64646464u;
-  u32x4 l, h;
+  u32x4 x, h;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const uint32_t ml = (uint32_t)raw[w] & 0x0F0F0F0Fu;
-    const uint32_t mh = (uint32_t)raw[w] & 0xF0F0F0F0u;
-    // result bytes: (m.b0, 0x64, m.b1, 0x64) and (m.b2, 0x64, m.b3, 0x64)
-    l[2 * w] = __builtin_amdgcn_perm(kExp, ml, 0x04010400u);
-    l[2 * w + 1] = __builtin_amdgcn_perm(kExp, ml, 0x04030402u);
-    h[2 * w] = __builtin_amdgcn_perm(kExp, mh, 0x04010400u);
-    h[2 * w + 1] = __builtin_amdgcn_perm(kExp, mh, 0x04030402u);
+    // result bytes: (b0, 0x64, b1, 0x64) and (b2, 0x64, b3, 0x64)
+    x[2 * w] = __builtin_amdgcn_perm(kExp, (uint32_t)raw[w], 0x04010400u);
+    x[2 * w + 1] = __builtin_amdgcn_perm(kExp, (uint32_t)raw[w], 0x04030402u);
+    h[2 * w] = x[2 * w] & 0xFFF0FFF0u;
+    h[2 * w + 1] = x[2 * w + 1] & 0xFFF0FFF0u;
   }
-  lo = __builtin_bit_cast(f16x8, l);
+  whole = __builtin_bit_cast(f16x8, x);
   hi = __builtin_bit_cast(f16x8, h);
 }
+
+template <int V>
+struct StageTag {
+  static constexpr int value = V;
+};
 
 // The 4-bit counterpart of stream_tokens: same contract, same chunk pipeline.
 template <int QG, int BS, typename OnBoundary>
 __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, int h, int t_begin,
                                                   int t_end, int chunks_per_part, uint8_t* lds,
-                                                  WaveState& w, OnBoundary on_boundary) {
+                                                  const i32x2* tab, WaveState& w,
+                                                  OnBoundary on_boundary) {
   static_assert(BS == 16 || BS == 32, "kv block size");
   static_assert(QG >= 1 && QG <= 16, "query group size");
   const int lane = threadIdx.x & 63;
@@ -474,23 +513,6 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     return id < nb_max ? id : nb_max;
   };
 
-  // Centroid table: entry x = {hi pair, lo pair} of (c[x & 15], c[x >> 4]),
-  // the first value of each pair in the low half.
-  i32x2* tab = reinterpret_cast<i32x2*>(lds + kTq4TableOff);
-  {
-    const float cl = a.centroids[lane & 15];
-    const uint16_t chi = f32_to_bf16_rne(cl);
-    const uint16_t clo = f32_to_bf16_rne(cl - __uint_as_float((uint32_t)chi << 16));
-    const int pair_hl = (int)((uint32_t)chi | ((uint32_t)clo << 16));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int x = lane + 64 * i;
-      const uint32_t e0 = (uint32_t)__shfl(pair_hl, x & 15, 64);  // c[x & 15]: hi | lo << 16
-      const uint32_t e1 = (uint32_t)__shfl(pair_hl, x >> 4, 64);  // c[x >> 4]
-      tab[x] = i32x2{(int)((e0 & 0xFFFFu) | (e1 << 16)), (int)((e0 >> 16) | (e1 & 0xFFFF0000u))};
-    }
-  }
-
   // q operands, duplicated pairs: qdup[2c + half] = dims 8c + 4 half + (0, 1, 0,
   // 1, 2, 3, 2, 3) of this lane's 32 (the d-permutation of stream_tokens).
   bf16x8 qdup[8];
@@ -514,30 +536,23 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       }
   }
 
-  // Issue chunk c: K index rows (16 B per lane and tile) into registers, V
-  // index rows and the metadata into LDS stage `st`.
-  i32x4 kraw[2];
+  // Issue chunk c into LDS stage `st`: its 32 rows, 8 per LDS-direct load
+  // (lane l lands at byte 16 l of the load's 1 KiB: row 8j + l/8, slot l % 8,
+  // so it fetches piece (l % 8) ^ tq4_row_swz(row)), then the metadata.
   auto issue = [&](int c, int st) {
     const int jb = (c * CHUNK) / BS;
     const uint32_t blkA = block_id(jb);
     uint32_t blkB = blkA;
     if (BS == 16) blkB = (jb + 1 < n_blocks) ? block_id(jb + 1) : blkA;
+    uint8_t* rdst = lds + st * kTq4RowStage;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const uint32_t blk = (BS == 32 || t == 0) ? blkA : blkB;
-      const int slot = BS == 32 ? 16 * t + r : r;
-      const uint8_t* src = a.tq4 + blk * block_bytes + ((size_t)h * BS + slot) * D + 16 * b;
-      kraw[t] = *reinterpret_cast<const i32x4*>(src);
-    }
-    uint8_t* vdst = lds + st * kTq4VStage;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int tok = 16 * j + (lane >> 2);
-      const int piece = (lane & 3) ^ ((tok >> 1) & 3);
-      const uint32_t blk = (BS == 32 || tok < 16) ? blkA : blkB;
-      const int slot = BS == 32 ? tok : (tok & 15);
-      const uint8_t* src = a.tq4 + blk * block_bytes + ((size_t)h * BS + slot) * D + 64 + 16 * piece;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(vdst + 1024 * j), 16, 0,
+    for (int j = 0; j < 4; ++j) {
+      const int row = 8 * j + (lane >> 3);
+      const int piece = (lane & 7) ^ tq4_row_swz(row);
+      const uint32_t blk = (BS == 32 || row < 16) ? blkA : blkB;
+      const int slot = BS == 32 ? row : (row & 15);
+      const uint8_t* src = a.tq4 + blk * block_bytes + ((size_t)h * BS + slot) * D + 16 * piece;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(rdst + 1024 * j), 16, 0,
                                        kCachePolicyStreaming);
     }
     {
@@ -554,18 +569,31 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
 
   const int tr_tok = 16 * (r >> 3) + 4 * b + ((r >> 1) & 3);
   const int tr_half = 8 * (r & 1);
+  const int tr_swz = tq4_row_swz(tr_tok);
 
   issue(0, 0);
   int next_boundary = chunks_per_part;
   int part_done = 0;
-  for (int c = 0; c < n_chunks; ++c) {
-    const int st = c & 1;
-    // Drain chunk c and take everything it needs out of LDS (metadata, V index
-    // rows, and the centroids of its K indices) before chunk c+1's LDS-direct
-    // loads are issued.
+  // Lane (r, b)'s K pieces: row 16 t + r, piece b.
+  const int k_slot = b ^ tq4_row_swz(r);
+  // One chunk; the stage is a compile-time constant (the loop below is unrolled
+  // by two), so every stage address is a fixed offset from a loop-invariant
+  // base.
+  auto step = [&](int c, auto stage) {
+    constexpr int st = decltype(stage)::value;
+    // Chunk c has landed in stage st.  Its stage reads are issued first: an
+    // LDS read of the staging area after the next chunk's LDS-direct loads
+    // would wait for them.  Then chunk c + 1 goes to stage st ^ 1 (last read
+    // for chunk c - 1, whose values have all been used), and the centroid
+    // lookups, which read only the table, follow.
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* rows = lds + st * kTq4RowStage;
+    i32x4 kraw[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      kraw[t] = *reinterpret_cast<const i32x4*>(rows + (16 * t + r) * D + 16 * (k_slot ^ (4 * t)));
     const uint8_t* meta = lds + kTq4MetaOff + st * kTq4MetaStage;
     typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
     const f16x4 kn0 = *reinterpret_cast<const f16x4*>(meta + 2 * (4 * b));
@@ -575,11 +603,13 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     const f16x4 vz0h = *reinterpret_cast<const f16x4*>(meta + 128 + 2 * (4 * b));
     const f16x4 vz1h = *reinterpret_cast<const f16x4*>(meta + 128 + 2 * (16 + 4 * b));
     i32x2 vraw[4];
-    const uint8_t* vt = lds + st * kTq4VStage;
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc)
       vraw[pc] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (lds_i32x2*)(vt + tq4_v_lds_offset(tr_tok, pc) + tr_half));
+          (lds_i32x2*)(rows + tr_tok * D + 16 * ((4 + pc) ^ tr_swz) + tr_half));
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 < n_chunks) issue(c + 1, st ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
     // K operands: kop[t][2cc + hf] = (hi, lo) of index bytes 2hf and 2hf + 1 of
     // dword cc, i.e. dims 8cc + 4hf + (0, 1, 0, 1, 2, 3, 2, 3).
     bf16x8 kop[2][8];
@@ -593,8 +623,6 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
         kop[t][2 * cc] = __builtin_bit_cast(bf16x8, i32x4{e0[0], e0[1], e1[0], e1[1]});
         kop[t][2 * cc + 1] = __builtin_bit_cast(bf16x8, i32x4{e2[0], e2[1], e3[0], e3[1]});
       }
-    __builtin_amdgcn_sched_barrier(0);
-    if (c + 1 < n_chunks) issue(c + 1, st ^ 1);
     if (c == next_boundary) {
       on_boundary(part_done, w);
       ++part_done;
@@ -611,27 +639,29 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][k], qdup[k], s1, 0, 0, 0);
     }
 
-    // ---- scale by the K norm, mask ----
-    float y[8], vs[8], vz[8];
+    // ---- logits y = s * kn, mask ----
+    // y is the base-2 logit divided by qk_scale_log2: the factor enters with
+    // the exponent, exp2(y c - m2), one fused multiply-add.  The fp16 K norm,
+    // V scale and V zero point enter their products through mixed-precision
+    // fused multiply-adds, with no separate conversion.
+    const float c2 = a.qk_scale_log2;
+    float y[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      y[i] = s0[i] * ((float)kn0[i] * a.qk_scale_log2);
-      y[4 + i] = s1[i] * ((float)kn1[i] * a.qk_scale_log2);
-      vs[i] = (float)vs0h[i];
-      vs[4 + i] = (float)vs1h[i];
-      vz[i] = (float)vz0h[i];
-      vz[4 + i] = (float)vz1h[i];
+      y[i] = __builtin_fmaf((float)kn0[i], s0[i], 0.f);
+      y[4 + i] = __builtin_fmaf((float)kn1[i], s1[i], 0.f);
     }
+    f16x4 vs0 = vs0h, vs1 = vs1h, vz0 = vz0h, vz1 = vz1h;
     if (nvalid < CHUNK) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const bool v0 = 4 * b + i < nvalid, v1 = 16 + 4 * b + i < nvalid;
         y[i] = v0 ? y[i] : kNegInf;
         y[4 + i] = v1 ? y[4 + i] : kNegInf;
-        vs[i] = v0 ? vs[i] : 0.f;
-        vs[4 + i] = v1 ? vs[4 + i] : 0.f;
-        vz[i] = v0 ? vz[i] : 0.f;
-        vz[4 + i] = v1 ? vz[4 + i] : 0.f;
+        vs0[i] = v0 ? vs0[i] : (_Float16)0;
+        vs1[i] = v1 ? vs1[i] : (_Float16)0;
+        vz0[i] = v0 ? vz0[i] : (_Float16)0;
+        vz1[i] = v1 ? vz1[i] : (_Float16)0;
       }
     }
 
@@ -640,24 +670,26 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
 #pragma unroll
     for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
     mx = wave_max_xor16_32(mx);
-    const float m2_new = fmaxf(w.m2, mx);
+    const float m2_new = fmaxf(w.m2, mx * c2);  // c2 > 0: the max commutes with it
     const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
     float pr[8];
     float psum = 0.f, zs = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(y[i] - m2_new);
+      pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c2, -m2_new));
       psum += pr[i];
-      zs += pr[i] * vz[i];
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zs = __builtin_fmaf((float)vz0[i], pr[i], zs);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zs = __builtin_fmaf((float)vz1[i], pr[4 + i], zs);
     w.lsum = w.lsum * alpha + psum;
     w.zsum = w.zsum * alpha + zs;
     w.m2 = m2_new;
 
     // ---- V-scale reference and P operand ----
-    float vmax = vs[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) vmax = fmaxf(vmax, vs[i]);
+    const f16x4 vsm = __builtin_elementwise_max(vs0, vs1);
+    float vmax = fmaxf(fmaxf((float)vsm[0], (float)vsm[1]), fmaxf((float)vsm[2], (float)vsm[3]));
     vmax = wave_max_xor16_32(vmax);
     const float sigma_new = fmaxf(w.sigma, vmax);
     const float inv_sigma = sigma_new > 0.f ? 1.0f / sigma_new : 0.f;
@@ -665,7 +697,10 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     w.sigma = sigma_new;
     f16x8 pop;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pop[i] = (_Float16)(pr[i] * (vs[i] * inv_sigma));
+    for (int i = 0; i < 4; ++i) {
+      pop[i] = (_Float16)(pr[i] * __builtin_fmaf((float)vs0[i], inv_sigma, 0.f));
+      pop[4 + i] = (_Float16)(pr[4 + i] * __builtin_fmaf((float)vs1[i], inv_sigma, 0.f));
+    }
     if (__ballot(acc_scale != 1.0f)) {  // a factor of exactly 1 changes no bits
 #pragma unroll
       for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
@@ -679,25 +714,31 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       w.corr = c;
     }
 
-    // ---- PV: acc[2pc + par] (dims 32 pc + 2m + par, m = 4b + i) += V^T P ----
+    // ---- PV: acc[2pc], acc[2pc + 1] (dim pair 32 pc + 2m, m = 4b + i) += V^T P ----
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc) {
-      f16x8 vlo, vhi;
-      tq4_nibbles_f16(vraw[pc], vlo, vhi);
-      w.acc[2 * pc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vlo, pop, w.acc[2 * pc], 0, 0, 0);
+      f16x8 vwhole, vhi;
+      tq4_nibbles_f16(vraw[pc], vwhole, vhi);
+      w.acc[2 * pc] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vwhole, pop, w.acc[2 * pc], 0, 0, 0);
       w.acc[2 * pc + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vhi, pop, w.acc[2 * pc + 1], 0, 0, 0);
     }
+  };
+  for (int c = 0; c < n_chunks; c += 2) {
+    step(c, StageTag<0>{});
+    if (c + 1 < n_chunks) step(c + 1, StageTag<1>{});
   }
 }
 
 // One stream call for either format (lds_v: the wave's staging area, lds_sc:
-// the fp8 scale stages inside it).
+// the fp8 scale stages inside it, lds_tab: the wave's 4-bit centroid table).
 template <int QG, int BS, bool TQ4, typename OnBoundary>
 __device__ __forceinline__ void stream_any(const StreamArgs& a, int s, int h, int t_begin, int t_end,
                                            int chunks_per_part, uint8_t* lds_v, float* lds_sc,
-                                           WaveState& w, OnBoundary on_boundary) {
+                                           const i32x2* lds_tab, WaveState& w,
+                                           OnBoundary on_boundary) {
   if constexpr (TQ4)
-    stream_tokens_tq4<QG, BS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, w, on_boundary);
+    stream_tokens_tq4<QG, BS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_tab, w,
+                              on_boundary);
   else
     stream_tokens<QG, BS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_sc, w, on_boundary);
 }
@@ -705,13 +746,21 @@ __device__ __forceinline__ void stream_any(const StreamArgs& a, int s, int h, in
 // Clamp a device-side sequence length into [0, cap].
 __device__ __forceinline__ int clamp_len(int L, int cap) { return L < 0 ? 0 : (L > cap ? cap : L); }
 
+// Per-wave LDS staging area: for fp8, two 4 KiB V stages + two 256 B scale
+// stages; for 4-bit, two 4 KiB row stages + two 256 B metadata stages.  After
+// the stream the same bytes hold the wave's normalised partial (up to 16 rows
+// x 512 B) and its max logits / exp sums (2 x 16 floats).
+constexpr int kWaveLds = 2 * CHUNK * D + 2 * 2 * CHUNK * 4;
+static_assert(kTq4WaveLds <= kWaveLds, "4-bit staging area");
+static_assert(16 * D * 4 + 2 * 16 * 4 <= kWaveLds, "merge area must fit the staging area");
+
 // Split-K partition kernel: one wave per group of `parts_per_wave`
 // consecutive partitions of one (s, h); writes the partial triple of every
 // live partition in the group (STEP G).
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq_partition_kernel(PartitionArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v[2 * CHUNK * D];
-  __shared__ __attribute__((aligned(16))) float lds_sc[2 * 2 * CHUNK];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_stage[kWaveLds];
+  __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
   const int lane = threadIdx.x;
   const int r = lane & 15;
   const int b = lane >> 4;
@@ -729,6 +778,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq
   const int t_begin = p0 * E;
   if (t_begin >= L) return;  // dead partitions: nothing is written
   const int t_end = min(t_begin + min(ppw, P - p0) * E, L);
+  if constexpr (TQ4) build_tq4_table(lds_tab, a.st.centroids, lane, 64);
 
   // Partial triple of partition p: o_p = acc * sigma / l_p, m_p (natural
   // log units), l_p; then the running state restarts.
@@ -752,17 +802,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq
   WaveState w;
   w.reset();
   const int chunks_per_part = E / CHUNK;
-  stream_any<QG, BS, TQ4>(a.st, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_sc, w,
+  stream_any<QG, BS, TQ4>(a.st, s, h, t_begin, t_end, chunks_per_part, lds_stage,
+                          reinterpret_cast<float*>(lds_stage + 2 * CHUNK * D), lds_tab, w,
                           [&](int k, WaveState& ws) { store_partial(p0 + k, ws); });
   const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
   store_partial(p0 + (n_chunks - 1) / chunks_per_part, w);
 }
 
-// Per-wave LDS: two 4 KiB V stages + two 256 B scale stages; after the stream
-// the same bytes hold the wave's normalised partial (up to 16 rows x 512 B)
-// and its max logits / exp sums (2 x 16 floats).
-constexpr int kWaveLds = 2 * CHUNK * D + 2 * 2 * CHUNK * 4;
-static_assert(16 * D * 4 + 2 * 16 * 4 <= kWaveLds, "merge area must fit the staging area");
 
 // Log-sum-exp merge of n partials j = 0..n-1 for 4 columns, in j order:
 // o = sum_j (l_j e^{m_j - M} / sum_j' l_j' e^{m_j' - M}) o_j.  ld_o(j) returns
@@ -821,9 +867,14 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 o) {
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
   __shared__ int last_arrival;
+  if constexpr (TQ4) {  // before any return: every thread reaches the barrier
+    build_tq4_table(lds_tab, a.st.centroids, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int r = lane & 15;
   const int b = lane >> 4;
@@ -861,7 +912,8 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
     WaveState w;
     w.reset();
     stream_any<QG, BS, TQ4>(a.st, s, h, t_begin, t_end, 0x7fffffff, region,
-                            reinterpret_cast<float*>(region + 2 * CHUNK * D), w,
+                            reinterpret_cast<float*>(region + 2 * CHUNK * D),
+                            lds_tab, w,
                             [](int, WaveState&) {});
     f32x4 o[8];
     const float l = w.template finish_as<TQ4>(o);
@@ -1047,6 +1099,7 @@ template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   using Lay = FlatLayout<QG>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
   __shared__ int piece_sh[2 * kFlatWaves];        // s*Hkv+h of wave v's first (2v) / last
                                                   // (2v+1) piece, -1: none
   __shared__ int piece_ea[2 * kFlatWaves];        // list offset of that (s, h)'s first entry
@@ -1055,13 +1108,17 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   constexpr int TG = kTokensPerTileGroup;
   constexpr int kItems = QG * (D / 4);  // (row, 4 columns) items of one merge, <= blockDim
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
   const int S = a.num_seqs;
   const int Hkv = a.st.num_kv_heads;
   const int G = gridDim.x;
   const int g = blockIdx.x;
   auto len_of = [&](int s) { return clamp_len(a.seq_lens[s], a.len_cap); };
+  if constexpr (TQ4) {  // before any return: every thread reaches the barrier
+    build_tq4_table(lds_tab, a.st.centroids, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
 
   // Tile groups per kv head, per wave in registers: lane l holds the clamped
   // lengths of sequences s = l + 64 i (i < k <= 4); per slice i an inclusive
@@ -1150,7 +1207,8 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
       WaveState st;
       st.reset();
       stream_any<QG, BS, TQ4>(a.st, s, h, k0 * TG, min(k1 * TG, L), 0x7fffffff, area,
-                              reinterpret_cast<float*>(area + 2 * CHUNK * D), st,
+                              reinterpret_cast<float*>(area + 2 * CHUNK * D),
+                              lds_tab, st,
                               [](int, WaveState&) {});
       f32x4 o[8];
       const float l = st.template finish_as<TQ4>(o);
@@ -1335,7 +1393,7 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(ReduceArgs a) {
   const int live = (L + a.partition_tokens - 1) / a.partition_tokens;  // <= P (host-validated)
   const size_t row_sh = (size_t)sh * P * QG;  // (s, h, p = 0, g = 0)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bool staged = live > 1 && live <= kMergeMaxParts;
   if (staged) {
     for (int g = wave; g < QG; g += 4) {
@@ -1540,6 +1598,8 @@ void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_gro
 template <int QG, int BS, bool TQ4>
 hipError_t launch_flat_t(const FlatArgs& a, hipStream_t stream) {
   constexpr size_t lds = (size_t)kFlatWaves * FlatLayout<QG>::kArea;
+  static_assert(lds + (TQ4 ? kTq4TableEntries * 8 : 0) + 1024 <= 160 * 1024,
+                "LDS per workgroup");
   // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
   // the runtime needs none, and must not leak into the launch status.
   static const bool lds_opt_in = [] {

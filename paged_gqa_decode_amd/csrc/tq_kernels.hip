@@ -52,6 +52,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
@@ -90,6 +91,15 @@ __device__ __forceinline__ float wave_sum_xor16_32(float x) {
   const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
+
+// x of lane r + 8 (mod 16) of the same 16-lane row (DPP row_ror:8).
+__device__ __forceinline__ float row_ror8(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+}
+
+// The 4-bit stream's softmax runs on 4 tokens per lane instead of 8 when the
+// query group fits in 8 MFMA columns (lanes r >= 8 then hold the second tile).
+constexpr bool tq4_compact_softmax(int QG) { return QG <= 8; }
 
 // 8 fp8 e4m3fn codes (two dwords) -> 8 bf16, exact.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(int w0, int w1) {
@@ -139,6 +149,7 @@ struct WaveState {
   float sigma;
   float zsum;  // 4-bit format: this lane's share of sum_t p_t * vzero_t
   float corr;  // 4-bit format: this lane's share of sum_t P'_t (the f16 P operand)
+  float inv_sigma;  // 1 / sigma (0 while sigma is 0), recomputed only when sigma grows
   f32x4 acc[8];
   __device__ __forceinline__ void reset() {
     m2 = kNegInf;
@@ -146,6 +157,7 @@ struct WaveState {
     sigma = 0.f;
     zsum = 0.f;
     corr = 0.f;
+    inv_sigma = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
@@ -164,10 +176,13 @@ struct WaveState {
   // - acc[2pc + 1]) sigma + zsum) / l and o_odd = ((acc[2pc + 1] - 1024 corr)
   // sigma / 16 + zsum) / l; o is returned interleaved, o[2pc + half] = d = 32 pc
   // + 8b + 4 half + 0..3.
+  template <int QG>
   __device__ __forceinline__ float finish_tq4(f32x4 o[8]) const {
-    const float l = wave_sum_xor16_32(lsum);
-    const float z = wave_sum_xor16_32(zsum);
-    const float c1024 = 1024.0f * wave_sum_xor16_32(corr);
+    // With the compact softmax, lanes r and r + 8 hold the two tiles of query r.
+    auto pair = [](float x) { return tq4_compact_softmax(QG) ? x + row_ror8(x) : x; };
+    const float l = wave_sum_xor16_32(pair(lsum));
+    const float z = wave_sum_xor16_32(pair(zsum));
+    const float c1024 = 1024.0f * wave_sum_xor16_32(pair(corr));
     const float f = sigma / l;
     const float f16th = f * 0.0625f;
     const float zl = z / l;
@@ -180,10 +195,10 @@ struct WaveState {
     }
     return l;
   }
-  template <bool TQ4>
+  template <bool TQ4, int QG>
   __device__ __forceinline__ float finish_as(f32x4 o[8]) const {
     if constexpr (TQ4)
-      return finish_tq4(o);
+      return finish_tq4<QG>(o);
     else
       return finish(o);
   }
@@ -374,10 +389,14 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
     float vmax = fmaxf(fmaxf(fmaxf(vs0[0], vs0[1]), fmaxf(vs0[2], vs0[3])),
                        fmaxf(fmaxf(vs1[0], vs1[1]), fmaxf(vs1[2], vs1[3])));
     vmax = wave_max_xor16_32(vmax);
-    const float sigma_new = fmaxf(w.sigma, vmax);
-    const float inv_sigma = sigma_new > 0.f ? 1.0f / sigma_new : 0.f;
-    const float acc_scale = alpha * (w.sigma * inv_sigma);
-    w.sigma = sigma_new;
+    float acc_scale = alpha;
+    if (vmax > w.sigma) {  // uniform: vmax is a wave-wide maximum
+      const float inv = 1.0f / vmax;
+      acc_scale = alpha * (w.sigma * inv);
+      w.sigma = vmax;
+      w.inv_sigma = inv;
+    }
+    const float inv_sigma = w.inv_sigma;
     f16x8 pop;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -490,6 +509,7 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
                                                   OnBoundary on_boundary) {
   static_assert(BS == 16 || BS == 32, "kv block size");
   static_assert(QG >= 1 && QG <= 16, "query group size");
+  constexpr bool kCompact = tq4_compact_softmax(QG);
   const int lane = threadIdx.x & 63;
   const int r = lane & 15;
   const int b = lane >> 4;
@@ -595,13 +615,22 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     for (int t = 0; t < 2; ++t)
       kraw[t] = *reinterpret_cast<const i32x4*>(rows + (16 * t + r) * D + 16 * (k_slot ^ (4 * t)));
     const uint8_t* meta = lds + kTq4MetaOff + st * kTq4MetaStage;
-    typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-    const f16x4 kn0 = *reinterpret_cast<const f16x4*>(meta + 2 * (4 * b));
-    const f16x4 kn1 = *reinterpret_cast<const f16x4*>(meta + 2 * (16 + 4 * b));
-    const f16x4 vs0h = *reinterpret_cast<const f16x4*>(meta + 64 + 2 * (4 * b));
-    const f16x4 vs1h = *reinterpret_cast<const f16x4*>(meta + 64 + 2 * (16 + 4 * b));
-    const f16x4 vz0h = *reinterpret_cast<const f16x4*>(meta + 128 + 2 * (4 * b));
-    const f16x4 vz1h = *reinterpret_cast<const f16x4*>(meta + 128 + 2 * (16 + 4 * b));
+    // Metadata of this lane's tokens: 4b + i and 16 + 4b + i, or with the
+    // compact softmax only tile r / 8 (see below).
+    f16x4 kn0, kn1, vs0h, vs1h, vz0h, vz1h;
+    if constexpr (kCompact) {
+      const int mo = 2 * (16 * (r >> 3) + 4 * b);
+      kn0 = *reinterpret_cast<const f16x4*>(meta + mo);
+      vs0h = *reinterpret_cast<const f16x4*>(meta + 64 + mo);
+      vz0h = *reinterpret_cast<const f16x4*>(meta + 128 + mo);
+    } else {
+      kn0 = *reinterpret_cast<const f16x4*>(meta + 2 * (4 * b));
+      kn1 = *reinterpret_cast<const f16x4*>(meta + 2 * (16 + 4 * b));
+      vs0h = *reinterpret_cast<const f16x4*>(meta + 64 + 2 * (4 * b));
+      vs1h = *reinterpret_cast<const f16x4*>(meta + 64 + 2 * (16 + 4 * b));
+      vz0h = *reinterpret_cast<const f16x4*>(meta + 128 + 2 * (4 * b));
+      vz1h = *reinterpret_cast<const f16x4*>(meta + 128 + 2 * (16 + 4 * b));
+    }
     i32x2 vraw[4];
 #pragma unroll
     for (int pc = 0; pc < 4; ++pc)
@@ -639,79 +668,157 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][k], qdup[k], s1, 0, 0, 0);
     }
 
-    // ---- logits y = s * kn, mask ----
-    // y is the base-2 logit divided by qk_scale_log2: the factor enters with
-    // the exponent, exp2(y c - m2), one fused multiply-add.  The fp16 K norm,
-    // V scale and V zero point enter their products through mixed-precision
-    // fused multiply-adds, with no separate conversion.
-    const float c2 = a.qk_scale_log2;
-    float y[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      y[i] = __builtin_fmaf((float)kn0[i], s0[i], 0.f);
-      y[4 + i] = __builtin_fmaf((float)kn1[i], s1[i], 0.f);
-    }
-    f16x4 vs0 = vs0h, vs1 = vs1h, vz0 = vz0h, vz1 = vz1h;
-    if (nvalid < CHUNK) {
+    // ---- softmax and P operand ----
+    f16x8 pop;
+    if constexpr (kCompact) {
+      // QG <= 8 uses only query columns r < 8, so lanes r >= 8 take over tile
+      // 1 of query r - 8 (the MFMA's results moved by 8 lanes within each row):
+      // each lane then handles 4 tokens, 16 (r / 8) + 4b + i, instead of 8.
+      // The max reductions add one step across the two halves of a row; the
+      // sums are paired up the same way at the end (finish_tq4).  The P
+      // operand of lane r < 8 is its own 4 values followed by lane r + 8's.
+      const float c2 = a.qk_scale_log2;
+      float y[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const bool v0 = 4 * b + i < nvalid, v1 = 16 + 4 * b + i < nvalid;
-        y[i] = v0 ? y[i] : kNegInf;
-        y[4 + i] = v1 ? y[4 + i] : kNegInf;
-        vs0[i] = v0 ? vs0[i] : (_Float16)0;
-        vs1[i] = v1 ? vs1[i] : (_Float16)0;
-        vz0[i] = v0 ? vz0[i] : (_Float16)0;
-        vz1[i] = v1 ? vz1[i] : (_Float16)0;
+        const float sc = __int_as_float(__builtin_amdgcn_update_dpp(
+            __float_as_int(s0[i]), __float_as_int(s1[i]), 0x118, 0xF, 0xC, false));  // row_shr:8
+        y[i] = __builtin_fmaf((float)kn0[i], sc, 0.f);
       }
-    }
+      f16x4 vs = vs0h, vz = vz0h;
+      if (nvalid < CHUNK) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool v = 16 * (r >> 3) + 4 * b + i < nvalid;
+          y[i] = v ? y[i] : kNegInf;
+          vs[i] = v ? vs[i] : (_Float16)0;
+          vz[i] = v ? vz[i] : (_Float16)0;
+        }
+      }
+      float mx = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
+      mx = fmaxf(mx, row_ror8(mx));
+      mx = wave_max_xor16_32(mx);
+      const float m2_new = fmaxf(w.m2, mx * c2);  // c2 > 0: the max commutes with it
+      const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
+      float pr[4];
+      float psum = 0.f, zs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c2, -m2_new));
+        psum += pr[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zs = __builtin_fmaf((float)vz[i], pr[i], zs);
+      w.lsum = w.lsum * alpha + psum;
+      w.zsum = w.zsum * alpha + zs;
+      w.m2 = m2_new;
 
-    // ---- online softmax (base 2) ----
-    float mx = y[0];
+      float vmax = fmaxf(fmaxf((float)vs[0], (float)vs[1]), fmaxf((float)vs[2], (float)vs[3]));
+      vmax = fmaxf(vmax, row_ror8(vmax));
+      vmax = wave_max_xor16_32(vmax);
+      float acc_scale = alpha;
+      if (vmax > w.sigma) {  // uniform: vmax is a wave-wide maximum
+        const float inv = 1.0f / vmax;
+        acc_scale = alpha * (w.sigma * inv);
+        w.sigma = vmax;
+        w.inv_sigma = inv;
+      }
+      const float inv_sigma = w.inv_sigma;
+      const f16x2 own01 = {(_Float16)(pr[0] * __builtin_fmaf((float)vs[0], inv_sigma, 0.f)),
+                           (_Float16)(pr[1] * __builtin_fmaf((float)vs[1], inv_sigma, 0.f))};
+      const f16x2 own23 = {(_Float16)(pr[2] * __builtin_fmaf((float)vs[2], inv_sigma, 0.f)),
+                           (_Float16)(pr[3] * __builtin_fmaf((float)vs[3], inv_sigma, 0.f))};
+      const int o01 = __builtin_bit_cast(int, own01), o23 = __builtin_bit_cast(int, own23);
+      const int t01 = __builtin_amdgcn_update_dpp(0, o01, 0x128, 0xF, 0xF, false);  // row_ror:8
+      const int t23 = __builtin_amdgcn_update_dpp(0, o23, 0x128, 0xF, 0xF, false);
+      pop = __builtin_bit_cast(f16x8, i32x4{o01, o23, t01, t23});
+      if (__ballot(acc_scale != 1.0f)) {  // a factor of exactly 1 changes no bits
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
-    mx = wave_max_xor16_32(mx);
-    const float m2_new = fmaxf(w.m2, mx * c2);  // c2 > 0: the max commutes with it
-    const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
-    float pr[8];
-    float psum = 0.f, zs = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c2, -m2_new));
-      psum += pr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) zs = __builtin_fmaf((float)vz0[i], pr[i], zs);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) zs = __builtin_fmaf((float)vz1[i], pr[4 + i], zs);
-    w.lsum = w.lsum * alpha + psum;
-    w.zsum = w.zsum * alpha + zs;
-    w.m2 = m2_new;
-
-    // ---- V-scale reference and P operand ----
-    const f16x4 vsm = __builtin_elementwise_max(vs0, vs1);
-    float vmax = fmaxf(fmaxf((float)vsm[0], (float)vsm[1]), fmaxf((float)vsm[2], (float)vsm[3]));
-    vmax = wave_max_xor16_32(vmax);
-    const float sigma_new = fmaxf(w.sigma, vmax);
-    const float inv_sigma = sigma_new > 0.f ? 1.0f / sigma_new : 0.f;
-    const float acc_scale = alpha * (w.sigma * inv_sigma);
-    w.sigma = sigma_new;
-    f16x8 pop;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pop[i] = (_Float16)(pr[i] * __builtin_fmaf((float)vs0[i], inv_sigma, 0.f));
-      pop[4 + i] = (_Float16)(pr[4 + i] * __builtin_fmaf((float)vs1[i], inv_sigma, 0.f));
-    }
-    if (__ballot(acc_scale != 1.0f)) {  // a factor of exactly 1 changes no bits
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
-      w.corr *= acc_scale;
-    }
-    {  // corr += sum of this lane's 8 P' values, exactly as the MFMA sees them
+        for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
+        w.corr *= acc_scale;
+      }
+      // corr += this lane's own 4 P' values; lane r + 8's are added at the end
       const f16x2 one = {(_Float16)1, (_Float16)1};
-      float c = w.corr;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_fdot2(f16x2{pop[2 * i], pop[2 * i + 1]}, one, c, false);
-      w.corr = c;
+      w.corr = __builtin_amdgcn_fdot2(own23, one, __builtin_amdgcn_fdot2(own01, one, w.corr, false),
+                                      false);
+    } else {
+      // ---- logits y = s * kn, mask ----
+      // y is the base-2 logit divided by qk_scale_log2: the factor enters with
+      // the exponent, exp2(y c - m2), one fused multiply-add.  The fp16 K norm,
+      // V scale and V zero point enter their products through mixed-precision
+      // fused multiply-adds, with no separate conversion.
+      const float c2 = a.qk_scale_log2;
+      float y[8];
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[i] = __builtin_fmaf((float)kn0[i], s0[i], 0.f);
+        y[4 + i] = __builtin_fmaf((float)kn1[i], s1[i], 0.f);
+      }
+      f16x4 vs0 = vs0h, vs1 = vs1h, vz0 = vz0h, vz1 = vz1h;
+      if (nvalid < CHUNK) {
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool v0 = 4 * b + i < nvalid, v1 = 16 + 4 * b + i < nvalid;
+          y[i] = v0 ? y[i] : kNegInf;
+          y[4 + i] = v1 ? y[4 + i] : kNegInf;
+          vs0[i] = v0 ? vs0[i] : (_Float16)0;
+          vs1[i] = v1 ? vs1[i] : (_Float16)0;
+          vz0[i] = v0 ? vz0[i] : (_Float16)0;
+          vz1[i] = v1 ? vz1[i] : (_Float16)0;
+        }
+      }
+
+      // ---- online softmax (base 2) ----
+      float mx = y[0];
+  #pragma unroll
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
+      mx = wave_max_xor16_32(mx);
+      const float m2_new = fmaxf(w.m2, mx * c2);  // c2 > 0: the max commutes with it
+      const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
+      float pr[8];
+      float psum = 0.f, zs = 0.f;
+  #pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c2, -m2_new));
+        psum += pr[i];
+      }
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) zs = __builtin_fmaf((float)vz0[i], pr[i], zs);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) zs = __builtin_fmaf((float)vz1[i], pr[4 + i], zs);
+      w.lsum = w.lsum * alpha + psum;
+      w.zsum = w.zsum * alpha + zs;
+      w.m2 = m2_new;
+
+      // ---- V-scale reference and P operand ----
+      const f16x4 vsm = __builtin_elementwise_max(vs0, vs1);
+      float vmax = fmaxf(fmaxf((float)vsm[0], (float)vsm[1]), fmaxf((float)vsm[2], (float)vsm[3]));
+      vmax = wave_max_xor16_32(vmax);
+      float acc_scale = alpha;
+      if (vmax > w.sigma) {  // uniform: vmax is a wave-wide maximum
+        const float inv = 1.0f / vmax;
+        acc_scale = alpha * (w.sigma * inv);
+        w.sigma = vmax;
+        w.inv_sigma = inv;
+      }
+      const float inv_sigma = w.inv_sigma;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pop[i] = (_Float16)(pr[i] * __builtin_fmaf((float)vs0[i], inv_sigma, 0.f));
+        pop[4 + i] = (_Float16)(pr[4 + i] * __builtin_fmaf((float)vs1[i], inv_sigma, 0.f));
+      }
+      if (__ballot(acc_scale != 1.0f)) {  // a factor of exactly 1 changes no bits
+  #pragma unroll
+        for (int i = 0; i < 8; ++i) w.acc[i] *= acc_scale;
+        w.corr *= acc_scale;
+      }
+      {  // corr += sum of this lane's 8 P' values, exactly as the MFMA sees them
+        const f16x2 one = {(_Float16)1, (_Float16)1};
+        float c = w.corr;
+  #pragma unroll
+        for (int i = 0; i < 4; ++i) c = __builtin_amdgcn_fdot2(f16x2{pop[2 * i], pop[2 * i + 1]}, one, c, false);
+        w.corr = c;
+      }
     }
 
     // ---- PV: acc[2pc], acc[2pc + 1] (dim pair 32 pc + 2m, m = 4b + i) += V^T P ----
@@ -784,7 +891,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq
   // log units), l_p; then the running state restarts.
   auto store_partial = [&](int p, WaveState& w) {
     f32x4 o[8];
-    const float l = w.template finish_as<TQ4>(o);
+    const float l = w.template finish_as<TQ4, QG>(o);
     if (r < QG) {
       const size_t row = ((size_t)(s * Hkv + h) * P + p) * QG + r;
       float* dst = a.o + row * D;
@@ -916,7 +1023,7 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
                             lds_tab, w,
                             [](int, WaveState&) {});
     f32x4 o[8];
-    const float l = w.template finish_as<TQ4>(o);
+    const float l = w.template finish_as<TQ4, QG>(o);
     if (r < QG) {
 #pragma unroll
       for (int dblk = 0; dblk < 8; ++dblk)
@@ -1211,7 +1318,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
                               lds_tab, st,
                               [](int, WaveState&) {});
       f32x4 o[8];
-      const float l = st.template finish_as<TQ4>(o);
+      const float l = st.template finish_as<TQ4, QG>(o);
       if (k0 == 0 && k1 == n) {  // the whole (s, h)
         const int r = lane & 15, b = lane >> 4;
         if (r < QG) {

@@ -73,6 +73,18 @@ constexpr int kCachePolicyStreaming = 2;
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
 constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 
+// max(a, b) for operands that are not NaN, as one v_med3_f32 against +inf:
+// fmaxf would first quiet each operand that the compiler cannot prove is no
+// signalling NaN (every value that comes from another lane or from memory),
+// one extra instruction per operand.
+__device__ __forceinline__ float fmax_nn(float a, float b) {
+  // +inf from an opaque scalar move, or the compiler folds the median back
+  // into a maximum and reinstates the quieting.
+  float inf;
+  asm("s_mov_b32 %0, 0x7f800000" : "=s"(inf));
+  return __builtin_amdgcn_fmed3f(a, b, inf);
+}
+
 // Reductions over the lanes l, l^16, l^32, l^48 (the four 16-lane groups) by
 // the gfx950 lane swaps, no LDS round trip: v_permlane16_swap of a value with
 // itself leaves {own, partner l^16} in the two results (in some order), and
@@ -80,9 +92,9 @@ constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
 // every lane gets the same bits, as with a pair of xor shuffles.
 __device__ __forceinline__ float wave_max_xor16_32(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  x = fmax_nn(__uint_as_float(p[0]), __uint_as_float(p[1]));
   const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+  return fmax_nn(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
 __device__ __forceinline__ float wave_sum_xor16_32(float x) {
@@ -94,7 +106,8 @@ __device__ __forceinline__ float wave_sum_xor16_32(float x) {
 
 // x of lane r + 8 (mod 16) of the same 16-lane row (DPP row_ror:8).
 __device__ __forceinline__ float row_ror8(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(x), __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
 // The 4-bit stream's softmax runs on 4 tokens per lane instead of 8 when the
@@ -371,9 +384,9 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
     // ---- online softmax (base 2) ----
     float mx = y[0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
+    for (int i = 1; i < 8; ++i) mx = fmax_nn(mx, y[i]);
     mx = wave_max_xor16_32(mx);
-    const float m2_new = fmaxf(w.m2, mx);
+    const float m2_new = fmax_nn(w.m2, mx);
     const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
     float pr[8];
     float psum = 0.f;
@@ -386,8 +399,8 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
     w.m2 = m2_new;
 
     // ---- V-scale reference and P operand ----
-    float vmax = fmaxf(fmaxf(fmaxf(vs0[0], vs0[1]), fmaxf(vs0[2], vs0[3])),
-                       fmaxf(fmaxf(vs1[0], vs1[1]), fmaxf(vs1[2], vs1[3])));
+    float vmax = fmax_nn(fmax_nn(fmax_nn(vs0[0], vs0[1]), fmax_nn(vs0[2], vs0[3])),
+                         fmax_nn(fmax_nn(vs1[0], vs1[1]), fmax_nn(vs1[2], vs1[3])));
     vmax = wave_max_xor16_32(vmax);
     float acc_scale = alpha;
     if (vmax > w.sigma) {  // uniform: vmax is a wave-wide maximum
@@ -558,33 +571,40 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
 
   // Issue chunk c into LDS stage `st`: its 32 rows, 8 per LDS-direct load
   // (lane l lands at byte 16 l of the load's 1 KiB: row 8j + l/8, slot l % 8,
-  // so it fetches piece (l % 8) ^ tq4_row_swz(row)), then the metadata.
+  // so it fetches piece (l % 8) ^ tq4_row_swz(row)), then the metadata (LDS
+  // dword l < 48 = field l / 16, tokens 2 (l % 16) and +1).  Every address is
+  // a wave-uniform block base plus a per-lane 32-bit offset fixed for the
+  // stream.
+  uint32_t row_off[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 8 * j + (lane >> 3);
+    const int piece = (lane & 7) ^ tq4_row_swz(row);
+    const int slot = BS == 32 ? row : (row & 15);
+    row_off[j] = (uint32_t)(slot * D + 16 * piece);
+  }
+  const int ml = lane < 48 ? lane : 0;
+  const uint32_t meta_off = (uint32_t)(4 * (BS == 32 ? ml : (ml >> 4) * 8 + (ml & 7)));
+  const bool meta_second = BS == 16 && (ml & 15) >= 8;  // tokens 16..31: the second block
+  const size_t head_off = (size_t)h * BS * D;
   auto issue = [&](int c, int st) {
     const int jb = (c * CHUNK) / BS;
     const uint32_t blkA = block_id(jb);
     uint32_t blkB = blkA;
     if (BS == 16) blkB = (jb + 1 < n_blocks) ? block_id(jb + 1) : blkA;
+    const uint8_t* recA = a.tq4 + (size_t)blkA * block_bytes;
+    const uint8_t* recB = a.tq4 + (size_t)blkB * block_bytes;
     uint8_t* rdst = lds + st * kTq4RowStage;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = 8 * j + (lane >> 3);
-      const int piece = (lane & 7) ^ tq4_row_swz(row);
-      const uint32_t blk = (BS == 32 || row < 16) ? blkA : blkB;
-      const int slot = BS == 32 ? row : (row & 15);
-      const uint8_t* src = a.tq4 + blk * block_bytes + ((size_t)h * BS + slot) * D + 16 * piece;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(rdst + 1024 * j), 16, 0,
-                                       kCachePolicyStreaming);
+      const uint8_t* rec = (BS == 32 || j < 2) ? recA : recB;
+      __builtin_amdgcn_global_load_lds(rec + head_off + row_off[j], (lds_void*)(rdst + 1024 * j),
+                                       16, 0, kCachePolicyStreaming);
     }
-    {
-      // LDS dword l (l < 48) = field l / 16, tokens 2 (l % 16) and +1.
-      const int l = lane < 48 ? lane : 0;
-      const int field = l >> 4, pair = l & 15;
-      const uint32_t blk = (BS == 32 || pair < 8) ? blkA : blkB;
-      const int dword = BS == 32 ? l : field * 8 + (pair & 7);
-      const uint8_t* src = a.tq4 + blk * block_bytes + meta_base + 4 * dword;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(lds + kTq4MetaOff + st * kTq4MetaStage), 4,
-                                       0, kCachePolicyStreaming);
-    }
+    const uint8_t* mrec = meta_second ? recB : recA;
+    __builtin_amdgcn_global_load_lds(mrec + meta_base + meta_off,
+                                     (lds_void*)(lds + kTq4MetaOff + st * kTq4MetaStage), 4, 0,
+                                     kCachePolicyStreaming);
   };
 
   const int tr_tok = 16 * (r >> 3) + 4 * b + ((r >> 1) & 3);
@@ -695,26 +715,24 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
           vz[i] = v ? vz[i] : (_Float16)0;
         }
       }
-      float mx = fmaxf(fmaxf(y[0], y[1]), fmaxf(y[2], y[3]));
-      mx = fmaxf(mx, row_ror8(mx));
+      float mx = fmax_nn(fmax_nn(y[0], y[1]), fmax_nn(y[2], y[3]));
+      mx = fmax_nn(mx, row_ror8(mx));
       mx = wave_max_xor16_32(mx);
-      const float m2_new = fmaxf(w.m2, mx * c2);  // c2 > 0: the max commutes with it
+      const float m2_new = fmax_nn(w.m2, mx * c2);  // c2 > 0: the max commutes with it
       const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
       float pr[4];
-      float psum = 0.f, zs = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c2, -m2_new));
-        psum += pr[i];
-      }
+      for (int i = 0; i < 4; ++i) pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(y[i], c2, -m2_new));
+      const float psum = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+      float zs = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) zs = __builtin_fmaf((float)vz[i], pr[i], zs);
       w.lsum = w.lsum * alpha + psum;
       w.zsum = w.zsum * alpha + zs;
       w.m2 = m2_new;
 
-      float vmax = fmaxf(fmaxf((float)vs[0], (float)vs[1]), fmaxf((float)vs[2], (float)vs[3]));
-      vmax = fmaxf(vmax, row_ror8(vmax));
+      float vmax = fmax_nn(fmax_nn((float)vs[0], (float)vs[1]), fmax_nn((float)vs[2], (float)vs[3]));
+      vmax = fmax_nn(vmax, row_ror8(vmax));
       vmax = wave_max_xor16_32(vmax);
       float acc_scale = alpha;
       if (vmax > w.sigma) {  // uniform: vmax is a wave-wide maximum
@@ -771,9 +789,9 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       // ---- online softmax (base 2) ----
       float mx = y[0];
   #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, y[i]);
+      for (int i = 1; i < 8; ++i) mx = fmax_nn(mx, y[i]);
       mx = wave_max_xor16_32(mx);
-      const float m2_new = fmaxf(w.m2, mx * c2);  // c2 > 0: the max commutes with it
+      const float m2_new = fmax_nn(w.m2, mx * c2);  // c2 > 0: the max commutes with it
       const float alpha = __builtin_amdgcn_exp2f(w.m2 - m2_new);
       float pr[8];
       float psum = 0.f, zs = 0.f;
@@ -792,7 +810,7 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
 
       // ---- V-scale reference and P operand ----
       const f16x4 vsm = __builtin_elementwise_max(vs0, vs1);
-      float vmax = fmaxf(fmaxf((float)vsm[0], (float)vsm[1]), fmaxf((float)vsm[2], (float)vsm[3]));
+      float vmax = fmax_nn(fmax_nn((float)vsm[0], (float)vsm[1]), fmax_nn((float)vsm[2], (float)vsm[3]));
       vmax = wave_max_xor16_32(vmax);
       float acc_scale = alpha;
       if (vmax > w.sigma) {  // uniform: vmax is a wave-wide maximum

@@ -133,17 +133,24 @@ def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10)
     ps = src[2 * kvb:2 * kvb + groups * 8 * chunks * 256]
     pat_bytes = 2 * kvb + ps.numel()
     pt = best(lambda w: probe.pattern(pk, pv, ps, chunks, w, sink), pat_bytes, (groups,))
-    del src, dst, sink, pk, pv, ps
+    # The 4-bit format's byte pattern: the same 2048 x 128 chunks of 4 KiB of rows and 192 B of
+    # metadata = 1.1241 GB, the bandwidth workload's bytes in that format.
+    rows4 = src[:groups * 8 * chunks * 4096]
+    meta4 = src[rows4.numel():rows4.numel() + groups * 8 * chunks * 256]
+    pat4_bytes = groups * 8 * chunks * (4096 + 192)
+    pt4 = best(lambda w: probe.pattern4(rows4, meta4, chunks, w, sink), pat4_bytes, (groups,))
+    del src, dst, sink, pk, pv, ps, rows4, meta4
     torch.cuda.empty_cache()
     return {"read_bytes": nread, "copy_bytes": ncopy, "reps": reps,
             "read_gbs": round(rd[0], 1), "read_workgroups": rd[1],
             "pattern_bytes": pat_bytes, "pattern_gbs": round(pt[0], 1),
+            "pattern4_bytes": pat4_bytes, "pattern4_gbs": round(pt4[0], 1),
             "copy_gbs": round(cp[0], 1), "copy_workgroups": cp[1]}
 
 
 PROFILE_KERNELS = ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel", "tq_merge_kernel",
                    "tq_kv_write_kernel", "tq_flat_kernel[tq4]", "tq_partition_kernel[tq4]",
-                   "probe_pattern_kernel")
+                   "probe_pattern_kernel", "probe_pattern4_kernel")
 PROFILE_CMD = ("rocprofv3 {what} -d <dir>/{sub} -o {sub} --output-format csv -- "
                "python3 bench.py --workload {wl} --steps 20 --warmup 3 --no-cpu-baseline")
 
@@ -275,7 +282,8 @@ def main() -> int:
     if not args.no_probe:
         probe_res = hbm_probe(dev)
         log(f"[bench] HBM probe: read {probe_res['read_gbs']} GB/s, copy {probe_res['copy_gbs']} GB/s, "
-            f"decode byte pattern without arithmetic {probe_res['pattern_gbs']} GB/s")
+            f"decode byte pattern without arithmetic {probe_res['pattern_gbs']} GB/s (4-bit: "
+            f"{probe_res['pattern4_gbs']} GB/s)")
     log(f"[bench] generating {wl.name} on {dev}")
     inp = workloads.make_inputs(wl, device=dev)
     torch.cuda.synchronize()
@@ -440,6 +448,9 @@ def main() -> int:
                   "bytes_per_step": bytes4,
                   "token_heads_per_s": round(tok_s, 1),
                   "vs_fp8_token_heads_per_s": round(tok_s / tok_s_fp8, 3)}
+    if probe_res:
+        res["tq4"]["frac_of_decode_pattern"] = round(
+            res["tq4"]["GBps"] / probe_res["pattern4_gbs"], 4)
     log(f"[bench] 4-bit format: step {best4 * 1e3:.1f} us ({res['tq4']['GBps']} GB/s, "
         f"{res['tq4']['pct_of_hbm_peak']}% of peak), {tok_s / 1e9:.1f} G token-heads/s = "
         f"{res['tq4']['vs_fp8_token_heads_per_s']}x the fp8 step")

@@ -19,6 +19,12 @@
  *   * 4096 and scales + (w * chunks_per_wave + c) * 256, one chunk in flight
  *   ahead, and writes one digest per workgroup to sink.  kv_bytes and
  *   scale_bytes are the buffer sizes (checked); all 16-byte aligned.
+ * tq_probe_pattern4: the same for the 4-bit format's stream: wave w reads
+ *   chunks_per_wave chunks, each 4096 bytes of rows from rows + (w *
+ *   chunks_per_wave + c) * 4096 (four 1 KiB LDS-direct loads) and 192 bytes of
+ *   metadata from meta + (w * chunks_per_wave + c) * 256, into LDS, one chunk
+ *   in flight ahead; rows_bytes and meta_bytes are the buffer sizes (checked);
+ *   16-byte aligned.
  */
 #ifndef TQ_PROBE_H
 #define TQ_PROBE_H
@@ -37,6 +43,9 @@ int32_t tq_probe_copy(void* dst, const void* src, size_t n_bytes, int32_t num_wo
 int32_t tq_probe_pattern(const void* k, const void* v, const void* scales, size_t kv_bytes,
                          size_t scale_bytes, int32_t chunks_per_wave, int32_t num_workgroups,
                          uint32_t* sink, void* stream);
+int32_t tq_probe_pattern4(const void* rows, const void* meta, size_t rows_bytes, size_t meta_bytes,
+                          int32_t chunks_per_wave, int32_t num_workgroups, uint32_t* sink,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -126,6 +126,76 @@ extern "C" int32_t tq_probe_pattern(const void* k, const void* v, const void* sc
   return (int32_t)hipGetLastError();
 }
 
+// The byte pattern of the 4-bit format's stream with no arithmetic: per chunk
+// 32 rows of 128 B (4 KiB, four 1 KiB LDS-direct loads) and 192 B of
+// metadata (48 lanes x 4 B) into LDS, non-temporal, the next chunk issued once
+// the current one is drained and read.  Workgroups of 8 waves.
+constexpr int kPat4Rows = 4096, kPat4Meta = 256, kPat4MetaUsed = 192;
+__global__ __launch_bounds__(512) void probe_pattern4_kernel(const uint8_t* __restrict__ rows,
+                                                             const uint8_t* __restrict__ meta,
+                                                             int chunks, uint32_t* __restrict__ sink) {
+  __shared__ __attribute__((aligned(16))) uint8_t sa[8][kPat4Rows + kPat4Meta];
+  __shared__ __attribute__((aligned(16))) uint8_t sb[8][kPat4Rows + kPat4Meta];
+  constexpr int kWaitVmcnt0 = (0x7 << 4) | (0xF << 8);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t gw = (size_t)blockIdx.x * 8 + wave;
+  const uint8_t* rw = rows + gw * (size_t)chunks * kPat4Rows;
+  const uint8_t* mw = meta + gw * (size_t)chunks * kPat4Meta;
+  int lacc = 0;
+  auto issue = [&](int c, uint8_t* st) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(rw + (size_t)c * kPat4Rows + 1024 * j + 16 * lane,
+                                       (lds_void*)(st + 1024 * j), 16, 0, 2);
+    const int l = lane < kPat4MetaUsed / 4 ? lane : 0;
+    __builtin_amdgcn_global_load_lds(mw + (size_t)c * kPat4Meta + 4 * l,
+                                     (lds_void*)(st + kPat4Rows), 4, 0, 2);
+  };
+  if (chunks > 0) issue(0, sa[wave]);
+  for (int c = 0; c < chunks; c += 2) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    lacc += *reinterpret_cast<const int*>(sa[wave] + 64 * lane) +
+            *reinterpret_cast<const int*>(sa[wave] + kPat4Rows + 4 * (lane & 31));
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 1 >= chunks) break;
+    issue(c + 1, sb[wave]);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    lacc += *reinterpret_cast<const int*>(sb[wave] + 64 * lane) +
+            *reinterpret_cast<const int*>(sb[wave] + kPat4Rows + 4 * (lane & 31));
+    __builtin_amdgcn_sched_barrier(0);
+    if (c + 2 < chunks) issue(c + 2, sa[wave]);
+  }
+  uint32_t x = (uint32_t)lacc;
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off, 64);
+  __shared__ uint32_t red[8];
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t y = 0;
+    for (int w = 0; w < 8; ++w) y ^= red[w];
+    sink[blockIdx.x] = y;
+  }
+}
+
+extern "C" int32_t tq_probe_pattern4(const void* rows, const void* meta, size_t rows_bytes,
+                                     size_t meta_bytes, int32_t chunks_per_wave,
+                                     int32_t num_workgroups, uint32_t* sink, void* stream) {
+  const size_t waves = (size_t)num_workgroups * 8;
+  if (!rows || !meta || !sink || ((uintptr_t)rows & 15) || ((uintptr_t)meta & 15) ||
+      num_workgroups < 1 || num_workgroups > 65536 || chunks_per_wave < 1 ||
+      waves * (size_t)chunks_per_wave * kPat4Rows > rows_bytes ||
+      waves * (size_t)chunks_per_wave * kPat4Meta > meta_bytes)
+    return (int32_t)hipErrorInvalidValue;
+  hipLaunchKernelGGL(probe_pattern4_kernel, dim3(num_workgroups), dim3(512), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(rows),
+                     static_cast<const uint8_t*>(meta), chunks_per_wave, sink);
+  return (int32_t)hipGetLastError();
+}
+
 extern "C" int32_t tq_probe_read(const void* src, size_t n_bytes, uint32_t* sink,
                                  int32_t num_workgroups, void* stream) {
   if (!src || !sink || (n_bytes & 15) || ((uintptr_t)src & 15) || num_workgroups < 1 ||

@@ -9,7 +9,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libtqprobe.so")
-EXPORTED_SYMBOLS = ("tq_probe_read", "tq_probe_copy", "tq_probe_pattern")
+EXPORTED_SYMBOLS = ("tq_probe_read", "tq_probe_copy", "tq_probe_pattern", "tq_probe_pattern4")
 _lib = None
 
 
@@ -29,6 +29,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                          ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
                                          ctypes.c_void_p]
         lib.tq_probe_pattern.restype = ctypes.c_int32
+        lib.tq_probe_pattern4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_size_t, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_void_p, ctypes.c_void_p]
+        lib.tq_probe_pattern4.restype = ctypes.c_int32
         _lib = lib
     return _lib
 
@@ -62,3 +66,16 @@ def pattern(k: torch.Tensor, v: torch.Tensor, scales: torch.Tensor, chunks_per_w
                                          int(num_workgroups), sink.data_ptr(), s)
     if rc:
         raise RuntimeError(f"tq_probe_pattern failed: hipError {rc}")
+
+
+def pattern4(rows: torch.Tensor, meta: torch.Tensor, chunks_per_wave: int, num_workgroups: int,
+             sink: torch.Tensor, stream=None) -> None:
+    """The 4-bit format's byte pattern with no arithmetic (tq_probe_pattern4)."""
+    assert rows.is_cuda and meta.is_cuda and sink.is_cuda and sink.numel() >= num_workgroups
+    s = (stream or torch.cuda.current_stream()).cuda_stream
+    rc = load_library().tq_probe_pattern4(rows.data_ptr(), meta.data_ptr(),
+                                          rows.numel() * rows.element_size(),
+                                          meta.numel() * meta.element_size(), int(chunks_per_wave),
+                                          int(num_workgroups), sink.data_ptr(), s)
+    if rc:
+        raise RuntimeError(f"tq_probe_pattern4 failed: hipError {rc}")

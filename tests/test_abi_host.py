@@ -45,6 +45,8 @@ def test_probe_library_exports_its_header():
     # argument errors are reported without touching the device
     assert plib.tq_probe_read(0, 16, 0x10000, 1, None) != 0
     assert plib.tq_probe_copy(0x10000, 0x10000, 17, 1, None) != 0
+    assert plib.tq_probe_pattern4(0, 0x10000, 4096, 256, 1, 1, 0x10000, None) != 0
+    assert plib.tq_probe_pattern4(0x10000, 0x10000, 4095, 256, 1, 1, 0x10000, None) != 0
 
 
 def test_every_header_is_covered():

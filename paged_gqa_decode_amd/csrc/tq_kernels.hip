@@ -1574,16 +1574,25 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(ReduceArgs a) {
   }
 }
 
-// KV-cache writer: one wave per (new token t, kv head h).  Lane l holds
-// dims 2l, 2l+1 of the K row and of the V row; each row is quantized on its
-// own: s = absmax / 448, codes = e4m3fn(x / s) (IEEE fp32 division, round to
-// nearest even, clamped to +-448 so the convert never overflows), all-zero
-// rows get s = 0 and codes 0.  The 128 codes of a row go out as one 128-byte
-// store across the wave; lanes 0 and 1 write the K and V scales.  A slot
-// outside [0, NB*BS) is skipped (negative: padding by convention).
+// KV-cache writer: 8 lanes per (new token t, kv head h) row, 8 rows per wave
+// (32 per 256-thread workgroup); lane j of a row holds dims 16j .. 16j+15 of
+// its K row and of its V row, loaded as two 16-byte pieces each, so a wave
+// reads 2 KiB of each contiguous input.  Each row is quantized on its own: s
+// = absmax / 448 (absmax over the row's 8 lanes), codes = e4m3fn(x / s) (IEEE
+// fp32 division, round to nearest even, clamped to +-448 so the convert never
+// overflows), all-zero rows get s = 0 and codes 0.  A row's 128 codes go out as
+// one 16-byte store per lane, a whole 128-byte line; lanes 0 and 1 of the row
+// write the K and V scales.  A slot outside [0, NB*BS) is skipped (negative:
+// padding by convention).
+constexpr int kKvRowsPerWg = 32;
+
 __global__ __launch_bounds__(256) void tq_kv_write_kernel(KvWriteArgs a) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (t, h)
+  const int j = lane & 7;
+  const int64_t row = (int64_t)blockIdx.x * kKvRowsPerWg + (threadIdx.x >> 3);  // (t, h)
+  // A row's 8 lanes are alike in every branch below, and every cross-lane
+  // step stays within them.
   if (row >= (int64_t)a.num_tokens * a.num_kv_heads) return;
   const int Hkv = a.num_kv_heads;
   const int t = (int)(row / Hkv);
@@ -1593,26 +1602,45 @@ __global__ __launch_bounds__(256) void tq_kv_write_kernel(KvWriteArgs a) {
   const int BS = a.kv_block_size;
   const int blk = slot / BS;
   const int off = slot % BS;
-  const size_t src = (size_t)row * D + 2 * lane;
-  const size_t dst = (((size_t)blk * Hkv + h) * BS + off) * D + 2 * lane;
+  const size_t src = (size_t)row * D + 16 * j;                           // bf16 elements
+  const size_t dst = (((size_t)blk * Hkv + h) * BS + off) * D + 16 * j;  // bytes
+  u32x4 in[2][2];
 #pragma unroll
   for (int field = 0; field < 2; ++field) {
-    const uint32_t pair = *reinterpret_cast<const uint32_t*>((field == 0 ? a.k_new : a.v_new) + src);
-    const float x0 = __uint_as_float(pair << 16);
-    const float x1 = __uint_as_float(pair & 0xffff0000u);
-    float amax = fmaxf(fabsf(x0), fabsf(x1));
+    const u32x4* p = reinterpret_cast<const u32x4*>((field == 0 ? a.k_new : a.v_new) + src);
+    in[field][0] = p[0];
+    in[field][1] = p[1];
+  }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    const float scale = amax / 448.0f;
-    uint32_t codes = 0;
-    if (scale > 0.f) {
-      const float q0 = fminf(fmaxf(x0 / scale, -448.0f), 448.0f);
-      const float q1 = fminf(fmaxf(x1 / scale, -448.0f), 448.0f);
-      codes = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false) & 0xffffu;
+  for (int field = 0; field < 2; ++field) {
+    float x[16];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const uint32_t pair = in[field][w >> 2][w & 3];
+      x[2 * w] = __uint_as_float(pair << 16);
+      x[2 * w + 1] = __uint_as_float(pair & 0xffff0000u);
     }
-    *reinterpret_cast<uint16_t*>((field == 0 ? a.k : a.v) + dst) = (uint16_t)codes;
-    if (lane == 0)
-      a.scales[(((size_t)blk * Hkv + h) * 2 + field) * BS + off] = scale;
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+    for (int o = 4; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+    const float scale = amax / 448.0f;
+    u32x4 codes = {0u, 0u, 0u, 0u};
+    if (scale > 0.f) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float q0 = fminf(fmaxf(x[4 * w] / scale, -448.0f), 448.0f);
+        const float q1 = fminf(fmaxf(x[4 * w + 1] / scale, -448.0f), 448.0f);
+        const float q2 = fminf(fmaxf(x[4 * w + 2] / scale, -448.0f), 448.0f);
+        const float q3 = fminf(fmaxf(x[4 * w + 3] / scale, -448.0f), 448.0f);
+        int c = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+        c = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, c, true);
+        codes[w] = (uint32_t)c;
+      }
+    }
+    *reinterpret_cast<u32x4*>((field == 0 ? a.k : a.v) + dst) = codes;
+    if (j == field) a.scales[(((size_t)blk * Hkv + h) * 2 + field) * BS + off] = scale;
   }
 }
 
@@ -1786,7 +1814,8 @@ hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_g
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   const int64_t rows = (int64_t)a.num_tokens * a.num_kv_heads;
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(tq_kv_write_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(tq_kv_write_kernel, dim3((unsigned)((rows + kKvRowsPerWg - 1) / kKvRowsPerWg)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -44,6 +44,12 @@
  *     a block-table entry to [0, num_blocks-1].  A caller that breaks the
  *     contract (a length above ext->max_seq_len, a block id outside the
  *     pool) gets wrong numbers, never an out-of-bounds access.
+ *   - Debugging such a caller: with TQ_VALIDATE=1 in the environment (read on
+ *     every call), each decode entry point first enqueues a check kernel that
+ *     prints, by device printf, every sequence whose length is outside [0,
+ *     ext->max_seq_len] and the first block-table entry of each sequence that
+ *     is outside [0, num_blocks) for a token below its length.  The decode
+ *     then runs as always (clamped).  Off by default; for debugging only.
  */
 #ifndef TQ_DECODE_H
 #define TQ_DECODE_H

@@ -3,6 +3,7 @@
 // device before every check has passed.
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <hip/hip_runtime_api.h>
 
@@ -106,6 +107,25 @@ tq_status hip_status(hipError_t e) {
 }
 
 // The partition kernel of either format, after the checks.
+// TQ_VALIDATE=1 in the environment (read on every call): before a decode,
+// enqueue the check kernel that prints lengths outside [0, max_seq_len] and
+// block-table entries outside [0, num_blocks) (device printf, debug only; the
+// decode itself clamps both and proceeds).
+hipError_t maybe_validate(const tq::StreamArgs& st, const int32_t* seq_lens, int32_t kv_block_size,
+                          const tq_extent* ext, void* stream) {
+  const char* v = getenv("TQ_VALIDATE");
+  if (!v || v[0] != '1') return hipSuccess;
+  tq::ValidateArgs a;
+  a.bt = st.bt;
+  a.seq_lens = seq_lens;
+  a.num_seqs = ext->num_seqs;
+  a.max_blocks = ext->max_blocks_per_seq;
+  a.num_blocks = ext->num_blocks;
+  a.kv_block_size = kv_block_size;
+  a.max_seq_len = ext->max_seq_len;
+  return tq::launch_validate(a, static_cast<hipStream_t>(stream));
+}
+
 tq_status run_partition(const tq::StreamArgs& st, const int32_t* seq_lens,
                         const tq_partials* partials, int32_t query_group_size,
                         int32_t kv_block_size, int32_t E, const tq_extent* ext, bool tq4,
@@ -122,6 +142,8 @@ tq_status run_partition(const tq::StreamArgs& st, const int32_t* seq_lens,
   a.partition_tokens = E;
   a.parts_per_wave = 1;  // chosen by the launcher
   a.len_cap = ext->max_seq_len;
+  const hipError_t v = maybe_validate(st, seq_lens, kv_block_size, ext, stream);
+  if (v != hipSuccess) return hip_status(v);
   return hip_status(tq::launch_partition(a, ext->num_seqs, query_group_size, kv_block_size, tq4,
                                          static_cast<hipStream_t>(stream)));
 }
@@ -133,6 +155,8 @@ tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out
                     const tq_extent* ext, void* workspace, size_t workspace_bytes, bool tq4,
                     void* stream) {
   if (!aligned16(out) || (workspace && !aligned16(workspace))) return TQ_ERR_MISALIGNED;
+  const hipError_t v = maybe_validate(st, seq_lens, kv_block_size, ext, stream);
+  if (v != hipSuccess) return hip_status(v);
   const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
   const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
   if (flat_groups > 0 && workspace &&

@@ -115,6 +115,19 @@ struct KvWriteArgs {
   int32_t num_slots;            // NB * BS: slots at or past it are skipped
 };
 
+// The debug check run before a decode when TQ_VALIDATE=1: one wave per
+// sequence reports, by device printf, a length outside [0, max_seq_len] and
+// the first block-table entry for t < L outside [0, num_blocks).
+struct ValidateArgs {
+  const int32_t* bt;        // int32 [S][max_blocks]
+  const int32_t* seq_lens;  // int32 [S]
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t kv_block_size;
+  int32_t max_seq_len;
+};
+
 // Enqueue the kernels; each returns the launch status (hipGetLastError after
 // the launch).  launch_partition chooses parts_per_wave and launch_fused the
 // waves per workgroup from the sizes.
@@ -127,5 +140,6 @@ hipError_t launch_flat(const FlatArgs& a, int query_group_size, int kv_block_siz
                        hipStream_t stream);
 hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t stream);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream);
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream);
 
 }  // namespace tq

@@ -1644,6 +1644,32 @@ __global__ __launch_bounds__(256) void tq_kv_write_kernel(KvWriteArgs a) {
   }
 }
 
+// The TQ_VALIDATE debug check (see ValidateArgs).  Reads only: lengths are
+// clamped into [0, max_seq_len] before they size the block walk, so every
+// block-table read stays inside the caller's [S][max_blocks] table.
+__global__ __launch_bounds__(64) void tq_validate_kernel(ValidateArgs a) {
+  const int s = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int L = a.seq_lens[s];
+  if (lane == 0 && (L < 0 || L > a.max_seq_len))
+    printf("tq_validate: seq_lens[%d] = %d is outside [0, %d]\n", s, L, a.max_seq_len);
+  const int Lc = L < 0 ? 0 : (L > a.max_seq_len ? a.max_seq_len : L);
+  const int n = (Lc + a.kv_block_size - 1) / a.kv_block_size;
+  const int32_t* row = a.bt + (size_t)s * a.max_blocks;
+  for (int j0 = 0; j0 < n; j0 += 64) {
+    const int j = j0 + lane;
+    const int id = j < n ? row[j] : 0;
+    const uint64_t bad = __ballot(j < n && (id < 0 || id >= a.num_blocks));
+    if (bad) {
+      const int first = __builtin_ctzll(bad);
+      if (lane == first)
+        printf("tq_validate: block_tables[%d][%d] = %d is outside [0, %d) (token %d < seq_lens %d)\n",
+               s, j, id, a.num_blocks, j * a.kv_block_size, Lc);
+      break;  // one report per sequence; uniform over the wave
+    }
+  }
+}
+
 }  // namespace
 
 int choose_parts_per_wave(int64_t units, int num_partitions) {
@@ -1816,6 +1842,11 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(tq_kv_write_kernel, dim3((unsigned)((rows + kKvRowsPerWg - 1) / kKvRowsPerWg)),
                      dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate(const ValidateArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(tq_validate_kernel, dim3((unsigned)a.num_seqs), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -10,7 +10,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libtqdecode.so")
-SOURCES = [os.path.join(CSRC, "tq_kernels.hip"), os.path.join(CSRC, "tq_api.cpp")]
+SOURCES = [os.path.join(CSRC, "tq_kernels.hip"), os.path.join(CSRC, "tq_api.cpp"),
+           os.path.join(CSRC, "tq_plan.cpp")]
 PROBE_LIB = os.path.join(PKG, "libtqprobe.so")
 PROBE_SOURCES = [os.path.join(CSRC, "tq_probe.hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -11,6 +11,12 @@ namespace tq {
 constexpr int kHeadDim = 128;
 constexpr int kTokensPerTileGroup = 256;
 
+// The flat fused kernel: waves per workgroup, and the sequences its length
+// scan handles (64 lanes x kFlatSlices).
+constexpr int kFlatWaves = 8;
+constexpr int kFlatSlices = 4;
+constexpr int kFlatMaxSeqs = 64 * kFlatSlices;
+
 // What every decode kernel reads to stream one (sequence, kv head).  The fp8
 // format uses k, v and scales; the 4-bit record format tq4 and centroids.
 struct StreamArgs {
@@ -127,6 +133,9 @@ struct ValidateArgs {
   int32_t kv_block_size;
   int32_t max_seq_len;
 };
+
+// Partitions of one (s, h) that one wave of the partition kernel walks.
+int choose_parts_per_wave(int64_t units, int num_partitions);
 
 // Enqueue the kernels; each returns the launch status (hipGetLastError after
 // the launch).  launch_partition chooses parts_per_wave and launch_fused the

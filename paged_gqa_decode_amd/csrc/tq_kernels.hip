@@ -1136,9 +1136,6 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
 // follow from the device-side lengths and the grid alone.  Zero-length
 // sequences are not in the list: workgroup g zeroes the rows of sequences g,
 // g+G, ... that have none.
-constexpr int kFlatSlices = 4;                 // sequences per lane in the length scan
-constexpr int kFlatMaxSeqs = 64 * kFlatSlices;
-constexpr int kFlatWaves = 8;       // waves per workgroup
 
 // Inclusive prefix sum over the 64 lanes of a wave by DPP: shifts by 1, 2, 4, 8
 // within each 16-lane row, then row 0's and row 2's last lane added to rows 1
@@ -1671,90 +1668,6 @@ __global__ __launch_bounds__(64) void tq_validate_kernel(ValidateArgs a) {
 }
 
 }  // namespace
-
-int choose_parts_per_wave(int64_t units, int num_partitions) {
-  // Keep enough waves for many rounds over every SIMD; past that, longer
-  // per-wave streams amortize each wave's start-up (length, block-table and
-  // first-chunk loads, one after the other).
-  constexpr int64_t kMinWaves = 32768;
-  int64_t ppw = units / kMinWaves;
-  if (ppw < 1) ppw = 1;
-  if (ppw > num_partitions) ppw = num_partitions;
-  return (int)ppw;
-}
-
-constexpr int kMaxSplits = 16;
-
-size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size) {
-  if (splits <= 1) return 0;
-  const size_t rows = (size_t)seq_heads * splits * query_group_size;
-  return round256((size_t)seq_heads * 4) + round256(rows * D * 4) + 2 * round256(rows * 4);
-}
-
-void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size) {
-  const size_t rows = (size_t)seq_heads * a->splits * query_group_size;
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  a->counters = reinterpret_cast<int32_t*>(p);
-  p += round256((size_t)seq_heads * 4);
-  a->ws_o = reinterpret_cast<float*>(p);
-  p += round256(rows * D * 4);
-  a->ws_m = reinterpret_cast<float*>(p);
-  p += round256(rows * 4);
-  a->ws_l = reinterpret_cast<float*>(p);
-}
-
-FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes) {
-  // About kTargetWaves waves on the device (one resident round at two waves
-  // per SIMD; measured best across the workloads), each with at least one tile
-  // group of work; at most 8 waves per workgroup (the register budget of
-  // __launch_bounds__(512)), then more workgroups per (s, h) if the workspace
-  // can hold their partials.
-  constexpr int64_t kTargetWaves = 2048;
-  const int64_t n_tg = max_seq_len > 0 ? (max_seq_len + kTokensPerTileGroup - 1) / kTokensPerTileGroup : 1;
-  int64_t waves_per_sh = (kTargetWaves + seq_heads - 1) / seq_heads;
-  if (waves_per_sh > n_tg) waves_per_sh = n_tg;
-  if (waves_per_sh < 1) waves_per_sh = 1;
-  FusedPlan plan;
-  plan.waves = (int)(waves_per_sh < 8 ? waves_per_sh : 8);
-  int64_t splits = (waves_per_sh + plan.waves - 1) / plan.waves;
-  if (splits > kMaxSplits) splits = kMaxSplits;
-  while (splits > 1 && fused_workspace_bytes(seq_heads, (int)splits, query_group_size) > ws_bytes) --splits;
-  plan.splits = (int)splits;
-  return plan;
-}
-
-int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len) {
-  // One resident round at two waves per SIMD (256 workgroups of 8 waves, one
-  // per CU), or fewer when the list cannot fill them: at most one wave per tile
-  // group.
-  constexpr int64_t kFlatGroups = 256;
-  static_assert(kFlatGroups * kFlatWaves <= 65536, "waves per launch");
-  if (num_seqs < 1 || num_seqs > kFlatMaxSeqs || num_kv_heads < 1 || max_seq_len <= 0) return 0;
-  const int64_t n_tg = (max_seq_len + kTokensPerTileGroup - 1) / kTokensPerTileGroup;
-  const int64_t t_max = num_seqs * num_kv_heads * n_tg;
-  if (t_max > (int64_t(1) << 30)) return 0;
-  const int64_t groups = (t_max + kFlatWaves - 1) / kFlatWaves;
-  return (int)(groups < kFlatGroups ? groups : kFlatGroups);
-}
-
-size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size) {
-  const size_t rows = (size_t)2 * n_groups * query_group_size;
-  return round256((size_t)seq_heads * 4) + round256(rows * D * 4) + 2 * round256(rows * 4);
-}
-
-void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size) {
-  const size_t rows = (size_t)2 * a->n_groups * query_group_size;
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  a->counters = reinterpret_cast<int32_t*>(p);
-  p += round256((size_t)seq_heads * 4);
-  a->ws_o = reinterpret_cast<float*>(p);
-  p += round256(rows * D * 4);
-  a->ws_m = reinterpret_cast<float*>(p);
-  p += round256(rows * 4);
-  a->ws_l = reinterpret_cast<float*>(p);
-}
 
 // Run LAUNCH_T<QG, BS, TQ4>(args...) for the runtime sizes and format.
 #define TQ_DISPATCH(LAUNCH_T, qg, bs, tq4, ...)                                              \

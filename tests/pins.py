@@ -259,6 +259,42 @@ def pin_split_merge(orc):
         assert_close(out, ref, 1e-13, f"split merge P={P} E={E}")
 
 
+def pin_partials_closed_form(orc):
+    """Each partial of the split-K triple against its definition, computed independently per
+    partition with torch float64 on gathered rows: m_p = max over the partition's tokens of the
+    scaled logit x = scale * q.k (natural-log units, as the page's STEP G defines them), l_p =
+    sum exp(x - m_p), o_p = sum exp(x - m_p) v / l_p; dead partitions stay NaN.  With one token
+    per partition this is m_p = x_t, l_p = 1, o_p = v_t."""
+    p = tiny_problem(seed=12, lens=(1, 9, 14), S=3, BS=4, max_blocks=6)
+    S, Hq, D = p["q"].shape
+    Hkv = p["k"].shape[1]
+    QG = Hq // Hkv
+    for P, E in ((14, 1), (5, 3), (2, 7)):
+        o, m, l = orc.partials(p["q"], p["k"], p["v"], p["sc"], p["bt"], p["sl"], p["scale"], P, E)
+        for s in range(S):
+            L = int(p["sl"][s])
+            for h in range(Hkv):
+                K = dense_rows(p, s, h, 0)
+                V = dense_rows(p, s, h, 1)
+                Q = p["q"][s, h * QG:(h + 1) * QG].to(torch.float64)
+                x = (Q @ K.T) * p["scale"]  # [QG][L]
+                for pp in range(P):
+                    t0, t1 = pp * E, min((pp + 1) * E, L)
+                    if t0 >= L:
+                        assert np.all(np.isnan(m[s, h, pp])), "dead partition written"
+                        continue
+                    xp = x[:, t0:t1]
+                    mp = xp.max(dim=1).values
+                    w = torch.exp(xp - mp[:, None])
+                    lp = w.sum(dim=1)
+                    op = (w @ V[t0:t1]) / lp[:, None]
+                    assert_close(m[s, h, pp], mp.numpy(), 1e-13, f"m_p P={P} E={E}")
+                    assert_close(l[s, h, pp], lp.numpy(), 1e-13, f"l_p P={P} E={E}")
+                    assert_close(o[s, h, pp], op.numpy(), 1e-13, f"o_p P={P} E={E}")
+                    if t1 - t0 == 1:
+                        assert np.all(l[s, h, pp] == 1.0), "one token: l_p = exp(0) = 1 exactly"
+
+
 def pin_v_scale_linearity(orc):
     """Doubling every V scale doubles the output exactly (power-of-two scaling)."""
     p = tiny_problem(seed=11, lens=(6, 19, 2))
@@ -528,5 +564,5 @@ ALL_PINS = [pin_e4m3fn_points, pin_e4m3fn_library, pin_bf16_library, pin_dense_b
             pin_single_token, pin_zero_query, pin_constant_v, pin_two_token_golden,
             pin_block_permutation, pin_split_merge, pin_v_scale_linearity, pin_dominant_token,
             pin_zero_length, pin_e4m3fn_encode_roundtrip, pin_e4m3fn_encode_ties_and_saturation,
-            pin_e4m3fn_encode_library, pin_kv_write_quantizer, pin_kv_write_matches_library_quantizer,
+            pin_e4m3fn_encode_library, pin_kv_write_quantizer, pin_partials_closed_form, pin_kv_write_matches_library_quantizer,
             pin_f16_library, pin_tq4_golden_record, pin_tq4_matches_fp8_form, pin_tq4_constant_v]

@@ -56,6 +56,17 @@ MUTANTS = [
     ("tq4_centroid_off_by_one", "pb->centroids[idx]", "pb->centroids[(idx + 1) & 15]"),
     ("tq4_meta_head_stride", "(int64_t)h * 3 * pb->BS * 2;", "(int64_t)h * 2 * pb->BS * 2;"),
     ("tq4_rows_slot_major", "((int64_t)h * pb->BS + slot) * pb->D", "((int64_t)slot * pb->Hkv + h) * pb->D"),
+    # the partial triple's m_p in log2 units with a merge that matches: the merged result is
+    # unchanged, only the partials' definition catches it
+    ("partials_and_merge_log2_units",
+     ("rc = orc_attend(&pb, s, h, g, t0, t1, xbuf, o + r * D, &m[r], &l[r]);",
+      "double w = l[r] * exp(m[r] - M);"),
+     ("rc = orc_attend(&pb, s, h, g, t0, t1, xbuf, o + r * D, &m[r], &l[r]); m[r] *= 1.4426950408889634;",
+      "double w = l[r] * exp2(m[r] - M);")),
+    # unnormalised partial outputs with a merge that does not weight by l_p
+    ("partials_unnormalised_merge_without_l",
+     ("for (int d = 0; d < pb->D; ++d) o[d] /= l;", "double w = l[r] * exp(m[r] - M);"),
+     ("", "double w = exp(m[r] - M);")),
     ("tq4_block_stride", "(int64_t)pb->Hkv * 3 * pb->BS * 2;\n}", "(int64_t)pb->Hkv * 2 * pb->BS * 2;\n}"),
 ]
 
@@ -63,8 +74,12 @@ MUTANTS = [
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(tmp_path, name, old, new):
     src = oracle.source_text()
-    assert src.count(old) >= 1, f"mutation site for {name} not found in oracle.c"
-    mutated = src.replace(old, new, 1)
+    # a mutant is one replacement, or several applied together (tuples of sites)
+    olds, news = (old, new) if isinstance(old, tuple) else ((old,), (new,))
+    mutated = src
+    for o_, n_ in zip(olds, news):
+        assert mutated.count(o_) >= 1, f"mutation site for {name} not found in oracle.c"
+        mutated = mutated.replace(o_, n_, 1)
     orc = oracle.build_variant(mutated, os.path.join(str(tmp_path), f"mut_{name}.so"))
     failed = []
     for pin in pins.ALL_PINS:

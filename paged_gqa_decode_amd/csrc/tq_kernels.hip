@@ -514,7 +514,10 @@ struct StageTag {
   static constexpr int value = V;
 };
 
-// The 4-bit counterpart of stream_tokens: same contract, same chunk pipeline.
+// The 4-bit counterpart of stream_tokens: the same contract and the same
+// one-chunk-ahead pipeline.  lds is the wave's staging area (kTq4WaveLds
+// bytes); tab the workgroup's centroid table, which build_tq4_table has
+// written before any wave streams.
 template <int QG, int BS, typename OnBoundary>
 __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, int h, int t_begin,
                                                   int t_end, int chunks_per_part, uint8_t* lds,

@@ -340,6 +340,38 @@ def main() -> int:
         log(f"[bench] {wl.name} {name}: step {pth['ms_per_step'] * 1e3:.1f} us "
             f"({kv_bytes / (pth['ms_per_step'] * 1e-3) / 1e9:.0f} GB/s); first kernel "
             f"{pth['k1_avg'] * 1e3:.1f} us, second kernel {pth['k2_avg'] * 1e3:.1f} us")
+    # Single steps, each timed alone by two events on the launch stream (the event pair adds a
+    # few microseconds to each interval): "cold" with a 1 GiB read before each step (clean
+    # evictions of the L2s and the 256 MB last-level cache, nothing left to write back), and
+    # "warm" the same way without it.  Reported next to the back-to-back figures; for the
+    # 2.2 GB bandwidth workload the two agree.
+    from paged_gqa_decode_amd import probe as _probe
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    flush_sink = torch.empty(4096, dtype=torch.int32, device=dev)
+
+    def single(*kernels, evict, reps=20):
+        times = []
+        for i in range(reps + 2):
+            if evict:
+                _probe.read(flush, flush_sink, 4096, stream=stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for k in kernels:
+                k()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                times.append(e0.elapsed_time(e1))
+        times.sort()
+        return round(times[len(times) // 2] * 1e3, 2)
+
+    single_us = {"cold": {"two_kernel": single(dec, red, evict=True), "fused": single(fused, evict=True)},
+                 "warm": {"two_kernel": single(dec, red, evict=False), "fused": single(fused, evict=False)}}
+    del flush, flush_sink
+    torch.cuda.empty_cache()
+    log(f"[bench] {wl.name} single steps (median of 20): cold (1 GiB read before each) "
+        f"two-kernel {single_us['cold']['two_kernel']} us, fused {single_us['cold']['fused']} us; "
+        f"warm two-kernel {single_us['warm']['two_kernel']} us, fused {single_us['warm']['fused']} us")
     head = min(paths, key=lambda n: paths[n]["ms_per_step"])
     ms_per_step = paths[head]["ms_per_step"]
     k1_avg = paths[head]["k1_avg"]
@@ -375,6 +407,7 @@ def main() -> int:
             "fused": {"step": round(paths["fused"]["ms_per_step"] * 1e3, 2),
                       "tq_decode_fused": round(paths["fused"]["k1_avg"] * 1e3, 2)},
         },
+        "single_step_us": single_us,
         "roofline": {"bound": "hbm", "achieved": round(k1_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(k1_gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(wl.name, head), "kernel": KERNEL_NAMES[head],

@@ -363,15 +363,17 @@ def main() -> int:
             if i >= 2:
                 times.append(e0.elapsed_time(e1))
         times.sort()
-        return round(times[len(times) // 2] * 1e3, 2)
+        n = len(times)
+        return {"median": round(times[n // 2] * 1e3, 2), "p10": round(times[n // 10] * 1e3, 2),
+                "p90": round(times[(9 * n) // 10] * 1e3, 2)}
 
     single_us = {"cold": {"two_kernel": single(dec, red, evict=True), "fused": single(fused, evict=True)},
                  "warm": {"two_kernel": single(dec, red, evict=False), "fused": single(fused, evict=False)}}
     del flush, flush_sink
     torch.cuda.empty_cache()
     log(f"[bench] {wl.name} single steps (median of 20): cold (1 GiB read before each) "
-        f"two-kernel {single_us['cold']['two_kernel']} us, fused {single_us['cold']['fused']} us; "
-        f"warm two-kernel {single_us['warm']['two_kernel']} us, fused {single_us['warm']['fused']} us")
+        f"two-kernel {single_us['cold']['two_kernel']['median']} us, fused {single_us['cold']['fused']['median']} us; "
+        f"warm two-kernel {single_us['warm']['two_kernel']['median']} us, fused {single_us['warm']['fused']['median']} us")
     head = min(paths, key=lambda n: paths[n]["ms_per_step"])
     ms_per_step = paths[head]["ms_per_step"]
     k1_avg = paths[head]["k1_avg"]

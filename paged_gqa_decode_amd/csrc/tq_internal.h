@@ -44,6 +44,7 @@ struct PartitionArgs {
   int32_t partition_tokens;  // E = 256 * G
   int32_t parts_per_wave;    // consecutive partitions of one (s, h) walked by one wave
   int32_t len_cap;           // device lengths are clamped to [0, len_cap]
+  int32_t num_seqs;          // S
 };
 
 struct FusedArgs {
@@ -91,7 +92,14 @@ struct FlatArgs {
 
 // Workgroups of the flat plan for these sizes (0: the flat kernel does not
 // apply), the workspace bytes it needs, and the carving of that workspace.
-int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len);
+// unit_tokens: the tokens of one list entry (a tile group for the fused path,
+// a partition for the two-kernel path).
+int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
+                     int unit_tokens = kTokensPerTileGroup);
+// Workgroups of the flat partition kernel (tq_partition_flat_kernel) for
+// these sizes, or 0 when the per-partition kernel runs instead.
+int plan_partition_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
+                               int partition_tokens, bool tq4);
 size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size);
 void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size);
 

@@ -882,6 +882,28 @@ constexpr int kWaveLds = 2 * CHUNK * D + 2 * 2 * CHUNK * 4;
 static_assert(kTq4WaveLds <= kWaveLds, "4-bit staging area");
 static_assert(16 * D * 4 + 2 * 16 * 4 <= kWaveLds, "merge area must fit the staging area");
 
+// Partial triple of partition p of (s, h) = sh: o_p = acc * sigma / l_p, m_p
+// (natural log units), l_p, rows r < QG; then the running state restarts.
+template <int QG, bool TQ4>
+__device__ __forceinline__ void store_partial(const PartitionArgs& a, int sh, int p, WaveState& w) {
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, b = lane >> 4;
+  f32x4 o[8];
+  const float l = w.template finish_as<TQ4, QG>(o);
+  if (r < QG) {
+    const size_t row = ((size_t)sh * a.num_partitions + p) * QG + r;
+    float* dst = a.o + row * D;
+#pragma unroll
+    for (int dblk = 0; dblk < 8; ++dblk)
+      *reinterpret_cast<f32x4*>(dst + out_col<TQ4>(dblk, b)) = o[dblk];
+    if (b == 0) {
+      a.ml[row] = w.m2 * kLn2;
+      a.es[row] = l;
+    }
+  }
+  w.reset();
+}
+
 // Split-K partition kernel: one wave per group of `parts_per_wave`
 // consecutive partitions of one (s, h); writes the partial triple of every
 // live partition in the group (STEP G).
@@ -890,8 +912,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq
   __shared__ __attribute__((aligned(16))) uint8_t lds_stage[kWaveLds];
   __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
   const int lane = threadIdx.x;
-  const int r = lane & 15;
-  const int b = lane >> 4;
   const int P = a.num_partitions;
   const int Hkv = a.st.num_kv_heads;
   const int E = a.partition_tokens;
@@ -908,33 +928,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq
   const int t_end = min(t_begin + min(ppw, P - p0) * E, L);
   if constexpr (TQ4) build_tq4_table(lds_tab, a.st.centroids, lane, 64);
 
-  // Partial triple of partition p: o_p = acc * sigma / l_p, m_p (natural
-  // log units), l_p; then the running state restarts.
-  auto store_partial = [&](int p, WaveState& w) {
-    f32x4 o[8];
-    const float l = w.template finish_as<TQ4, QG>(o);
-    if (r < QG) {
-      const size_t row = ((size_t)(s * Hkv + h) * P + p) * QG + r;
-      float* dst = a.o + row * D;
-#pragma unroll
-      for (int dblk = 0; dblk < 8; ++dblk)
-        *reinterpret_cast<f32x4*>(dst + out_col<TQ4>(dblk, b)) = o[dblk];
-      if (b == 0) {
-        a.ml[row] = w.m2 * kLn2;
-        a.es[row] = l;
-      }
-    }
-    w.reset();
-  };
-
   WaveState w;
   w.reset();
   const int chunks_per_part = E / CHUNK;
   stream_any<QG, BS, TQ4>(a.st, s, h, t_begin, t_end, chunks_per_part, lds_stage,
                           reinterpret_cast<float*>(lds_stage + 2 * CHUNK * D), lds_tab, w,
-                          [&](int k, WaveState& ws) { store_partial(p0 + k, ws); });
+                          [&](int k, WaveState& ws) { store_partial<QG, TQ4>(a, sh, p0 + k, ws); });
   const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
-  store_partial(p0 + (n_chunks - 1) / chunks_per_part, w);
+  store_partial<QG, TQ4>(a, sh, p0 + (n_chunks - 1) / chunks_per_part, w);
 }
 
 
@@ -1498,6 +1499,113 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   }
 }
 
+// Split-K partition kernel over one flat work list: the live partitions of
+// every (s, h) in (s, h, p) order, dealt evenly to the waves of n_groups
+// workgroups of kFlatWaves waves (one resident round), as tq_flat_kernel deals
+// tile groups.  A wave's run is cut at (s, h) boundaries; each piece is one
+// stream whose partials are written at every partition end (STEP G), so the
+// partials are bit for bit those of tq_partition_kernel.  No merge and no
+// barrier after the set-up: a wave with nothing to do returns.  Used for the
+// 4-bit format, whose per-partition waves would each build the centroid
+// table and fill the pipeline for only 8 chunks.
+template <int QG, int BS, bool TQ4>
+__global__ __launch_bounds__(64 * kFlatWaves) void tq_partition_flat_kernel(PartitionArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
+  __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int W = blockDim.x >> 6;
+  const int S = a.num_seqs;
+  const int Hkv = a.st.num_kv_heads;
+  const int E = a.partition_tokens;
+  auto len_of = [&](int s) { return clamp_len(a.seq_lens[s], a.len_cap); };
+  if constexpr (TQ4) {  // before any return: every thread reaches the barrier
+    build_tq4_table(lds_tab, a.st.centroids, threadIdx.x, blockDim.x);
+    __syncthreads();
+  }
+
+  // Live partitions per kv head: lane l holds the clamped lengths of sequences
+  // s = l + 64 i (i < k <= kFlatSlices); per slice an inclusive scan over the
+  // lanes gives the list offsets within the slice.
+  const int k = (S + 63) >> 6;
+  int len_r[kFlatSlices], incl_r[kFlatSlices], slice_total[kFlatSlices];
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < kFlatSlices; ++i) len_r[i] = a.seq_lens[min(lane + 64 * i, S - 1)];
+#pragma unroll
+  for (int i = 0; i < kFlatSlices; ++i) {
+    len_r[i] = (i < k && lane + 64 * i < S) ? clamp_len(len_r[i], a.len_cap) : 0;
+    incl_r[i] = 0;
+    slice_total[i] = 0;
+    if (i < k) {
+      incl_r[i] = wave_inclusive_scan((len_r[i] + E - 1) / E);
+      slice_total[i] = __builtin_amdgcn_readlane(incl_r[i], 63);
+      total += slice_total[i];
+    }
+  }
+  const int T = total * Hkv;
+
+  // Nu = min(waves, T) waves in use; wave x takes q or q + 1 entries, the first
+  // `rem` waves one more.
+  const int Nw = gridDim.x * W;
+  const int Nu = T < Nw ? T : Nw;
+  const int gw = blockIdx.x * W + wave;
+  if (gw >= Nu) return;
+  const int q = T / Nu, rem = T - q * Nu;
+  const int A = gw * q + (gw < rem ? gw : rem);
+  const int B = A + q + (gw < rem ? 1 : 0);
+  // Locate entry A: its slice, then the first lane of the slice whose
+  // sequences reach past it.  base = list offset of (s, h = 0).
+  int s = S - 1, L = 0, n = 0, base = 0;
+  {
+    int sb = 0;
+#pragma unroll
+    for (int i = 0; i < kFlatSlices; ++i) {
+      if (i < k && A >= sb * Hkv && A < (sb + slice_total[i]) * Hkv) {
+        const int ln = __builtin_ctzll(__ballot((sb + incl_r[i]) * Hkv > A));
+        L = __builtin_amdgcn_readlane(len_r[i], ln);
+        n = (L + E - 1) / E;
+        s = 64 * i + ln;
+        base = (sb + __builtin_amdgcn_readlane(incl_r[i], ln) - n) * Hkv;
+      }
+      sb += slice_total[i];
+    }
+  }
+
+  uint8_t* area = lds_dyn + wave * kWaveLds;
+  const int chunks_per_part = E / CHUNK;
+  int h = n > 0 ? (A - base) / n : Hkv;
+  int k0 = n > 0 ? (A - base) - h * n : 0;
+  int pos = A;
+  while (h < Hkv) {  // h >= Hkv only if the lengths changed under the kernel
+    const int k1 = min(n, k0 + (B - pos));
+    const int sh = s * Hkv + h;
+    const int t_begin = k0 * E, t_end = min(k1 * E, L);
+    WaveState w;
+    w.reset();
+    stream_any<QG, BS, TQ4>(a.st, s, h, t_begin, t_end, chunks_per_part, area,
+                            reinterpret_cast<float*>(area + 2 * CHUNK * D), lds_tab, w,
+                            [&](int j, WaveState& ws) { store_partial<QG, TQ4>(a, sh, k0 + j, ws); });
+    const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
+    store_partial<QG, TQ4>(a, sh, k0 + (n_chunks - 1) / chunks_per_part, w);
+    pos += k1 - k0;
+    if (pos >= B) break;
+    // Next (s, h) of the list: the next kv head, or the next non-empty sequence.
+    k0 = 0;
+    if (++h == Hkv) {
+      h = 0;
+      do {
+        if (++s >= S) {
+          h = Hkv;
+          break;
+        }
+        L = len_of(s);
+        n = (L + E - 1) / E;
+      } while (n == 0);
+    }
+  }
+}
+
 // Merge of the split-K partials: one 256-thread block per (sequence, kv
 // head).  Each wave takes query rows g = wave, wave + 4, ...; its lanes read
 // the live partitions' max logits and exp sums, reduce M = max m_p and
@@ -1720,8 +1828,33 @@ hipError_t launch_partition_t(const PartitionArgs& a, dim3 grid, hipStream_t str
   return hipGetLastError();
 }
 
+template <int QG, int BS, bool TQ4>
+hipError_t launch_partition_flat_t(const PartitionArgs& a, int n_groups, hipStream_t stream) {
+  constexpr size_t lds = (size_t)kFlatWaves * kWaveLds;
+  static_assert(lds + (TQ4 ? kTq4TableEntries * 8 : 0) <= 160 * 1024, "LDS per workgroup");
+  // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
+  // the runtime needs none, and must not leak into the launch status.
+  static const bool lds_opt_in = [] {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_partition_flat_kernel<QG, BS, TQ4>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    (void)hipGetLastError();
+    return true;
+  }();
+  (void)lds_opt_in;
+  hipLaunchKernelGGL((tq_partition_flat_kernel<QG, BS, TQ4>), dim3((unsigned)n_groups),
+                     dim3(64 * kFlatWaves), lds, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
                             int kv_block_size, bool tq4, hipStream_t stream) {
+  a.num_seqs = num_seqs;
+  const int flat_groups =
+      plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap, a.partition_tokens, tq4);
+  if (flat_groups > 0) {
+    a.parts_per_wave = 0;  // unused by the flat kernel
+    TQ_DISPATCH(launch_partition_flat_t, query_group_size, kv_block_size, tq4, a, flat_groups, stream);
+  }
   const int64_t units = (int64_t)num_seqs * a.st.num_kv_heads * a.num_partitions;
   a.parts_per_wave = choose_parts_per_wave(units, a.num_partitions);
   const int64_t groups = (a.num_partitions + a.parts_per_wave - 1) / a.parts_per_wave;

@@ -12,6 +12,7 @@ namespace tq {
 namespace {
 constexpr int D = kHeadDim;
 constexpr int kMaxSplits = 16;  // workgroups per (s, h) of the per-(s, h) fused plan
+constexpr int kFlatGroupsMax = 256;  // workgroups of the flat kernels: one per CU
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
@@ -64,18 +65,32 @@ FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, s
   return plan;
 }
 
-int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len) {
+int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len, int unit_tokens) {
   // One resident round at two waves per SIMD (256 workgroups of 8 waves, one
-  // per CU), or fewer when the list cannot fill them: at most one wave per tile
-  // group.
-  constexpr int64_t kFlatGroups = 256;
+  // per CU), or fewer when the list cannot fill them: at most one wave per list
+  // entry.
+  constexpr int64_t kFlatGroups = kFlatGroupsMax;
   static_assert(kFlatGroups * kFlatWaves <= 65536, "waves per launch");
-  if (num_seqs < 1 || num_seqs > kFlatMaxSeqs || num_kv_heads < 1 || max_seq_len <= 0) return 0;
-  const int64_t n_tg = (max_seq_len + kTokensPerTileGroup - 1) / kTokensPerTileGroup;
+  if (num_seqs < 1 || num_seqs > kFlatMaxSeqs || num_kv_heads < 1 || max_seq_len <= 0 ||
+      unit_tokens < 1)
+    return 0;
+  const int64_t n_tg = (max_seq_len + unit_tokens - 1) / unit_tokens;
   const int64_t t_max = num_seqs * num_kv_heads * n_tg;
   if (t_max > (int64_t(1) << 30)) return 0;
   const int64_t groups = (t_max + kFlatWaves - 1) / kFlatWaves;
   return (int)(groups < kFlatGroups ? groups : kFlatGroups);
+}
+
+int plan_partition_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
+                               int partition_tokens, bool tq4) {
+  // The 4-bit format only, and only when the partitions (bounded by the
+  // longest length) fill the resident round at least twice: measured faster
+  // than one wave per partition there (7-12 %), slower with fewer partitions
+  // than that, and no faster for fp8.
+  if (!tq4 || num_seqs < 1 || num_kv_heads < 1 || max_seq_len <= 0 || partition_tokens < 1) return 0;
+  const int64_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
+  if (num_seqs * num_kv_heads * parts < 2 * kFlatWaves * kFlatGroupsMax) return 0;
+  return plan_flat_groups(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
 }
 
 size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size) {

@@ -32,6 +32,15 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
   require(kv_block_size == 16 || kv_block_size == 32, "BS");
   require(a.o && a.ml && a.es && a.seq_lens && a.st.bt && a.st.q, "partition pointers");
   require(tq4 ? (a.st.tq4 && a.st.centroids) : (a.st.k && a.st.v && a.st.scales), "format");
+  // The launcher's plan: the flat kernel's grid, else one wave per run of partitions.
+  const int flat_groups = plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap,
+                                                     a.partition_tokens, tq4);
+  require(flat_groups >= 0 && flat_groups <= 256 && (tq4 || flat_groups == 0), "flat partition plan");
+  if (flat_groups == 0) {
+    const int ppw = choose_parts_per_wave((int64_t)num_seqs * a.st.num_kv_heads * a.num_partitions,
+                                          a.num_partitions);
+    require(ppw >= 1 && ppw <= a.num_partitions, "parts per wave");
+  }
   g_log.last_tq4 = tq4;
   return hipSuccess;
 }

@@ -121,3 +121,51 @@ def test_tq4_single_tile_group_identity(qg, bs):
         for P, G in ((1, 1), (3, 1), (1, 5), (2, 2)):
             assert np.array_equal(bits(gpu_tq4(inp, path, num_partitions=P, tile_groups=G)),
                                   bits(ref)), (path, P, G)
+
+
+# Batches whose partitions (bounded by the longest length) fill the device's resident round
+# of 2048 waves at least twice take the flat partition kernel for the 4-bit format; smaller
+# ones take one wave per partition.
+FLAT_CASES = [(8, 32, 1, 64, 4, 4096), (16, 16, 2, 48, 8, 6000), (6, 32, 5, 128, 8, 6400)]
+
+
+@pytest.mark.parametrize("qg,bs,G,S,hkv,max_len", FLAT_CASES,
+                         ids=[f"qg{c[0]}_bs{c[1]}_G{c[2]}" for c in FLAT_CASES])
+def test_tq4_flat_partition_kernel(qg, bs, G, S, hkv, max_len):
+    """The batch's partials (flat partition kernel) equal bit for bit those of the same
+    sequences decoded one at a time (one wave per partition), written entries and untouched
+    ones alike; the merged batch matches the oracle."""
+    E = 256 * G
+    rng = np.random.default_rng(70 + qg + G)
+    lens = rng.integers(0, max_len + 1, size=S)
+    lens[:6] = (max_len, 0, 1, E - 1, E, E + 1)
+    lens = tuple(int(x) for x in lens)
+    P = -(-max_len // E)
+    assert S * hkv * P >= 2 * 2048 and hkv * P < 2 * 2048
+    wl = workloads.small_workload(name="tq4flat", num_seqs=S, num_kv_heads=hkv, query_group_size=qg,
+                                  kv_block_size=bs, seq_lens=lens, tile_groups_per_partition=G,
+                                  seed=80 + qg)
+    inp = workloads.make_inputs_tq4(wl, device="cuda", seq_lens=lens, num_partitions=P)
+    say(f"[tq4 flat partition] qg={qg} bs={bs} G={G} S={S} Hkv={hkv} P={P}")
+
+    def partials(sl):
+        n = sl.stop - sl.start
+        part = tq.alloc_partials(n, hkv, P, qg, "cuda")
+        for t in (part.out, part.max_logits, part.exp_sums):
+            t.fill_(float("nan"))
+        tq.tq4_decode(inp.q[sl].contiguous(), inp.cache, inp.centroids,
+                      inp.block_tables[sl].contiguous(), inp.seq_lens[sl].contiguous(), part, hkv,
+                      qg, bs, G, inp.softmax_scale, num_partitions=P, max_seq_len=max_len)
+        torch.cuda.synchronize()
+        return part
+
+    whole = partials(slice(0, S))
+    for s in (0, 1, 2, 3, 4, 5, S // 2, S - 1):
+        one = partials(slice(s, s + 1))
+        for a, b in ((whole.out, one.out), (whole.max_logits, one.max_logits),
+                     (whole.exp_sums, one.exp_sums)):
+            assert torch.equal(a[s:s + 1].view(torch.int32), b.view(torch.int32)), (s, lens[s])
+    out = torch.empty((S, hkv * qg, 128), dtype=torch.bfloat16, device="cuda")
+    tq.tq_decode_reduce(whole, inp.seq_lens, out, hkv, qg, G, num_partitions=P, max_seq_len=max_len)
+    torch.cuda.synchronize()
+    compare(out, oracle_tq4(inp), f"tq4 flat partition qg{qg} bs{bs} G{G}")

@@ -150,7 +150,7 @@ def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10)
 
 PROFILE_KERNELS = ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel", "tq_merge_kernel",
                    "tq_kv_write_kernel", "tq_flat_kernel[tq4]", "tq_partition_kernel[tq4]",
-                   "probe_pattern_kernel", "probe_pattern4_kernel")
+                   "tq_partition_flat_kernel[tq4]", "probe_pattern_kernel", "probe_pattern4_kernel")
 PROFILE_CMD = ("rocprofv3 {what} -d <dir>/{sub} -o {sub} --output-format csv -- "
                "python3 bench.py --workload {wl} --steps 20 --warmup 3 --no-cpu-baseline")
 
@@ -226,7 +226,7 @@ def summarize_rocprof(prof_dir: str, workload: str) -> None:
     lines += ["", f"Counter calibration with the 1 GiB copy probe: bytes = FETCH_SIZE x 1024 x "
               f"{f_scale:.4f}, WRITE_SIZE x 1024 x {w_scale:.4f}.", ""]
     for name in ("tq_flat_kernel", "tq_fused_kernel", "tq_partition_kernel", "tq_flat_kernel[tq4]",
-                 "tq_partition_kernel[tq4]"):
+                 "tq_partition_kernel[tq4]", "tq_partition_flat_kernel[tq4]"):
         if name not in fetch or name not in write:
             continue
         fb = fetch[name] * 1024.0 * f_scale

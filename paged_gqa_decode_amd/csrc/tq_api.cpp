@@ -115,7 +115,7 @@ hipError_t maybe_validate(const tq::StreamArgs& st, const int32_t* seq_lens, int
                           const tq_extent* ext, void* stream) {
   const char* v = getenv("TQ_VALIDATE");
   if (!v || v[0] != '1') return hipSuccess;
-  tq::ValidateArgs a;
+  tq::ValidateArgs a{};
   a.bt = st.bt;
   a.seq_lens = seq_lens;
   a.num_seqs = ext->num_seqs;
@@ -132,7 +132,7 @@ tq_status run_partition(const tq::StreamArgs& st, const int32_t* seq_lens,
                         void* stream) {
   if (!aligned16(partials->out) || !aligned4(partials->max_logits) || !aligned4(partials->exp_sums))
     return TQ_ERR_MISALIGNED;
-  tq::PartitionArgs a;
+  tq::PartitionArgs a{};
   a.st = st;
   a.seq_lens = seq_lens;
   a.o = partials->out;
@@ -161,7 +161,7 @@ tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out
   const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
   if (flat_groups > 0 && workspace &&
       workspace_bytes >= tq::flat_workspace_bytes(seq_heads, flat_groups, query_group_size)) {
-    tq::FlatArgs f;
+    tq::FlatArgs f{};
     f.st = st;
     f.seq_lens = seq_lens;
     f.out = static_cast<uint16_t*>(out);
@@ -174,7 +174,7 @@ tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out
   }
   const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size,
                                             workspace ? workspace_bytes : 0);
-  tq::FusedArgs a;
+  tq::FusedArgs a{};
   a.st = st;
   a.seq_lens = seq_lens;
   a.out = static_cast<uint16_t*>(out);
@@ -198,7 +198,7 @@ tq_status tq_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_cach
                     const tq_extent* ext, void* stream) {
   if (!partials || !partials->out || !partials->max_logits || !partials->exp_sums)
     return TQ_ERR_NULL;
-  tq::StreamArgs st;
+  tq::StreamArgs st{};
   int32_t E = 0;
   tq_status rc = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
                               query_group_size, kv_block_size, tile_groups_per_partition,
@@ -216,7 +216,7 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
                           const tq_extent* ext, void* workspace, size_t workspace_bytes,
                           void* stream) {
   if (!out) return TQ_ERR_NULL;
-  tq::StreamArgs st;
+  tq::StreamArgs st{};
   int32_t E = 0;
   tq_status rc = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
                               query_group_size, kv_block_size, tile_groups_per_partition,
@@ -233,7 +233,7 @@ tq_status tq4_decode(const void* q_rot, const uint8_t* kv_cache, const float* ce
                      const tq_extent* ext, void* stream) {
   if (!partials || !partials->out || !partials->max_logits || !partials->exp_sums)
     return TQ_ERR_NULL;
-  tq::StreamArgs st;
+  tq::StreamArgs st{};
   int32_t E = 0;
   tq_status rc = check_decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads,
                                   query_group_size, kv_block_size, tile_groups_per_partition,
@@ -250,7 +250,7 @@ tq_status tq4_decode_fused(const void* q_rot, const uint8_t* kv_cache, const flo
                            const tq_extent* ext, void* workspace, size_t workspace_bytes,
                            void* stream) {
   if (!out) return TQ_ERR_NULL;
-  tq::StreamArgs st;
+  tq::StreamArgs st{};
   int32_t E = 0;
   tq_status rc = check_decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads,
                                   query_group_size, kv_block_size, tile_groups_per_partition,
@@ -289,7 +289,7 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
   if (!aligned16(partials->out) || !aligned4(partials->max_logits) ||
       !aligned4(partials->exp_sums) || !aligned4(seq_lens) || !aligned16(out))
     return TQ_ERR_MISALIGNED;
-  tq::ReduceArgs a;
+  tq::ReduceArgs a{};
   a.o = partials->out;
   a.ml = partials->max_logits;
   a.es = partials->exp_sums;
@@ -318,7 +318,7 @@ tq_status tq_kv_write(const void* k_new, const void* v_new, const int32_t* slot_
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
       !aligned16(kv_scales) || !aligned4(slot_mapping))
     return TQ_ERR_MISALIGNED;
-  tq::KvWriteArgs a;
+  tq::KvWriteArgs a{};
   a.k_new = static_cast<const uint16_t*>(k_new);
   a.v_new = static_cast<const uint16_t*>(v_new);
   a.slot_mapping = slot_mapping;

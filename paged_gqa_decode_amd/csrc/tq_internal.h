@@ -45,6 +45,7 @@ struct PartitionArgs {
   int32_t parts_per_wave;    // consecutive partitions of one (s, h) walked by one wave
   int32_t len_cap;           // device lengths are clamped to [0, len_cap]
   int32_t num_seqs;          // S
+  int32_t nt_partials;       // 1: partials stored with the non-temporal bit
 };
 
 struct FusedArgs {
@@ -141,6 +142,11 @@ struct ValidateArgs {
   int32_t kv_block_size;
   int32_t max_seq_len;
 };
+
+// Whether the partition kernel stores the partials with the non-temporal bit:
+// for fp8 when their bytes (bounded by S * Hkv * P * QG * 520) are large.
+bool partials_nontemporal(int64_t num_seqs, int num_kv_heads, int num_partitions,
+                          int query_group_size, bool tq4);
 
 // Partitions of one (s, h) that one wave of the partition kernel walks.
 int choose_parts_per_wave(int64_t units, int num_partitions);

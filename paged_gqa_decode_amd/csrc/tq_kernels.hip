@@ -56,6 +56,7 @@ typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) int i32x2;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
@@ -68,6 +69,8 @@ constexpr float kLn2 = 0.693147180559945309417f;
 // of gfx940-family cache-policy operands.  Every KV byte is read once; with
 // NT the V / scale stream measured 8-9% faster on the bandwidth workload.
 constexpr int kCachePolicyStreaming = 2;
+// Word 3 of a gfx9 buffer resource for raw (untyped) buffer loads and stores.
+constexpr int kBufferDword3 = 0x00020000;
 
 // s_waitcnt with vmcnt = 0 and the other counters left at their maxima
 // (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
@@ -494,7 +497,6 @@ __device__ __forceinline__ void build_tq4_table(i32x2* tab, const float* centroi
 // accumulators; the odd dims from the second less 1024 times the sum of the P
 // operand (WaveState::corr), carried at 16x.
 __device__ __forceinline__ void tq4_nibbles_f16(i32x2 raw, f16x8& whole, f16x8& hi) {
-  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   constexpr uint32_t kExp = 0x64646464u;
   u32x4 x, h;
 #pragma unroll
@@ -884,22 +886,40 @@ static_assert(16 * D * 4 + 2 * 16 * 4 <= kWaveLds, "merge area must fit the stag
 
 // Partial triple of partition p of (s, h) = sh: o_p = acc * sigma / l_p, m_p
 // (natural log units), l_p, rows r < QG; then the running state restarts.
+// With a.nt_partials (a uniform branch) o_p goes out through buffer stores
+// that carry the non-temporal bit: a plain store and a non-temporal one in the
+// two arms of a branch would be merged into one plain store by the compiler.
 template <int QG, bool TQ4>
 __device__ __forceinline__ void store_partial(const PartitionArgs& a, int sh, int p, WaveState& w) {
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, b = lane >> 4;
   f32x4 o[8];
   const float l = w.template finish_as<TQ4, QG>(o);
-  if (r < QG) {
-    const size_t row = ((size_t)sh * a.num_partitions + p) * QG + r;
-    float* dst = a.o + row * D;
+  const size_t block = ((size_t)sh * a.num_partitions + p) * QG;  // the partition's first row
+  if (a.nt_partials) {
+    // The partition's QG x 128 floats as one buffer with a wave-uniform base.
+    const uint64_t base = reinterpret_cast<uint64_t>(a.o + block * D);
+    float* base_u = reinterpret_cast<float*>(
+        ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(base >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)base));
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(base_u, 0, QG * D * 4, kBufferDword3);
+    if (r < QG) {
+#pragma unroll
+      for (int dblk = 0; dblk < 8; ++dblk)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[dblk]), rs,
+                                               (r * D + out_col<TQ4>(dblk, b)) * 4, 0,
+                                               kCachePolicyStreaming);
+    }
+  } else if (r < QG) {
+    float* dst = a.o + (block + r) * D;
 #pragma unroll
     for (int dblk = 0; dblk < 8; ++dblk)
       *reinterpret_cast<f32x4*>(dst + out_col<TQ4>(dblk, b)) = o[dblk];
-    if (b == 0) {
-      a.ml[row] = w.m2 * kLn2;
-      a.es[row] = l;
-    }
+  }
+  if (r < QG && b == 0) {
+    a.ml[block + r] = w.m2 * kLn2;
+    a.es[block + r] = l;
   }
   w.reset();
 }
@@ -1695,7 +1715,6 @@ __global__ __launch_bounds__(256) void tq_merge_kernel(ReduceArgs a) {
 constexpr int kKvRowsPerWg = 32;
 
 __global__ __launch_bounds__(256) void tq_kv_write_kernel(KvWriteArgs a) {
-  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
   const int lane = threadIdx.x & 63;
   const int j = lane & 7;
   const int64_t row = (int64_t)blockIdx.x * kKvRowsPerWg + (threadIdx.x >> 3);  // (t, h)
@@ -1849,6 +1868,8 @@ hipError_t launch_partition_flat_t(const PartitionArgs& a, int n_groups, hipStre
 hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
                             int kv_block_size, bool tq4, hipStream_t stream) {
   a.num_seqs = num_seqs;
+  a.nt_partials = partials_nontemporal(num_seqs, a.st.num_kv_heads, a.num_partitions,
+                                       query_group_size, tq4) ? 1 : 0;
   const int flat_groups =
       plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap, a.partition_tokens, tq4);
   if (flat_groups > 0) {

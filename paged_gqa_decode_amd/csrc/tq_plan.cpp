@@ -27,6 +27,20 @@ int choose_parts_per_wave(int64_t units, int num_partitions) {
   return (int)ppw;
 }
 
+bool partials_nontemporal(int64_t num_seqs, int num_kv_heads, int num_partitions,
+                          int query_group_size, bool tq4) {
+  // Measured on the fp8 partition kernel: with 51-136 MB of partials (bound)
+  // the non-temporal bit made the kernel 6-10 % faster, and the whole
+  // two-kernel step up to 4 % (the merge then reads the partials from HBM
+  // instead of the last-level cache); with 17 MB the step was up to 4 %
+  // slower.  The 4-bit partition kernel, bound by its arithmetic, gained
+  // nothing and its step lost 3-5 %.
+  constexpr int64_t kMinBytes = int64_t(24) << 20;
+  const int64_t bytes =
+      num_seqs * num_kv_heads * num_partitions * (int64_t)query_group_size * (D + 2) * 4;
+  return !tq4 && bytes >= kMinBytes;
+}
+
 size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size) {
   if (splits <= 1) return 0;
   const size_t rows = (size_t)seq_heads * splits * query_group_size;

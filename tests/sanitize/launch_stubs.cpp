@@ -36,6 +36,9 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
   const int flat_groups = plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap,
                                                      a.partition_tokens, tq4);
   require(flat_groups >= 0 && flat_groups <= 256 && (tq4 || flat_groups == 0), "flat partition plan");
+  const bool nt = partials_nontemporal(num_seqs, a.st.num_kv_heads, a.num_partitions,
+                                       query_group_size, tq4);
+  require(!(nt && tq4), "partial store policy");
   if (flat_groups == 0) {
     const int ppw = choose_parts_per_wave((int64_t)num_seqs * a.st.num_kv_heads * a.num_partitions,
                                           a.num_partitions);

@@ -100,6 +100,16 @@ __device__ __forceinline__ float wave_max_xor16_32(float x) {
   return fmax_nn(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
 
+// Maximum over all 64 lanes: rotations by 8, 4, 2, 1 within each 16-lane row
+// (DPP row_ror), then across the rows.
+__device__ __forceinline__ float wave_max_all(float x) {
+  x = fmax_nn(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));
+  x = fmax_nn(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));
+  x = fmax_nn(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));
+  x = fmax_nn(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));
+  return wave_max_xor16_32(x);
+}
+
 __device__ __forceinline__ float wave_sum_xor16_32(float x) {
   const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
@@ -442,7 +452,7 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
 //
 // Per-wave LDS of the 4-bit stream: two 4 KiB row stages and two 256 B
 // metadata stages ([3][32] fp16), in the same 8.5 KiB staging area as the fp8
-// stream's; the 2 KiB centroid table is a workgroup's LDS array of its own.
+// stream's; the 1 KiB centroid table is a workgroup's LDS array of its own.
 //  * A chunk's 32 rows of 128 B (a whole block's slots of one kv head when
 //    BS = 32, two 2 KiB runs when BS = 16) arrive whole, by LDS-direct loads
 //    of 1 KiB each, and K is read back from LDS.  Splitting each row between a
@@ -454,12 +464,10 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
 //    16-byte bank groups within every 8 and 16 lanes.
 //  * The table is a separate LDS object, one per workgroup, so that the
 //    compiler can see that reading it never waits for the row stages'
-//    LDS-direct loads.  It maps an index byte to the centroids c of its two nibbles as two
-//    bf16 pairs, hi = bf16(c) then lo = bf16(c - hi): about 16 significant bits
-//    together, so the QK product does not round the codebook to bf16's 8.  The
-//    lo parts enter the contraction as extra dims against a duplicated q: one
-//    MFMA operand = (hi, lo) of two index bytes = dims (d0, d1, d0, d1, d2, d3,
-//    d2, d3), q = (q0, q1, q0, q1, q2, q3, q2, q3).
+//    LDS-direct loads.  It maps an index byte to the f16 centroids of its two
+//    nibbles, and QK runs on f16 MFMAs with q converted to f16: 11
+//    significant bits of the codebook, where bf16's 8 would miss the 1e-2
+//    bound on outlier-heavy queries.
 constexpr int kTq4RowStage = CHUNK * D;
 constexpr int kTq4MetaStage = 256;
 constexpr int kTq4MetaOff = 2 * kTq4RowStage;
@@ -470,23 +478,15 @@ __device__ __forceinline__ int tq4_row_swz(int row) {
   return (row & 7) ^ ((row >> 3) & 1) ^ ((row >> 2) & 4);
 }
 
-// bf16(c) in the low half, bf16(c - bf16(c)) in the high half.
-__device__ __forceinline__ uint32_t bf16_hi_lo(float c) {
-  const uint16_t hi = f32_to_bf16_rne(c);
-  const uint16_t lo = f32_to_bf16_rne(c - __uint_as_float((uint32_t)hi << 16));
-  return (uint32_t)hi | ((uint32_t)lo << 16);
-}
-
 // The centroid table, written by threads tid, tid + nthreads, ...: entry x =
-// {hi pair, lo pair} of (c[x & 15], c[x >> 4]), the first value of each pair
-// in the low half.  One table serves every wave of a workgroup, at a fixed
-// LDS address, so a lookup's address is the index byte times 8 (one shift)
-// plus a constant offset.
-__device__ __forceinline__ void build_tq4_table(i32x2* tab, const float* centroids, int tid,
+// (f16(c[x & 15]), f16(c[x >> 4])), the first in the low half.  One table
+// serves every wave of a workgroup, at a fixed LDS address, so a lookup's
+// address is the index byte times 4 (one shift) plus a constant offset.
+__device__ __forceinline__ void build_tq4_table(uint32_t* tab, const float* centroids, int tid,
                                                 int nthreads) {
   for (int x = tid; x < kTq4TableEntries; x += nthreads) {
-    const uint32_t e0 = bf16_hi_lo(centroids[x & 15]), e1 = bf16_hi_lo(centroids[x >> 4]);
-    tab[x] = i32x2{(int)((e0 & 0xFFFFu) | (e1 << 16)), (int)((e0 >> 16) | (e1 & 0xFFFF0000u))};
+    const f16x2 e = {(_Float16)centroids[x & 15], (_Float16)centroids[x >> 4]};
+    tab[x] = __builtin_bit_cast(uint32_t, e);
   }
 }
 
@@ -523,7 +523,7 @@ struct StageTag {
 template <int QG, int BS, typename OnBoundary>
 __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, int h, int t_begin,
                                                   int t_end, int chunks_per_part, uint8_t* lds,
-                                                  const i32x2* tab, WaveState& w,
+                                                  const uint32_t* tab, WaveState& w,
                                                   OnBoundary on_boundary) {
   static_assert(BS == 16 || BS == 32, "kv block size");
   static_assert(QG >= 1 && QG <= 16, "query group size");
@@ -551,9 +551,12 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     return id < nb_max ? id : nb_max;
   };
 
-  // q operands, duplicated pairs: qdup[2c + half] = dims 8c + 4 half + (0, 1, 0,
-  // 1, 2, 3, 2, 3) of this lane's 32 (the d-permutation of stream_tokens).
-  bf16x8 qdup[8];
+  // q operands in f16, dims 32b + 8c + 0..7 of row r (the d-permutation of
+  // stream_tokens).  bf16 -> f16 is exact for magnitudes in [2^-14, 2^15); a
+  // group whose largest |q| reaches 2^15 is first scaled by a power of two,
+  // 2^-qexp, which the logit scale c2 takes back.
+  f16x8 qf[4];
+  float c2 = a.qk_scale_log2;
   {
     bf16x8 qop[4];
     if (r < QG) {
@@ -564,14 +567,22 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
 #pragma unroll
       for (int c = 0; c < 4; ++c) qop[c] = bf16x8{};
     }
+    float qmax = 0.f;
 #pragma unroll
     for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int o = 4 * hf;
-        qdup[2 * c + hf] = bf16x8{qop[c][o], qop[c][o + 1], qop[c][o], qop[c][o + 1],
-                                  qop[c][o + 2], qop[c][o + 3], qop[c][o + 2], qop[c][o + 3]};
-      }
+      for (int j = 0; j < 8; ++j) qmax = fmax_nn(qmax, __builtin_fabsf((float)qop[c][j]));
+    qmax = wave_max_all(qmax);
+    float qscale = 1.f;
+    if (qmax >= 32768.f) {  // uniform
+      const int qexp = __builtin_amdgcn_frexp_expf(qmax) - 15;  // qmax * 2^-qexp < 2^15
+      qscale = __builtin_ldexpf(1.f, -qexp);
+      c2 = __builtin_ldexpf(c2, qexp);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[c][j] = (_Float16)((float)qop[c][j] * qscale);
   }
 
   // Issue chunk c into LDS stage `st`: its 32 rows, 8 per LDS-direct load
@@ -664,18 +675,16 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     __builtin_amdgcn_sched_barrier(0);
     if (c + 1 < n_chunks) issue(c + 1, st ^ 1);
     __builtin_amdgcn_sched_barrier(0);
-    // K operands: kop[t][2cc + hf] = (hi, lo) of index bytes 2hf and 2hf + 1 of
-    // dword cc, i.e. dims 8cc + 4hf + (0, 1, 0, 1, 2, 3, 2, 3).
-    bf16x8 kop[2][8];
+    // K operands: kop[t][cc] = the centroids of the 4 index bytes of dword cc,
+    // dims 8cc + 0..7.
+    f16x8 kop[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         const uint32_t x = (uint32_t)kraw[t][cc];
-        const i32x2 e0 = tab[x & 0xFF], e1 = tab[(x >> 8) & 0xFF], e2 = tab[(x >> 16) & 0xFF],
-                    e3 = tab[x >> 24];
-        kop[t][2 * cc] = __builtin_bit_cast(bf16x8, i32x4{e0[0], e0[1], e1[0], e1[1]});
-        kop[t][2 * cc + 1] = __builtin_bit_cast(bf16x8, i32x4{e2[0], e2[1], e3[0], e3[1]});
+        kop[t][cc] = __builtin_bit_cast(
+            f16x8, u32x4{tab[x & 0xFF], tab[(x >> 8) & 0xFF], tab[(x >> 16) & 0xFF], tab[x >> 24]});
       }
     if (c == next_boundary) {
       on_boundary(part_done, w);
@@ -688,9 +697,9 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     // ---- QK^T: C[token 4b+i][query r] for tiles 0 and 1 ----
     f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[0][k], qdup[k], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[1][k], qdup[k], s1, 0, 0, 0);
+    for (int k = 0; k < 4; ++k) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[0][k], qf[k], s0, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kop[1][k], qf[k], s1, 0, 0, 0);
     }
 
     // ---- softmax and P operand ----
@@ -702,7 +711,6 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       // The max reductions add one step across the two halves of a row; the
       // sums are paired up the same way at the end (finish_tq4).  The P
       // operand of lane r < 8 is its own 4 values followed by lane r + 8's.
-      const float c2 = a.qk_scale_log2;
       float y[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -770,7 +778,6 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       // the exponent, exp2(y c - m2), one fused multiply-add.  The fp16 K norm,
       // V scale and V zero point enter their products through mixed-precision
       // fused multiply-adds, with no separate conversion.
-      const float c2 = a.qk_scale_log2;
       float y[8];
   #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -864,7 +871,7 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
 template <int QG, int BS, bool TQ4, typename OnBoundary>
 __device__ __forceinline__ void stream_any(const StreamArgs& a, int s, int h, int t_begin, int t_end,
                                            int chunks_per_part, uint8_t* lds_v, float* lds_sc,
-                                           const i32x2* lds_tab, WaveState& w,
+                                           const uint32_t* lds_tab, WaveState& w,
                                            OnBoundary on_boundary) {
   if constexpr (TQ4)
     stream_tokens_tq4<QG, BS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_tab, w,
@@ -930,7 +937,7 @@ __device__ __forceinline__ void store_partial(const PartitionArgs& a, int sh, in
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq_partition_kernel(PartitionArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_stage[kWaveLds];
-  __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries : 1];
   const int lane = threadIdx.x;
   const int P = a.num_partitions;
   const int Hkv = a.st.num_kv_heads;
@@ -1016,7 +1023,7 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 o) {
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries : 1];
   __shared__ int last_arrival;
   if constexpr (TQ4) {  // before any return: every thread reaches the barrier
     build_tq4_table(lds_tab, a.st.centroids, threadIdx.x, blockDim.x);
@@ -1245,7 +1252,7 @@ template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   using Lay = FlatLayout<QG>;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries : 1];
   __shared__ int piece_sh[2 * kFlatWaves];        // s*Hkv+h of wave v's first (2v) / last
                                                   // (2v+1) piece, -1: none
   __shared__ int piece_ea[2 * kFlatWaves];        // list offset of that (s, h)'s first entry
@@ -1531,7 +1538,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64 * kFlatWaves) void tq_partition_flat_kernel(PartitionArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  __shared__ __attribute__((aligned(16))) i32x2 lds_tab[TQ4 ? kTq4TableEntries : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;

@@ -134,3 +134,36 @@ def test_v_magnitude_equivariance(path):
         sc[:, :, 1, :] *= 2.0 ** e
         got = gpu_decode(dataclasses.replace(inp, kv_scales=sc), path=path).float()
         assert torch.equal(got, ref * 2.0 ** e)
+
+
+def test_partials_independent_of_batch_and_store_policy():
+    """A batch with 24 MiB or more of fp8 partials (bound S * Hkv * P * QG * 520 B) stores
+    them with the non-temporal bit; one sequence alone stores them plainly.  The partials of
+    each sequence are the same bits either way, written entries and untouched ones alike."""
+    S, hkv, qg, bs, P = 64, 8, 8, 16, 16
+    assert S * hkv * P * qg * 520 >= 24 << 20 and hkv * P * qg * 520 < 24 << 20
+    rng = np.random.default_rng(44)
+    lens = rng.integers(0, 256 * P + 1, size=S)
+    lens[:5] = (256 * P, 0, 1, 255, 257)
+    lens = tuple(int(x) for x in lens)
+    wl = workloads.small_workload(name="ntpartials", num_seqs=S, num_kv_heads=hkv,
+                                  query_group_size=qg, kv_block_size=bs, seq_lens=lens, seed=45)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=P)
+    say(f"[bitwise] partials of a {S}-sequence batch against one sequence at a time")
+
+    def partials(sl):
+        part = tq.alloc_partials(sl.stop - sl.start, hkv, P, qg, "cuda")
+        for t in (part.out, part.max_logits, part.exp_sums):
+            t.fill_(float("nan"))
+        tq.tq_decode(inp.q[sl].contiguous(), inp.k_cache, inp.v_cache, inp.kv_scales,
+                     inp.block_tables[sl].contiguous(), inp.seq_lens[sl].contiguous(), part, hkv,
+                     qg, bs, 1, inp.softmax_scale, num_partitions=P, max_seq_len=256 * P)
+        torch.cuda.synchronize()
+        return part
+
+    whole = partials(slice(0, S))
+    for s in (0, 1, 2, 3, 4, S // 2, S - 1):
+        one = partials(slice(s, s + 1))
+        for a, b in ((whole.out, one.out), (whole.max_logits, one.max_logits),
+                     (whole.exp_sums, one.exp_sums)):
+            assert torch.equal(a[s:s + 1].view(torch.int32), b.view(torch.int32)), (s, lens[s])

@@ -169,3 +169,22 @@ def test_tq4_flat_partition_kernel(qg, bs, G, S, hkv, max_len):
     tq.tq_decode_reduce(whole, inp.seq_lens, out, hkv, qg, G, num_partitions=P, max_seq_len=max_len)
     torch.cuda.synchronize()
     compare(out, oracle_tq4(inp), f"tq4 flat partition qg{qg} bs{bs} G{G}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_tq4_query_power_of_two_scaling(path):
+    """The query enters the 4-bit path's MFMA in f16.  q * 2^k with softmax_scale * 2^-k has
+    the same logits: the output is the same bits, for k = 8 (|q| stays below 2^15) and k = 16
+    (|q| passes 2^15, and the kernel scales q down by a power of two before the conversion).
+    Elements of q below 2^-10 are zeroed first, so no value becomes an f16 subnormal."""
+    inp = _small((1, 77, 300, 700), qg=8, bs=32, P=3, seed=61)
+    q = inp.q.float()
+    q = torch.where(q.abs() < 2.0 ** -10, torch.zeros_like(q), q).to(torch.bfloat16)
+    base = dataclasses.replace(inp, q=q)
+    say(f"[tq4 q scaling] {path}, max |q| {q.float().abs().max().item():.2f}")
+    ref = gpu_tq4(base, path)
+    for k in (8, 16):
+        scaled = dataclasses.replace(base, q=(q.float() * 2.0 ** k).to(torch.bfloat16),
+                                     softmax_scale=base.softmax_scale * 2.0 ** -k)
+        assert float(scaled.q.float().abs().max()) >= (2.0 ** 15 if k == 16 else 0.0)
+        assert np.array_equal(bits(gpu_tq4(scaled, path)), bits(ref)), k

@@ -591,36 +591,40 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
   // dword l < 48 = field l / 16, tokens 2 (l % 16) and +1).  Every address is
   // a wave-uniform block base plus a per-lane 32-bit offset fixed for the
   // stream.
+  // The loads are buffer loads to LDS: a buffer resource over the block's
+  // record (scalar registers) plus a 32-bit lane offset fixed for the stream (a
+  // record is below 2^31 bytes), so issuing a chunk takes no vector address
+  // arithmetic.
   uint32_t row_off[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int row = 8 * j + (lane >> 3);
     const int piece = (lane & 7) ^ tq4_row_swz(row);
     const int slot = BS == 32 ? row : (row & 15);
-    row_off[j] = (uint32_t)(slot * D + 16 * piece);
+    row_off[j] = (uint32_t)(h * BS * D + slot * D + 16 * piece);
   }
   const int ml = lane < 48 ? lane : 0;
-  const uint32_t meta_off = (uint32_t)(4 * (BS == 32 ? ml : (ml >> 4) * 8 + (ml & 7)));
+  const uint32_t meta_off =
+      (uint32_t)meta_base + (uint32_t)(4 * (BS == 32 ? ml : (ml >> 4) * 8 + (ml & 7)));
   const bool meta_second = BS == 16 && (ml & 15) >= 8;  // tokens 16..31: the second block
-  const size_t head_off = (size_t)h * BS * D;
   auto issue = [&](int c, int st) {
     const int jb = (c * CHUNK) / BS;
     const uint32_t blkA = block_id(jb);
     uint32_t blkB = blkA;
     if (BS == 16) blkB = (jb + 1 < n_blocks) ? block_id(jb + 1) : blkA;
-    const uint8_t* recA = a.tq4 + (size_t)blkA * block_bytes;
-    const uint8_t* recB = a.tq4 + (size_t)blkB * block_bytes;
+    const __amdgpu_buffer_rsrc_t recA = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.tq4) + (size_t)blkA * block_bytes, 0, (int)block_bytes, kBufferDword3);
+    const __amdgpu_buffer_rsrc_t recB = BS == 32 ? recA : __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a.tq4) + (size_t)blkB * block_bytes, 0, (int)block_bytes, kBufferDword3);
     uint8_t* rdst = lds + st * kTq4RowStage;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint8_t* rec = (BS == 32 || j < 2) ? recA : recB;
-      __builtin_amdgcn_global_load_lds(rec + head_off + row_off[j], (lds_void*)(rdst + 1024 * j),
-                                       16, 0, kCachePolicyStreaming);
-    }
-    const uint8_t* mrec = meta_second ? recB : recA;
-    __builtin_amdgcn_global_load_lds(mrec + meta_base + meta_off,
-                                     (lds_void*)(lds + kTq4MetaOff + st * kTq4MetaStage), 4, 0,
-                                     kCachePolicyStreaming);
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((BS == 32 || j < 2) ? recA : recB,
+                                               (lds_void*)(rdst + 1024 * j), 16, row_off[j], 0, 0,
+                                               kCachePolicyStreaming);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(meta_second ? recB : recA,
+                                             (lds_void*)(lds + kTq4MetaOff + st * kTq4MetaStage), 4,
+                                             meta_off, 0, 0, kCachePolicyStreaming);
   };
 
   const int tr_tok = 16 * (r >> 3) + 4 * b + ((r >> 1) & 3);

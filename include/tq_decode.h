@@ -145,12 +145,11 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
 
 /*
  * tq_decode_fused -- the whole decode step in one launch, bf16 out directly.
- * Work is split into tile groups of 256 tokens, the unit of work of the page's
- * kernel.  With a large enough workspace (tq_fused_workspace_bytes) and at
- * most 256 sequences, the live tile groups of all (sequence s, kv head h)
- * pairs form one list in (s, h, tile group) order, dealt evenly to the waves
- * of one resident round of workgroups (8 waves each): every wave streams the
- * same number of tile groups to within one, however ragged the lengths.  Each
+ * With a large enough workspace (tq_fused_workspace_bytes) and at most 256
+ * sequences, the live 32-token chunks of all (sequence s, kv head h) pairs
+ * form one list in (s, h, chunk) order, dealt evenly to the waves of one
+ * resident round of workgroups (8 waves each): every wave streams the same
+ * number of chunks to within one, however ragged the lengths.  Each
  * wave keeps one online softmax per (s, h) it touches; the partial results (o,
  * m, l, as in STEP G of tq_decode_kernel) of an (s, h) split across waves are
  * merged by log-sum-exp with the formula of tq_decode_reduce, first in LDS
@@ -159,8 +158,9 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
  * workgroup order and writes out.  This is the in-launch merge across
  * partitions that the page's partial triple implies, with no second launch.
  * Without a workspace (or with more than 256 sequences, or too few bytes)
- * each (s, h) gets its own workgroups instead, its tile groups dealt in
- * contiguous runs to them, with the same merges.
+ * each (s, h) gets its own workgroups instead, its tile groups (256 tokens,
+ * the page's unit of work) dealt in contiguous runs to them, with the same
+ * merges.
  *   out        bf16 [S][Hkv*QG][128], fully overwritten (L_s = 0 gives zeros)
  *   workspace  NULL, or device memory of workspace_bytes bytes, 16-byte
  *              aligned; ZERO-FILLED before its first use (it holds arrival
@@ -171,10 +171,10 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
  * function of the sizes, ext->max_seq_len, workspace_bytes and the device-side
  * lengths, so repeated calls are bit-identical, and one launch serves any
  * lengths up to ext->max_seq_len (a captured graph may be replayed with new
- * lengths).  An (s, h) with one tile group of context (L <= 256) is computed
- * by one wave, bit-identical to tq_decode + tq_decode_reduce; otherwise the
- * two paths differ only by rounding.  Other arguments and errors are those of
- * tq_decode.
+ * lengths).  An (s, h) that one wave computes whole (L <= 32 with the list,
+ * L <= 256 with per-(s, h) workgroups) is bit-identical to tq_decode +
+ * tq_decode_reduce; otherwise the two paths differ only by rounding.  Other
+ * arguments and errors are those of tq_decode.
  */
 tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
                           const float* kv_scales, const int32_t* block_tables,

@@ -16,6 +16,10 @@ constexpr int kTokensPerTileGroup = 256;
 constexpr int kFlatWaves = 8;
 constexpr int kFlatSlices = 4;
 constexpr int kFlatMaxSeqs = 64 * kFlatSlices;
+// Tokens per entry of the flat fused kernel's work list: one 32-token chunk,
+// so that the list splits evenly over the waves even when the tile groups are
+// few per wave (ragged and long-context batches).
+constexpr int kFlatUnitTokens = 32;
 
 // What every decode kernel reads to stream one (sequence, kv head).  The fp8
 // format uses k, v and scales; the 4-bit record format tq4 and centroids.
@@ -96,7 +100,7 @@ struct FlatArgs {
 // unit_tokens: the tokens of one list entry (a tile group for the fused path,
 // a partition for the two-kernel path).
 int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
-                     int unit_tokens = kTokensPerTileGroup);
+                     int unit_tokens = kFlatUnitTokens);
 // Workgroups of the flat partition kernel (tq_partition_flat_kernel) for
 // these sizes, or 0 when the per-partition kernel runs instead.
 int plan_partition_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,

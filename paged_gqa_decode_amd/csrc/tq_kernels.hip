@@ -1147,12 +1147,14 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   }
 }
 
-// Fused decode over a flat work list, dealt evenly.  The live tile groups (256
-// tokens) of all (s, h) form one list in (s, h, tile group) order, T entries
-// long.  The grid's G workgroups of W waves hold N = G*W waves, of which the
-// first Nu = min(N, T) take consecutive ranges of q = T / Nu entries, the
-// first T % Nu of them one more: every wave streams the same number of tile
-// groups, to within one, however ragged the lengths are.  Workgroup g holds
+// Fused decode over a flat work list, dealt evenly.  The live 32-token chunks
+// (kFlatUnitTokens) of all (s, h) form one list in (s, h, chunk) order, T
+// entries long.  The grid's G workgroups of W waves hold N = G*W waves, of
+// which the first Nu = min(N, T) take consecutive ranges of q = T / Nu
+// entries, the first T % Nu of them one more: every wave streams the same
+// number of chunks, to within one, however ragged the lengths are.  (With
+// whole tile groups as entries, long-context batches of a few tile groups per
+// wave left half the waves one tile group longer than the rest.)  Workgroup g holds
 // the waves g*W .. g*W+W-1.
 // A wave's range is cut into segments at (s, h) boundaries; each segment gets
 // one online softmax.  A segment that holds a whole (s, h) is finished by its
@@ -1260,9 +1262,11 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   __shared__ int piece_sh[2 * kFlatWaves];        // s*Hkv+h of wave v's first (2v) / last
                                                   // (2v+1) piece, -1: none
   __shared__ int piece_ea[2 * kFlatWaves];        // list offset of that (s, h)'s first entry
-  __shared__ int piece_n[2 * kFlatWaves];         // its tile groups
+  __shared__ int piece_n[2 * kFlatWaves];         // its entries
   __shared__ int arrived_last[2];
-  constexpr int TG = kTokensPerTileGroup;
+  constexpr int TG = kFlatUnitTokens;  // tokens per list entry, a power of two
+  constexpr int ush = __builtin_ctz(TG);
+  static_assert(TG == 1 << ush && TG % CHUNK == 0, "list entries are whole chunks");
   constexpr int kItems = QG * (D / 4);  // (row, 4 columns) items of one merge, <= blockDim
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1277,7 +1281,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
     __syncthreads();
   }
 
-  // Tile groups per kv head, per wave in registers: lane l holds the clamped
+  // List entries per kv head, per wave in registers: lane l holds the clamped
   // lengths of sequences s = l + 64 i (i < k <= 4); per slice i an inclusive
   // scan over the lanes gives the list offsets within the slice.
   const int k = (S + 63) >> 6;
@@ -1292,7 +1296,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
     incl_r[i] = 0;
     slice_total[i] = 0;
     if (i < k) {
-      incl_r[i] = wave_inclusive_scan((len_r[i] + TG - 1) / TG);
+      incl_r[i] = wave_inclusive_scan((len_r[i] + TG - 1) >> ush);
       slice_total[i] = __builtin_amdgcn_readlane(incl_r[i], 63);
       total += slice_total[i];
     }
@@ -1340,7 +1344,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
       if (i < k && A >= sb * Hkv && A < (sb + slice_total[i]) * Hkv) {
         const int ln = __builtin_ctzll(__ballot((sb + incl_r[i]) * Hkv > A));
         L = __builtin_amdgcn_readlane(len_r[i], ln);
-        n = (L + TG - 1) / TG;
+        n = (L + TG - 1) >> ush;
         s = 64 * i + ln;
         base = (sb + __builtin_amdgcn_readlane(incl_r[i], ln) - n) * Hkv;
       }
@@ -1401,7 +1405,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
             break;
           }
           L = len_of(s);
-          n = (L + TG - 1) / TG;
+          n = (L + TG - 1) >> ush;
         } while (n == 0);
       }
     }

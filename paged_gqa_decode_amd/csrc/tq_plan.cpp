@@ -88,8 +88,8 @@ int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len, int un
   if (num_seqs < 1 || num_seqs > kFlatMaxSeqs || num_kv_heads < 1 || max_seq_len <= 0 ||
       unit_tokens < 1)
     return 0;
-  const int64_t n_tg = (max_seq_len + unit_tokens - 1) / unit_tokens;
-  const int64_t t_max = num_seqs * num_kv_heads * n_tg;
+  const int64_t n_units = (max_seq_len + unit_tokens - 1) / unit_tokens;
+  const int64_t t_max = num_seqs * num_kv_heads * n_units;
   if (t_max > (int64_t(1) << 30)) return 0;
   const int64_t groups = (t_max + kFlatWaves - 1) / kFlatWaves;
   return (int)(groups < kFlatGroups ? groups : kFlatGroups);

@@ -165,12 +165,13 @@ def _flat_bytes(seq_heads, groups, QG):
 
 
 def test_fused_workspace_bytes():
-    # the flat work list: 256 workgroups of 8 waves once the list has 2048 tile groups
+    # the flat work list of 32-token entries: 256 workgroups of 8 waves once it has 2048
     assert tq.fused_workspace_bytes(128, 8, 8, 8192) == _flat_bytes(1024, 256, 8)
     assert tq.fused_workspace_bytes(16, 4, 16, 40960) == _flat_bytes(64, 256, 16)
-    # a shorter list: at most one wave per tile group (4 tile groups: one workgroup)
-    assert tq.fused_workspace_bytes(4, 1, 16, 200) == _flat_bytes(4, 1, 16)
-    assert tq.fused_workspace_bytes(256, 1, 6, 256) == _flat_bytes(256, 32, 6)
+    assert tq.fused_workspace_bytes(256, 1, 6, 256) == _flat_bytes(256, 256, 6)
+    # a shorter list: at most one wave per entry (4 x 7 entries: four workgroups)
+    assert tq.fused_workspace_bytes(4, 1, 16, 200) == _flat_bytes(4, 4, 16)
+    assert tq.fused_workspace_bytes(1, 1, 8, 32) == _flat_bytes(1, 1, 8)
     assert tq.fused_workspace_bytes(16, 4, 7, 40960) == 0  # unsupported QG
     # more than 256 sequences: workgroups per (s, h) instead, split by the per-(s, h) plan
     assert tq.fused_workspace_bytes(257, 8, 8, 8192) == 0   # 2056 (s, h): one workgroup each

@@ -55,17 +55,21 @@ def test_block_relabelling_is_invisible(bs, path):
 
 @pytest.mark.parametrize("qg,bs", [(8, 16), (16, 32), (6, 32)])
 def test_single_live_partition_identity(qg, bs):
-    """L <= 256: (P=1, G=1), (P=3, G=1), (P=1, G=5), (P=2, G=2) give the same bits,
-    through the two-kernel path and the fused path alike."""
+    """L <= 256: (P=1, G=1), (P=3, G=1), (P=1, G=5), (P=2, G=2) give the same bits on each
+    path.  Across the paths the bits agree for the sequences the fused path does not split
+    (L <= 32, one entry of its work list); longer ones it may split between waves."""
     lens = (1, 16, 31, 100, 255, 256)
     inp = small(lens, qg=qg, bs=bs, P=1, seed=30 + qg)
-    outs = []
+    first = {}
     for path in PATHS:
         for P, G in ((1, 1), (3, 1), (1, 5), (2, 2)):
             say(f"[bitwise] single live partition qg={qg} bs={bs} P={P} G={G} {path}")
-            outs.append(bits(gpu_decode(inp, num_partitions=P, tile_groups=G, path=path)))
-    for o in outs[1:]:
-        assert np.array_equal(o, outs[0])
+            o = bits(gpu_decode(inp, num_partitions=P, tile_groups=G, path=path))
+            first.setdefault(path, o)
+            assert np.array_equal(o, first[path]), (path, P, G)
+    whole = [i for i, L in enumerate(lens) if L <= 32]
+    a, b = (first[p] for p in PATHS)
+    assert np.array_equal(a[whole], b[whole])
 
 
 @pytest.mark.parametrize("path", PATHS)

@@ -110,3 +110,65 @@ def test_capture_at_length_one_without_host_lengths(path):
         for s_, L in enumerate(lens):
             if L == 0:
                 assert (got[s_].float() == 0).all()
+
+
+@pytest.mark.parametrize("path", ["two_kernel", "fused"])
+def test_tq4_graph_replay_matches_eager(path):
+    """The 4-bit record format's paths captured and replayed with new queries and lengths
+    (zero and the captured bound included): every replay equals an eager call bit for bit."""
+    lens0 = (2500, 1, 4096, 900, 64)
+    S, Hkv, QG, BS, G, P = 5, 2, 16, 16, 2, 8
+    maxlen = 4096
+    wl = workloads.small_workload(name="graph4", num_seqs=S, num_kv_heads=Hkv, query_group_size=QG,
+                                  kv_block_size=BS, seq_lens=lens0, tile_groups_per_partition=G,
+                                  seed=41)
+    inp = workloads.make_inputs_tq4(wl, device="cuda", seq_lens=lens0, num_partitions=P)
+    out = torch.empty((S, Hkv * QG, 128), dtype=torch.bfloat16, device="cuda")
+    part = tq.alloc_partials(S, Hkv, P, QG, "cuda")
+    ws = torch.zeros(max(tq.fused_workspace_bytes(S, Hkv, QG, maxlen), 256), dtype=torch.uint8,
+                     device="cuda")
+    q = inp.q.clone()
+    seq_lens = inp.seq_lens.clone()
+
+    def step():
+        if path == "fused":
+            tq.tq4_decode_fused(q, inp.cache, inp.centroids, inp.block_tables, seq_lens, out, Hkv,
+                                QG, BS, G, inp.softmax_scale, num_partitions=P, max_seq_len=maxlen,
+                                workspace=ws)
+        else:
+            tq.tq4_decode(q, inp.cache, inp.centroids, inp.block_tables, seq_lens, part, Hkv, QG,
+                          BS, G, inp.softmax_scale, num_partitions=P, max_seq_len=maxlen)
+            tq.tq_decode_reduce(part, seq_lens, out, Hkv, QG, G, num_partitions=P,
+                                max_seq_len=maxlen)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say(f"[graph] capture 4-bit {path}")
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda").manual_seed(6)
+    for rep, lens in enumerate(((2500, 1, 4096, 900, 64), (0, 4096, 31, 32, 4000),
+                                (4096, 4096, 4096, 4096, 4096))):
+        q.copy_(torch.randn(q.shape, generator=gen, device="cuda").to(torch.bfloat16))
+        seq_lens.copy_(torch.tensor(lens, dtype=torch.int32))
+        torch.cuda.synchronize()
+        say(f"[graph] replay {rep} 4-bit {path} lens={lens}")
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        out.fill_(float("nan"))
+        step()
+        torch.cuda.synchronize()
+        assert torch.equal(got.view(torch.int16), out.view(torch.int16)), f"replay {rep} differs"
+        assert torch.isfinite(got.float()).all()
+        for s_, L in enumerate(lens):
+            if L == 0:
+                assert (got[s_].float() == 0).all()
+    if path == "fused":
+        assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "counters must stay re-armed"

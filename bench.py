@@ -246,6 +246,71 @@ def summarize_rocprof(prof_dir: str, workload: str) -> None:
     print("\n".join(lines))
 
 
+# Two rocprofv3 --pmc passes (each within the per-pass limits of 8 SQ and 2 GRBM
+# counters) for the occupancy, issue and stall figures of the decode kernels.
+COUNTER_PASSES = (
+    ("pmc1", ("SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
+              "SQ_INSTS_MFMA", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_LDS", "GRBM_GUI_ACTIVE")),
+    ("pmc2", ("SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_ANY", "SQ_WAIT_ANY",
+              "SQ_INSTS_SALU", "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE")),
+)
+COUNTER_KERNELS = ("tq_flat_kernel", "tq_partition_kernel", "tq_merge_kernel", "tq_kv_write_kernel",
+                   "tq_flat_kernel[tq4]", "tq_partition_flat_kernel[tq4]", "probe_pattern_kernel",
+                   "probe_pattern4_kernel")
+MI355X_XCDS, MI355X_CUS, MI355X_SIMDS = 8, 256, 1024
+
+
+def summarize_counters(prof_dir: str, workload: str) -> None:
+    """Write profiles/counters_<workload>.md from the COUNTER_PASSES runs under prof_dir:
+    per kernel, the average over its dispatches of every counter, and ratios derived from
+    them (cycles = GRBM_GUI_ACTIVE / 8 XCDs; quad-cycle counters times 4)."""
+    vals = {}
+    for sub, _ in COUNTER_PASSES:
+        for r in _csv_rows(os.path.join(prof_dir, sub, f"{sub}_counter_collection.csv")):
+            k = _kernel_key(r["Kernel_Name"])
+            vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    avg = {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in vals.items()}
+    names = [c for _, cs in COUNTER_PASSES for c in cs if c != "GRBM_GUI_ACTIVE"]
+    lines = [f"# rocprofv3 SQ counters, {workload} (bench.py, every decode kernel)", "",
+             "Commands (run from the repository root; <dir> = an output directory):", ""]
+    for sub, cs in COUNTER_PASSES:
+        lines.append("    " + PROFILE_CMD.format(what="--pmc " + " ".join(cs), sub=sub, wl=workload))
+    lines += [f"    python3 bench.py --summarize-counters <dir> --workload {workload}", "",
+              f"Kernel source sha256: {kernel_sha()}", "",
+              "Averages per dispatch (counters as rocprofv3 reports them, summed over the device).", "",
+              "| kernel | GRBM_GUI_ACTIVE | " + " | ".join(names) + " |",
+              "|---|" + "---|" * (len(names) + 1)]
+    for k in COUNTER_KERNELS:
+        if k not in avg:
+            continue
+        a = avg[k]
+        lines.append(f"| {k} | {a.get('GRBM_GUI_ACTIVE', float('nan')):.4g} | " +
+                     " | ".join(f"{a.get(c, float('nan')):.4g}" for c in names) + " |")
+    lines += ["", "Derived (cycles = GRBM_GUI_ACTIVE / 8, the kernel's duration in one XCD's clocks; "
+              "SQ_WAVE_CYCLES and SQ_ACTIVE_INST_VALU count quad-cycles):", "",
+              "| kernel | cycles | waves per SIMD (4 SQ_WAVE_CYCLES / 1024 SIMDs / cycles) | "
+              "VALU busy (4 SQ_ACTIVE_INST_VALU / 1024 / cycles) | MFMA busy "
+              "(SQ_VALU_MFMA_BUSY_CYCLES / 1024 / cycles) | LDS bank-conflict cycles "
+              "(SQ_LDS_BANK_CONFLICT / 256 CUs / cycles) | VALU instructions per wave |",
+              "|---|---|---|---|---|---|---|"]
+    for k in COUNTER_KERNELS:
+        if k not in avg:
+            continue
+        a = avg[k]
+        cyc = a.get("GRBM_GUI_ACTIVE", float("nan")) / MI355X_XCDS
+        pct = lambda x: f"{100 * x:.1f} %"  # noqa: E731
+        lines.append(
+            f"| {k} | {cyc:.4g} | {4 * a.get('SQ_WAVE_CYCLES', float('nan')) / MI355X_SIMDS / cyc:.2f} | "
+            f"{pct(4 * a.get('SQ_ACTIVE_INST_VALU', float('nan')) / MI355X_SIMDS / cyc)} | "
+            f"{pct(a.get('SQ_VALU_MFMA_BUSY_CYCLES', float('nan')) / MI355X_SIMDS / cyc)} | "
+            f"{pct(a.get('SQ_LDS_BANK_CONFLICT', float('nan')) / MI355X_CUS / cyc)} | "
+            f"{a.get('SQ_INSTS_VALU', float('nan')) / a.get('SQ_WAVES', float('nan')):.0f} |")
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -257,9 +322,14 @@ def main() -> int:
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read/copy probe")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 output under DIR and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="write profiles/counters_<workload>.md from the SQ counter passes under DIR")
     args = ap.parse_args()
     if args.summarize_rocprof:
         summarize_rocprof(args.summarize_rocprof, args.workload)
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): this library runs "

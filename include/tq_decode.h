@@ -145,7 +145,7 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
 
 /*
  * tq_decode_fused -- the whole decode step in one launch, bf16 out directly.
- * With a large enough workspace (tq_fused_workspace_bytes) and at most 256
+ * With a large enough workspace (tq_fused_workspace_bytes) and at most 1024
  * sequences, the live 32-token chunks of all (sequence s, kv head h) pairs
  * form one list in (s, h, chunk) order, dealt evenly to the waves of one
  * resident round of workgroups (8 waves each): every wave streams the same
@@ -157,7 +157,7 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
  * workgroups, through `workspace`: the last workgroup to finish merges them in
  * workgroup order and writes out.  This is the in-launch merge across
  * partitions that the page's partial triple implies, with no second launch.
- * Without a workspace (or with more than 256 sequences, or too few bytes)
+ * Without a workspace (or with more than 1024 sequences, or too few bytes)
  * each (s, h) gets its own workgroups instead, its tile groups (256 tokens,
  * the page's unit of work) dealt in contiguous runs to them, with the same
  * merges.

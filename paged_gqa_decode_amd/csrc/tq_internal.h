@@ -14,7 +14,7 @@ constexpr int kTokensPerTileGroup = 256;
 // The flat fused kernel: waves per workgroup, and the sequences its length
 // scan handles (64 lanes x kFlatSlices).
 constexpr int kFlatWaves = 8;
-constexpr int kFlatSlices = 4;
+constexpr int kFlatSlices = 16;
 constexpr int kFlatMaxSeqs = 64 * kFlatSlices;
 // Tokens per entry of the flat fused kernel's work list: one 32-token chunk,
 // so that the list splits evenly over the waves even when the tile groups are

@@ -1282,14 +1282,16 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   }
 
   // List entries per kv head, per wave in registers: lane l holds the clamped
-  // lengths of sequences s = l + 64 i (i < k <= 4); per slice i an inclusive
+  // lengths of sequences s = l + 64 i (i < k <= kFlatSlices); per slice i an inclusive
   // scan over the lanes gives the list offsets within the slice.
   const int k = (S + 63) >> 6;
   int len_r[kFlatSlices], incl_r[kFlatSlices], slice_total[kFlatSlices];
   int total = 0;
-  // All loads first (in bounds, unconditional), so they share one wait.
+  // All loads first (in bounds; slices past k skipped by uniform branches), so
+  // they share one wait.
 #pragma unroll
-  for (int i = 0; i < kFlatSlices; ++i) len_r[i] = a.seq_lens[min(lane + 64 * i, S - 1)];
+  for (int i = 0; i < kFlatSlices; ++i)
+    len_r[i] = i < k ? a.seq_lens[min(lane + 64 * i, S - 1)] : 0;
 #pragma unroll
   for (int i = 0; i < kFlatSlices; ++i) {
     len_r[i] = (i < k && lane + 64 * i < S) ? clamp_len(len_r[i], a.len_cap) : 0;
@@ -1566,7 +1568,8 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_partition_flat_kernel(Part
   int len_r[kFlatSlices], incl_r[kFlatSlices], slice_total[kFlatSlices];
   int total = 0;
 #pragma unroll
-  for (int i = 0; i < kFlatSlices; ++i) len_r[i] = a.seq_lens[min(lane + 64 * i, S - 1)];
+  for (int i = 0; i < kFlatSlices; ++i)
+    len_r[i] = i < k ? a.seq_lens[min(lane + 64 * i, S - 1)] : 0;
 #pragma unroll
   for (int i = 0; i < kFlatSlices; ++i) {
     len_r[i] = (i < k && lane + 64 * i < S) ? clamp_len(len_r[i], a.len_cap) : 0;

@@ -173,9 +173,10 @@ def test_fused_workspace_bytes():
     assert tq.fused_workspace_bytes(4, 1, 16, 200) == _flat_bytes(4, 4, 16)
     assert tq.fused_workspace_bytes(1, 1, 8, 32) == _flat_bytes(1, 1, 8)
     assert tq.fused_workspace_bytes(16, 4, 7, 40960) == 0  # unsupported QG
-    # more than 256 sequences: workgroups per (s, h) instead, split by the per-(s, h) plan
-    assert tq.fused_workspace_bytes(257, 8, 8, 8192) == 0   # 2056 (s, h): one workgroup each
-    assert tq.fused_workspace_bytes(257, 1, 8, 40960) == 0  # 257 (s, h): one workgroup of 8 waves
+    assert tq.fused_workspace_bytes(1024, 8, 8, 2048) == _flat_bytes(8192, 256, 8)
+    # more than 1024 sequences: workgroups per (s, h) instead, split by the per-(s, h) plan
+    assert tq.fused_workspace_bytes(1025, 8, 8, 8192) == 0   # 8200 (s, h): one workgroup each
+    assert tq.fused_workspace_bytes(1025, 1, 8, 40960) == 0  # 1025 (s, h): one workgroup each
 
 
 def call_tq4(lib, *, fused=False, q=A, cache=A, cent=A, bt=A, sl=A, out=A, QG=8, BS=16, G=1, Hkv=2,

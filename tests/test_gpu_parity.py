@@ -195,8 +195,8 @@ def _fused_vs_oracle(inp, S, Hkv, QG, BS, maxlen, P, ws_bytes=None, what=""):
 
 
 def test_even_split_one_long_sequence():
-    """One (s, h) of 160 tile groups: one wave per tile group, 20 workgroups, and a merge of
-    20 workgroup partials (more than the merge keeps in registers)."""
+    """One (s, h) of 1280 32-token entries: one wave per entry, 160 workgroups, and a merge of
+    160 workgroup partials (more than the merge keeps in registers)."""
     lens = (40960,)
     wl = workloads.small_workload(name="onelong", num_seqs=1, num_kv_heads=1, query_group_size=16,
                                   kv_block_size=32, seq_lens=lens, seed=41)
@@ -223,9 +223,9 @@ def test_even_split_ragged_with_empty_sequences():
             assert (out[s].float() == 0).all()
 
 
-@pytest.mark.parametrize("S", [256, 257])
+@pytest.mark.parametrize("S", [1024, 1025])
 def test_even_split_sequence_limit(S):
-    """256 sequences take the even split, 257 the per-(s, h) workgroups; both match the oracle."""
+    """1024 sequences take the even split, 1025 the per-(s, h) workgroups; both match the oracle."""
     rng = np.random.default_rng(45 + S)
     lens = tuple(int(x) for x in rng.integers(1, 700, size=S))
     wl = workloads.small_workload(name=f"lim{S}", num_seqs=S, num_kv_heads=1, query_group_size=8,

@@ -131,7 +131,8 @@ def test_tq4_single_tile_group_identity(qg, bs):
 # Batches whose partitions (bounded by the longest length) fill the device's resident round
 # of 2048 waves at least twice take the flat partition kernel for the 4-bit format; smaller
 # ones take one wave per partition.
-FLAT_CASES = [(8, 32, 1, 64, 4, 4096), (16, 16, 2, 48, 8, 6000), (6, 32, 5, 128, 8, 6400)]
+FLAT_CASES = [(8, 32, 1, 64, 4, 4096), (16, 16, 2, 48, 8, 6000), (6, 32, 5, 128, 8, 6400),
+              (8, 16, 1, 600, 2, 1024)]
 
 
 @pytest.mark.parametrize("qg,bs,G,S,hkv,max_len", FLAT_CASES,

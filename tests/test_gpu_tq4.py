@@ -194,3 +194,33 @@ def test_tq4_query_power_of_two_scaling(path):
                                      softmax_scale=base.softmax_scale * 2.0 ** -k)
         assert float(scaled.q.float().abs().max()) >= (2.0 ** 15 if k == 16 else 0.0)
         assert np.array_equal(bits(gpu_tq4(scaled, path)), bits(ref)), k
+
+
+def test_tq4_fused_workspace_modes():
+    """tq4_decode_fused with no workspace (one workgroup per (s, h)), with room for exactly two
+    workgroups per (s, h) (the per-(s, h) plan split in two, merged by the last arrival), and
+    with the full workspace (the even split over the whole batch): all match the oracle, and
+    the arrival counters are left at zero."""
+    lens = (5000, 37, 3000, 8191)
+    S, Hkv, QG, BS, P = 4, 1, 16, 32, 32
+    wl = workloads.small_workload(name="tq4ws", num_seqs=S, num_kv_heads=Hkv, query_group_size=QG,
+                                  kv_block_size=BS, seq_lens=lens, seed=19)
+    inp = workloads.make_inputs_tq4(wl, device="cuda", seq_lens=lens, num_partitions=P)
+    ref = oracle_tq4(inp)
+    maxlen = max(lens)
+    rows = S * Hkv * 2 * QG
+    two = 256 + ((rows * 512 + 255) // 256) * 256 + 2 * ((rows * 4 + 255) // 256) * 256
+    full = tq.fused_workspace_bytes(S, Hkv, QG, maxlen)
+    assert full > two
+    for what, nbytes in (("no workspace", 0), ("two workgroups per (s, h)", two),
+                         ("full workspace", full)):
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+        out = torch.empty((S, Hkv * QG, 128), dtype=torch.bfloat16, device="cuda")
+        say(f"[tq4 workspace] {what}")
+        tq.tq4_decode_fused(inp.q, inp.cache, inp.centroids, inp.block_tables, inp.seq_lens, out,
+                            Hkv, QG, BS, 1, inp.softmax_scale, num_partitions=P, max_seq_len=maxlen,
+                            workspace=ws)
+        torch.cuda.synchronize()
+        compare(out, ref, f"tq4 fused, {what}")
+        if ws is not None:
+            assert int(ws[:256].view(torch.int32).abs().sum()) == 0, "counters must be re-armed"

@@ -78,8 +78,8 @@ size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size
 // Carve the workspace for `splits` into the pointers of `a`.
 void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size);
 
-// Fused decode over one flat work list (the live tile groups of every (s, h)
-// in (s, h, tile group) order) dealt evenly to the waves of n_groups
+// Fused decode over one flat work list (the live 32-token chunks of every (s, h)
+// in (s, h, chunk) order) dealt evenly to the waves of n_groups
 // workgroups of 8 waves.
 struct FlatArgs {
   StreamArgs st;
@@ -97,7 +97,7 @@ struct FlatArgs {
 
 // Workgroups of the flat plan for these sizes (0: the flat kernel does not
 // apply), the workspace bytes it needs, and the carving of that workspace.
-// unit_tokens: the tokens of one list entry (a tile group for the fused path,
+// unit_tokens: the tokens of one list entry (a 32-token chunk for the fused path,
 // a partition for the two-kernel path).
 int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
                      int unit_tokens = kFlatUnitTokens);

@@ -1539,7 +1539,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
 // Split-K partition kernel over one flat work list: the live partitions of
 // every (s, h) in (s, h, p) order, dealt evenly to the waves of n_groups
 // workgroups of kFlatWaves waves (one resident round), as tq_flat_kernel deals
-// tile groups.  A wave's run is cut at (s, h) boundaries; each piece is one
+// its chunks.  A wave's run is cut at (s, h) boundaries; each piece is one
 // stream whose partials are written at every partition end (STEP G), so the
 // partials are bit for bit those of tq_partition_kernel.  No merge and no
 // barrier after the set-up: a wave with nothing to do returns.  Used for the

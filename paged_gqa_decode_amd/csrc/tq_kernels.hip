@@ -1773,12 +1773,28 @@ __global__ __launch_bounds__(256) void tq_kv_write_kernel(KvWriteArgs a) {
     const float scale = amax / 448.0f;
     u32x4 codes = {0u, 0u, 0u, 0u};
     if (scale > 0.f) {
+      // The quotients x / scale, rounded as an IEEE division rounds them, with
+      // one division per row: for y = RN(1 / scale), q0 = RN(x y) is within
+      // an ulp of x / scale, the residual x - q0 scale is exact in one fused
+      // multiply-add, and RN(q0 + r y) is the correctly rounded quotient
+      // (Markstein's theorem), given no underflow or overflow in these steps:
+      // scale in [2^-90, FLT_MAX] (quotients that could reach an fp8 code are
+      // then normal, and so are their residuals).  Zero quotients take the
+      // sign of x, as the division's do.  Other rows divide.
+      const bool one_div = scale >= 0x1p-90f && scale <= __FLT_MAX__;
+      const float y = 1.0f / scale;
+      auto quot = [&](float v) {
+        if (!one_div) return v / scale;
+        const float q0 = v * y;
+        const float r = __builtin_fmaf(-q0, scale, v);
+        return __builtin_copysignf(__builtin_fmaf(r, y, q0), v);
+      };
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float q0 = fminf(fmaxf(x[4 * w] / scale, -448.0f), 448.0f);
-        const float q1 = fminf(fmaxf(x[4 * w + 1] / scale, -448.0f), 448.0f);
-        const float q2 = fminf(fmaxf(x[4 * w + 2] / scale, -448.0f), 448.0f);
-        const float q3 = fminf(fmaxf(x[4 * w + 3] / scale, -448.0f), 448.0f);
+        const float q0 = fminf(fmaxf(quot(x[4 * w]), -448.0f), 448.0f);
+        const float q1 = fminf(fmaxf(quot(x[4 * w + 1]), -448.0f), 448.0f);
+        const float q2 = fminf(fmaxf(quot(x[4 * w + 2]), -448.0f), 448.0f);
+        const float q3 = fminf(fmaxf(quot(x[4 * w + 3]), -448.0f), 448.0f);
         int c = __builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
         c = __builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, c, true);
         codes[w] = (uint32_t)c;

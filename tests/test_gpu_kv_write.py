@@ -72,3 +72,32 @@ def test_written_cache_decodes():
         out = tq.decode(q, k, v, sc, bt_t, lens, max_seq_len=L, fused=fused)
         torch.cuda.synchronize()
         compare(out, ref, f"decode of the written cache, fused={fused}")
+
+
+def test_kv_write_magnitudes_bit_exact():
+    """Rows scaled by powers of two from 2^-120 to 2^100 (so that the per-row scale falls on
+    both sides of the writer's one-division range, [2^-90, FLT_MAX]), each row's values spread
+    over many binades, some exact zeros and negative zeros: codes and scales bit for bit
+    against the oracle."""
+    T, Hkv, bs = 2048, 4, 32
+    NB = T * Hkv // bs + 8
+    g = torch.Generator().manual_seed(77)
+    x = torch.randn((2, T, Hkv, 128), generator=g)
+    x *= torch.exp2(torch.randint(-20, 1, (2, T, Hkv, 128), generator=g).float())
+    x *= torch.exp2(torch.randint(-120, 101, (2, T, Hkv, 1), generator=g).float())
+    x[:, ::7, :, ::5] = 0.0
+    x[:, ::11, :, ::9] = -0.0
+    rows = x.to(torch.bfloat16)
+    rng = np.random.default_rng(78)
+    slots = rng.permutation(NB * bs)[:T].astype(np.int32)
+    kc = torch.zeros((NB, Hkv, bs, 128), dtype=torch.uint8)
+    vc = torch.zeros_like(kc)
+    sc = torch.zeros((NB, Hkv, 2, bs), dtype=torch.float32)
+    ref_k, ref_v, ref_s = oracle.kv_write(rows[0], rows[1], slots, kc, vc, sc)
+    gk, gv, gs = kc.cuda(), vc.cuda(), sc.cuda()
+    say(f"[kv_write] magnitudes T={T}")
+    tq.tq_kv_write(rows[0].cuda(), rows[1].cuda(), torch.from_numpy(slots).cuda(), gk, gv, gs)
+    torch.cuda.synchronize()
+    assert np.array_equal(gs.cpu().numpy().view(np.uint32), ref_s.view(np.uint32)), "scales differ"
+    assert np.array_equal(gk.cpu().numpy(), ref_k), "K codes differ from the oracle"
+    assert np.array_equal(gv.cpu().numpy(), ref_v), "V codes differ from the oracle"

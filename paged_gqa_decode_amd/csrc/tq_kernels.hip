@@ -1854,7 +1854,7 @@ __global__ __launch_bounds__(64) void tq_validate_kernel(ValidateArgs a) {
 template <int QG, int BS, bool TQ4>
 hipError_t launch_flat_t(const FlatArgs& a, hipStream_t stream) {
   constexpr size_t lds = (size_t)kFlatWaves * FlatLayout<QG>::kArea;
-  static_assert(lds + (TQ4 ? kTq4TableEntries * 8 : 0) + 1024 <= 160 * 1024,
+  static_assert(lds + (TQ4 ? kTq4TableEntries * 4 : 0) + 1024 <= 160 * 1024,
                 "LDS per workgroup");
   // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
   // the runtime needs none, and must not leak into the launch status.
@@ -1883,20 +1883,26 @@ hipError_t launch_partition_t(const PartitionArgs& a, dim3 grid, hipStream_t str
 
 template <int QG, int BS, bool TQ4>
 hipError_t launch_partition_flat_t(const PartitionArgs& a, int n_groups, hipStream_t stream) {
-  constexpr size_t lds = (size_t)kFlatWaves * kWaveLds;
-  static_assert(lds + (TQ4 ? kTq4TableEntries * 8 : 0) <= 160 * 1024, "LDS per workgroup");
-  // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
-  // the runtime needs none, and must not leak into the launch status.
-  static const bool lds_opt_in = [] {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_partition_flat_kernel<QG, BS, TQ4>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    (void)hipGetLastError();
-    return true;
-  }();
-  (void)lds_opt_in;
-  hipLaunchKernelGGL((tq_partition_flat_kernel<QG, BS, TQ4>), dim3((unsigned)n_groups),
-                     dim3(64 * kFlatWaves), lds, stream, a);
-  return hipGetLastError();
+  if constexpr (!TQ4) {
+    // The plan chooses this kernel for the 4-bit format only; no fp8 instance is built.
+    (void)a, (void)n_groups, (void)stream;
+    return hipErrorInvalidValue;
+  } else {
+    constexpr size_t lds = (size_t)kFlatWaves * kWaveLds;
+    static_assert(lds + kTq4TableEntries * 4 <= 160 * 1024, "LDS per workgroup");
+    // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
+    // the runtime needs none, and must not leak into the launch status.
+    static const bool lds_opt_in = [] {
+      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tq_partition_flat_kernel<QG, BS, TQ4>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      (void)hipGetLastError();
+      return true;
+    }();
+    (void)lds_opt_in;
+    hipLaunchKernelGGL((tq_partition_flat_kernel<QG, BS, TQ4>), dim3((unsigned)n_groups),
+                       dim3(64 * kFlatWaves), lds, stream, a);
+    return hipGetLastError();
+  }
 }
 
 hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,

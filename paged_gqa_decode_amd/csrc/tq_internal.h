@@ -16,6 +16,10 @@ constexpr int kTokensPerTileGroup = 256;
 constexpr int kFlatWaves = 8;
 constexpr int kFlatSlices = 16;
 constexpr int kFlatMaxSeqs = 64 * kFlatSlices;
+// Workgroups of the flat kernels at most (one per CU), and per lane of a wave
+// that walks them all.
+constexpr int kFlatGroupsMax = 256;
+constexpr int kFlatGroupsPerLane = kFlatGroupsMax / 64;
 // Tokens per entry of the flat fused kernel's work list: one 32-token chunk,
 // so that the list splits evenly over the waves even when the tile groups are
 // few per wave (ragged and long-context batches).

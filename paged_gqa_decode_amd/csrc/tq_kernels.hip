@@ -117,6 +117,17 @@ __device__ __forceinline__ float wave_sum_xor16_32(float x) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Sum over all 64 lanes: rotations by 8, 4, 2, 1 within each 16-lane row,
+// then across the rows.  The lanes add in different orders, so lane 0's sum is
+// broadcast: every lane returns the same bits.
+__device__ __forceinline__ float wave_sum_all(float x) {
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false));
+  x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_sum_xor16_32(x))));
+}
+
 // x of lane r + 8 (mod 16) of the same 16-lane row (DPP row_ror:8).
 __device__ __forceinline__ float row_ror8(float x) {
   return __int_as_float(
@@ -1009,6 +1020,28 @@ __device__ __forceinline__ float ld_coherent(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// The same device-coherent accesses as buffer loads and stores with the sc1
+// cache policy (what an agent-scope relaxed access is on gfx940-family
+// devices), 16 bytes at a time and free for the compiler to batch: a buffer
+// resource over one workspace array (wave-uniform base) and a 32-bit byte
+// offset.
+constexpr int kCachePolicyAgent = 16;  // sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, kBufferDword3);
+}
+__device__ __forceinline__ void st_coherent4(__amdgpu_buffer_rsrc_t rs, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kCachePolicyAgent);
+}
+__device__ __forceinline__ void st_coherent1(__amdgpu_buffer_rsrc_t rs, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, off, 0, kCachePolicyAgent);
+}
+__device__ __forceinline__ f32x4 ld_coherent4(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCachePolicyAgent));
+}
+__device__ __forceinline__ float ld_coherent1(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCachePolicyAgent));
+}
+
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 o) {
   const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
   const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
@@ -1190,7 +1223,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 
 // Log-sum-exp merge of n <= NMAX partials (the formula of lse_merge4) with
 // every load issued up front, so the loads take one round trip.
-constexpr int kFlatMergeRegs = 16;
 template <int NMAX, typename LdO, typename LdM, typename LdL>
 __device__ __forceinline__ f32x4 lse_merge4_regs(int n, LdO ld_o, LdM ld_m, LdL ld_l,
                                                  float* m_out = nullptr, float* l_out = nullptr) {
@@ -1433,6 +1465,10 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   const int t = threadIdx.x;
   const int item_g = t / (D / 4);
   const int item_col = 4 * (t % (D / 4));
+  const size_t ws_rows = (size_t)2 * G * QG;  // the workspace's partial rows
+  const __amdgpu_buffer_rsrc_t rs_o = coherent_rsrc(a.ws_o, ws_rows * D * 4);
+  const __amdgpu_buffer_rsrc_t rs_m = coherent_rsrc(a.ws_m, ws_rows * 4);
+  const __amdgpu_buffer_rsrc_t rs_l = coherent_rsrc(a.ws_l, ws_rows * 4);
   int ext_sh[2] = {-1, -1};
   int ext_ea[2] = {0, 0};
   int ext_n[2] = {0, 0};
@@ -1470,13 +1506,11 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
       if (inside) {
         store_bf16x4(a.out + ((size_t)sh * QG + item_g) * D + item_col, o);
       } else {
-        const size_t rec = 2 * (size_t)g + slot;
-        float* dst = a.ws_o + (rec * QG + item_g) * D + item_col;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) st_coherent(dst + i, o[i]);
+        const uint32_t row = (2 * (uint32_t)g + slot) * QG + item_g;
+        st_coherent4(rs_o, (row * D + item_col) * 4, o);
         if (item_col == 0) {
-          st_coherent(a.ws_m + rec * QG + item_g, m);
-          st_coherent(a.ws_l + rec * QG + item_g, l);
+          st_coherent1(rs_m, row * 4, m);
+          st_coherent1(rs_l, row * 4, l);
         }
       }
     }
@@ -1509,30 +1543,60 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
                                                __HIP_MEMORY_SCOPE_AGENT) == count[x] - 1;
   }
   __syncthreads();
+  // The last arrival merges the n partials of workgroups g_first .. g_first +
+  // n - 1 in workgroup order.  First the coefficients c_j = l_j e^{m_j - M} /
+  // sum_j' l_j' e^{m_j' - M} of each query row, one row per wave at a time,
+  // the lanes over j (n <= G <= 256), into LDS (the staging areas are free by
+  // now); then every item thread sums c_j o_j for its 4 columns, eight
+  // partials' loads in flight at once.
+  float* coef = reinterpret_cast<float*>(lds_dyn);  // [QG][n]
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
-    if (ext_sh[x] < 0 || !arrived_last[x]) continue;
+    if (ext_sh[x] < 0 || !arrived_last[x]) continue;  // uniform over the workgroup
     if (t == 0)  // re-arm for the next call; every workgroup of this launch is in
       __hip_atomic_store(a.counters + ext_sh[x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int n = count[x], gf = g_first[x], fs = first_slot[x];
+    auto rec = [&](int j) -> uint32_t { return 2 * (uint32_t)(gf + j) + (j == 0 ? fs : 0); };
+    for (int g = wave; g < QG; g += W) {
+      float mj[kFlatGroupsPerLane], lj[kFlatGroupsPerLane];
+#pragma unroll
+      for (int i = 0; i < kFlatGroupsPerLane; ++i) {
+        const int j = lane + 64 * i;
+        const bool valid = j < n;
+        mj[i] = valid ? ld_coherent1(rs_m, (rec(j) * QG + g) * 4) : kNegInf;
+        lj[i] = valid ? ld_coherent1(rs_l, (rec(j) * QG + g) * 4) : 0.f;
+      }
+      float M = mj[0];
+#pragma unroll
+      for (int i = 1; i < kFlatGroupsPerLane; ++i) M = fmax_nn(M, mj[i]);
+      M = wave_max_all(M);
+      float e[kFlatGroupsPerLane], sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < kFlatGroupsPerLane; ++i) {
+        e[i] = lj[i] * __expf(mj[i] - M);
+        sum += e[i];
+      }
+      const float inv = 1.0f / wave_sum_all(sum);
+#pragma unroll
+      for (int i = 0; i < kFlatGroupsPerLane; ++i)
+        if (lane + 64 * i < n) coef[g * n + lane + 64 * i] = e[i] * inv;
+    }
+    __syncthreads();
     if (t < kItems) {
-      const int gf = g_first[x], fs = first_slot[x];
-      auto rec = [&](int j) -> size_t { return 2 * (size_t)(gf + j) + (j == 0 ? fs : 0); };
-      auto ld_o = [&](int j) {
-        const float* src = a.ws_o + (rec(j) * QG + item_g) * D + item_col;
-        return f32x4{ld_coherent(src), ld_coherent(src + 1), ld_coherent(src + 2),
-                     ld_coherent(src + 3)};
-      };
-      auto ld_m = [&](int j) { return ld_coherent(a.ws_m + rec(j) * QG + item_g); };
-      auto ld_l = [&](int j) { return ld_coherent(a.ws_l + rec(j) * QG + item_g); };
-      f32x4 o;
-      if (count[x] <= kFlatMergeRegs) {
-        o = lse_merge4_regs<kFlatMergeRegs>(count[x], ld_o, ld_m, ld_l);
-      } else {
-        float m, l;
-        o = lse_merge4(count[x], ld_o, ld_m, ld_l, &m, &l);
+      f32x4 o = {0.f, 0.f, 0.f, 0.f};
+      for (int j0 = 0; j0 < n; j0 += 8) {
+        f32x4 oj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          oj[u] = j0 + u < n ? ld_coherent4(rs_o, ((rec(j0 + u) * QG + item_g) * D + item_col) * 4)
+                             : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (j0 + u < n) o += coef[item_g * n + j0 + u] * oj[u];
       }
       store_bf16x4(a.out + ((size_t)ext_sh[x] * QG + item_g) * D + item_col, o);
     }
+    __syncthreads();  // the coefficients are read before x + 1 overwrites them
   }
 }
 

@@ -12,7 +12,6 @@ namespace tq {
 namespace {
 constexpr int D = kHeadDim;
 constexpr int kMaxSplits = 16;  // workgroups per (s, h) of the per-(s, h) fused plan
-constexpr int kFlatGroupsMax = 256;  // workgroups of the flat kernels: one per CU
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 

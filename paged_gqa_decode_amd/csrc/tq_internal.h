@@ -69,6 +69,9 @@ struct FusedArgs {
   float* ws_l;              // [S*Hkv][splits][QG]
 };
 
+// Workgroups per (s, h) of the per-(s, h) fused plan at most.
+constexpr int kFusedMaxSplits = 16;
+
 // How the fused kernel is launched: waves per workgroup and workgroups per (s, h).
 struct FusedPlan {
   int waves;

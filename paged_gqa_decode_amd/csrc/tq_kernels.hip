@@ -1009,22 +1009,52 @@ __device__ __forceinline__ f32x4 lse_merge4(int n, LdO ld_o, LdM ld_m, LdL ld_l,
   return o;
 }
 
-// Device-coherent (agent scope) loads and stores of the cross-workgroup
-// partials: relaxed atomics write through to, and read from, the point where
-// all XCDs see the same bytes, so no L2-wide write-back or invalidate is
-// needed around them.
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Log-sum-exp merge of n <= NMAX partials (the formula of lse_merge4) with
+// every load issued up front, so the loads take one round trip.
+template <int NMAX, typename LdO, typename LdM, typename LdL>
+__device__ __forceinline__ f32x4 lse_merge4_regs(int n, LdO ld_o, LdM ld_m, LdL ld_l,
+                                                 float* m_out = nullptr, float* l_out = nullptr) {
+  if (n == 1) {  // a single partial is returned as is
+    if (m_out) *m_out = ld_m(0);
+    if (l_out) *l_out = ld_l(0);
+    return ld_o(0);
+  }
+  float mj[NMAX], lj[NMAX];
+  f32x4 oj[NMAX];
+#pragma unroll
+  for (int j = 0; j < NMAX; ++j) {
+    if (j < n) {
+      mj[j] = ld_m(j);
+      lj[j] = ld_l(j);
+      oj[j] = ld_o(j);
+    }
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int j = 0; j < NMAX; ++j)
+    if (j < n) M = fmaxf(M, mj[j]);
+  float Wsum = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NMAX; ++j) {
+    if (j < n) {
+      const float wt = lj[j] * __expf(mj[j] - M);
+      Wsum += wt;
+      o += wt * oj[j];
+    }
+  }
+  if (m_out) *m_out = M;
+  if (l_out) *l_out = Wsum;
+  return o * (1.0f / Wsum);
 }
 
-// The same device-coherent accesses as buffer loads and stores with the sc1
-// cache policy (what an agent-scope relaxed access is on gfx940-family
-// devices), 16 bytes at a time and free for the compiler to batch: a buffer
-// resource over one workspace array (wave-uniform base) and a 32-bit byte
-// offset.
+// Device-coherent loads and stores of the cross-workgroup partials: buffer
+// accesses with the sc1 cache policy, what an agent-scope relaxed atomic
+// access is on gfx940-family devices.  They write through to, and read from,
+// the point where all XCDs see the same bytes, so no L2-wide write-back or
+// invalidate is needed around them; unlike atomics they move 16 bytes at a
+// time and the compiler may keep many in flight.  A buffer resource covers one
+// workspace array (wave-uniform base); offsets are 32-bit byte offsets.
 constexpr int kCachePolicyAgent = 16;  // sc1
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const float* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)bytes, kBufferDword3);
@@ -1125,7 +1155,11 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   // Merge this workgroup's waves.
   const float* lds_f = reinterpret_cast<const float*>(lds_dyn);
   constexpr int kWaveF = kWaveLds / 4;
-  const size_t wsrow0 = ((size_t)sh * splits + split) * QG;
+  const uint32_t wsrow0 = ((uint32_t)sh * splits + split) * QG;
+  const size_t ws_rows = (size_t)gridDim.x * QG;  // [S*Hkv][splits][QG]
+  const __amdgpu_buffer_rsrc_t rs_o = coherent_rsrc(a.ws_o, ws_rows * D * 4);
+  const __amdgpu_buffer_rsrc_t rs_m = coherent_rsrc(a.ws_m, ws_rows * 4);
+  const __amdgpu_buffer_rsrc_t rs_l = coherent_rsrc(a.ws_l, ws_rows * 4);
   for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x) {
     const int g = idx / (D / 4);
     const int col = 4 * (idx % (D / 4));
@@ -1138,12 +1172,10 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
     if (n_wg == 1) {
       store_bf16x4(out + g * D + col, o);
     } else {
-      float* dst = a.ws_o + (wsrow0 + g) * D + col;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st_coherent(dst + i, o[i]);
+      st_coherent4(rs_o, ((wsrow0 + g) * D + col) * 4, o);
       if (col == 0) {
-        st_coherent(a.ws_m + wsrow0 + g, m);
-        st_coherent(a.ws_l + wsrow0 + g, l);
+        st_coherent1(rs_m, (wsrow0 + g) * 4, m);
+        st_coherent1(rs_l, (wsrow0 + g) * 4, l);
       }
     }
   }
@@ -1162,20 +1194,15 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   if (!last_arrival) return;
   if (threadIdx.x == 0)  // re-arm for the next call; every arrival of this launch is in
     __hip_atomic_store(a.counters + sh, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const size_t row_sh = (size_t)sh * splits * QG;
+  // At most kFusedMaxSplits partials: every load of the merge in flight at once.
+  const uint32_t row_sh = (uint32_t)sh * splits * QG;
   for (int idx = threadIdx.x; idx < QG * (D / 4); idx += blockDim.x) {
     const int g = idx / (D / 4);
     const int col = 4 * (idx % (D / 4));
-    float m, l;
-    const f32x4 o = lse_merge4(
-        n_wg,
-        [&](int j) {
-          const float* src = a.ws_o + (row_sh + (size_t)j * QG + g) * D + col;
-          return f32x4{ld_coherent(src), ld_coherent(src + 1), ld_coherent(src + 2),
-                       ld_coherent(src + 3)};
-        },
-        [&](int j) { return ld_coherent(a.ws_m + row_sh + (size_t)j * QG + g); },
-        [&](int j) { return ld_coherent(a.ws_l + row_sh + (size_t)j * QG + g); }, &m, &l);
+    const f32x4 o = lse_merge4_regs<kFusedMaxSplits>(
+        n_wg, [&](int j) { return ld_coherent4(rs_o, ((row_sh + j * QG + g) * D + col) * 4); },
+        [&](int j) { return ld_coherent1(rs_m, (row_sh + j * QG + g) * 4); },
+        [&](int j) { return ld_coherent1(rs_l, (row_sh + j * QG + g) * 4); });
     store_bf16x4(out + g * D + col, o);
   }
 }
@@ -1221,44 +1248,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
   return v;
 }
 
-// Log-sum-exp merge of n <= NMAX partials (the formula of lse_merge4) with
-// every load issued up front, so the loads take one round trip.
-template <int NMAX, typename LdO, typename LdM, typename LdL>
-__device__ __forceinline__ f32x4 lse_merge4_regs(int n, LdO ld_o, LdM ld_m, LdL ld_l,
-                                                 float* m_out = nullptr, float* l_out = nullptr) {
-  if (n == 1) {  // a single partial is returned as is
-    if (m_out) *m_out = ld_m(0);
-    if (l_out) *l_out = ld_l(0);
-    return ld_o(0);
-  }
-  float mj[NMAX], lj[NMAX];
-  f32x4 oj[NMAX];
-#pragma unroll
-  for (int j = 0; j < NMAX; ++j) {
-    if (j < n) {
-      mj[j] = ld_m(j);
-      lj[j] = ld_l(j);
-      oj[j] = ld_o(j);
-    }
-  }
-  float M = kNegInf;
-#pragma unroll
-  for (int j = 0; j < NMAX; ++j)
-    if (j < n) M = fmaxf(M, mj[j]);
-  float Wsum = 0.f;
-  f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < NMAX; ++j) {
-    if (j < n) {
-      const float wt = lj[j] * __expf(mj[j] - M);
-      Wsum += wt;
-      o += wt * oj[j];
-    }
-  }
-  if (m_out) *m_out = M;
-  if (l_out) *l_out = Wsum;
-  return o * (1.0f / Wsum);
-}
 
 template <int QG>
 struct FlatLayout {

@@ -11,7 +11,6 @@ namespace tq {
 
 namespace {
 constexpr int D = kHeadDim;
-constexpr int kMaxSplits = 16;  // workgroups per (s, h) of the per-(s, h) fused plan
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
@@ -72,7 +71,7 @@ FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, s
   FusedPlan plan;
   plan.waves = (int)(waves_per_sh < 8 ? waves_per_sh : 8);
   int64_t splits = (waves_per_sh + plan.waves - 1) / plan.waves;
-  if (splits > kMaxSplits) splits = kMaxSplits;
+  if (splits > kFusedMaxSplits) splits = kFusedMaxSplits;
   while (splits > 1 && fused_workspace_bytes(seq_heads, (int)splits, query_group_size) > ws_bytes) --splits;
   plan.splits = (int)splits;
   return plan;

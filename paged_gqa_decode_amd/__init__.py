@@ -143,6 +143,63 @@ def partials_bytes(num_seqs, num_kv_heads, num_partitions, query_group_size) -> 
                                                 int(query_group_size)))
 
 
+_FP8_CODES = (torch.uint8, torch.float8_e4m3fn)
+
+
+def _expect(t, name: str, dtypes, shape) -> None:
+    """Refuse a tensor whose dtype or shape disagrees with what the entry point will read or
+    write through its pointer (None in `shape` matches any size).  Checked before the device,
+    so that a wrong layout never reaches a kernel."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    dtypes = dtypes if isinstance(dtypes, tuple) else (dtypes,)
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+    if t.dim() != len(shape) or any(w is not None and int(n) != int(w) for n, w in zip(t.shape, shape)):
+        want = tuple("*" if w is None else int(w) for w in shape)
+        raise ValueError(f"{name} must have shape {want}, not {tuple(t.shape)}")
+
+
+def _expect_partials(partials: "Partials", S: int, Hkv: int, P: int, QG: int) -> None:
+    _expect(partials.out, "partials.out", torch.float32, (S, Hkv, P, QG, HEAD_DIM))
+    _expect(partials.max_logits, "partials.max_logits", torch.float32, (S, Hkv, P, QG))
+    _expect(partials.exp_sums, "partials.exp_sums", torch.float32, (S, Hkv, P, QG))
+
+
+def _expect_pool(num_blocks: int, *tensors) -> None:
+    for t, name in tensors:
+        if num_blocks > int(t.shape[0]):
+            raise ValueError(f"num_blocks {num_blocks} exceeds the {int(t.shape[0])} blocks of {name}")
+
+
+def _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS):
+    """q, the fp8 cache pair with its scales, the block table and the lengths; returns S."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [S][Hkv*QG][128] tensor")
+    S = int(q.shape[0])
+    _expect(q, "q", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
+    _expect(k_cache, "k_cache", _FP8_CODES, (None, Hkv, BS, HEAD_DIM))
+    _expect(v_cache, "v_cache", _FP8_CODES, (None, Hkv, BS, HEAD_DIM))
+    _expect(kv_scales, "kv_scales", torch.float32, (None, Hkv, 2, BS))
+    _expect(block_tables, "block_tables", torch.int32, (S, None))
+    _expect(seq_lens, "seq_lens", torch.int32, (S,))
+    return S
+
+
+def _expect_tq4_inputs(lib, q_rot, kv_cache, centroids, block_tables, seq_lens, Hkv, QG, BS):
+    """q, the 4-bit record pool, the centroids, the block table and the lengths; returns S."""
+    if not isinstance(q_rot, torch.Tensor) or q_rot.dim() != 3:
+        raise ValueError("q_rot must be a [S][Hkv*QG][128] tensor")
+    S = int(q_rot.shape[0])
+    _expect(q_rot, "q_rot", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
+    bb = int(lib.tq4_block_bytes(int(Hkv), int(BS)))
+    _expect(kv_cache, "kv_cache", torch.uint8, (None, bb if bb > 0 else None))
+    _expect(centroids, "centroids", torch.float32, (16,))
+    _expect(block_tables, "block_tables", torch.int32, (S, None))
+    _expect(seq_lens, "seq_lens", torch.int32, (S,))
+    return S
+
+
 def _dev(t: torch.Tensor, name: str) -> int:
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{name} must be a torch tensor on the GPU")
@@ -163,13 +220,17 @@ def tq_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, partials: 
               max_seq_len: int, num_blocks: Optional[int] = None, stream=None) -> None:
     """Enqueue the partition kernel (C ABI tq_decode); writes `partials` for live partitions."""
     lib = load_library()
+    Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
+    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS)
+    _expect_partials(partials, S, Hkv, int(num_partitions), QG)
+    nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    _expect_pool(nb, (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_scales, "kv_scales"))
     ptrs = [_dev(t, n) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                                     (kv_scales, "kv_scales"), (block_tables, "block_tables"),
                                     (seq_lens, "seq_lens"))]
     for t, n in ((partials.out, "partials.out"), (partials.max_logits, "partials.max_logits"),
                  (partials.exp_sums, "partials.exp_sums")):
         _dev(t, n)
-    nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
     ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
     ps = partials._struct()
     st = lib.tq_decode(*ptrs, ctypes.byref(ps), int(num_kv_heads), int(query_group_size),
@@ -184,6 +245,12 @@ def tq_decode_reduce(partials: Partials, seq_lens, out, num_kv_heads: int, query
                      stream=None) -> None:
     """Enqueue the merge kernel (C ABI tq_decode_reduce) into bf16 `out` [S][Hkv*QG][128]."""
     lib = load_library()
+    if not isinstance(out, torch.Tensor) or out.dim() != 3:
+        raise ValueError("out must be a [S][Hkv*QG][128] tensor")
+    S, Hkv, QG = int(out.shape[0]), int(num_kv_heads), int(query_group_size)
+    _expect(out, "out", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
+    _expect(seq_lens, "seq_lens", torch.int32, (S,))
+    _expect_partials(partials, S, Hkv, int(num_partitions), QG)
     for t, n in ((partials.out, "partials.out"), (partials.max_logits, "partials.max_logits"),
                  (partials.exp_sums, "partials.exp_sums")):
         _dev(t, n)
@@ -217,10 +284,14 @@ def tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
     """Enqueue the one-launch decode (C ABI tq_decode_fused) into bf16 `out` [S][Hkv*QG][128].
     `workspace`: None or a zero-filled uint8 device tensor (see alloc_fused_workspace)."""
     lib = load_library()
+    Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
+    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS)
+    _expect(out, "out", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
+    nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    _expect_pool(nb, (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_scales, "kv_scales"))
     ptrs = [_dev(t, n) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                                     (kv_scales, "kv_scales"), (block_tables, "block_tables"),
                                     (seq_lens, "seq_lens"), (out, "out"))]
-    nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
     ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
@@ -244,13 +315,17 @@ def tq4_decode(q_rot, kv_cache, centroids, block_tables, seq_lens, partials: Par
                max_seq_len: int, num_blocks: Optional[int] = None, stream=None) -> None:
     """Enqueue the partition kernel over the 4-bit record format (C ABI tq4_decode)."""
     lib = load_library()
+    Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
+    S = _expect_tq4_inputs(lib, q_rot, kv_cache, centroids, block_tables, seq_lens, Hkv, QG, BS)
+    _expect_partials(partials, S, Hkv, int(num_partitions), QG)
+    nb = int(kv_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    _expect_pool(nb, (kv_cache, "kv_cache"))
     ptrs = [_dev(t, n) for t, n in ((q_rot, "q_rot"), (kv_cache, "kv_cache"),
                                     (centroids, "centroids"), (block_tables, "block_tables"),
                                     (seq_lens, "seq_lens"))]
     for t, n in ((partials.out, "partials.out"), (partials.max_logits, "partials.max_logits"),
                  (partials.exp_sums, "partials.exp_sums")):
         _dev(t, n)
-    nb = int(kv_cache.shape[0]) if num_blocks is None else int(num_blocks)
     ext = _extent(q_rot.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
     ps = partials._struct()
     st = lib.tq4_decode(*ptrs, ctypes.byref(ps), int(num_kv_heads), int(query_group_size),
@@ -267,10 +342,14 @@ def tq4_decode_fused(q_rot, kv_cache, centroids, block_tables, seq_lens, out, nu
                      stream=None) -> None:
     """Enqueue the one-launch decode over the 4-bit record format (C ABI tq4_decode_fused)."""
     lib = load_library()
+    Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
+    S = _expect_tq4_inputs(lib, q_rot, kv_cache, centroids, block_tables, seq_lens, Hkv, QG, BS)
+    _expect(out, "out", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
+    nb = int(kv_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    _expect_pool(nb, (kv_cache, "kv_cache"))
     ptrs = [_dev(t, n) for t, n in ((q_rot, "q_rot"), (kv_cache, "kv_cache"),
                                     (centroids, "centroids"), (block_tables, "block_tables"),
                                     (seq_lens, "seq_lens"), (out, "out"))]
-    nb = int(kv_cache.shape[0]) if num_blocks is None else int(num_blocks)
     ext = _extent(q_rot.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
@@ -328,10 +407,17 @@ def tq_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, kv_scales, *, stre
     """Enqueue the KV-cache writer (C ABI tq_kv_write): quantize the new bf16 K/V rows
     [T][Hkv][128] and store them at slot_mapping (int32 [T], negative = skip)."""
     lib = load_library()
-    T, Hkv, D = k_new.shape
-    NB, Hkv2, BS, D2 = k_cache.shape
-    if v_new.shape != k_new.shape or Hkv2 != Hkv or D2 != D or tuple(slot_mapping.shape) != (T,):
-        raise ValueError("inconsistent shapes")
+    if not isinstance(k_new, torch.Tensor) or k_new.dim() != 3 or not isinstance(k_cache, torch.Tensor) \
+            or k_cache.dim() != 4:
+        raise ValueError("k_new must be [T][Hkv][128] and k_cache [NB][Hkv][BS][128]")
+    T, Hkv, D = (int(n) for n in k_new.shape)
+    NB, BS = int(k_cache.shape[0]), int(k_cache.shape[2])
+    _expect(k_new, "k_new", torch.bfloat16, (T, Hkv, HEAD_DIM))
+    _expect(v_new, "v_new", torch.bfloat16, (T, Hkv, HEAD_DIM))
+    _expect(slot_mapping, "slot_mapping", torch.int32, (T,))
+    _expect(k_cache, "k_cache", _FP8_CODES, (NB, Hkv, BS, HEAD_DIM))
+    _expect(v_cache, "v_cache", _FP8_CODES, (NB, Hkv, BS, HEAD_DIM))
+    _expect(kv_scales, "kv_scales", torch.float32, (NB, Hkv, 2, BS))
     if T == 0:
         return
     ptrs = [_dev(t, n) for t, n in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"),

@@ -285,3 +285,91 @@ def test_kv_write_rejects(lib, kw, status):
 
 def test_kv_write_zero_tokens_is_a_noop(lib):
     assert call_kv_write(lib, ptrs=[0] * 6, T=0) == tq.TQ_OK
+
+
+def _fp8_args(S=2, Hkv=2, QG=8, BS=16, NB=4, mb=3):
+    import torch
+    return dict(q=torch.zeros((S, Hkv * QG, 128), dtype=torch.bfloat16),
+                k_cache=torch.zeros((NB, Hkv, BS, 128), dtype=torch.uint8),
+                v_cache=torch.zeros((NB, Hkv, BS, 128), dtype=torch.uint8),
+                kv_scales=torch.zeros((NB, Hkv, 2, BS), dtype=torch.float32),
+                block_tables=torch.zeros((S, mb), dtype=torch.int32),
+                seq_lens=torch.ones((S,), dtype=torch.int32))
+
+
+@pytest.mark.parametrize("field,bad,err", [
+    ("q", lambda a: a["q"].float(), TypeError),
+    ("q", lambda a: a["q"][:, :12].contiguous(), ValueError),
+    ("k_cache", lambda a: a["k_cache"].to(__import__("torch").int8), TypeError),
+    ("v_cache", lambda a: a["v_cache"][:, :, :8].contiguous(), ValueError),
+    ("kv_scales", lambda a: a["kv_scales"].double(), TypeError),
+    ("kv_scales", lambda a: a["kv_scales"][:, :1].contiguous(), ValueError),
+    ("block_tables", lambda a: a["block_tables"].long(), TypeError),
+    ("block_tables", lambda a: a["block_tables"][:1].contiguous(), ValueError),
+    ("seq_lens", lambda a: a["seq_lens"].long(), TypeError),
+    ("seq_lens", lambda a: a["seq_lens"][:1].contiguous(), ValueError),
+])
+@pytest.mark.parametrize("entry", ["tq_decode", "tq_decode_fused"])
+def test_binding_refuses_wrong_layouts(entry, field, bad, err):
+    """A tensor of the wrong dtype or shape is refused before any pointer reaches the
+    library (checked ahead of the device, so CPU tensors show it)."""
+    import torch
+    a = _fp8_args()
+    a[field] = bad(a)
+    common = (2, 8, 16, 1, 0.1)
+    kw = dict(num_partitions=1, max_seq_len=1)
+    with pytest.raises(err, match=field):
+        if entry == "tq_decode":
+            part = tq.Partials(out=torch.zeros((2, 2, 1, 8, 128)), max_logits=torch.zeros((2, 2, 1, 8)),
+                               exp_sums=torch.zeros((2, 2, 1, 8)))
+            tq.tq_decode(*a.values(), part, *common, **kw)
+        else:
+            out = torch.zeros((2, 16, 128), dtype=torch.bfloat16)
+            tq.tq_decode_fused(*a.values(), out, *common, **kw)
+
+
+def test_binding_refuses_wrong_partials_and_pool():
+    import torch
+    a = _fp8_args()
+    good = dict(out=torch.zeros((2, 2, 3, 8, 128)), max_logits=torch.zeros((2, 2, 3, 8)),
+                exp_sums=torch.zeros((2, 2, 3, 8)))
+    for name, t in (("out", torch.zeros((2, 2, 2, 8, 128))), ("max_logits", torch.zeros((2, 2, 3, 6))),
+                    ("exp_sums", torch.zeros((2, 2, 3, 8), dtype=torch.float16))):
+        part = tq.Partials(**{**good, name: t})
+        with pytest.raises((TypeError, ValueError), match=f"partials.{name}"):
+            tq.tq_decode(*a.values(), part, 2, 8, 16, 1, 0.1, num_partitions=3, max_seq_len=1)
+        with pytest.raises((TypeError, ValueError), match=f"partials.{name}"):
+            tq.tq_decode_reduce(part, a["seq_lens"], torch.zeros((2, 16, 128), dtype=torch.bfloat16),
+                                2, 8, 1, num_partitions=3, max_seq_len=1)
+    with pytest.raises(ValueError, match="num_blocks"):
+        tq.tq_decode(*a.values(), tq.Partials(**good), 2, 8, 16, 1, 0.1, num_partitions=3,
+                     max_seq_len=1, num_blocks=5)
+    with pytest.raises(TypeError, match="out"):
+        tq.tq_decode_reduce(tq.Partials(**good), a["seq_lens"], torch.zeros((2, 16, 128)),
+                            2, 8, 1, num_partitions=3, max_seq_len=1)
+
+
+def test_binding_refuses_wrong_tq4_and_writer_layouts():
+    import torch
+    S, Hkv, QG, BS = 2, 2, 8, 16
+    bb = tq.tq4_block_bytes(Hkv, BS)
+    q = torch.zeros((S, Hkv * QG, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((S, 3), dtype=torch.int32)
+    sl = torch.ones((S,), dtype=torch.int32)
+    out = torch.zeros((S, Hkv * QG, 128), dtype=torch.bfloat16)
+    cent = torch.zeros((16,), dtype=torch.float32)
+    with pytest.raises(ValueError, match="kv_cache"):
+        tq.tq4_decode_fused(q, torch.zeros((4, bb - 1), dtype=torch.uint8), cent, bt, sl, out, Hkv, QG,
+                            BS, 1, 0.1, num_partitions=1, max_seq_len=1)
+    with pytest.raises(ValueError, match="centroids"):
+        tq.tq4_decode_fused(q, torch.zeros((4, bb), dtype=torch.uint8), cent[:8].contiguous(), bt, sl,
+                            out, Hkv, QG, BS, 1, 0.1, num_partitions=1, max_seq_len=1)
+    k = torch.zeros((4, Hkv, BS, 128), dtype=torch.uint8)
+    sc = torch.zeros((4, Hkv, 2, BS), dtype=torch.float32)
+    rows = torch.zeros((5, Hkv, 128), dtype=torch.bfloat16)
+    with pytest.raises(TypeError, match="slot_mapping"):
+        tq.tq_kv_write(rows, rows, torch.zeros((5,), dtype=torch.int64), k, k, sc)
+    with pytest.raises(ValueError, match="kv_scales"):
+        tq.tq_kv_write(rows, rows, torch.zeros((5,), dtype=torch.int32), k, k, sc[:, :, :1].contiguous())
+    with pytest.raises(TypeError, match="v_new"):
+        tq.tq_kv_write(rows, rows.float(), torch.zeros((5,), dtype=torch.int32), k, k, sc)

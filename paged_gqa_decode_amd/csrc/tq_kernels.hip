@@ -484,6 +484,13 @@ constexpr int kTq4MetaStage = 256;
 constexpr int kTq4MetaOff = 2 * kTq4RowStage;
 constexpr int kTq4WaveLds = kTq4MetaOff + 2 * kTq4MetaStage;
 constexpr int kTq4TableEntries = 256;
+// Columns of the wide centroid table: every entry repeated in 32 adjacent
+// dwords, lane l reading the copy in column l % 32, so that the bank a lookup
+// hits follows from the lane whatever the index byte (random index bytes
+// otherwise pile several lanes onto one bank).  32 KiB: the fused flat kernel
+// at QG <= 8 has the room (its staging takes 133 KiB at QG = 16).
+constexpr int kTq4WideCols = 32;
+constexpr int tq4_flat_table_cols(int qg, bool tq4) { return tq4 && qg <= 8 ? kTq4WideCols : 1; }
 
 __device__ __forceinline__ int tq4_row_swz(int row) {
   return (row & 7) ^ ((row >> 3) & 1) ^ ((row >> 2) & 4);
@@ -493,11 +500,14 @@ __device__ __forceinline__ int tq4_row_swz(int row) {
 // (f16(c[x & 15]), f16(c[x >> 4])), the first in the low half.  One table
 // serves every wave of a workgroup, at a fixed LDS address, so a lookup's
 // address is the index byte times 4 (one shift) plus a constant offset.
+template <int COLS = 1>
 __device__ __forceinline__ void build_tq4_table(uint32_t* tab, const float* centroids, int tid,
                                                 int nthreads) {
-  for (int x = tid; x < kTq4TableEntries; x += nthreads) {
+  static_assert(COLS == 1 || COLS == kTq4WideCols, "table columns");
+  for (int i = tid; i < kTq4TableEntries * COLS; i += nthreads) {
+    const int x = i / COLS;
     const f16x2 e = {(_Float16)centroids[x & 15], (_Float16)centroids[x >> 4]};
-    tab[x] = __builtin_bit_cast(uint32_t, e);
+    tab[i] = __builtin_bit_cast(uint32_t, e);
   }
 }
 
@@ -529,9 +539,9 @@ struct StageTag {
 
 // The 4-bit counterpart of stream_tokens: the same contract and the same
 // one-chunk-ahead pipeline.  lds is the wave's staging area (kTq4WaveLds
-// bytes); tab the workgroup's centroid table, which build_tq4_table has
+// bytes); tab the workgroup's centroid table in COLS columns, which build_tq4_table has
 // written before any wave streams.
-template <int QG, int BS, typename OnBoundary>
+template <int QG, int BS, int COLS, typename OnBoundary>
 __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, int h, int t_begin,
                                                   int t_end, int chunks_per_part, uint8_t* lds,
                                                   const uint32_t* tab, WaveState& w,
@@ -540,6 +550,7 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
   static_assert(QG >= 1 && QG <= 16, "query group size");
   constexpr bool kCompact = tq4_compact_softmax(QG);
   const int lane = threadIdx.x & 63;
+  const uint32_t tab_col = (uint32_t)(lane & (COLS - 1)) << 2;  // byte offset of the lane's column
   const int r = lane & 15;
   const int b = lane >> 4;
   const int Hkv = a.num_kv_heads;
@@ -698,8 +709,21 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
         const uint32_t x = (uint32_t)kraw[t][cc];
-        kop[t][cc] = __builtin_bit_cast(
-            f16x8, u32x4{tab[x & 0xFF], tab[(x >> 8) & 0xFF], tab[(x >> 16) & 0xFF], tab[x >> 24]});
+        if constexpr (COLS == 1) {
+          kop[t][cc] = __builtin_bit_cast(
+              f16x8, u32x4{tab[x & 0xFF], tab[(x >> 8) & 0xFF], tab[(x >> 16) & 0xFF], tab[x >> 24]});
+        } else {
+          // Entry e's copies start at byte 128 e: each index byte lands there
+          // with one shift and one mask, and the lane's column ORs in.
+          static_assert(COLS * 4 == 128, "wide table row");
+          const char* tb = reinterpret_cast<const char*>(tab);
+          auto at = [&](uint32_t row) {
+            return *reinterpret_cast<const uint32_t*>(tb + (row | tab_col));
+          };
+          kop[t][cc] = __builtin_bit_cast(
+              f16x8, u32x4{at((x << 7) & 0x7F80u), at((x >> 1) & 0x7F80u), at((x >> 9) & 0x7F80u),
+                           at((x >> 17) & 0x7F80u)});
+        }
       }
     if (c == next_boundary) {
       on_boundary(part_done, w);
@@ -883,13 +907,13 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
 
 // One stream call for either format (lds_v: the wave's staging area, lds_sc:
 // the fp8 scale stages inside it, lds_tab: the wave's 4-bit centroid table).
-template <int QG, int BS, bool TQ4, typename OnBoundary>
+template <int QG, int BS, bool TQ4, int COLS = 1, typename OnBoundary>
 __device__ __forceinline__ void stream_any(const StreamArgs& a, int s, int h, int t_begin, int t_end,
                                            int chunks_per_part, uint8_t* lds_v, float* lds_sc,
                                            const uint32_t* lds_tab, WaveState& w,
                                            OnBoundary on_boundary) {
   if constexpr (TQ4)
-    stream_tokens_tq4<QG, BS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_tab, w,
+    stream_tokens_tq4<QG, BS, COLS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_tab, w,
                               on_boundary);
   else
     stream_tokens<QG, BS>(a, s, h, t_begin, t_end, chunks_per_part, lds_v, lds_sc, w, on_boundary);
@@ -1278,8 +1302,9 @@ __device__ __forceinline__ void store_piece(float* P, const f32x4 o[8], float m,
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   using Lay = FlatLayout<QG>;
+  constexpr int kTabCols = tq4_flat_table_cols(QG, TQ4);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries * kTabCols : 1];
   __shared__ int piece_sh[2 * kFlatWaves];        // s*Hkv+h of wave v's first (2v) / last
                                                   // (2v+1) piece, -1: none
   __shared__ int piece_ea[2 * kFlatWaves];        // list offset of that (s, h)'s first entry
@@ -1298,7 +1323,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   const int g = blockIdx.x;
   auto len_of = [&](int s) { return clamp_len(a.seq_lens[s], a.len_cap); };
   if constexpr (TQ4) {  // before any return: every thread reaches the barrier
-    build_tq4_table(lds_tab, a.st.centroids, threadIdx.x, blockDim.x);
+    build_tq4_table<kTabCols>(lds_tab, a.st.centroids, threadIdx.x, blockDim.x);
     __syncthreads();
   }
 
@@ -1390,7 +1415,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
       const int sh = s * Hkv + h;
       WaveState st;
       st.reset();
-      stream_any<QG, BS, TQ4>(a.st, s, h, k0 * TG, min(k1 * TG, L), 0x7fffffff, area,
+      stream_any<QG, BS, TQ4, kTabCols>(a.st, s, h, k0 * TG, min(k1 * TG, L), 0x7fffffff, area,
                               reinterpret_cast<float*>(area + 2 * CHUNK * D),
                               lds_tab, st,
                               [](int, WaveState&) {});
@@ -1907,7 +1932,8 @@ __global__ __launch_bounds__(64) void tq_validate_kernel(ValidateArgs a) {
 template <int QG, int BS, bool TQ4>
 hipError_t launch_flat_t(const FlatArgs& a, hipStream_t stream) {
   constexpr size_t lds = (size_t)kFlatWaves * FlatLayout<QG>::kArea;
-  static_assert(lds + (TQ4 ? kTq4TableEntries * 4 : 0) + 1024 <= 160 * 1024,
+  static_assert(lds + (TQ4 ? kTq4TableEntries * 4 * tq4_flat_table_cols(QG, TQ4) : 0) + 1024 <=
+                    160 * 1024,
                 "LDS per workgroup");
   // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
   // the runtime needs none, and must not leak into the launch status.

@@ -66,34 +66,73 @@ def measured_traffic(workload: str, path_name: str):
     return t.get("hbm_bytes_per_launch")
 
 
+def cpu_info():
+    """CPU model, physical cores and logical CPUs of the host (from /proc/cpuinfo), and the
+    CPUs this process may run on."""
+    model, phys, logical = None, set(), 0
+    try:
+        with open("/proc/cpuinfo") as f:
+            cur = {}
+            for ln in f.read().splitlines() + [""]:
+                if not ln.strip():
+                    if cur:
+                        logical += 1
+                        phys.add((cur.get("physical id"), cur.get("core id")))
+                        model = model or cur.get("model name")
+                    cur = {}
+                    continue
+                k, _, v = ln.partition(":")
+                cur[k.strip()] = v.strip()
+    except OSError:
+        pass
+    return {"cpu_model": model, "physical_cores": len(phys) or None, "logical_cpus": logical or None,
+            "cpus_available": len(os.sched_getaffinity(0))}
+
+
+# The oracle's threads: every CPU this process may use, at most 16 (a one-GPU box's share of
+# its host's CPUs, whatever the host has in all).
+CPU_BASELINE_MAX_THREADS = 16
+
+
 def cpu_baseline(inp, budget_s: float):
-    """Time the fp64 oracle (as it stands) on whole (sequence, kv head) units of the workload."""
+    """Time the fp64 oracle (as it stands) on whole (sequence, kv head) units of the workload:
+    with all the threads it may use, and with one thread on a smaller sample."""
     import oracle
 
     c = inp.to("cpu")
     wl = inp.wl
-    threads = max(1, min(16, os.cpu_count() or 1))
+    info = cpu_info()
+    threads = max(1, min(CPU_BASELINE_MAX_THREADS, info["cpus_available"]))
     units = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_kv_heads)]
+    lens = c.seq_lens.numpy()
 
-    def run(n):
+    def run(n, nthreads):
         sel = units[:n]
         t0 = time.perf_counter()
         oracle.decode(c.q, c.k_cache, c.v_cache, c.kv_scales, c.block_tables, c.seq_lens,
-                      inp.softmax_scale, units=sel, nthreads=threads)
+                      inp.softmax_scale, units=sel, nthreads=nthreads)
         return time.perf_counter() - t0, sel
 
-    # calibrate on `threads` units, then size the sample to about budget_s
-    dt, sel = run(threads)
-    n = max(threads, min(len(units), int(threads * budget_s / max(dt, 1e-3))))
-    n = (n // threads) * threads or threads
-    dt, sel = run(n)
-    lens = c.seq_lens.numpy()
-    kv_bytes = sum(int(lens[s]) for s, _ in sel) * KV_BYTES_PER_TOKEN_HEAD
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+    def sized(nthreads, budget):
+        # calibrate on `nthreads` units, then size the sample to about `budget` seconds
+        dt, sel = run(nthreads, nthreads)
+        n = max(nthreads, min(len(units), int(nthreads * budget / max(dt, 1e-3))))
+        n = (n // nthreads) * nthreads or nthreads
+        dt, sel = run(n, nthreads)
+        kv_bytes = sum(int(lens[s]) for s, _ in sel) * KV_BYTES_PER_TOKEN_HEAD
+        return kv_bytes / dt / 1e9, dt, sel
+
+    gbs, dt, sel = sized(threads, budget_s)
+    gbs1, dt1, sel1 = sized(1, budget_s / 3)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "threads": threads, "cpu_model": info["cpu_model"],
+            "physical_cores": info["physical_cores"], "logical_cpus": info["logical_cpus"],
+            "cpus_available": info["cpus_available"],
+            "one_thread": {"value": round(gbs1, 4), "unit": "GB/s",
+                           "sample": f"{len(sel1)} units, {dt1:.1f} s wall"},
             "sample": f"{len(sel)} of {len(units)} (sequence, kv head) units of {wl.name} "
                       f"({int(lens[sel[0][0]])} tokens each, all {wl.query_group_size} query rows), "
-                      f"fp64 C oracle, {dt:.1f} s wall"}
+                      f"fp64 C oracle on {threads} threads, {dt:.1f} s wall"}
 
 
 def hbm_probe(dev, read_gib: float = 4.0, copy_gib: float = 1.0, reps: int = 10):

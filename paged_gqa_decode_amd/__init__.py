@@ -14,6 +14,7 @@ partial triple), ``tq_decode_reduce`` (log-sum-exp merge into bf16), plus
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -214,6 +215,18 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _on_stream(stream):
+    """Context in which `stream` (a torch stream, a raw hipStream_t handle, or None for the
+    current stream) is torch's current stream: temporaries allocated inside it belong to that
+    stream in torch's caching allocator, so that they are ordered with the kernels enqueued
+    there and are not handed out again while those kernels may still use them."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(_stream(stream))
+    return torch.cuda.stream(stream)
+
+
 def tq_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, partials: Partials,
               num_kv_heads: int, query_group_size: int, kv_block_size: int,
               tile_groups_per_partition: int, softmax_scale: float, *, num_partitions: int,
@@ -370,6 +383,15 @@ def decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, *, num_kv_hea
                stream=None) -> torch.Tensor:
     """decode() for the 4-bit record format: kv_cache uint8 [NB][tq4_block_bytes],
     centroids fp32 [16], q_rot bf16 [S][Hq][128].  Returns bf16 [S][Hq][128]."""
+    with _on_stream(stream):
+        return _decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads,
+                           kv_block_size, num_partitions, tile_groups_per_partition,
+                           softmax_scale, max_seq_len, partials, out, fused, workspace, stream)
+
+
+def _decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads, kv_block_size,
+                num_partitions, tile_groups_per_partition, softmax_scale, max_seq_len, partials,
+                out, fused, workspace, stream):
     S, Hq, D = q_rot.shape
     Hkv, BS = int(num_kv_heads), int(kv_block_size)
     if D != HEAD_DIM or Hq % Hkv:
@@ -445,7 +467,18 @@ def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partit
     given, which synchronizes the stream; under graph capture it is the block
     table's capacity (max_blocks_per_seq * BS) instead, so that nothing is read
     back and the captured launches serve any lengths up to it.
-    ``num_partitions`` defaults to ceil(max_seq_len / (256 * G))."""
+    ``num_partitions`` defaults to ceil(max_seq_len / (256 * G)).
+    ``stream``: a torch stream or raw hipStream_t (None: the current stream); the
+    temporaries allocated here are allocated on it."""
+    with _on_stream(stream):
+        return _decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_partitions,
+                       tile_groups_per_partition, softmax_scale, max_seq_len, partials, out, fused,
+                       workspace, stream)
+
+
+def _decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_partitions,
+            tile_groups_per_partition, softmax_scale, max_seq_len, partials, out, fused, workspace,
+            stream):
     S, Hq, D = q.shape
     NB, Hkv, BS, Dk = k_cache.shape
     if D != HEAD_DIM or Dk != HEAD_DIM or Hq % Hkv:

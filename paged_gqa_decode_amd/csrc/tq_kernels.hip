@@ -34,9 +34,9 @@
 //    column: the A operand of a 16x16x32 f16 MFMA (O^T = V^T P), converted
 //    fp8 -> f16 exactly in registers.
 //  * The V scale is folded into P: the B operand is p_t * vs_t / sigma in
-//    f16, where sigma is the running maximum V scale since the last restart,
-//    so the operand stays in [0, 1] whatever the data's magnitude; acc is
-//    rescaled when sigma grows, together with the softmax rescale.
+//    f16, where sigma is the running maximum |V scale| since the last restart,
+//    so the operand stays in [-1, 1] whatever the data's magnitude or sign;
+//    acc is rescaled when sigma grows, together with the softmax rescale.
 //  * Tokens past the sequence end inside the last chunk may hold any bytes
 //    (NaN codes or scales included): their logits are selected to -inf, their
 //    P and V operand bytes to zero, so they cannot reach the result.
@@ -178,7 +178,7 @@ __device__ __forceinline__ int v_lds_offset(int tok, int piece) {
 
 // Running state of one wave's online softmax over its tokens (row r = lane%16
 // of the query group): m2 = running max of the log2-scaled logits, lsum = this
-// lane's share of the running exp sum, sigma = running max V scale (the P
+// lane's share of the running exp sum, sigma = running max |V scale| (the P
 // operand's reference), acc = O^T tile (d = 16 dblk + 4b + i, query r).
 struct WaveState {
   float m2;
@@ -423,8 +423,10 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
     w.m2 = m2_new;
 
     // ---- V-scale reference and P operand ----
-    float vmax = fmax_nn(fmax_nn(fmax_nn(vs0[0], vs0[1]), fmax_nn(vs0[2], vs0[3])),
-                         fmax_nn(fmax_nn(vs1[0], vs1[1]), fmax_nn(vs1[2], vs1[3])));
+    // sigma tracks the largest |V scale|, so |P operand| <= 1 for scales of either sign.
+    auto ab = [](float x) { return __builtin_fabsf(x); };
+    float vmax = fmax_nn(fmax_nn(fmax_nn(ab(vs0[0]), ab(vs0[1])), fmax_nn(ab(vs0[2]), ab(vs0[3]))),
+                         fmax_nn(fmax_nn(ab(vs1[0]), ab(vs1[1])), fmax_nn(ab(vs1[2]), ab(vs1[3]))));
     vmax = wave_max_xor16_32(vmax);
     float acc_scale = alpha;
     if (vmax > w.sigma) {  // uniform: vmax is a wave-wide maximum
@@ -783,7 +785,8 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       w.zsum = w.zsum * alpha + zs;
       w.m2 = m2_new;
 
-      float vmax = fmax_nn(fmax_nn((float)vs[0], (float)vs[1]), fmax_nn((float)vs[2], (float)vs[3]));
+      auto ab = [](_Float16 x) { return __builtin_fabsf((float)x); };  // sigma: largest |V scale|
+      float vmax = fmax_nn(fmax_nn(ab(vs[0]), ab(vs[1])), fmax_nn(ab(vs[2]), ab(vs[3])));
       vmax = fmax_nn(vmax, row_ror8(vmax));
       vmax = wave_max_xor16_32(vmax);
       float acc_scale = alpha;
@@ -860,7 +863,9 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
       w.m2 = m2_new;
 
       // ---- V-scale reference and P operand ----
-      const f16x4 vsm = __builtin_elementwise_max(vs0, vs1);
+      // sigma: the largest |V scale|
+      const f16x4 vsm = __builtin_elementwise_max(__builtin_elementwise_abs(vs0),
+                                                  __builtin_elementwise_abs(vs1));
       float vmax = fmax_nn(fmax_nn((float)vsm[0], (float)vsm[1]), fmax_nn((float)vsm[2], (float)vsm[3]));
       vmax = wave_max_xor16_32(vmax);
       float acc_scale = alpha;
@@ -1096,6 +1101,18 @@ __device__ __forceinline__ float ld_coherent1(__amdgpu_buffer_rsrc_t rs, uint32_
   return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, kCachePolicyAgent));
 }
 
+// The release half of the cross-workgroup exchange: wait until every store
+// this thread issued has completed (vmcnt = 0; the sc1 stores are then visible
+// to all XCDs), before the barrier that precedes the arrival count.  Written as
+// inline assembly with a memory clobber, so that the compiler may not move any
+// memory access across it (the s_waitcnt builtin alone does not touch memory
+// in the compiler's model, so a store could be scheduled after it).  The
+// order store -> s_waitcnt vmcnt(0) -> s_barrier -> atomic add is checked in
+// the built assembly by a CPU test.
+__device__ __forceinline__ void drain_stores_release() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 __device__ __forceinline__ void store_bf16x4(uint16_t* dst, f32x4 o) {
   const uint32_t lo = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
   const uint32_t hi = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
@@ -1209,7 +1226,7 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   // (vmcnt drained) before the barrier, and only then is the arrival counted.
   // Acquire: the last arrival reads the partials with coherent loads issued
   // after its count returned.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  drain_stores_release();
   __syncthreads();
   if (threadIdx.x == 0)
     last_arrival = __hip_atomic_fetch_add(a.counters + sh, 1, __ATOMIC_RELAXED,
@@ -1538,7 +1555,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
 
   // Release: every thread's coherent stores complete before the barrier, and
   // only then does the workgroup count itself in.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  drain_stores_release();
   __syncthreads();
   int count[2] = {0, 0}, g_first[2] = {0, 0}, first_slot[2] = {0, 0};
 #pragma unroll

@@ -58,6 +58,18 @@ def compare(got_bf16: torch.Tensor, ref: np.ndarray, what: str, max_abs=MAX_ABS,
     return mx, mean
 
 
+_REFS = {}
+
+
+def cached_ref(key, compute):
+    """The oracle's result for `key`, computed once per test session (the largest, the
+    bandwidth workload's 1024 (s, h) units, takes about 10 s on 16 threads)."""
+    if key not in _REFS:
+        say(f"  oracle: computing the reference for {key}")
+        _REFS[key] = compute()
+    return _REFS[key]
+
+
 def units_rows(out: torch.Tensor, units, QG):
     """Rows of a [S][Hkv*QG][D] output for the given (s, h) units -> [n][QG][D]."""
     return torch.stack([out[s, h * QG:(h + 1) * QG] for s, h in units])

@@ -11,7 +11,9 @@ OracleError) when that build of the oracle disagrees with:
     the mean of V; constant V returns V; a hand-derived two-token example;
   * invariants: physical-block permutation with a consistent table, split-K
     merge == unsplit for many partition counts, V-scale linearity, an
-    isolated dominant token returns that token's V row.
+    isolated dominant token returns that token's V row, tables that share
+    blocks equal a copy with the shared blocks duplicated, scales of either
+    sign.
 
 ``test_oracle_pins.py`` runs them against the oracle; ``test_oracle_mutants.py``
 plants plausible mistakes in copies of oracle.c and checks that every planted
@@ -328,6 +330,49 @@ def pin_dominant_token(orc):
                 assert_close(got[0, h * QG + g], vt, 1e-30, f"dominant token t*={tstar}")
 
 
+def pin_aliased_blocks(orc):
+    """Tables that share physical blocks (prefix sharing: one sequence's first blocks named by
+    another's table, one block named by every entry of a table): the oracle against the
+    brute-force gather + softmax, and bit for bit against a copy in which every shared block
+    is duplicated so that no two entries name the same block."""
+    p = tiny_problem(S=4, lens=(13, 13, 6, 20), BS=4, seed=14, extra_blocks=2, max_blocks=6)
+    bt = p["bt"].clone()
+    bt[1, :3] = bt[0, :3]      # sequence 1 shares its first 3 blocks with sequence 0
+    bt[2, :2] = bt[0, :2]      # sequence 2 lies inside sequence 0's blocks
+    bt[3, :5] = bt[3, 0]       # every entry of sequence 3 names one block
+    p["bt"] = bt
+    got = run(orc, p)
+    assert_close(got, _bruteforce(p), 1e-12, "aliased bruteforce")
+    NB = p["k"].shape[0]
+    seen, extra = set(), []
+    bt2 = bt.clone()
+    for s, L in enumerate(p["sl"].tolist()):
+        for j in range(-(-L // 4)):
+            b = int(bt[s, j])
+            if b in seen:
+                bt2[s, j] = NB + len(extra)
+                extra.append(b)
+            seen.add(b)
+    assert extra
+    src = torch.tensor(extra, dtype=torch.int64)
+    q = dict(p, bt=bt2, k=torch.cat([p["k"], p["k"][src]]), v=torch.cat([p["v"], p["v"][src]]),
+             sc=torch.cat([p["sc"], p["sc"][src]]))
+    assert np.array_equal(run(orc, q), got), "duplicating shared blocks changed the output"
+
+
+def pin_signed_scales(orc):
+    """K and V scales of either sign (code * scale, whatever the sign): against the brute-force
+    gather + softmax; negating every V scale negates the output exactly."""
+    p = tiny_problem(seed=15, lens=(9, 26, 3))
+    rng = np.random.default_rng(16)
+    p["sc"] = p["sc"] * torch.from_numpy(rng.choice([-1.0, 1.0], size=p["sc"].shape).astype(np.float32))
+    got = run(orc, p)
+    assert_close(got, _bruteforce(p), 1e-12, "signed scales bruteforce")
+    sc = p["sc"].clone()
+    sc[:, :, 1, :] = -sc[:, :, 1, :]
+    assert np.array_equal(run(orc, dict(p, sc=sc)), -got)
+
+
 def pin_zero_length(orc):
     p = tiny_problem(seed=13, lens=(0, 5, 0))
     got = run(orc, p)
@@ -565,4 +610,5 @@ ALL_PINS = [pin_e4m3fn_points, pin_e4m3fn_library, pin_bf16_library, pin_dense_b
             pin_block_permutation, pin_split_merge, pin_v_scale_linearity, pin_dominant_token,
             pin_zero_length, pin_e4m3fn_encode_roundtrip, pin_e4m3fn_encode_ties_and_saturation,
             pin_e4m3fn_encode_library, pin_kv_write_quantizer, pin_partials_closed_form, pin_kv_write_matches_library_quantizer,
-            pin_f16_library, pin_tq4_golden_record, pin_tq4_matches_fp8_form, pin_tq4_constant_v]
+            pin_f16_library, pin_tq4_golden_record, pin_tq4_matches_fp8_form, pin_tq4_constant_v,
+            pin_aliased_blocks, pin_signed_scales]

@@ -27,13 +27,17 @@ def small(lens, qg=8, bs=16, hkv=2, seed=5, P=None):
 
 
 @pytest.mark.parametrize("path", PATHS)
-@pytest.mark.parametrize("name", ["w2_s32_ctx4k", "w3_s64_ragged"])
+@pytest.mark.parametrize("name", ["w2_s32_ctx4k", "w3_s64_ragged", "w4_s128_ctx8k"])
 def test_run_to_run_determinism(path, name):
+    """The same bits on repeated runs; on the bandwidth workload (32 partitions per (s, h), 1024
+    (s, h)), three runs, so that a read of partials or staged V before they are complete
+    would show as a difference."""
     inp = workloads.make_inputs(workloads.WORKLOADS[name], device="cuda")
-    say(f"[bitwise] {name} twice, {path}")
-    a = gpu_decode(inp, path=path)
-    b = gpu_decode(inp, path=path)
-    assert np.array_equal(bits(a), bits(b))
+    reps = 3 if name == "w4_s128_ctx8k" else 2
+    say(f"[bitwise] {name} {reps} times, {path}")
+    first = bits(gpu_decode(inp, path=path))
+    for _ in range(reps - 1):
+        assert np.array_equal(bits(gpu_decode(inp, path=path)), first)
 
 
 @pytest.mark.parametrize("path", PATHS)

@@ -1,31 +1,25 @@
 """HIP path vs the fp64 oracle, element by element (bf16 out: max abs <= 1e-2,
 mean abs <= 1e-3).  Needs an MI355X."""
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from gpu_util import PATHS, compare, gpu_decode, oracle_decode, say, units_rows
+from gpu_util import PATHS, cached_ref, compare, gpu_decode, oracle_decode, say
 
 pytestmark = pytest.mark.gpu
 
-# (workload, sampled (s, h) units or None for every unit)
-WORKLOAD_CASES = [
-    ("w1_tiny", None),
-    ("w2_s32_ctx4k", None),
-    ("w3_s64_ragged", None),
-    ("w4_s128_ctx8k", 64),
-    ("w5_s16_long", None),
-]
+WORKLOADS = ["w1_tiny", "w2_s32_ctx4k", "w3_s64_ragged", "w4_s128_ctx8k", "w5_s16_long"]
 
 
-_REF_CACHE = {}
-
-
+@pytest.mark.parametrize("name", WORKLOADS)
 @pytest.mark.parametrize("path", PATHS)
-@pytest.mark.parametrize("name,sample", WORKLOAD_CASES, ids=[c[0] for c in WORKLOAD_CASES])
-def test_workload_parity(name, sample, path):
+def test_workload_parity(path, name):
+    """Every output element of each workload, both paths, against one oracle reference per
+    workload (the bandwidth workload w4 included: 1024 (s, h) units x 8 rows x 128)."""
     wl = workloads.WORKLOADS[name]
     say(f"[parity] {name} {path}: generating on cuda:0")
     inp = workloads.make_inputs(wl, device="cuda")
@@ -33,22 +27,8 @@ def test_workload_parity(name, sample, path):
         f"BS={wl.kv_block_size} P={inp.num_partitions} G={wl.tile_groups_per_partition} "
         f"NB={inp.num_blocks} maxL={int(inp.seq_lens.max())}")
     out = gpu_decode(inp, path=path)
-    QG = wl.query_group_size
-    if sample is None:
-        if name not in _REF_CACHE:
-            _REF_CACHE.clear()
-            _REF_CACHE[name] = oracle_decode(inp)
-        compare(out, _REF_CACHE[name], f"{name} {path}")
-    else:
-        rng = np.random.default_rng(wl.seed)
-        all_units = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_kv_heads)]
-        idx = rng.choice(len(all_units), size=sample, replace=False)
-        units = [all_units[i] for i in sorted(idx)]
-        ref = oracle_decode(inp, units=units)
-        compare(units_rows(out, units, QG), ref, f"{name} {path} ({sample} sampled units)")
-        # at full size: every output finite and bounded by the largest |V| value
-        o = out.float()
-        assert torch.isfinite(o).all()
+    ref = cached_ref(("fp8", name), lambda: oracle_decode(inp))
+    compare(out, ref, f"{name} {path}")
 
 
 SWEEP_LENS = (1, 15, 16, 17, 31, 32, 33, 255, 256, 257, 300, 513, 1000)
@@ -234,3 +214,27 @@ def test_even_split_sequence_limit(S):
     inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=3)
     say(f"[even] S={S}")
     _fused_vs_oracle(inp, S, 1, 8, 32, maxlen, 3, what=f"fused, S={S}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_signed_scales(path):
+    """K and V scales of either sign (the format reads code * scale, nothing makes a scale
+    non-negative): a random half of them negated, and a batch whose V scales are all negative,
+    against the oracle."""
+    lens = (1, 40, 333, 1000)
+    wl = workloads.small_workload(name="signed", num_seqs=len(lens), num_kv_heads=2,
+                                  query_group_size=8, kv_block_size=16, seq_lens=lens, seed=47)
+    inp = workloads.make_inputs(wl, device="cuda", seq_lens=lens, num_partitions=4)
+    g = torch.Generator(device="cuda").manual_seed(48)
+    flip = torch.where(torch.rand(inp.kv_scales.shape, generator=g, device="cuda") < 0.5, -1.0, 1.0)
+    mixed = dataclasses.replace(inp, kv_scales=inp.kv_scales * flip)
+    say(f"[signed scales] {path}: half of the K and V scales negated")
+    compare(gpu_decode(mixed, path=path), oracle_decode(mixed), f"{path} mixed-sign scales")
+    sc = inp.kv_scales.clone()
+    sc[:, :, 1, :] = -sc[:, :, 1, :]
+    neg = dataclasses.replace(inp, kv_scales=sc)
+    say(f"[signed scales] {path}: every V scale negative")
+    out = gpu_decode(neg, path=path)
+    compare(out, oracle_decode(neg), f"{path} negative V scales")
+    # negating every V scale negates the output exactly
+    assert torch.equal(out.float(), -gpu_decode(inp, path=path).float())

@@ -11,7 +11,7 @@ import torch
 import oracle
 import paged_gqa_decode_amd as tq
 import workloads
-from gpu_util import ORACLE_THREADS, PATHS, compare, say, units_rows
+from gpu_util import ORACLE_THREADS, PATHS, cached_ref, compare, say
 
 pytestmark = pytest.mark.gpu
 
@@ -58,31 +58,63 @@ def test_tq4_small_sweep(qg, bs, path):
         compare(out, oracle_tq4(inp), f"tq4 {path} qg{qg} bs{bs} G{G} P{P}")
 
 
-WORKLOAD_CASES = [("w2_s32_ctx4k", None), ("w3_s64_ragged", None), ("w4_s128_ctx8k", 64),
-                  ("w5_s16_long", None)]
-_REF = {}
+WORKLOADS = ["w2_s32_ctx4k", "w3_s64_ragged", "w4_s128_ctx8k", "w5_s16_long"]
 
 
+@pytest.mark.parametrize("name", WORKLOADS)
 @pytest.mark.parametrize("path", PATHS)
-@pytest.mark.parametrize("name,sample", WORKLOAD_CASES, ids=[c[0] for c in WORKLOAD_CASES])
-def test_tq4_workload_parity(name, sample, path):
+def test_tq4_workload_parity(path, name):
+    """Every output element of each workload in the 4-bit format, both paths, against one
+    oracle reference per workload (w4: 1024 (s, h) units x 8 rows x 128)."""
     wl = workloads.WORKLOADS[name]
     say(f"[tq4 parity] {name} {path}: generating")
     inp = workloads.make_inputs_tq4(wl, device="cuda")
     out = gpu_tq4(inp, path)
-    if sample is None:
-        if name not in _REF:
-            _REF.clear()
-            _REF[name] = oracle_tq4(inp)
-        compare(out, _REF[name], f"tq4 {name} {path}")
-    else:
-        rng = np.random.default_rng(wl.seed)
-        all_units = [(s, h) for s in range(wl.num_seqs) for h in range(wl.num_kv_heads)]
-        idx = rng.choice(len(all_units), size=sample, replace=False)
-        units = [all_units[i] for i in sorted(idx)]
-        compare(units_rows(out, units, wl.query_group_size), oracle_tq4(inp, units=units),
-                f"tq4 {name} {path} ({sample} sampled units)")
-        assert torch.isfinite(out.float()).all()
+    ref = cached_ref(("tq4", name), lambda: oracle_tq4(inp))
+    compare(out, ref, f"tq4 {name} {path}")
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_tq4_bandwidth_workload_repeat_runs(path):
+    """The bandwidth workload (32 partitions per (s, h) on the two-kernel path, the even split
+    over 2048 waves on the fused one) decoded three times: the same bits each time."""
+    inp = workloads.make_inputs_tq4(workloads.WORKLOADS["w4_s128_ctx8k"], device="cuda")
+    say(f"[tq4 bitwise] w4 three times, {path}")
+    first = bits(gpu_tq4(inp, path))
+    for _ in range(2):
+        assert np.array_equal(bits(gpu_tq4(inp, path)), first)
+
+
+@pytest.mark.parametrize("path", PATHS)
+def test_tq4_signed_metadata(path):
+    """fp16 K norms and V scales of either sign (sign bits set on a random half), against the
+    oracle; every V scale negative with zero points 0 negates the output exactly."""
+    inp = _small((1, 40, 333, 1000), qg=16, bs=32, P=4, seed=63)
+    Hkv, BS = inp.wl.num_kv_heads, inp.wl.kv_block_size
+    data_bytes = Hkv * BS * 128
+    meta = inp.cache[:, data_bytes:].contiguous().view(torch.int16).view(-1, Hkv, 3, BS)
+    g = torch.Generator(device="cuda").manual_seed(64)
+    signs = (torch.rand(meta[:, :, :2].shape, generator=g, device="cuda") < 0.5).to(torch.int16)
+    mixed_meta = meta.clone()
+    mixed_meta[:, :, :2] ^= signs * -32768  # flip the fp16 sign bit of K norm / V scale
+    cache = inp.cache.clone()
+    cache[:, data_bytes:] = mixed_meta.view(torch.uint8).view(cache.shape[0], -1)
+    mixed = dataclasses.replace(inp, cache=cache)
+    say(f"[tq4 signed metadata] {path}: half the K norms and V scales negated")
+    compare(gpu_tq4(mixed, path), oracle_tq4(mixed), f"tq4 {path} mixed-sign metadata")
+    neg_meta = meta.clone()
+    neg_meta[:, :, 1] |= -32768  # every V scale negative
+    neg_meta[:, :, 2] = 0        # zero points 0: v = -|scale| * index
+    pos_meta = meta.clone()
+    pos_meta[:, :, 2] = 0
+    outs = []
+    for m in (pos_meta, neg_meta):
+        c = inp.cache.clone()
+        c[:, data_bytes:] = m.view(torch.uint8).view(c.shape[0], -1)
+        x = dataclasses.replace(inp, cache=c)
+        outs.append(gpu_tq4(x, path))
+        compare(outs[-1], oracle_tq4(x), f"tq4 {path} V scales {'negative' if m is neg_meta else 'positive'}")
+    assert torch.equal(outs[1].float(), -outs[0].float())
 
 
 def _small(lens, qg=8, bs=16, hkv=2, seed=5, P=None):

@@ -29,7 +29,8 @@
  *   - Every pointer argument is a DEVICE pointer (HIP device memory) owned
  *     by the caller, except `ext` and `partials`, which point to HOST structs
  *     read during the call only.  The library allocates nothing, keeps no
- *     state other than a thread-local last HIP error, never synchronizes, and
+ *     state other than a thread-local last HIP error (and, for
+ *     tq_decode_fused_static only, its static scratch), never synchronizes, and
  *     enqueues its kernels on `stream` (a hipStream_t; NULL = the null
  *     stream).  All calls are asynchronous and reentrant.
  *   - q, k_cache, v_cache, kv_scales, the partial buffers and out must be
@@ -64,6 +65,9 @@ extern "C" {
 #define TQ_ABI_VERSION 1
 #define TQ_HEAD_DIM 128
 #define TQ_TOKENS_PER_TILE_GROUP 256 /* 16 tiles of 16 tokens */
+/* Device memory per GPU of tq_decode_fused_static's scratch, and its counter region. */
+#define TQ_STATIC_SCRATCH_BYTES ((size_t)8 << 20)
+#define TQ_STATIC_COUNTER_BYTES ((size_t)1 << 20)
 
 typedef enum {
   TQ_OK = 0,
@@ -74,7 +78,9 @@ typedef enum {
                              or a size that overflows the index types */
   TQ_ERR_COVERAGE = 5,    /* max_seq_len < 0, > P*G*256 or > max_blocks_per_seq*BS */
   TQ_ERR_SCALE = 6,       /* softmax_scale not finite or <= 0 */
-  TQ_ERR_HIP = 7          /* a HIP launch failed; see tq_last_hip_error() */
+  TQ_ERR_HIP = 7,         /* a HIP launch failed; see tq_last_hip_error() */
+  TQ_ERR_SCRATCH = 8      /* tq_decode_fused_static: the batch needs more than the static
+                             scratch holds */
 } tq_status;
 
 /* Sizes that a decode step needs besides the named arguments (host struct). */
@@ -163,9 +169,13 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
  * merges.
  *   out        bf16 [S][Hkv*QG][128], fully overwritten (L_s = 0 gives zeros)
  *   workspace  NULL, or device memory of workspace_bytes bytes, 16-byte
- *              aligned; ZERO-FILLED before its first use (it holds arrival
- *              counters that every call leaves at zero again).  Calls that run
- *              concurrently must not share a workspace.
+ *              aligned; ZERO-FILLED before its first use.  Its first
+ *              round_up(4 * S * Hkv, 256) bytes hold arrival counters that every
+ *              call leaves at zero again; the partials follow them, so a call
+ *              with another S * Hkv would find its counters where an earlier
+ *              call left partials: reuse a workspace only for calls with the
+ *              same num_seqs and num_kv_heads, or zero-fill it again first.
+ *              Calls that run concurrently must not share a workspace.
  * tile_groups_per_partition and ext->num_partitions bound the context as for
  * tq_decode (coverage check); the split itself is the library's choice: a
  * function of the sizes, ext->max_seq_len, workspace_bytes and the device-side
@@ -183,6 +193,35 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
                           int32_t tile_groups_per_partition, float softmax_scale,
                           const tq_extent* ext, void* workspace, size_t workspace_bytes,
                           void* stream);
+
+/*
+ * tq_decode_fused_static -- tq_decode_fused for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops and harnesses
+ * that forbid hipMalloc): the same decode, with the library's own static
+ * scratch in place of the caller's workspace.  The split, and so every output
+ * bit, is the one tq_decode_fused takes with a zero-filled workspace of
+ * tq_fused_workspace_bytes() bytes.
+ *   Scratch: TQ_STATIC_SCRATCH_BYTES (8 MiB) of device memory per GPU that the
+ *   library runs on, held until the process ends: arrival counters in the
+ *   first TQ_STATIC_COUNTER_BYTES (1 MiB, 4 B per (s, h)), workgroup partials
+ *   after them.  Its device address is taken once per GPU, on the first call
+ *   on it (the calling thread's current device must be the one `stream`
+ *   belongs to); that call also enqueues the scratch's zero fill on `stream`.
+ *   Every call leaves the counters at zero; the partials keep the last call's
+ *   contents.  All calls on one GPU share its scratch: calls that overlap in
+ *   time on one GPU (other streams, other threads) race and give wrong results.
+ *   This entry point allocates nothing and frees nothing.
+ *   Returns TQ_ERR_SCRATCH, before anything is enqueued, when the batch needs
+ *   more than the scratch holds: more than 262144 (sequence, kv head) pairs,
+ *   or more than 7 MiB of partials (the even split needs at most 4.1 MiB).
+ * Other arguments and errors are those of tq_decode_fused.
+ */
+tq_status tq_decode_fused_static(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                 const float* kv_scales, const int32_t* block_tables,
+                                 const int32_t* seq_lens, void* out, int32_t num_kv_heads,
+                                 int32_t query_group_size, int32_t kv_block_size,
+                                 int32_t tile_groups_per_partition, float softmax_scale,
+                                 const tq_extent* ext, void* stream);
 
 /* Workspace bytes for the fastest split of tq_decode_fused at these sizes (0:
  * it needs none).  Depends on num_seqs, max_seq_len, num_kv_heads and

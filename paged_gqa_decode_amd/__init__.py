@@ -32,9 +32,12 @@ SUPPORTED_QUERY_GROUP_SIZES = (6, 8, 16)
 SUPPORTED_KV_BLOCK_SIZES = (16, 32)
 
 TQ_OK, TQ_ERR_NULL, TQ_ERR_MISALIGNED, TQ_ERR_UNSUPPORTED, TQ_ERR_SHAPE, TQ_ERR_COVERAGE, \
-    TQ_ERR_SCALE, TQ_ERR_HIP = range(8)
+    TQ_ERR_SCALE, TQ_ERR_HIP, TQ_ERR_SCRATCH = range(9)
+STATIC_SCRATCH_BYTES = 8 << 20
+STATIC_COUNTER_BYTES = 1 << 20
 
-EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_decode_fused", "tq_fused_workspace_bytes",
+EXPORTED_SYMBOLS = ("tq_decode", "tq_decode_reduce", "tq_decode_fused", "tq_decode_fused_static",
+                    "tq_fused_workspace_bytes",
                     "tq4_decode", "tq4_decode_fused", "tq4_block_bytes", "tq_kv_write",
                     "tq_partials_bytes", "tq_status_str", "tq_last_hip_error", "tq_abi_version")
 
@@ -78,6 +81,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq_decode_fused.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float,
                                     ctypes.POINTER(Extent), P, ctypes.c_size_t, P]
     lib.tq_decode_fused.restype = ctypes.c_int
+    lib.tq_decode_fused_static.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, ctypes.c_float,
+                                           ctypes.POINTER(Extent), P]
+    lib.tq_decode_fused_static.restype = ctypes.c_int
     lib.tq4_decode.argtypes = [P, P, P, P, P, ctypes.POINTER(PartialsStruct), i32, i32, i32, i32,
                                ctypes.c_float, ctypes.POINTER(Extent), P]
     lib.tq4_decode.restype = ctypes.c_int
@@ -315,6 +321,29 @@ def tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
                              ctypes.byref(ext), ws_ptr, ws_bytes, _stream(stream))
     if st != TQ_OK:
         raise TqError(st, "tq_decode_fused")
+
+
+def tq_decode_fused_static(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
+                           num_kv_heads: int, query_group_size: int, kv_block_size: int,
+                           tile_groups_per_partition: int, softmax_scale: float, *,
+                           num_partitions: int, max_seq_len: int, num_blocks: Optional[int] = None,
+                           stream=None) -> None:
+    """Enqueue the one-launch decode with the library's static scratch (C ABI
+    tq_decode_fused_static): nothing is allocated, here or in the library."""
+    lib = load_library()
+    Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
+    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS)
+    _expect(out, "out", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
+    nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
+    _expect_pool(nb, (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_scales, "kv_scales"))
+    ptrs = [_dev(t, n) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
+                                    (kv_scales, "kv_scales"), (block_tables, "block_tables"),
+                                    (seq_lens, "seq_lens"), (out, "out"))]
+    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    st = lib.tq_decode_fused_static(*ptrs, Hkv, QG, BS, int(tile_groups_per_partition),
+                                    float(softmax_scale), ctypes.byref(ext), _stream(stream))
+    if st != TQ_OK:
+        raise TqError(st, "tq_decode_fused_static")
 
 
 def tq4_block_bytes(num_kv_heads: int, kv_block_size: int) -> int:

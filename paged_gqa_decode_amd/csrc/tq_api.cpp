@@ -150,17 +150,21 @@ tq_status run_partition(const tq::StreamArgs& st, const int32_t* seq_lens,
 
 // The fused decode of either format, after the checks: the even split when
 // it applies and the workspace holds it, else workgroups per (s, h).
+// counters > 0: the workspace's counters take a fixed region of that many bytes
+// (the static scratch) instead of the first counter_bytes(S * Hkv).
 tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out,
                     int32_t num_kv_heads, int32_t query_group_size, int32_t kv_block_size,
                     const tq_extent* ext, void* workspace, size_t workspace_bytes, bool tq4,
-                    void* stream) {
+                    void* stream, size_t counters = 0) {
   if (!aligned16(out) || (workspace && !aligned16(workspace))) return TQ_ERR_MISALIGNED;
   const hipError_t v = maybe_validate(st, seq_lens, kv_block_size, ext, stream);
   if (v != hipSuccess) return hip_status(v);
   const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
   const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
-  if (flat_groups > 0 && workspace &&
-      workspace_bytes >= tq::flat_workspace_bytes(seq_heads, flat_groups, query_group_size)) {
+  const size_t cb = counters ? counters : tq::counter_bytes(seq_heads);
+  const bool counters_fit = workspace && cb >= tq::counter_bytes(seq_heads) && workspace_bytes >= cb;
+  if (flat_groups > 0 && counters_fit &&
+      workspace_bytes - cb >= tq::flat_partial_bytes(flat_groups, query_group_size)) {
     tq::FlatArgs f{};
     f.st = st;
     f.seq_lens = seq_lens;
@@ -168,12 +172,12 @@ tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out
     f.len_cap = ext->max_seq_len;
     f.num_seqs = ext->num_seqs;
     f.n_groups = flat_groups;
-    tq::bind_flat_workspace(&f, workspace, seq_heads, query_group_size);
+    tq::bind_flat_workspace(&f, workspace, seq_heads, query_group_size, counters);
     return hip_status(tq::launch_flat(f, query_group_size, kv_block_size, tq4,
                                       static_cast<hipStream_t>(stream)));
   }
   const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size,
-                                            workspace ? workspace_bytes : 0);
+                                            workspace ? workspace_bytes : 0, counters);
   tq::FusedArgs a{};
   a.st = st;
   a.seq_lens = seq_lens;
@@ -182,7 +186,7 @@ tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out
   a.splits = plan.splits;
   a.counters = nullptr;
   a.ws_o = a.ws_m = a.ws_l = nullptr;
-  if (plan.splits > 1) tq::bind_fused_workspace(&a, workspace, seq_heads, query_group_size);
+  if (plan.splits > 1) tq::bind_fused_workspace(&a, workspace, seq_heads, query_group_size, counters);
   return hip_status(tq::launch_fused(a, ext->num_seqs, plan.waves, query_group_size, kv_block_size,
                                      tq4, static_cast<hipStream_t>(stream)));
 }
@@ -224,6 +228,38 @@ tq_status tq_decode_fused(const void* q, const uint8_t* k_cache, const uint8_t* 
   if (rc != TQ_OK) return rc;
   return run_fused(st, seq_lens, out, num_kv_heads, query_group_size, kv_block_size, ext,
                    workspace, workspace_bytes, false, stream);
+}
+
+static_assert(tq::kStaticScratchBytes == TQ_STATIC_SCRATCH_BYTES &&
+                  tq::kStaticCounterBytes == TQ_STATIC_COUNTER_BYTES,
+              "the header states the static scratch sizes");
+
+tq_status tq_decode_fused_static(const void* q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                 const float* kv_scales, const int32_t* block_tables,
+                                 const int32_t* seq_lens, void* out, int32_t num_kv_heads,
+                                 int32_t query_group_size, int32_t kv_block_size,
+                                 int32_t tile_groups_per_partition, float softmax_scale,
+                                 const tq_extent* ext, void* stream) {
+  if (!out) return TQ_ERR_NULL;
+  tq::StreamArgs st{};
+  int32_t E = 0;
+  tq_status rc = check_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_kv_heads,
+                              query_group_size, kv_block_size, tile_groups_per_partition,
+                              softmax_scale, ext, &st, &E);
+  if (rc != TQ_OK) return rc;
+  // The split tq_decode_fused takes with a workspace of tq_fused_workspace_bytes():
+  // its counters must fit the fixed counter region, its partials the rest.
+  const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
+  const size_t need = tq_fused_workspace_bytes(ext, num_kv_heads, query_group_size);
+  const size_t cb = tq::counter_bytes(seq_heads);
+  const size_t partials = need > cb ? need - cb : 0;
+  if (cb > tq::kStaticCounterBytes || partials > tq::kStaticScratchBytes - tq::kStaticCounterBytes)
+    return TQ_ERR_SCRATCH;
+  void* scratch = nullptr;
+  const hipError_t e = tq::static_scratch(&scratch, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e);
+  return run_fused(st, seq_lens, out, num_kv_heads, query_group_size, kv_block_size, ext, scratch,
+                   tq::kStaticCounterBytes + partials, false, stream, tq::kStaticCounterBytes);
 }
 
 tq_status tq4_decode(const void* q_rot, const uint8_t* kv_cache, const float* centroids,
@@ -350,6 +386,7 @@ const char* tq_status_str(tq_status status) {
     case TQ_ERR_COVERAGE: return "max_seq_len is negative or exceeds num_partitions*256*G or max_blocks_per_seq*kv_block_size";
     case TQ_ERR_SCALE: return "softmax_scale must be finite and > 0";
     case TQ_ERR_HIP: return "HIP launch failed (see tq_last_hip_error)";
+    case TQ_ERR_SCRATCH: return "the batch needs more than the library's static scratch holds (tq_decode_fused_static)";
   }
   return "unknown status";
 }

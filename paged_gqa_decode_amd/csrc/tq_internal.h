@@ -78,12 +78,21 @@ struct FusedPlan {
   int splits;
 };
 
+// A workspace holds the arrival counters first (4 B per (s, h), rounded up to
+// 256 B: counter_bytes), then the partials.  `counters` > 0 in the functions
+// below gives the counters a fixed region of that many bytes instead (the
+// library's static scratch, shared by calls of any size, so that one call's
+// partials never land on another call's counters).
+size_t counter_bytes(int64_t seq_heads);
 // Plan for these sizes with `ws_bytes` of workspace (0: none), and the
 // workspace bytes a plan needs (counters first, at a fixed offset).
-FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes);
+FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes,
+                     size_t counters = 0);
+size_t fused_partial_bytes(int64_t seq_heads, int splits, int query_group_size);
 size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size);
 // Carve the workspace for `splits` into the pointers of `a`.
-void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size);
+void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size,
+                          size_t counters = 0);
 
 // Fused decode over one flat work list (the live 32-token chunks of every (s, h)
 // in (s, h, chunk) order) dealt evenly to the waves of n_groups
@@ -112,8 +121,19 @@ int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
 // these sizes, or 0 when the per-partition kernel runs instead.
 int plan_partition_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
                                int partition_tokens, bool tq4);
+size_t flat_partial_bytes(int n_groups, int query_group_size);
 size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size);
-void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size);
+void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size,
+                         size_t counters = 0);
+
+// The library's static scratch for tq_decode_fused_static: kStaticScratchBytes
+// of device memory per GPU, the first kStaticCounterBytes of them the arrival
+// counters.  static_scratch() returns this device's copy (the address comes
+// from hipGetSymbolAddress on the first call on each device, which also
+// enqueues its zero fill on `stream`).
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
+constexpr size_t kStaticCounterBytes = size_t(1) << 20;
+hipError_t static_scratch(void** ptr, hipStream_t stream);
 
 struct ReduceArgs {
   const float* o;

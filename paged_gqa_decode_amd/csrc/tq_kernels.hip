@@ -43,9 +43,18 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "tq_internal.h"
 
 namespace tq {
+
+// The static scratch of tq_decode_fused_static (device memory each GPU holds
+// until the process ends): arrival counters in the first kStaticCounterBytes,
+// workgroup partials after them.  Host code never passes this name to a
+// kernel; it takes the device address from static_scratch().
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
@@ -1926,7 +1935,43 @@ __global__ __launch_bounds__(64) void tq_validate_kernel(ValidateArgs a) {
   }
 }
 
+// Zero n16 16-byte words at p (a grid-stride loop, every access below n16).
+__global__ __launch_bounds__(256) void tq_zero_fill_kernel(u32x4* p, uint32_t n16) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n16; i += gridDim.x * 256u)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 }  // namespace
+
+hipError_t static_scratch(void** ptr, hipStream_t stream) {
+  // One device address per GPU, taken once with that GPU current; the first
+  // call on a GPU also enqueues the zero fill of its copy on `stream`, ahead
+  // of the caller's kernel (the counters must start at zero; every call
+  // leaves them at zero again).
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* dev_ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!dev_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    static_assert(kStaticScratchBytes % 16 == 0 && kStaticScratchBytes / 16 < (size_t(1) << 32),
+                  "scratch size");
+    hipLaunchKernelGGL(tq_zero_fill_kernel, dim3(256), dim3(256), 0, stream, static_cast<u32x4*>(p),
+                       (uint32_t)(kStaticScratchBytes / 16));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    dev_ptr[dev] = p;
+  }
+  *ptr = dev_ptr[dev];
+  return hipSuccess;
+}
 
 // Run LAUNCH_T<QG, BS, TQ4>(args...) for the runtime sizes and format.
 #define TQ_DISPATCH(LAUNCH_T, qg, bs, tq4, ...)                                              \

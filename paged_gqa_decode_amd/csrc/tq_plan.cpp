@@ -39,17 +39,25 @@ bool partials_nontemporal(int64_t num_seqs, int num_kv_heads, int num_partitions
   return !tq4 && bytes >= kMinBytes;
 }
 
-size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size) {
+size_t counter_bytes(int64_t seq_heads) { return round256((size_t)seq_heads * 4); }
+
+size_t fused_partial_bytes(int64_t seq_heads, int splits, int query_group_size) {
   if (splits <= 1) return 0;
   const size_t rows = (size_t)seq_heads * splits * query_group_size;
-  return round256((size_t)seq_heads * 4) + round256(rows * D * 4) + 2 * round256(rows * 4);
+  return round256(rows * D * 4) + 2 * round256(rows * 4);
 }
 
-void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size) {
+size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size) {
+  if (splits <= 1) return 0;
+  return counter_bytes(seq_heads) + fused_partial_bytes(seq_heads, splits, query_group_size);
+}
+
+void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_group_size,
+                          size_t counters) {
   const size_t rows = (size_t)seq_heads * a->splits * query_group_size;
   uint8_t* p = static_cast<uint8_t*>(ws);
   a->counters = reinterpret_cast<int32_t*>(p);
-  p += round256((size_t)seq_heads * 4);
+  p += counters ? counters : counter_bytes(seq_heads);
   a->ws_o = reinterpret_cast<float*>(p);
   p += round256(rows * D * 4);
   a->ws_m = reinterpret_cast<float*>(p);
@@ -57,7 +65,8 @@ void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_g
   a->ws_l = reinterpret_cast<float*>(p);
 }
 
-FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes) {
+FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes,
+                     size_t counters) {
   // About kTargetWaves waves on the device (one resident round at two waves
   // per SIMD; measured best across the workloads), each with at least one tile
   // group of work; at most 8 waves per workgroup (the register budget of
@@ -72,7 +81,11 @@ FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, s
   plan.waves = (int)(waves_per_sh < 8 ? waves_per_sh : 8);
   int64_t splits = (waves_per_sh + plan.waves - 1) / plan.waves;
   if (splits > kFusedMaxSplits) splits = kFusedMaxSplits;
-  while (splits > 1 && fused_workspace_bytes(seq_heads, (int)splits, query_group_size) > ws_bytes) --splits;
+  // The counters take their fixed region (counters > 0) or the first bytes the sizes need.
+  const size_t cb = counters ? counters : counter_bytes(seq_heads);
+  while (splits > 1 && (cb < counter_bytes(seq_heads) ||
+                        cb + fused_partial_bytes(seq_heads, (int)splits, query_group_size) > ws_bytes))
+    --splits;
   plan.splits = (int)splits;
   return plan;
 }
@@ -105,16 +118,21 @@ int plan_partition_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_l
   return plan_flat_groups(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
 }
 
-size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size) {
+size_t flat_partial_bytes(int n_groups, int query_group_size) {
   const size_t rows = (size_t)2 * n_groups * query_group_size;
-  return round256((size_t)seq_heads * 4) + round256(rows * D * 4) + 2 * round256(rows * 4);
+  return round256(rows * D * 4) + 2 * round256(rows * 4);
 }
 
-void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size) {
+size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size) {
+  return counter_bytes(seq_heads) + flat_partial_bytes(n_groups, query_group_size);
+}
+
+void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size,
+                         size_t counters) {
   const size_t rows = (size_t)2 * a->n_groups * query_group_size;
   uint8_t* p = static_cast<uint8_t*>(ws);
   a->counters = reinterpret_cast<int32_t*>(p);
-  p += round256((size_t)seq_heads * 4);
+  p += counters ? counters : counter_bytes(seq_heads);
   a->ws_o = reinterpret_cast<float*>(p);
   p += round256(rows * D * 4);
   a->ws_m = reinterpret_cast<float*>(p);

@@ -56,8 +56,8 @@ def test_every_header_is_covered():
 
 def test_abi_version_and_status_strings(lib):
     assert tq.abi_version() == 1
-    for st in range(8):
-        assert tq.status_str(st)
+    for st in range(9):
+        assert tq.status_str(st) != "unknown status"
     assert tq.status_str(99) == "unknown status"
     assert tq.last_hip_error() == 0
 
@@ -373,3 +373,21 @@ def test_binding_refuses_wrong_tq4_and_writer_layouts():
         tq.tq_kv_write(rows, rows, torch.zeros((5,), dtype=torch.int32), k, k, sc[:, :, :1].contiguous())
     with pytest.raises(TypeError, match="v_new"):
         tq.tq_kv_write(rows, rows.float(), torch.zeros((5,), dtype=torch.int32), k, k, sc)
+
+
+def test_static_entry_point_rejects_before_touching_the_device(lib):
+    """tq_decode_fused_static: the argument checks of tq_decode_fused, then TQ_ERR_SCRATCH for a
+    batch whose counters (4 B per (s, h)) pass the static scratch's 1 MiB counter region; none
+    of these calls reaches the device."""
+    assert tq.STATIC_SCRATCH_BYTES == 8 << 20 and tq.STATIC_COUNTER_BYTES == 1 << 20
+
+    def call(S, Hkv, ptrs=None, QG=8, scale=0.088, maxlen=64):
+        ext = tq.Extent(S, 8, 4, 1, maxlen, 128)
+        return lib.tq_decode_fused_static(*(ptrs or [A] * 7), Hkv, QG, 16, 1, scale,
+                                          ctypes.byref(ext), None)
+
+    assert call(2, 2, ptrs=[A] * 6 + [0]) == tq.TQ_ERR_NULL
+    assert call(2, 2, QG=7) == tq.TQ_ERR_UNSUPPORTED
+    assert call(2, 2, scale=0.0) == tq.TQ_ERR_SCALE
+    assert call(1024, 257) == tq.TQ_ERR_SCRATCH      # 263168 (s, h) counters > 1 MiB
+    assert call(2048, 129) == tq.TQ_ERR_SCRATCH      # the per-(s, h) plan, same bound

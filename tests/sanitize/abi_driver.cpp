@@ -86,6 +86,28 @@ void run_valid(const Case& c) {
       g_log.ws = nullptr;
     }
   }
+  // The entry point that allocates nothing: the static scratch (host memory in the stand-in).
+  {
+    const int launches = g_log.fused + g_log.flat;
+    EXPECT(tq_decode_fused_static(fake(1), (const uint8_t*)fake(2), (const uint8_t*)fake(3),
+                                  (const float*)fake(4), (const int32_t*)fake(5),
+                                  (const int32_t*)fake(6), fake(7), c.Hkv, c.QG, c.BS, c.G, scale,
+                                  &e, nullptr) == TQ_OK);
+    EXPECT(g_log.fused + g_log.flat == launches + 1);
+    g_log.ws = nullptr;
+  }
+}
+
+void run_static_limits() {
+  // More (sequence, kv head) pairs than the static counter region holds: refused, no launch.
+  const Case c = {1024, 257, 8, 16, 1, 2, 300, 64, 32};
+  const tq_extent e = extent(c);
+  const LaunchLog before = g_log;
+  EXPECT(tq_decode_fused_static(fake(1), (const uint8_t*)fake(2), (const uint8_t*)fake(3),
+                                (const float*)fake(4), (const int32_t*)fake(5),
+                                (const int32_t*)fake(6), fake(7), c.Hkv, c.QG, c.BS, c.G, 0.088f,
+                                &e, nullptr) == TQ_ERR_SCRATCH);
+  EXPECT(g_log.fused == before.fused && g_log.flat == before.flat && g_log.scratch == before.scratch);
 }
 
 void run_invalid() {
@@ -166,6 +188,7 @@ int main() {
   };
   for (const Case& c : valid) run_valid(c);
   run_invalid();
+  run_static_limits();
   setenv("TQ_VALIDATE", "1", 1);
   const int v0 = g_log.validate;
   run_valid(valid[1]);

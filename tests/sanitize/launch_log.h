@@ -3,7 +3,7 @@
 #include <stddef.h>
 
 struct LaunchLog {
-  int partition = 0, fused = 0, flat = 0, reduce = 0, kv_write = 0, validate = 0;
+  int partition = 0, fused = 0, flat = 0, reduce = 0, kv_write = 0, validate = 0, scratch = 0;
   bool last_tq4 = false;
   const void* ws = nullptr;  // the workspace the driver passed, to check the carving
   size_t ws_bytes = 0;

@@ -88,6 +88,18 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t) {
   return hipSuccess;
 }
 
+// The static scratch of tq_decode_fused_static: real host memory of the same size, recorded
+// as the workspace so that the launch stand-ins check the carving against it.
+hipError_t static_scratch(void** ptr, hipStream_t) {
+  static uint8_t* mem = static_cast<uint8_t*>(aligned_alloc(256, kStaticScratchBytes));
+  require(mem != nullptr, "scratch stand-in");
+  ++g_log.scratch;
+  g_log.ws = mem;
+  g_log.ws_bytes = kStaticScratchBytes;
+  *ptr = mem;
+  return hipSuccess;
+}
+
 hipError_t launch_validate(const ValidateArgs& a, hipStream_t) {
   ++g_log.validate;
   require(a.num_seqs >= 1 && a.bt && a.seq_lens, "validate args");

@@ -10,8 +10,9 @@ definition and the readings taken where that page is silent.
 
 Array conventions (numpy, C-contiguous):
   q_bits        uint16 [S][Hkv*QG][D]   bfloat16 bit patterns
-  k_codes       uint8  [NB][Hkv][BS][D] OCP e4m3fn codes
-  v_codes       uint8  [NB][Hkv][BS][D]
+  k_codes       uint8  [NB][Hkv][BS][D] OCP e4m3fn codes (layout "head"), or
+                       [NB][BS][Hkv][D] (layout "slot", the page's data-region order)
+  v_codes       uint8  the same as k_codes
   kv_scales     float32 [NB][Hkv][2][BS] (field 0 = K, field 1 = V)
   block_tables  int32  [S][max_blocks_per_seq]
   seq_lens      int32  [S]
@@ -36,6 +37,9 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 ORC_OK, ORC_ERR_ARGS, ORC_ERR_BLOCK, ORC_ERR_NOMEM = 0, 1, 2, 3
+# Order of the K / V rows inside a cache block: head-major [Hkv][BS] or slot-major [BS][Hkv]
+# (the page's data region).
+LAYOUTS = {"head": 0, "slot": 1}
 
 
 class OracleError(RuntimeError):
@@ -65,35 +69,36 @@ class Oracle:
         lib.orc_dec_bf16.argtypes = [ctypes.c_uint16]
         lib.orc_dec_bf16.restype = ctypes.c_double
         lib.orc_decode.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
-                                   ctypes.c_float, P, i32, P, i32]
+                                   ctypes.c_float, i32, P, i32, P, i32]
         lib.orc_decode.restype = ctypes.c_int
         lib.orc_partials.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
-                                     ctypes.c_float, i32, i32, P, P, P]
+                                     ctypes.c_float, i32, i32, i32, P, P, P]
         lib.orc_partials.restype = ctypes.c_int
         lib.orc_merge.argtypes = [P, P, P, P, i32, i32, i32, i32, i32, i32, P]
         lib.orc_merge.restype = ctypes.c_int
         lib.orc_enc_e4m3fn.argtypes = [ctypes.c_float]
         lib.orc_enc_e4m3fn.restype = ctypes.c_uint8
-        lib.orc_kv_write.argtypes = [P, P, P, i32, i32, i32, i32, i32, P, P, P]
+        lib.orc_kv_write.argtypes = [P, P, P, i32, i32, i32, i32, i32, i32, P, P, P]
         lib.orc_kv_write.restype = ctypes.c_int
         lib.orc_dec_f16.argtypes = [ctypes.c_uint16]
         lib.orc_dec_f16.restype = ctypes.c_double
         lib.orc_decode_tq4.argtypes = [P, P, P, P, P, i32, i32, i32, i32, i32, i32, i32,
-                                       ctypes.c_float, P, i32, P, i32]
+                                       ctypes.c_float, i32, P, i32, P, i32]
         lib.orc_decode_tq4.restype = ctypes.c_int
-        lib.orc_dequant_tq4.argtypes = [P, P, i32, i32, i32, i32, i32, i32, P, P]
+        lib.orc_dequant_tq4.argtypes = [P, P, i32, i32, i32, i32, i32, i32, i32, P, P]
         lib.orc_dequant_tq4.restype = ctypes.c_int
         self.lib = lib
         self.path = lib_path
 
     def decode(self, q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens, softmax_scale,
-               units=None, nthreads: int = 1) -> np.ndarray:
-        """Unsplit decode attention in fp64.
+               units=None, nthreads: int = 1, layout: str = "head") -> np.ndarray:
+        """Unsplit decode attention in fp64.  ``layout``: "head" (codes [NB][Hkv][BS][D]) or
+        "slot" ([NB][BS][Hkv][D], the page's data-region order).
 
         Returns [S][Hkv*QG][D] when ``units`` is None, else [len(units)][QG][D]
         for the listed (s, h) pairs."""
         q, k, v, sc, bt, sl, (S, Hkv, QG, D, BS, NB, MB) = _problem(
-            q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens)
+            q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens, layout)
         if units is None:
             u = None
             n = S * Hkv
@@ -102,7 +107,7 @@ class Oracle:
             n = u.shape[0]
         out = np.empty((n, QG, D), dtype=np.float64)
         rc = self.lib.orc_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(sc), _ptr(bt), _ptr(sl), S, Hkv, QG,
-                                 D, BS, NB, MB, float(softmax_scale),
+                                 D, BS, NB, MB, float(softmax_scale), LAYOUTS[layout],
                                  None if u is None else _ptr(u), n, _ptr(out), int(nthreads))
         if rc:
             raise OracleError("orc_decode failed with code %d" % rc)
@@ -111,17 +116,17 @@ class Oracle:
         return out
 
     def partials(self, q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens, softmax_scale,
-                 num_partitions: int, partition_tokens: int):
+                 num_partitions: int, partition_tokens: int, layout: str = "head"):
         """Split-K partials (o [S][Hkv][P][QG][D], m, l [S][Hkv][P][QG]); dead entries are NaN."""
         q, k, v, sc, bt, sl, (S, Hkv, QG, D, BS, NB, MB) = _problem(
-            q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens)
+            q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens, layout)
         P, E = int(num_partitions), int(partition_tokens)
         o = np.full((S, Hkv, P, QG, D), np.nan)
         m = np.full((S, Hkv, P, QG), np.nan)
         l = np.full((S, Hkv, P, QG), np.nan)
         rc = self.lib.orc_partials(_ptr(q), _ptr(k), _ptr(v), _ptr(sc), _ptr(bt), _ptr(sl), S, Hkv,
-                                   QG, D, BS, NB, MB, float(softmax_scale), P, E, _ptr(o), _ptr(m),
-                                   _ptr(l))
+                                   QG, D, BS, NB, MB, float(softmax_scale), LAYOUTS[layout], P, E,
+                                   _ptr(o), _ptr(m), _ptr(l))
         if rc:
             raise OracleError("orc_partials failed with code %d" % rc)
         return o, m, l
@@ -141,8 +146,10 @@ class Oracle:
         return out
 
     def decode_tq4(self, q_bits, tq4_cache, centroids, block_tables, seq_lens, softmax_scale,
-                   num_kv_heads: int, kv_block_size: int, units=None, nthreads: int = 1) -> np.ndarray:
-        """Unsplit decode attention over the 4-bit record format, in fp64.  Returns
+                   num_kv_heads: int, kv_block_size: int, units=None, nthreads: int = 1,
+                   layout: str = "head") -> np.ndarray:
+        """Unsplit decode attention over the 4-bit record format, in fp64 (``layout``: the
+        order of a block's data rows, "head" [Hkv][BS][D] or "slot" [BS][Hkv][D]).  Returns
         [S][Hkv*QG][D], or [len(units)][QG][D] for the listed (s, h) pairs."""
         q = _np(q_bits, np.uint16)
         cache = _np(tq4_cache, np.uint8)
@@ -164,22 +171,22 @@ class Oracle:
             n = u.shape[0]
         out = np.empty((n, QG, D), dtype=np.float64)
         rc = self.lib.orc_decode_tq4(_ptr(q), _ptr(cache), _ptr(cent), _ptr(bt), _ptr(sl), S, Hkv, QG,
-                                     D, BS, NB, bt.shape[1], float(softmax_scale),
+                                     D, BS, NB, bt.shape[1], float(softmax_scale), LAYOUTS[layout],
                                      None if u is None else _ptr(u), n, _ptr(out), int(nthreads))
         if rc:
             raise OracleError("orc_decode_tq4 failed with code %d" % rc)
         return out.reshape(S, Hkv * QG, D) if units is None else out
 
     def dequant_tq4(self, tq4_cache, centroids, num_kv_heads: int, head_dim: int,
-                    kv_block_size: int, block: int, head: int, slot: int):
+                    kv_block_size: int, block: int, head: int, slot: int, layout: str = "head"):
         """The dequantized K and V rows (fp64 [D] each) of one (block, head, slot)."""
         cache = _np(tq4_cache, np.uint8)
         cent = _np(centroids, np.float32)
         k = np.empty(head_dim, dtype=np.float64)
         v = np.empty(head_dim, dtype=np.float64)
         rc = self.lib.orc_dequant_tq4(_ptr(cache), _ptr(cent), int(num_kv_heads), int(head_dim),
-                                      int(kv_block_size), int(block), int(head), int(slot), _ptr(k),
-                                      _ptr(v))
+                                      int(kv_block_size), LAYOUTS[layout], int(block), int(head),
+                                      int(slot), _ptr(k), _ptr(v))
         if rc:
             raise OracleError("orc_dequant_tq4 failed with code %d" % rc)
         return k, v
@@ -207,9 +214,11 @@ class Oracle:
         flat = np.array([self.lib.orc_enc_e4m3fn(float(x)) for x in v.reshape(-1)], dtype=np.uint8)
         return flat.reshape(v.shape)
 
-    def kv_write(self, k_new_bits, v_new_bits, slot_mapping, k_cache, v_cache, kv_scales):
+    def kv_write(self, k_new_bits, v_new_bits, slot_mapping, k_cache, v_cache, kv_scales,
+                 layout: str = "head"):
         """Quantize and scatter new K/V rows into copies of the cache arrays; returns them.
-        k_new/v_new: bf16 bits [T][Hkv][D]; slot_mapping int32 [T] (-1: skip)."""
+        k_new/v_new: bf16 bits [T][Hkv][D]; slot_mapping int32 [T] (-1: skip); the caches
+        [NB][Hkv][BS][D] ("head") or [NB][BS][Hkv][D] ("slot")."""
         kn = _np(k_new_bits, np.uint16)
         vn = _np(v_new_bits, np.uint16)
         sm = _np(slot_mapping, np.int32)
@@ -217,12 +226,12 @@ class Oracle:
         vc = _np(v_cache, np.uint8).copy()
         sc = _np(kv_scales, np.float32).copy()
         T, Hkv, D = kn.shape
-        NB, Hkv2, BS, D2 = kc.shape
+        NB, Hkv2, BS, D2 = kc.shape if layout == "head" else _swap12(kc.shape)
         if vn.shape != kn.shape or Hkv2 != Hkv or D2 != D or sm.shape != (T,) or vc.shape != kc.shape \
                 or sc.shape != (NB, Hkv, 2, BS):
             raise OracleError("inconsistent shapes")
-        rc = self.lib.orc_kv_write(_ptr(kn), _ptr(vn), _ptr(sm), T, Hkv, D, BS, NB, _ptr(kc), _ptr(vc),
-                                   _ptr(sc))
+        rc = self.lib.orc_kv_write(_ptr(kn), _ptr(vn), _ptr(sm), T, Hkv, D, BS, NB, LAYOUTS[layout],
+                                   _ptr(kc), _ptr(vc), _ptr(sc))
         if rc:
             raise OracleError("orc_kv_write failed with code %d" % rc)
         return kc, vc, sc
@@ -282,14 +291,20 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def _problem(q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens):
+def _swap12(shape):
+    return (shape[0], shape[2], shape[1], shape[3])
+
+
+def _problem(q_bits, k_codes, v_codes, kv_scales, block_tables, seq_lens, layout="head"):
     q = _np(q_bits, np.uint16)
     k = _np(k_codes, np.uint8)
     v = _np(v_codes, np.uint8)
     sc = _np(kv_scales, np.float32)
     bt = _np(block_tables, np.int32)
     sl = _np(seq_lens, np.int32)
-    NB, Hkv, BS, D = k.shape
+    if layout not in LAYOUTS:
+        raise OracleError(f"layout must be one of {sorted(LAYOUTS)}")
+    NB, Hkv, BS, D = k.shape if layout == "head" else _swap12(k.shape)
     S, Hq, Dq = q.shape
     if v.shape != k.shape or sc.shape != (NB, Hkv, 2, BS) or Dq != D or Hq % Hkv:
         raise OracleError("inconsistent shapes")

@@ -19,12 +19,14 @@
  *   out   = sum_t exp(x_t - max x) v_t / sum_t exp(x_t - max x)
  *
  * Cache format (the pages leave the "TQ" contents open; this library fixes
- * fp8): K and V are OCP e4m3fn codes k_cache/v_cache[NB][Hkv][BS][D], each
- * (token, kv head) row carrying one fp32 scale for K and one for V, stored as
- * SoA metadata per cache block: kv_scales[NB][Hkv][2][BS] (field 0 = K,
- * field 1 = V).  Both follow the kv_head-major order of the page's per-block
- * metadata region (kv head, then field, then slot).  Dequantized
- * k_t[d] = e4m3fn(code) * scale.
+ * fp8): K and V are OCP e4m3fn codes, one D-byte row per (block, kv head,
+ * slot), each row carrying one fp32 scale for K and one for V, stored as SoA
+ * metadata per cache block: kv_scales[NB][Hkv][2][BS] (field 0 = K, field 1 =
+ * V), the kv_head-major order of the page's per-block metadata region (kv
+ * head, then field, then slot).  The rows of a block are in one of two orders
+ * (`layout`, see orc_row): head-major k_cache/v_cache[NB][Hkv][BS][D], or
+ * slot-major [NB][BS][Hkv][D], the order of the page's data region.
+ * Dequantized k_t[d] = e4m3fn(code) * scale.
  *
  * Everything is fp64: bf16 q and fp8 codes decode exactly, the fp32 scales and
  * the fp32 softmax_scale are widened, and exp() is libm's double exp().
@@ -34,7 +36,8 @@
  * already rotated by the caller), in the reading this library takes where the
  * page leaves the constants open.  Cache block b is block_bytes =
  * Hkv*BS*D + Hkv*3*BS*2 bytes:
- *   data region  [Hkv][BS][D] bytes: the (head, slot) row holds the K indices
+ *   data region  [Hkv][BS][D] (head-major) or [BS][Hkv][D] (slot-major, the
+ *                page's order) bytes: the (head, slot) row holds the K indices
  *                in bytes 0..D/2-1 and the V indices in bytes D/2..D-1; dim d
  *                is byte d/2, low nibble for even d, high nibble for odd d
  *                (the page's word w, nibble n order, little-endian words);
@@ -63,6 +66,22 @@
 #define ORC_ERR_ARGS 1
 #define ORC_ERR_BLOCK 2 /* a block-table entry needed for t < L is outside [0, NB) */
 #define ORC_ERR_NOMEM 3
+
+/* Order of the 128-byte K / V rows inside a cache block (the scale / metadata
+ * region is [Hkv][field][BS] in both):
+ *   head-major: row (h, slot) is row h * BS + slot   -- [BS rows of head 0][head 1]...
+ *   slot-major: row (h, slot) is row slot * Hkv + h  -- the page's data region:
+ *     STEP F addresses it as slot * _stride_data_slot + kv_h * DATA_BYTES_PER_SLOT,
+ *     with _stride_data_slot = num_kv_heads * DATA_BYTES_PER_SLOT
+ *     (build_tq_decode_module, "Strides"). */
+#define ORC_LAYOUT_HEAD_MAJOR 0
+#define ORC_LAYOUT_SLOT_MAJOR 1
+
+/* Index of the row of (block blk, kv head h, slot) among the cache's rows. */
+static int64_t orc_row(int32_t layout, int32_t Hkv, int32_t BS, int64_t blk, int h, int slot) {
+  if (layout == ORC_LAYOUT_SLOT_MAJOR) return (blk * BS + slot) * Hkv + h;
+  return (blk * Hkv + h) * BS + slot;
+}
 
 /* OCP 8-bit floating point, E4M3 variant "fn": 1 sign, 4 exponent bits (bias
  * 7), 3 mantissa bits, no infinities, S.1111.111 is NaN, largest finite 448. */
@@ -110,6 +129,7 @@ typedef struct {
   const int32_t* seq_lens;
   int32_t S, Hkv, QG, D, BS, NB, max_blocks_per_seq;
   double scale;
+  int32_t layout; /* ORC_LAYOUT_HEAD_MAJOR or ORC_LAYOUT_SLOT_MAJOR: order of a block's rows */
   /* 4-bit record format when tq4_cache is set (k_cache, v_cache, kv_scales unused) */
   const uint8_t* tq4_cache;
   const float* centroids;
@@ -124,7 +144,7 @@ static int64_t orc_tq4_block_bytes(const orc_problem* pb) {
  * in the 4-bit record format. */
 static double orc_tq4_kv(const orc_problem* pb, int field, int blk, int slot, int h, int d) {
   const uint8_t* block = pb->tq4_cache + (int64_t)blk * orc_tq4_block_bytes(pb);
-  const uint8_t* row = block + ((int64_t)h * pb->BS + slot) * pb->D;
+  const uint8_t* row = block + orc_row(pb->layout, pb->Hkv, pb->BS, 0, h, slot) * pb->D;
   const uint8_t* meta = block + (int64_t)pb->Hkv * pb->BS * pb->D + (int64_t)h * 3 * pb->BS * 2;
   int byte = row[(field == 0 ? 0 : pb->D / 2) + d / 2];
   int idx = (d & 1) ? byte >> 4 : byte & 0xF;
@@ -146,7 +166,7 @@ static int orc_block(const orc_problem* pb, int s, int t, int* blk) {
 static double orc_kv(const orc_problem* pb, int field, int blk, int slot, int h, int d) {
   if (pb->tq4_cache) return orc_tq4_kv(pb, field, blk, slot, h, d);
   const uint8_t* cache = field == 0 ? pb->k_cache : pb->v_cache;
-  int64_t row = ((int64_t)blk * pb->Hkv + h) * pb->BS + slot;
+  int64_t row = orc_row(pb->layout, pb->Hkv, pb->BS, blk, h, slot);
   double code = orc_dec_e4m3fn(cache[row * pb->D + d]);
   double sc = (double)pb->kv_scales[(((int64_t)blk * pb->Hkv + h) * 2 + field) * pb->BS + slot];
   return code * sc;
@@ -250,6 +270,7 @@ static int orc_check(const orc_problem* pb) {
   if (pb->S < 1 || pb->Hkv < 1 || pb->QG < 1 || pb->D < 1 || pb->BS < 1 || pb->NB < 1 ||
       pb->max_blocks_per_seq < 1)
     return ORC_ERR_ARGS;
+  if (pb->layout != ORC_LAYOUT_HEAD_MAJOR && pb->layout != ORC_LAYOUT_SLOT_MAJOR) return ORC_ERR_ARGS;
   for (int s = 0; s < pb->S; ++s) {
     int L = pb->seq_lens[s];
     if (L < 0 || (int64_t)L > (int64_t)pb->max_blocks_per_seq * pb->BS) return ORC_ERR_ARGS;
@@ -270,10 +291,10 @@ static int orc_run(orc_problem pb, const int32_t* units, int32_t n_units, double
 int orc_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
                const float* kv_scales, const int32_t* block_tables, const int32_t* seq_lens,
                int32_t S, int32_t Hkv, int32_t QG, int32_t D, int32_t BS, int32_t NB,
-               int32_t max_blocks_per_seq, float softmax_scale, const int32_t* units,
-               int32_t n_units, double* out, int32_t nthreads) {
+               int32_t max_blocks_per_seq, float softmax_scale, int32_t layout,
+               const int32_t* units, int32_t n_units, double* out, int32_t nthreads) {
   orc_problem pb = {q, k_cache, v_cache, kv_scales, block_tables, seq_lens, S, Hkv, QG, D, BS,
-                    NB, max_blocks_per_seq, (double)softmax_scale, NULL, NULL};
+                    NB, max_blocks_per_seq, (double)softmax_scale, layout, NULL, NULL};
   return orc_run(pb, units, n_units, out, nthreads);
 }
 
@@ -285,25 +306,28 @@ int orc_decode(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache
 int orc_decode_tq4(const uint16_t* q, const uint8_t* cache, const float* centroids,
                    const int32_t* block_tables, const int32_t* seq_lens, int32_t S, int32_t Hkv,
                    int32_t QG, int32_t D, int32_t BS, int32_t NB, int32_t max_blocks_per_seq,
-                   float softmax_scale, const int32_t* units, int32_t n_units, double* out,
-                   int32_t nthreads) {
+                   float softmax_scale, int32_t layout, const int32_t* units, int32_t n_units,
+                   double* out, int32_t nthreads) {
   orc_problem pb = {q, NULL, NULL, NULL, block_tables, seq_lens, S, Hkv, QG, D, BS,
-                    NB, max_blocks_per_seq, (double)softmax_scale, cache, centroids};
+                    NB, max_blocks_per_seq, (double)softmax_scale, layout, cache, centroids};
   if (!cache) return ORC_ERR_ARGS;
   return orc_run(pb, units, n_units, out, nthreads);
 }
 
 /* Dequantized K and V rows (D values each) of (blk, h, slot) in the 4-bit record format. */
 int orc_dequant_tq4(const uint8_t* cache, const float* centroids, int32_t Hkv, int32_t D,
-                    int32_t BS, int32_t blk, int32_t h, int32_t slot, double* k, double* v) {
+                    int32_t BS, int32_t layout, int32_t blk, int32_t h, int32_t slot, double* k,
+                    double* v) {
   if (!cache || !centroids || !k || !v || Hkv < 1 || D < 2 || (D & 1) || BS < 1 || blk < 0 ||
-      h < 0 || h >= Hkv || slot < 0 || slot >= BS)
+      h < 0 || h >= Hkv || slot < 0 || slot >= BS ||
+      (layout != ORC_LAYOUT_HEAD_MAJOR && layout != ORC_LAYOUT_SLOT_MAJOR))
     return ORC_ERR_ARGS;
   orc_problem pb;
   memset(&pb, 0, sizeof pb);
   pb.Hkv = Hkv;
   pb.D = D;
   pb.BS = BS;
+  pb.layout = layout;
   pb.tq4_cache = cache;
   pb.centroids = centroids;
   for (int d = 0; d < D; ++d) {
@@ -358,10 +382,10 @@ static int orc_run(orc_problem pb, const int32_t* units, int32_t n_units, double
 int orc_partials(const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache,
                  const float* kv_scales, const int32_t* block_tables, const int32_t* seq_lens,
                  int32_t S, int32_t Hkv, int32_t QG, int32_t D, int32_t BS, int32_t NB,
-                 int32_t max_blocks_per_seq, float softmax_scale, int32_t P, int32_t E,
-                 double* o, double* m, double* l) {
+                 int32_t max_blocks_per_seq, float softmax_scale, int32_t layout, int32_t P,
+                 int32_t E, double* o, double* m, double* l) {
   orc_problem pb = {q, k_cache, v_cache, kv_scales, block_tables, seq_lens, S, Hkv, QG, D, BS,
-                    NB, max_blocks_per_seq, (double)softmax_scale, NULL, NULL};
+                    NB, max_blocks_per_seq, (double)softmax_scale, layout, NULL, NULL};
   int rc = orc_check(&pb);
   if (rc) return rc;
   if (P < 1 || E < 1 || !o || !m || !l) return ORC_ERR_ARGS;
@@ -457,10 +481,11 @@ uint8_t orc_enc_e4m3fn(float x) {
 }
 
 int orc_kv_write(const uint16_t* k_new, const uint16_t* v_new, const int32_t* slot_mapping,
-                 int32_t T, int32_t Hkv, int32_t D, int32_t BS, int32_t NB, uint8_t* k_cache,
-                 uint8_t* v_cache, float* kv_scales) {
+                 int32_t T, int32_t Hkv, int32_t D, int32_t BS, int32_t NB, int32_t layout,
+                 uint8_t* k_cache, uint8_t* v_cache, float* kv_scales) {
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !kv_scales || T < 0 ||
-      Hkv < 1 || D < 1 || BS < 1 || NB < 1)
+      Hkv < 1 || D < 1 || BS < 1 || NB < 1 ||
+      (layout != ORC_LAYOUT_HEAD_MAJOR && layout != ORC_LAYOUT_SLOT_MAJOR))
     return ORC_ERR_ARGS;
   for (int t = 0; t < T; ++t) {
     int32_t slot = slot_mapping[t];
@@ -470,7 +495,7 @@ int orc_kv_write(const uint16_t* k_new, const uint16_t* v_new, const int32_t* sl
     for (int h = 0; h < Hkv; ++h)
       for (int field = 0; field < 2; ++field) {
         const uint16_t* src = (field == 0 ? k_new : v_new) + ((int64_t)t * Hkv + h) * D;
-        uint8_t* dst = (field == 0 ? k_cache : v_cache) + (((int64_t)blk * Hkv + h) * BS + off) * D;
+        uint8_t* dst = (field == 0 ? k_cache : v_cache) + orc_row(layout, Hkv, BS, blk, h, off) * D;
         float absmax = 0.0f;
         for (int d = 0; d < D; ++d) {
           float x = (float)orc_dec_bf16(src[d]);

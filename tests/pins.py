@@ -373,6 +373,135 @@ def pin_signed_scales(orc):
     assert np.array_equal(run(orc, dict(p, sc=sc)), -got)
 
 
+def _slot_major(x):
+    """A head-major [NB][Hkv][BS][...] cache array as the slot-major [NB][BS][Hkv][...] one."""
+    return x.permute(0, 2, 1, 3).contiguous()
+
+
+def pin_slot_major_transposition(orc):
+    """The same cache in the slot-major row order (the page's data region) decodes, splits and
+    merges to the same bits as in the head-major order (pinned by the brute-force gather), and
+    the slot-major rows match a gather written here from the page's byte formula."""
+    for seed, kw in ((30, dict(lens=(5, 13, 22), BS=4)), (31, dict(S=2, Hkv=3, QG=2, BS=8, lens=(17, 40)))):
+        p = tiny_problem(seed=seed, **kw)
+        k2, v2 = _slot_major(p["k"]), _slot_major(p["v"])
+        ref = run(orc, p)
+        got = orc.decode(p["q"], k2, v2, p["sc"], p["bt"], p["sl"], p["scale"], layout="slot")
+        assert np.array_equal(got, ref), "slot-major decode differs from head-major"
+        o, m, l = orc.partials(p["q"], p["k"], p["v"], p["sc"], p["bt"], p["sl"], p["scale"], 6, 8)
+        o2, m2, l2 = orc.partials(p["q"], k2, v2, p["sc"], p["bt"], p["sl"], p["scale"], 6, 8,
+                                  layout="slot")
+        for a, b in ((o, o2), (m, m2), (l, l2)):
+            assert np.array_equal(np.nan_to_num(a, nan=7.0), np.nan_to_num(b, nan=7.0))
+        # gather from the flat slot-major bytes: byte (b, j, h, d) = b*BS*Hkv*D + j*Hkv*D + h*D + d
+        NB, Hkv, BS, D = p["k"].shape
+        flat_k, flat_v = k2.reshape(-1), v2.reshape(-1)
+        S, Hq, _ = p["q"].shape
+        QG = Hq // Hkv
+        want = np.zeros((S, Hq, D))
+        for s in range(S):
+            L = int(p["sl"][s])
+            for h in range(Hkv):
+                rows = []
+                for t in range(L):
+                    b, j = int(p["bt"][s, t // BS]), t % BS
+                    at = b * BS * Hkv * D + j * Hkv * D + h * D
+                    kv = [c[at:at + D].view(torch.float8_e4m3fn).to(torch.float64)
+                          * float(p["sc"][b, h, f, j]) for f, c in ((0, flat_k), (1, flat_v))]
+                    rows.append(kv)
+                if not rows:
+                    continue
+                K = torch.stack([r[0] for r in rows])
+                V = torch.stack([r[1] for r in rows])
+                Q = p["q"][s, h * QG:(h + 1) * QG].to(torch.float64)
+                want[s, h * QG:(h + 1) * QG] = (torch.softmax(Q @ K.T * p["scale"], -1) @ V).numpy()
+        assert_close(got, want, 1e-12, "slot-major gather")
+
+
+def pin_two_token_slot_major_golden(orc):
+    """tests/golden/two_token_slot_major.json: the two-token closed form, its bytes placed by
+    hand at the offsets of the page's slot-major data region."""
+    with open(os.path.join(GOLDEN, "two_token_slot_major.json")) as f:
+        g = json.load(f)
+    z = g["sizes"]
+    NB, BS, Hkv, D = z["num_blocks"], z["kv_block_size"], z["num_kv_heads"], z["head_dim"]
+    k = np.zeros(NB * BS * Hkv * D, dtype=np.uint8)
+    v = np.zeros_like(k)
+    for off, val in g["k_bytes"].items():
+        k[int(off)] = val
+    for off, val in g["v_bytes"].items():
+        v[int(off)] = val
+    sc = np.ones(NB * Hkv * 2 * BS, dtype=np.float32)
+    for off, val in g["scale_overrides"].items():
+        sc[int(off)] = val
+    q = np.zeros((1, Hkv, D), dtype=np.uint16)
+    q[0, 1, 0] = g["q_head1_d0_bf16_bits"]
+    out = orc.decode(q, k.reshape(NB, BS, Hkv, D), v.reshape(NB, BS, Hkv, D),
+                     sc.reshape(NB, Hkv, 2, BS), np.array([[1]], dtype=np.int32),
+                     np.array([2], dtype=np.int32), 1.0, layout="slot")
+    want = (2 - math.e / 2) / (1 + math.e)
+    assert abs(want - g["expected_head1_value"]) < 1e-15
+    assert_close(out[0, 1], np.full(D, want), 1e-14, "slot-major two-token closed form")
+    assert not out[0, 0].any()
+
+
+def pin_tq4_golden_record_slot_major(orc):
+    """tests/golden/tq4_record_slot_major.json: a record written byte by byte at offsets
+    derived by hand from the page's slot-major data region, dequantized, then a 3-token
+    decode over it (q = 0: the mean of the V rows; q = e_0: a closed-form softmax)."""
+    with open(os.path.join(GOLDEN, "tq4_record_slot_major.json")) as f:
+        g = json.load(f)
+    sz = g["sizes"]
+    NB, Hkv, BS, D = sz["num_blocks"], sz["num_kv_heads"], sz["kv_block_size"], sz["head_dim"]
+    cache = np.zeros(NB * sz["block_bytes"], dtype=np.uint8)
+    for off, val in g["bytes"].items():
+        cache[int(off)] = val
+    cache = cache.reshape(NB, sz["block_bytes"])
+    cent = np.asarray(g["centroids"], dtype=np.float32)
+    rec = g["record"]
+    k, v = orc.dequant_tq4(cache, cent, Hkv, D, BS, rec["block"], rec["head"], rec["slot"],
+                           layout="slot")
+    assert np.array_equal(k, np.asarray(g["expected_k"])), k
+    assert np.array_equal(v, np.asarray(g["expected_v"])), v
+    for (b, h, slot) in ((1, 0, 2), (1, 1, 1), (0, 1, 2)):
+        k0, v0 = orc.dequant_tq4(cache, cent, Hkv, D, BS, b, h, slot, layout="slot")
+        assert not k0.any() and not v0.any()
+    bt = np.array([[1]], dtype=np.int32)
+    sl = np.array([3], dtype=np.int32)
+    q = np.zeros((1, Hkv, D), dtype=np.uint16)
+    out = orc.decode_tq4(q, cache, cent, bt, sl, 1.0, Hkv, BS, layout="slot")
+    assert np.array_equal(out[0, 1], np.asarray(g["expected_v"]) / 3)
+    assert not out[0, 0].any()
+    q[0, 1, 0] = 0x3F80
+    out = orc.decode_tq4(q, cache, cent, bt, sl, 1.0, Hkv, BS, layout="slot")
+    w = math.exp(-14.0)
+    assert np.max(np.abs(out[0, 1] - np.asarray(g["expected_v"]) * w / (w + 2.0))) < 1e-15
+
+
+def pin_tq4_slot_major_transposition(orc):
+    """A 4-bit cache whose data rows are reordered head-major -> slot-major (metadata
+    untouched) decodes to the same bits with layout "slot"."""
+    p = _tq4_problem(6)
+    NB, Hkv, BS, D = p["cache"].shape[0], p["Hkv"], p["BS"], 128
+    data = p["cache"][:, :Hkv * BS * D].reshape(NB, Hkv, BS, D).transpose(0, 2, 1, 3).reshape(NB, -1)
+    cache2 = np.ascontiguousarray(np.concatenate([data, p["cache"][:, Hkv * BS * D:]], axis=1))
+    a = orc.decode_tq4(p["q"], p["cache"], p["cent"], p["bt"], p["sl"], 0.088, Hkv, BS)
+    b = orc.decode_tq4(p["q"], cache2, p["cent"], p["bt"], p["sl"], 0.088, Hkv, BS, layout="slot")
+    assert np.array_equal(a, b)
+
+
+def pin_kv_write_slot_major(orc):
+    """The writer into a slot-major cache leaves exactly the transposition of what it leaves in
+    the head-major one (codes; the scale region is the same in both)."""
+    kn, vn, sm, kc, vc, sc = _kv_write_problem(seed=5)
+    a = orc.kv_write(kn, vn, sm, kc, vc, sc)
+    b = orc.kv_write(kn, vn, sm, _slot_major(torch.from_numpy(kc)).numpy(),
+                     _slot_major(torch.from_numpy(vc)).numpy(), sc, layout="slot")
+    assert np.array_equal(_slot_major(torch.from_numpy(a[0])).numpy(), b[0])
+    assert np.array_equal(_slot_major(torch.from_numpy(a[1])).numpy(), b[1])
+    assert np.array_equal(a[2], b[2])
+
+
 def pin_zero_length(orc):
     p = tiny_problem(seed=13, lens=(0, 5, 0))
     got = run(orc, p)
@@ -611,4 +740,6 @@ ALL_PINS = [pin_e4m3fn_points, pin_e4m3fn_library, pin_bf16_library, pin_dense_b
             pin_zero_length, pin_e4m3fn_encode_roundtrip, pin_e4m3fn_encode_ties_and_saturation,
             pin_e4m3fn_encode_library, pin_kv_write_quantizer, pin_partials_closed_form, pin_kv_write_matches_library_quantizer,
             pin_f16_library, pin_tq4_golden_record, pin_tq4_matches_fp8_form, pin_tq4_constant_v,
-            pin_aliased_blocks, pin_signed_scales]
+            pin_aliased_blocks, pin_signed_scales, pin_slot_major_transposition,
+            pin_two_token_slot_major_golden, pin_tq4_golden_record_slot_major,
+            pin_tq4_slot_major_transposition, pin_kv_write_slot_major]

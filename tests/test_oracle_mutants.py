@@ -19,8 +19,7 @@ MUTANTS = [
     ("bf16_shift", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
     ("block_index_wrong_divisor", "t / pb->BS]", "t / (pb->BS + 1)]"),
     ("slot_off_by_one", "orc_kv(pb, 0, blk, t % pb->BS, h, d)", "orc_kv(pb, 0, blk, (t + 1) % pb->BS, h, d)"),
-    ("cache_head_ignored", "((int64_t)blk * pb->Hkv + h) * pb->BS + slot;",
-     "((int64_t)blk * pb->Hkv + 0) * pb->BS + slot;"),
+    ("cache_head_ignored", "return (blk * Hkv + h) * BS + slot;", "return (blk * Hkv + 0) * BS + slot;"),
     ("scale_field_ignored", "* 2 + field) * pb->BS + slot]", "* 2 + 0) * pb->BS + slot]"),
     ("scale_slot_ignored", "* 2 + field) * pb->BS + slot]", "* 2 + field) * pb->BS + 0]"),
     ("q_row_group_ignored", "(int64_t)h * pb->QG + g) * pb->D", "(int64_t)h * pb->QG + 0) * pb->D"),
@@ -55,7 +54,19 @@ MUTANTS = [
      "return (double)idx * orc_dec_f16(f[1]);"),
     ("tq4_centroid_off_by_one", "pb->centroids[idx]", "pb->centroids[(idx + 1) & 15]"),
     ("tq4_meta_head_stride", "(int64_t)h * 3 * pb->BS * 2;", "(int64_t)h * 2 * pb->BS * 2;"),
-    ("tq4_rows_slot_major", "((int64_t)h * pb->BS + slot) * pb->D", "((int64_t)slot * pb->Hkv + h) * pb->D"),
+    ("tq4_rows_slot_major", "orc_row(pb->layout, pb->Hkv, pb->BS, 0, h, slot)",
+     "orc_row(ORC_LAYOUT_SLOT_MAJOR, pb->Hkv, pb->BS, 0, h, slot)"),
+    # the slot-major row order (the page's data region) ignored everywhere, or in one reader
+    ("layout_ignored", "if (layout == ORC_LAYOUT_SLOT_MAJOR) return (blk * BS + slot) * Hkv + h;", ""),
+    ("slot_major_block_stride", "return (blk * BS + slot) * Hkv + h;", "return (blk * Hkv + slot) * Hkv + h;"),
+    ("slot_major_head_and_slot_swapped", "return (blk * BS + slot) * Hkv + h;",
+     "return (blk * BS + h) * Hkv + slot;"),
+    ("tq4_layout_ignored", "orc_row(pb->layout, pb->Hkv, pb->BS, 0, h, slot)",
+     "orc_row(ORC_LAYOUT_HEAD_MAJOR, pb->Hkv, pb->BS, 0, h, slot)"),
+    ("fp8_layout_ignored", "orc_row(pb->layout, pb->Hkv, pb->BS, blk, h, slot)",
+     "orc_row(ORC_LAYOUT_HEAD_MAJOR, pb->Hkv, pb->BS, blk, h, slot)"),
+    ("writer_layout_ignored", "orc_row(layout, Hkv, BS, blk, h, off)",
+     "orc_row(ORC_LAYOUT_HEAD_MAJOR, Hkv, BS, blk, h, off)"),
     # the partial triple's m_p in log2 units with a merge that matches: the merged result is
     # unchanged, only the partials' definition catches it
     ("partials_and_merge_log2_units",

@@ -356,6 +356,9 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="w4_s128_ctx8k")
+    ap.add_argument("--kv-layout", default="head", choices=("head", "slot"),
+                    help="order of the cache rows in a block: head-major (default) or the page's "
+                         "slot-major data region")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-probe", action="store_true", help="skip the HBM read/copy probe")
@@ -394,7 +397,7 @@ def main() -> int:
             f"decode byte pattern without arithmetic {probe_res['pattern_gbs']} GB/s (4-bit: "
             f"{probe_res['pattern4_gbs']} GB/s)")
     log(f"[bench] generating {wl.name} on {dev}")
-    inp = workloads.make_inputs(wl, device=dev)
+    inp = workloads.make_inputs(wl, device=dev, kv_layout=args.kv_layout)
     torch.cuda.synchronize()
     S, Hkv, QG, G = wl.num_seqs, wl.num_kv_heads, wl.query_group_size, wl.tile_groups_per_partition
     P = inp.num_partitions
@@ -408,7 +411,8 @@ def main() -> int:
     def dec():
         tq.tq_decode(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, inp.seq_lens,
                      part, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale, num_partitions=P,
-                     max_seq_len=maxlen, num_blocks=inp.num_blocks, stream=stream)
+                     max_seq_len=maxlen, num_blocks=inp.num_blocks, kv_layout=args.kv_layout,
+                     stream=stream)
 
     def red():
         tq.tq_decode_reduce(part, inp.seq_lens, out, Hkv, QG, G, num_partitions=P,
@@ -418,7 +422,7 @@ def main() -> int:
         tq.tq_decode_fused(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables,
                            inp.seq_lens, out, Hkv, QG, wl.kv_block_size, G, inp.softmax_scale,
                            num_partitions=P, max_seq_len=maxlen, num_blocks=inp.num_blocks,
-                           workspace=workspace, stream=stream)
+                           workspace=workspace, kv_layout=args.kv_layout, stream=stream)
 
     K = args.steps
 
@@ -509,6 +513,7 @@ def main() -> int:
         "config": {"workload": wl.name, "num_seqs": S, "num_kv_heads": Hkv, "query_group_size": QG,
                    "head_dim": 128, "context_tokens": maxlen, "kv_block_size": wl.kv_block_size,
                    "num_partitions": P, "tile_groups_per_partition": G, "path": head,
+                   "kv_layout": args.kv_layout,
                    "kv_format": "e4m3fn codes + fp32 scale per (token, kv head) for K and V",
                    "kv_bytes_per_step": kv_bytes},
         "paths_us": {
@@ -544,7 +549,7 @@ def main() -> int:
     slots = torch.randperm(inp.num_blocks * wl.kv_block_size, generator=gen, device=dev)[:T]
     slots = slots.to(torch.int32)
     write = lambda: tq.tq_kv_write(k_new, v_new, slots, inp.k_cache, inp.v_cache,  # noqa: E731
-                                   inp.kv_scales, stream=stream)
+                                   inp.kv_scales, kv_layout=args.kv_layout, stream=stream)
     w_ms = timed(write)
     w_bytes = T * Hkv * (512 + 264)
     res["kv_writer"] = {"tokens": T, "num_kv_heads": Hkv, "us": round(w_ms * 1e3, 2),
@@ -559,7 +564,7 @@ def main() -> int:
     del inp
     torch.cuda.empty_cache()
     log(f"[bench] generating {wl.name} in the 4-bit record format")
-    t4 = workloads.make_inputs_tq4(wl, device=dev)
+    t4 = workloads.make_inputs_tq4(wl, device=dev, kv_layout=args.kv_layout)
     part4 = tq.alloc_partials(S, Hkv, P, QG, dev)
     ws4 = tq.alloc_fused_workspace(S, Hkv, QG, maxlen, dev)
     bytes4 = t4.kv_bytes()
@@ -567,12 +572,13 @@ def main() -> int:
     def dec4():
         tq.tq4_decode(t4.q, t4.cache, t4.centroids, t4.block_tables, t4.seq_lens, part4, Hkv, QG,
                       wl.kv_block_size, G, t4.softmax_scale, num_partitions=P, max_seq_len=maxlen,
-                      stream=stream)
+                      kv_layout=args.kv_layout, stream=stream)
 
     def fused4():
         tq.tq4_decode_fused(t4.q, t4.cache, t4.centroids, t4.block_tables, t4.seq_lens, out, Hkv,
                             QG, wl.kv_block_size, G, t4.softmax_scale, num_partitions=P,
-                            max_seq_len=maxlen, workspace=ws4, stream=stream)
+                            max_seq_len=maxlen, workspace=ws4, kv_layout=args.kv_layout,
+                            stream=stream)
 
     def red4():
         tq.tq_decode_reduce(part4, t4.seq_lens, out, Hkv, QG, G, num_partitions=P,

@@ -16,14 +16,18 @@
  *
  * Cache format.  The page's 4-bit "TQ" contents are left open there; this
  * library stores K and V as OCP fp8 e4m3fn codes with one fp32 scale per
- * (token, kv head) for K and one for V, the scales kept as SoA metadata per
- * cache block in the kv_head -> field -> slot order of the page's per-block
- * metadata region:
- *   k_cache, v_cache : uint8 [num_blocks][Hkv][BS][128]   (e4m3fn codes)
- *   kv_scales        : fp32  [num_blocks][Hkv][2][BS]     (field 0 = K, 1 = V)
- * Both are kv-head-major inside a block, like the page's per-block metadata
- * region (kv head, then field, then slot): the BS rows of one (block, kv head)
- * are one contiguous 2 or 4 KiB range.  The dequantized value is code * scale.
+ * (token, kv head) for K and one for V (or, second format, the 4-bit record
+ * below).  The scales are SoA metadata per cache block in the kv_head ->
+ * field -> slot order of the page's per-block metadata region.  The 128-byte
+ * code rows of a block are in one of two orders, chosen by ext->kv_layout:
+ *   TQ_KV_LAYOUT_SLOT_MAJOR: the page's data region (STEP F of
+ *     tq_decode_kernel: slot stride num_kv_heads rows, kv head stride one row)
+ *     k_cache, v_cache : uint8 [num_blocks][BS][Hkv][128]   (e4m3fn codes)
+ *   TQ_KV_LAYOUT_HEAD_MAJOR (0, the default): the BS rows of one (block, kv
+ *     head) are one contiguous 2 or 4 KiB range, which streams faster
+ *     k_cache, v_cache : uint8 [num_blocks][Hkv][BS][128]
+ *   kv_scales          : fp32  [num_blocks][Hkv][2][BS]     (field 0 = K, 1 = V)
+ * The dequantized value is code * scale (scales of either sign).
  *
  * Memory and threading.
  *   - Every pointer argument is a DEVICE pointer (HIP device memory) owned
@@ -62,7 +66,7 @@
 extern "C" {
 #endif
 
-#define TQ_ABI_VERSION 1
+#define TQ_ABI_VERSION 2
 #define TQ_HEAD_DIM 128
 #define TQ_TOKENS_PER_TILE_GROUP 256 /* 16 tiles of 16 tokens */
 /* Device memory per GPU of tq_decode_fused_static's scratch, and its counter region. */
@@ -73,7 +77,8 @@ typedef enum {
   TQ_OK = 0,
   TQ_ERR_NULL = 1,        /* a required pointer is NULL */
   TQ_ERR_MISALIGNED = 2,  /* a data pointer is not 16-byte aligned */
-  TQ_ERR_UNSUPPORTED = 3, /* QG not in {6, 8, 16}, BS not in {16, 32}, head_dim != 128 */
+  TQ_ERR_UNSUPPORTED = 3, /* QG not in {6, 8, 16}, BS not in {16, 32}, head_dim != 128,
+                             or an unknown kv_layout */
   TQ_ERR_SHAPE = 4,       /* num_seqs, Hkv, num_blocks, max_blocks_per_seq, P or G < 1,
                              or a size that overflows the index types */
   TQ_ERR_COVERAGE = 5,    /* max_seq_len < 0, > P*G*256 or > max_blocks_per_seq*BS */
@@ -83,6 +88,11 @@ typedef enum {
                              scratch holds */
 } tq_status;
 
+/* Order of the 128-byte K / V rows inside a cache block (tq_extent.kv_layout;
+ * tq_kv_write's kv_layout); anything else is TQ_ERR_UNSUPPORTED. */
+#define TQ_KV_LAYOUT_HEAD_MAJOR 0 /* [Hkv][BS] rows */
+#define TQ_KV_LAYOUT_SLOT_MAJOR 1 /* [BS][Hkv] rows: the page's data region */
+
 /* Sizes that a decode step needs besides the named arguments (host struct). */
 typedef struct {
   int32_t num_seqs;           /* S: sequences in the batch (>= 1) */
@@ -91,6 +101,7 @@ typedef struct {
   int32_t num_partitions;     /* P: partitions per (sequence, kv head) (>= 1) */
   int32_t max_seq_len;        /* host-known upper bound of seq_lens[] (0 <= . <= P*E) */
   int32_t head_dim;           /* must be 128 */
+  int32_t kv_layout;          /* TQ_KV_LAYOUT_HEAD_MAJOR (0) or TQ_KV_LAYOUT_SLOT_MAJOR */
 } tq_extent;
 
 /* The split-K partial triple (host struct of device pointers), fp32:
@@ -111,8 +122,8 @@ typedef struct {
  * attend the QG query rows q[s][h*QG + g] to the cached tokens
  * [p*E, min((p+1)*E, L_s)) and write the partial triple.
  *   q              bf16 [S][Hkv*QG][128]
- *   k_cache        e4m3fn [NB][Hkv][BS][128]
- *   v_cache        e4m3fn [NB][Hkv][BS][128]
+ *   k_cache        e4m3fn [NB][Hkv][BS][128], or [NB][BS][Hkv][128] (ext->kv_layout)
+ *   v_cache        e4m3fn, the same layout as k_cache
  *   kv_scales      fp32 [NB][Hkv][2][BS]
  *   block_tables   int32 [S][max_blocks_per_seq]: token t of sequence s is slot
  *                  t % BS of block block_tables[s][t / BS]; entries at or past
@@ -236,9 +247,11 @@ size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,
  * norm, V as index * V scale + V zero point; the query rotated by the caller).
  * The page leaves the record's constants open; this library reads them as:
  *   kv_cache   uint8 [NB][tq4_block_bytes(Hkv, BS)], one cache block =
- *              data rows [Hkv][BS][128] bytes: per (kv head, slot) the K
- *              indices in bytes 0..63 and the V indices in bytes 64..127, dim
- *              d in byte d/2, low nibble for even d, high nibble for odd d;
+ *              data rows of 128 bytes, [BS][Hkv] (TQ_KV_LAYOUT_SLOT_MAJOR:
+ *              the page's data region, STEP F) or [Hkv][BS]
+ *              (TQ_KV_LAYOUT_HEAD_MAJOR, the default): per (kv head, slot) the
+ *              K indices in bytes 0..63 and the V indices in bytes 64..127,
+ *              dim d in byte d/2, low nibble for even d, high nibble for odd d;
  *              then metadata [Hkv][3][BS] IEEE fp16: field 0 = K norm, 1 = V
  *              scale, 2 = V zero point.  16-byte aligned.
  *   centroids  fp32 [16], the K codebook.  4-byte aligned.
@@ -274,8 +287,10 @@ size_t tq4_block_bytes(int32_t num_kv_heads, int32_t kv_block_size);
  * quantized on their own,
  *   s = fp32(absmax / 448),  code_d = e4m3fn(x_d / s)
  * (fp32 division, round to nearest even, saturating at +-448; an all-zero row
- * gives s = 0 and codes 0), and stored at k_cache / v_cache[block][h][offset]
- * with s at kv_scales[block][h][0 or 1][offset].  Other slots are untouched;
+ * gives s = 0 and codes 0), and stored in the row of (block, h, offset) of
+ * k_cache / v_cache, in the row order kv_layout names (as for tq_decode:
+ * [NB][Hkv][BS][128] or [NB][BS][Hkv][128]), with s at
+ * kv_scales[block][h][0 or 1][offset].  Other slots are untouched;
  * a negative slot (padding) or one at or past NB*BS is skipped.  The
  * per-block scale region follows the fp8 record writer of page
  * "vllm.models.deepseek_v41.amd.mono.attention.front" (stage_qkv), with this
@@ -283,13 +298,14 @@ size_t tq4_block_bytes(int32_t num_kv_heads, int32_t kv_block_size);
  *   k_new, v_new   bf16 [T][Hkv][128], finite values
  *   slot_mapping   int32 [T]
  *   k_cache, v_cache, kv_scales   as for tq_decode (written in place)
+ *   kv_layout      TQ_KV_LAYOUT_HEAD_MAJOR or TQ_KV_LAYOUT_SLOT_MAJOR
  * Tokens that map to the same slot race: the caller must not do that.
  * Errors as for tq_decode; num_tokens = 0 is a no-op.
  */
 tq_status tq_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                       uint8_t* k_cache, uint8_t* v_cache, float* kv_scales, int32_t num_tokens,
                       int32_t num_kv_heads, int32_t kv_block_size, int32_t num_blocks,
-                      int32_t head_dim, void* stream);
+                      int32_t head_dim, int32_t kv_layout, void* stream);
 
 /* Bytes of the three partial arrays for these sizes (each rounded up to 256 B),
  * laid out out | max_logits | exp_sums; 0 if the sizes are invalid. */

@@ -48,10 +48,16 @@ class TqError(RuntimeError):
         self.status = status
 
 
+# Order of the 128-byte K / V rows inside a cache block: "head" [Hkv][BS] (the default, the
+# faster stream) or "slot" [BS][Hkv] (the page's data region).
+KV_LAYOUTS = {"head": 0, "slot": 1}
+
+
 class Extent(ctypes.Structure):
     _fields_ = [("num_seqs", ctypes.c_int32), ("num_blocks", ctypes.c_int32),
                 ("max_blocks_per_seq", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
-                ("max_seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+                ("max_seq_len", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("kv_layout", ctypes.c_int32)]
 
 
 class PartialsStruct(ctypes.Structure):
@@ -92,7 +98,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.tq4_decode_fused.restype = ctypes.c_int
     lib.tq4_block_bytes.argtypes = [i32, i32]
     lib.tq4_block_bytes.restype = ctypes.c_size_t
-    lib.tq_kv_write.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, P]
+    lib.tq_kv_write.argtypes = [P, P, P, P, P, P, i32, i32, i32, i32, i32, i32, P]
     lib.tq_kv_write.restype = ctypes.c_int
     lib.tq_fused_workspace_bytes.argtypes = [ctypes.POINTER(Extent), i32, i32]
     lib.tq_fused_workspace_bytes.restype = ctypes.c_size_t
@@ -139,9 +145,23 @@ def alloc_partials(num_seqs: int, num_kv_heads: int, num_partitions: int, query_
                     exp_sums=torch.empty(shape, dtype=torch.float32, device=device))
 
 
-def _extent(num_seqs, num_blocks, max_blocks_per_seq, num_partitions, max_seq_len) -> Extent:
+def _layout(kv_layout: str) -> int:
+    if kv_layout not in KV_LAYOUTS:
+        raise ValueError(f"kv_layout must be one of {sorted(KV_LAYOUTS)}, not {kv_layout!r}")
+    return KV_LAYOUTS[kv_layout]
+
+
+def _extent(num_seqs, num_blocks, max_blocks_per_seq, num_partitions, max_seq_len,
+            kv_layout: str = "head") -> Extent:
     return Extent(int(num_seqs), int(num_blocks), int(max_blocks_per_seq), int(num_partitions),
-                  int(max_seq_len), HEAD_DIM)
+                  int(max_seq_len), HEAD_DIM, _layout(kv_layout))
+
+
+def cache_shape(num_blocks: int, num_kv_heads: int, kv_block_size: int, kv_layout: str = "head"):
+    """Shape of an fp8 k_cache / v_cache in the given row order."""
+    _layout(kv_layout)
+    return ((num_blocks, num_kv_heads, kv_block_size, HEAD_DIM) if kv_layout == "head"
+            else (num_blocks, kv_block_size, num_kv_heads, HEAD_DIM))
 
 
 def partials_bytes(num_seqs, num_kv_heads, num_partitions, query_group_size) -> int:
@@ -179,14 +199,16 @@ def _expect_pool(num_blocks: int, *tensors) -> None:
             raise ValueError(f"num_blocks {num_blocks} exceeds the {int(t.shape[0])} blocks of {name}")
 
 
-def _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS):
+def _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS,
+                       kv_layout="head"):
     """q, the fp8 cache pair with its scales, the block table and the lengths; returns S."""
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be a [S][Hkv*QG][128] tensor")
     S = int(q.shape[0])
     _expect(q, "q", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
-    _expect(k_cache, "k_cache", _FP8_CODES, (None, Hkv, BS, HEAD_DIM))
-    _expect(v_cache, "v_cache", _FP8_CODES, (None, Hkv, BS, HEAD_DIM))
+    shape = (None,) + cache_shape(1, Hkv, BS, kv_layout)[1:]
+    _expect(k_cache, "k_cache", _FP8_CODES, shape)
+    _expect(v_cache, "v_cache", _FP8_CODES, shape)
     _expect(kv_scales, "kv_scales", torch.float32, (None, Hkv, 2, BS))
     _expect(block_tables, "block_tables", torch.int32, (S, None))
     _expect(seq_lens, "seq_lens", torch.int32, (S,))
@@ -236,11 +258,13 @@ def _on_stream(stream):
 def tq_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, partials: Partials,
               num_kv_heads: int, query_group_size: int, kv_block_size: int,
               tile_groups_per_partition: int, softmax_scale: float, *, num_partitions: int,
-              max_seq_len: int, num_blocks: Optional[int] = None, stream=None) -> None:
+              max_seq_len: int, num_blocks: Optional[int] = None, kv_layout: str = "head",
+              stream=None) -> None:
     """Enqueue the partition kernel (C ABI tq_decode); writes `partials` for live partitions."""
     lib = load_library()
     Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
-    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS)
+    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS,
+                           kv_layout)
     _expect_partials(partials, S, Hkv, int(num_partitions), QG)
     nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
     _expect_pool(nb, (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_scales, "kv_scales"))
@@ -250,7 +274,7 @@ def tq_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, partials: 
     for t, n in ((partials.out, "partials.out"), (partials.max_logits, "partials.max_logits"),
                  (partials.exp_sums, "partials.exp_sums")):
         _dev(t, n)
-    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len, kv_layout)
     ps = partials._struct()
     st = lib.tq_decode(*ptrs, ctypes.byref(ps), int(num_kv_heads), int(query_group_size),
                        int(kv_block_size), int(tile_groups_per_partition), float(softmax_scale),
@@ -299,19 +323,21 @@ def tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out,
                     num_kv_heads: int, query_group_size: int, kv_block_size: int,
                     tile_groups_per_partition: int, softmax_scale: float, *, num_partitions: int,
                     max_seq_len: int, num_blocks: Optional[int] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+                    workspace: Optional[torch.Tensor] = None, kv_layout: str = "head",
+                    stream=None) -> None:
     """Enqueue the one-launch decode (C ABI tq_decode_fused) into bf16 `out` [S][Hkv*QG][128].
     `workspace`: None or a zero-filled uint8 device tensor (see alloc_fused_workspace)."""
     lib = load_library()
     Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
-    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS)
+    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS,
+                           kv_layout)
     _expect(out, "out", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
     nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
     _expect_pool(nb, (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_scales, "kv_scales"))
     ptrs = [_dev(t, n) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                                     (kv_scales, "kv_scales"), (block_tables, "block_tables"),
                                     (seq_lens, "seq_lens"), (out, "out"))]
-    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len, kv_layout)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _dev(workspace, "workspace")
@@ -327,19 +353,20 @@ def tq_decode_fused_static(q, k_cache, v_cache, kv_scales, block_tables, seq_len
                            num_kv_heads: int, query_group_size: int, kv_block_size: int,
                            tile_groups_per_partition: int, softmax_scale: float, *,
                            num_partitions: int, max_seq_len: int, num_blocks: Optional[int] = None,
-                           stream=None) -> None:
+                           kv_layout: str = "head", stream=None) -> None:
     """Enqueue the one-launch decode with the library's static scratch (C ABI
     tq_decode_fused_static): nothing is allocated, here or in the library."""
     lib = load_library()
     Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
-    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS)
+    S = _expect_fp8_inputs(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, Hkv, QG, BS,
+                           kv_layout)
     _expect(out, "out", torch.bfloat16, (S, Hkv * QG, HEAD_DIM))
     nb = int(k_cache.shape[0]) if num_blocks is None else int(num_blocks)
     _expect_pool(nb, (k_cache, "k_cache"), (v_cache, "v_cache"), (kv_scales, "kv_scales"))
     ptrs = [_dev(t, n) for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"),
                                     (kv_scales, "kv_scales"), (block_tables, "block_tables"),
                                     (seq_lens, "seq_lens"), (out, "out"))]
-    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ext = _extent(q.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len, kv_layout)
     st = lib.tq_decode_fused_static(*ptrs, Hkv, QG, BS, int(tile_groups_per_partition),
                                     float(softmax_scale), ctypes.byref(ext), _stream(stream))
     if st != TQ_OK:
@@ -354,7 +381,8 @@ def tq4_block_bytes(num_kv_heads: int, kv_block_size: int) -> int:
 def tq4_decode(q_rot, kv_cache, centroids, block_tables, seq_lens, partials: Partials,
                num_kv_heads: int, query_group_size: int, kv_block_size: int,
                tile_groups_per_partition: int, softmax_scale: float, *, num_partitions: int,
-               max_seq_len: int, num_blocks: Optional[int] = None, stream=None) -> None:
+               max_seq_len: int, num_blocks: Optional[int] = None, kv_layout: str = "head",
+              stream=None) -> None:
     """Enqueue the partition kernel over the 4-bit record format (C ABI tq4_decode)."""
     lib = load_library()
     Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
@@ -368,7 +396,8 @@ def tq4_decode(q_rot, kv_cache, centroids, block_tables, seq_lens, partials: Par
     for t, n in ((partials.out, "partials.out"), (partials.max_logits, "partials.max_logits"),
                  (partials.exp_sums, "partials.exp_sums")):
         _dev(t, n)
-    ext = _extent(q_rot.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ext = _extent(q_rot.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len,
+                  kv_layout)
     ps = partials._struct()
     st = lib.tq4_decode(*ptrs, ctypes.byref(ps), int(num_kv_heads), int(query_group_size),
                         int(kv_block_size), int(tile_groups_per_partition), float(softmax_scale),
@@ -381,7 +410,7 @@ def tq4_decode_fused(q_rot, kv_cache, centroids, block_tables, seq_lens, out, nu
                      query_group_size: int, kv_block_size: int, tile_groups_per_partition: int,
                      softmax_scale: float, *, num_partitions: int, max_seq_len: int,
                      num_blocks: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
-                     stream=None) -> None:
+                     kv_layout: str = "head", stream=None) -> None:
     """Enqueue the one-launch decode over the 4-bit record format (C ABI tq4_decode_fused)."""
     lib = load_library()
     Hkv, QG, BS = int(num_kv_heads), int(query_group_size), int(kv_block_size)
@@ -392,7 +421,8 @@ def tq4_decode_fused(q_rot, kv_cache, centroids, block_tables, seq_lens, out, nu
     ptrs = [_dev(t, n) for t, n in ((q_rot, "q_rot"), (kv_cache, "kv_cache"),
                                     (centroids, "centroids"), (block_tables, "block_tables"),
                                     (seq_lens, "seq_lens"), (out, "out"))]
-    ext = _extent(q_rot.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len)
+    ext = _extent(q_rot.shape[0], nb, block_tables.shape[1], num_partitions, max_seq_len,
+                  kv_layout)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr = _dev(workspace, "workspace")
@@ -409,18 +439,20 @@ def decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, *, num_kv_hea
                softmax_scale: Optional[float] = None, max_seq_len: Optional[int] = None,
                partials: Optional[Partials] = None, out: Optional[torch.Tensor] = None,
                fused: bool = False, workspace: Optional[torch.Tensor] = None,
-               stream=None) -> torch.Tensor:
-    """decode() for the 4-bit record format: kv_cache uint8 [NB][tq4_block_bytes],
-    centroids fp32 [16], q_rot bf16 [S][Hq][128].  Returns bf16 [S][Hq][128]."""
+               kv_layout: str = "head", stream=None) -> torch.Tensor:
+    """decode() for the 4-bit record format: kv_cache uint8 [NB][tq4_block_bytes] (data rows
+    in the order `kv_layout` names), centroids fp32 [16], q_rot bf16 [S][Hq][128].  Returns
+    bf16 [S][Hq][128]."""
     with _on_stream(stream):
         return _decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads,
                            kv_block_size, num_partitions, tile_groups_per_partition,
-                           softmax_scale, max_seq_len, partials, out, fused, workspace, stream)
+                           softmax_scale, max_seq_len, partials, out, fused, workspace, kv_layout,
+                           stream)
 
 
 def _decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads, kv_block_size,
                 num_partitions, tile_groups_per_partition, softmax_scale, max_seq_len, partials,
-                out, fused, workspace, stream):
+                out, fused, workspace, kv_layout, stream):
     S, Hq, D = q_rot.shape
     Hkv, BS = int(num_kv_heads), int(kv_block_size)
     if D != HEAD_DIM or Hq % Hkv:
@@ -443,38 +475,43 @@ def _decode_tq4(q_rot, kv_cache, centroids, block_tables, seq_lens, num_kv_heads
             workspace = alloc_fused_workspace(S, Hkv, QG, max_seq_len, q_rot.device)
         tq4_decode_fused(q_rot, kv_cache, centroids, block_tables, seq_lens, out, Hkv, QG, BS, G,
                          softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
-                         workspace=workspace, stream=stream)
+                         workspace=workspace, kv_layout=kv_layout, stream=stream)
         return out
     if partials is None:
         partials = alloc_partials(S, Hkv, num_partitions, QG, q_rot.device)
     tq4_decode(q_rot, kv_cache, centroids, block_tables, seq_lens, partials, Hkv, QG, BS, G,
-               softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len, stream=stream)
+               softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
+               kv_layout=kv_layout, stream=stream)
     tq_decode_reduce(partials, seq_lens, out, Hkv, QG, G, num_partitions=num_partitions,
                      max_seq_len=max_seq_len, stream=stream)
     return out
 
 
-def tq_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, kv_scales, *, stream=None) -> None:
+def tq_kv_write(k_new, v_new, slot_mapping, k_cache, v_cache, kv_scales, *,
+                kv_layout: str = "head", stream=None) -> None:
     """Enqueue the KV-cache writer (C ABI tq_kv_write): quantize the new bf16 K/V rows
-    [T][Hkv][128] and store them at slot_mapping (int32 [T], negative = skip)."""
+    [T][Hkv][128] and store them at slot_mapping (int32 [T], negative = skip) in a cache of
+    the given row order ([NB][Hkv][BS][128] "head" or [NB][BS][Hkv][128] "slot")."""
     lib = load_library()
     if not isinstance(k_new, torch.Tensor) or k_new.dim() != 3 or not isinstance(k_cache, torch.Tensor) \
             or k_cache.dim() != 4:
-        raise ValueError("k_new must be [T][Hkv][128] and k_cache [NB][Hkv][BS][128]")
+        raise ValueError("k_new must be [T][Hkv][128] and k_cache a 4-d cache tensor")
     T, Hkv, D = (int(n) for n in k_new.shape)
-    NB, BS = int(k_cache.shape[0]), int(k_cache.shape[2])
+    NB = int(k_cache.shape[0])
+    BS = int(k_cache.shape[2] if kv_layout == "head" else k_cache.shape[1])
     _expect(k_new, "k_new", torch.bfloat16, (T, Hkv, HEAD_DIM))
     _expect(v_new, "v_new", torch.bfloat16, (T, Hkv, HEAD_DIM))
     _expect(slot_mapping, "slot_mapping", torch.int32, (T,))
-    _expect(k_cache, "k_cache", _FP8_CODES, (NB, Hkv, BS, HEAD_DIM))
-    _expect(v_cache, "v_cache", _FP8_CODES, (NB, Hkv, BS, HEAD_DIM))
+    _expect(k_cache, "k_cache", _FP8_CODES, cache_shape(NB, Hkv, BS, kv_layout))
+    _expect(v_cache, "v_cache", _FP8_CODES, cache_shape(NB, Hkv, BS, kv_layout))
     _expect(kv_scales, "kv_scales", torch.float32, (NB, Hkv, 2, BS))
     if T == 0:
         return
     ptrs = [_dev(t, n) for t, n in ((k_new, "k_new"), (v_new, "v_new"), (slot_mapping, "slot_mapping"),
                                     (k_cache, "k_cache"), (v_cache, "v_cache"),
                                     (kv_scales, "kv_scales"))]
-    st = lib.tq_kv_write(*ptrs, int(T), int(Hkv), int(BS), int(NB), int(D), _stream(stream))
+    st = lib.tq_kv_write(*ptrs, int(T), int(Hkv), int(BS), int(NB), int(D), _layout(kv_layout),
+                         _stream(stream))
     if st != TQ_OK:
         raise TqError(st, "tq_kv_write")
 
@@ -483,14 +520,16 @@ def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partit
            tile_groups_per_partition: int = 1, softmax_scale: Optional[float] = None,
            max_seq_len: Optional[int] = None, partials: Optional[Partials] = None,
            out: Optional[torch.Tensor] = None, fused: bool = False,
-           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+           workspace: Optional[torch.Tensor] = None, kv_layout: str = "head",
+           stream=None) -> torch.Tensor:
     """Decode attention; returns bf16 [S][Hkv*QG][128].
 
     fused=False: tq_decode then tq_decode_reduce (partials in `partials` or
     allocated here); fused=True: tq_decode_fused with `workspace` (a zero-filled
     one is allocated here when None).
 
-    q bf16 [S][Hq][128]; k_cache/v_cache uint8 (e4m3fn codes) [NB][Hkv][BS][128];
+    q bf16 [S][Hq][128]; k_cache/v_cache uint8 (e4m3fn codes) [NB][Hkv][BS][128]
+    (kv_layout "head") or [NB][BS][Hkv][128] ("slot", the page's data-region order);
     kv_scales fp32 [NB][Hkv][2][BS]; block_tables/seq_lens int32.
     ``max_seq_len`` (an upper bound of seq_lens) is read from seq_lens when not
     given, which synchronizes the stream; under graph capture it is the block
@@ -502,14 +541,18 @@ def decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, *, num_partit
     with _on_stream(stream):
         return _decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_partitions,
                        tile_groups_per_partition, softmax_scale, max_seq_len, partials, out, fused,
-                       workspace, stream)
+                       workspace, kv_layout, stream)
 
 
 def _decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_partitions,
             tile_groups_per_partition, softmax_scale, max_seq_len, partials, out, fused, workspace,
-            stream):
+            kv_layout, stream):
     S, Hq, D = q.shape
-    NB, Hkv, BS, Dk = k_cache.shape
+    _layout(kv_layout)
+    if kv_layout == "head":
+        NB, Hkv, BS, Dk = k_cache.shape
+    else:
+        NB, BS, Hkv, Dk = k_cache.shape
     if D != HEAD_DIM or Dk != HEAD_DIM or Hq % Hkv:
         raise ValueError("head_dim must be 128 and num_q_heads a multiple of num_kv_heads")
     QG = Hq // Hkv
@@ -530,13 +573,13 @@ def _decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, num_partitio
             workspace = alloc_fused_workspace(S, Hkv, QG, max_seq_len, q.device)
         tq_decode_fused(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, out, Hkv, QG, BS, G,
                         softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
-                        num_blocks=NB, workspace=workspace, stream=stream)
+                        num_blocks=NB, workspace=workspace, kv_layout=kv_layout, stream=stream)
         return out
     if partials is None:
         partials = alloc_partials(S, Hkv, num_partitions, QG, q.device)
     tq_decode(q, k_cache, v_cache, kv_scales, block_tables, seq_lens, partials, Hkv, QG, BS, G,
               softmax_scale, num_partitions=num_partitions, max_seq_len=max_seq_len,
-              num_blocks=NB, stream=stream)
+              num_blocks=NB, kv_layout=kv_layout, stream=stream)
     tq_decode_reduce(partials, seq_lens, out, Hkv, QG, G, num_partitions=num_partitions,
                      max_seq_len=max_seq_len, stream=stream)
     return out

@@ -20,6 +20,19 @@ bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 bool supported_qg(int32_t qg) { return qg == 6 || qg == 8 || qg == 16; }
 bool supported_bs(int32_t bs) { return bs == 16 || bs == 32; }
 
+// Byte distances between the 128-byte rows of consecutive kv heads and slots
+// inside a cache block, for either row order.
+void set_row_strides(int32_t layout, int32_t num_kv_heads, int32_t kv_block_size,
+                     int32_t* head_stride, int32_t* slot_stride) {
+  if (layout == TQ_KV_LAYOUT_SLOT_MAJOR) {
+    *head_stride = TQ_HEAD_DIM;
+    *slot_stride = num_kv_heads * TQ_HEAD_DIM;
+  } else {
+    *head_stride = kv_block_size * TQ_HEAD_DIM;
+    *slot_stride = TQ_HEAD_DIM;
+  }
+}
+
 // Checks shared by both entry points.  On success fills partition_tokens and
 // len_cap (the device-side clamp of sequence lengths).
 tq_status check_common(const tq_extent* ext, int32_t num_kv_heads, int32_t query_group_size,
@@ -55,6 +68,9 @@ tq_status check_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_c
   if (s != TQ_OK) return s;
   if ((int64_t)ext->max_seq_len > (int64_t)ext->max_blocks_per_seq * kv_block_size)
     return TQ_ERR_COVERAGE;
+  if ((int64_t)num_kv_heads * kv_block_size * (TQ_HEAD_DIM + 3 * 2) > INT32_MAX) return TQ_ERR_SHAPE;
+  if (ext->kv_layout != TQ_KV_LAYOUT_HEAD_MAJOR && ext->kv_layout != TQ_KV_LAYOUT_SLOT_MAJOR)
+    return TQ_ERR_UNSUPPORTED;
   if (!isfinite(softmax_scale) || !(softmax_scale > 0.f)) return TQ_ERR_SCALE;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(kv_scales) ||
       !aligned4(block_tables) || !aligned4(seq_lens))
@@ -66,6 +82,8 @@ tq_status check_decode(const void* q, const uint8_t* k_cache, const uint8_t* v_c
   st->tq4 = nullptr;
   st->centroids = nullptr;
   st->tq4_block_bytes = 0;
+  set_row_strides(ext->kv_layout, num_kv_heads, kv_block_size, &st->row_head_stride,
+                  &st->row_slot_stride);
   st->bt = block_tables;
   st->num_kv_heads = num_kv_heads;
   st->max_blocks = ext->max_blocks_per_seq;
@@ -343,11 +361,14 @@ tq_status tq_decode_reduce(const tq_partials* partials, const int32_t* seq_lens,
 tq_status tq_kv_write(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                       uint8_t* k_cache, uint8_t* v_cache, float* kv_scales, int32_t num_tokens,
                       int32_t num_kv_heads, int32_t kv_block_size, int32_t num_blocks,
-                      int32_t head_dim, void* stream) {
+                      int32_t head_dim, int32_t kv_layout, void* stream) {
   if (num_tokens < 0 || num_kv_heads < 1 || num_blocks < 1) return TQ_ERR_SHAPE;
-  if (head_dim != TQ_HEAD_DIM || !supported_bs(kv_block_size)) return TQ_ERR_UNSUPPORTED;
+  if (head_dim != TQ_HEAD_DIM || !supported_bs(kv_block_size) ||
+      (kv_layout != TQ_KV_LAYOUT_HEAD_MAJOR && kv_layout != TQ_KV_LAYOUT_SLOT_MAJOR))
+    return TQ_ERR_UNSUPPORTED;
   if ((int64_t)num_blocks * kv_block_size > INT32_MAX ||
-      (int64_t)num_tokens * num_kv_heads > INT32_MAX / 2)
+      (int64_t)num_tokens * num_kv_heads > INT32_MAX / 2 ||
+      (int64_t)num_kv_heads * kv_block_size * TQ_HEAD_DIM > INT32_MAX)
     return TQ_ERR_SHAPE;
   if (num_tokens == 0) return TQ_OK;
   if (!k_new || !v_new || !slot_mapping || !k_cache || !v_cache || !kv_scales) return TQ_ERR_NULL;
@@ -361,6 +382,7 @@ tq_status tq_kv_write(const void* k_new, const void* v_new, const int32_t* slot_
   a.k = k_cache;
   a.v = v_cache;
   a.scales = kv_scales;
+  set_row_strides(kv_layout, num_kv_heads, kv_block_size, &a.row_head_stride, &a.row_slot_stride);
   a.num_tokens = num_tokens;
   a.num_kv_heads = num_kv_heads;
   a.kv_block_size = kv_block_size;
@@ -381,7 +403,7 @@ const char* tq_status_str(tq_status status) {
     case TQ_OK: return "ok";
     case TQ_ERR_NULL: return "a required pointer is NULL";
     case TQ_ERR_MISALIGNED: return "a data pointer is not 16-byte aligned";
-    case TQ_ERR_UNSUPPORTED: return "unsupported size (query_group_size in {6,8,16}, kv_block_size in {16,32}, head_dim 128)";
+    case TQ_ERR_UNSUPPORTED: return "unsupported size or layout (query_group_size in {6,8,16}, kv_block_size in {16,32}, head_dim 128, kv_layout 0 or 1)";
     case TQ_ERR_SHAPE: return "invalid or overflowing shape (a count < 1 or too large)";
     case TQ_ERR_COVERAGE: return "max_seq_len is negative or exceeds num_partitions*256*G or max_blocks_per_seq*kv_block_size";
     case TQ_ERR_SCALE: return "softmax_scale must be finite and > 0";

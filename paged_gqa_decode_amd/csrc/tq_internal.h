@@ -29,12 +29,18 @@ constexpr int kFlatUnitTokens = 32;
 // format uses k, v and scales; the 4-bit record format tq4 and centroids.
 struct StreamArgs {
   const uint16_t* q;        // bf16 [S][Hkv*QG][128]
-  const uint8_t* k;         // e4m3fn [NB][Hkv][BS][128]
-  const uint8_t* v;         // e4m3fn [NB][Hkv][BS][128]
+  const uint8_t* k;         // e4m3fn, NB blocks of Hkv*BS rows of 128 bytes
+  const uint8_t* v;         // e4m3fn, the same
   const float* scales;      // fp32 [NB][Hkv][2][BS]
   const uint8_t* tq4;       // 4-bit records [NB][tq4_block_bytes]
   const float* centroids;   // fp32 [16]
   int32_t tq4_block_bytes;  // Hkv*BS*128 + Hkv*3*BS*2
+  // Byte distance between the 128-byte rows of consecutive kv heads and of
+  // consecutive slots inside a block (both formats): head-major blocks
+  // [Hkv][BS][128] have (BS*128, 128), slot-major ones [BS][Hkv][128] (the
+  // page's data region) (128, Hkv*128).
+  int32_t row_head_stride;
+  int32_t row_slot_stride;
   const int32_t* bt;        // int32 [S][max_blocks]
   int32_t num_kv_heads;
   int32_t max_blocks;       // block-table row stride
@@ -152,9 +158,11 @@ struct KvWriteArgs {
   const uint16_t* k_new;        // bf16 [T][Hkv][128]
   const uint16_t* v_new;        // bf16 [T][Hkv][128]
   const int32_t* slot_mapping;  // [T]: block * BS + offset, negative = skip
-  uint8_t* k;                   // e4m3fn [NB][Hkv][BS][128]
+  uint8_t* k;                   // e4m3fn, NB blocks of Hkv*BS rows of 128 bytes
   uint8_t* v;
   float* scales;                // fp32 [NB][Hkv][2][BS]
+  int32_t row_head_stride;      // as in StreamArgs
+  int32_t row_slot_stride;
   int32_t num_tokens;
   int32_t num_kv_heads;
   int32_t kv_block_size;

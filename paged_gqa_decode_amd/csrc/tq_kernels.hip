@@ -172,10 +172,11 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Byte offset of the 128-byte row of (block, kv head, slot): each (block, kv
-// head) slice of BS rows is contiguous.
-__device__ __forceinline__ size_t row_offset(uint32_t blk, int slot, int BS, int Hkv, int h) {
-  return (((size_t)blk * Hkv + h) * BS + slot) * D;
+// Byte offset, inside its block, of the 128-byte row of (kv head h, slot): the
+// rows are head-major or slot-major (the page's data-region order) as the two
+// strides say.  Below 2^31 (a block holds Hkv*BS rows of 128 bytes).
+__device__ __forceinline__ uint32_t row_in_block(const StreamArgs& a, int h, int slot) {
+  return (uint32_t)(h * a.row_head_stride + slot * a.row_slot_stride);
 }
 
 // Byte offset in the V LDS tile of 16-byte piece `piece` of token row `tok`:
@@ -302,6 +303,20 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
     for (int c = 0; c < 4; ++c) qop[c] = bf16x8{};
   }
 
+  // Per-lane byte offsets inside a block, fixed for the stream: K pieces of
+  // token rows 16t + r (BS 32; row r of either block for BS 16) and V pieces
+  // of token rows 8j + lane / 8, in the swizzled piece order.
+  const size_t block_bytes = (size_t)Hkv * BS * D;
+  uint32_t k_off[2], v_off[4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) k_off[t] = row_in_block(a, h, BS == 32 ? 16 * t + r : r) + 32 * b;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tok = 8 * j + (lane >> 3);
+    const int piece = (lane & 7) ^ ((tok >> 1) & 7);
+    v_off[j] = row_in_block(a, h, BS == 32 ? tok : (tok & 15)) + 16 * piece;
+  }
+
   // Issue the loads of chunk c: K pieces into registers, V rows and scales
   // into LDS stage `st`.
   i32x4 kraw[2][2];
@@ -313,19 +328,15 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const uint32_t blk = (BS == 32 || t == 0) ? blkA : blkB;
-      const int slot = BS == 32 ? 16 * t + r : r;
-      const uint8_t* src = a.k + row_offset(blk, slot, BS, Hkv, h) + 32 * b;
+      const uint8_t* src = a.k + (size_t)blk * block_bytes + k_off[t];
       kraw[t][0] = *reinterpret_cast<const i32x4*>(src);
       kraw[t][1] = *reinterpret_cast<const i32x4*>(src + 16);
     }
     uint8_t* vdst = lds_v + st * (CHUNK * D);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int tok = 8 * j + (lane >> 3);
-      const int piece = (lane & 7) ^ ((tok >> 1) & 7);
-      const uint32_t blk = (BS == 32 || tok < 16) ? blkA : blkB;
-      const int slot = BS == 32 ? tok : (tok & 15);
-      const uint8_t* src = a.v + row_offset(blk, slot, BS, Hkv, h) + 16 * piece;
+      const uint32_t blk = (BS == 32 || j < 2) ? blkA : blkB;  // tokens 16..31: j >= 2
+      const uint8_t* src = a.v + (size_t)blk * block_bytes + v_off[j];
       __builtin_amdgcn_global_load_lds(src, (lds_void*)(vdst + 1024 * j), 16, 0,
                                        kCachePolicyStreaming);
     }
@@ -467,17 +478,18 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
 
 // ---------------------------------------------------------------------------
 // The 4-bit record format ("TQ" record of the tq_decode page).  A cache block
-// is [Hkv][BS][128] bytes of rows (K indices in bytes 0..63, V indices in
-// 64..127; dim d in byte d/2, low nibble for even d), then fp16 metadata
-// [Hkv][3][BS]: K norm, V scale, V zero point.  k = centroids[index] * norm,
-// v = index * scale + zero.
+// is Hkv*BS rows of 128 bytes, head-major [Hkv][BS] or slot-major [BS][Hkv]
+// (the page's data region; row_in_block), each with the K indices in bytes
+// 0..63 and the V indices in 64..127 (dim d in byte d/2, low nibble for even
+// d), then fp16 metadata [Hkv][3][BS]: K norm, V scale, V zero point.
+// k = centroids[index] * norm, v = index * scale + zero.
 //
 // Per-wave LDS of the 4-bit stream: two 4 KiB row stages and two 256 B
 // metadata stages ([3][32] fp16), in the same 8.5 KiB staging area as the fp8
 // stream's; the 1 KiB centroid table is a workgroup's LDS array of its own.
 //  * A chunk's 32 rows of 128 B (a whole block's slots of one kv head when
-//    BS = 32, two 2 KiB runs when BS = 16) arrive whole, by LDS-direct loads
-//    of 1 KiB each, and K is read back from LDS.  Splitting each row between a
+//    BS = 32, of two blocks when BS = 16) arrive whole, by LDS-direct loads
+//    of 8 rows each, and K is read back from LDS.  Splitting each row between a
 //    K register load and a V LDS load instead (two requests per 128-byte line)
 //    streams about 13 % slower on this GPU.
 //  * Row R's 16-byte pieces p = 0..7 (K: 0..3, V: 4..7) sit at slot
@@ -634,7 +646,7 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
     const int row = 8 * j + (lane >> 3);
     const int piece = (lane & 7) ^ tq4_row_swz(row);
     const int slot = BS == 32 ? row : (row & 15);
-    row_off[j] = (uint32_t)(h * BS * D + slot * D + 16 * piece);
+    row_off[j] = row_in_block(a, h, slot) + 16 * piece;
   }
   const int ml = lane < 48 ? lane : 0;
   const uint32_t meta_off =
@@ -1851,8 +1863,9 @@ __global__ __launch_bounds__(256) void tq_kv_write_kernel(KvWriteArgs a) {
   const int BS = a.kv_block_size;
   const int blk = slot / BS;
   const int off = slot % BS;
-  const size_t src = (size_t)row * D + 16 * j;                           // bf16 elements
-  const size_t dst = (((size_t)blk * Hkv + h) * BS + off) * D + 16 * j;  // bytes
+  const size_t src = (size_t)row * D + 16 * j;  // bf16 elements
+  const size_t dst = (size_t)blk * Hkv * BS * D +
+                     (uint32_t)(h * a.row_head_stride + off * a.row_slot_stride) + 16 * j;  // bytes
   u32x4 in[2][2];
 #pragma unroll
   for (int field = 0; field < 2; ++field) {

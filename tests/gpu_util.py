@@ -35,7 +35,7 @@ def gpu_decode(inp: workloads.Inputs, num_partitions=None, tile_groups=None, par
     res = tq.decode(inp.q, inp.k_cache, inp.v_cache, inp.kv_scales, inp.block_tables, inp.seq_lens,
                     num_partitions=P, tile_groups_per_partition=G,
                     softmax_scale=inp.softmax_scale, max_seq_len=maxlen, partials=partials,
-                    out=out, fused=(path == "fused"))
+                    out=out, fused=(path == "fused"), kv_layout=inp.kv_layout)
     torch.cuda.synchronize()
     return res
 
@@ -43,7 +43,8 @@ def gpu_decode(inp: workloads.Inputs, num_partitions=None, tile_groups=None, par
 def oracle_decode(inp: workloads.Inputs, units=None):
     c = inp.to("cpu")
     return oracle.decode(c.q, c.k_cache, c.v_cache, c.kv_scales, c.block_tables, c.seq_lens,
-                         inp.softmax_scale, units=units, nthreads=ORACLE_THREADS)
+                         inp.softmax_scale, units=units, nthreads=ORACLE_THREADS,
+                         layout=inp.kv_layout)
 
 
 def compare(got_bf16: torch.Tensor, ref: np.ndarray, what: str, max_abs=MAX_ABS, mean_abs=MEAN_ABS):

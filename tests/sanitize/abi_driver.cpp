@@ -30,6 +30,7 @@ void* fake(uintptr_t i) { return reinterpret_cast<void*>(uintptr_t(0x10000000) +
 
 struct Case {
   int S, Hkv, QG, BS, G, P, maxlen, NB, mb;
+  int layout = TQ_KV_LAYOUT_HEAD_MAJOR;
 };
 
 tq_extent extent(const Case& c) {
@@ -40,6 +41,7 @@ tq_extent extent(const Case& c) {
   e.num_partitions = c.P;
   e.max_seq_len = c.maxlen;
   e.head_dim = 128;
+  e.kv_layout = c.layout;
   return e;
 }
 
@@ -147,10 +149,11 @@ void run_invalid() {
   EXPECT(g_log.partition == before.partition);  // nothing launched
 
   // the writer
-  auto kvw = [&](int T, int Hkv, int BS, int NB, int hd, const void* kn) {
+  auto kvw = [&](int T, int Hkv, int BS, int NB, int hd, const void* kn, int layout = 0) {
     return tq_kv_write(kn, fake(21), (const int32_t*)fake(22), (uint8_t*)fake(23),
-                       (uint8_t*)fake(24), (float*)fake(25), T, Hkv, BS, NB, hd, nullptr);
+                       (uint8_t*)fake(24), (float*)fake(25), T, Hkv, BS, NB, hd, layout, nullptr);
   };
+  EXPECT(kvw(4, 2, 16, 8, 128, fake(20), 2) == TQ_ERR_UNSUPPORTED);
   EXPECT(kvw(0, 2, 16, 8, 128, nullptr) == TQ_OK);
   EXPECT(kvw(4, 2, 16, 8, 128, nullptr) == TQ_ERR_NULL);
   EXPECT(kvw(4, 2, 24, 8, 128, fake(20)) == TQ_ERR_UNSUPPORTED);
@@ -162,12 +165,14 @@ void run_invalid() {
   EXPECT(g_log.kv_write == before.kv_write);
   EXPECT(kvw(4, 2, 16, 8, 128, fake(20)) == TQ_OK);
   EXPECT(g_log.kv_write == before.kv_write + 1);
+  EXPECT(kvw(4, 2, 16, 8, 128, fake(20), TQ_KV_LAYOUT_SLOT_MAJOR) == TQ_OK);
+  EXPECT(g_log.kv_write == before.kv_write + 2);
 
   // sizes of the 4-bit record, status strings, version
   EXPECT(tq4_block_bytes(8, 32) == (size_t)8 * 32 * 134);
   EXPECT(tq4_block_bytes(8, 24) == 0);
   EXPECT(tq4_block_bytes(0, 32) == 0);
-  for (int s = 0; s < 8; ++s) EXPECT(strlen(tq_status_str((tq_status)s)) > 0);
+  for (int s = 0; s < 9; ++s) EXPECT(strlen(tq_status_str((tq_status)s)) > 0);
   EXPECT(strcmp(tq_status_str((tq_status)99), "unknown status") == 0);
   EXPECT(tq_abi_version() == TQ_ABI_VERSION);
   EXPECT(tq_last_hip_error() == 0);
@@ -187,6 +192,10 @@ int main() {
       {1, 1, 8, 32, 4096, 1, 1 << 20, 40000, 1 << 15},  // one very long sequence
   };
   for (const Case& c : valid) run_valid(c);
+  for (Case c : valid) {  // the page's slot-major row order
+    c.layout = TQ_KV_LAYOUT_SLOT_MAJOR;
+    run_valid(c);
+  }
   run_invalid();
   run_static_limits();
   setenv("TQ_VALIDATE", "1", 1);

@@ -17,6 +17,12 @@ void require(bool ok, const char* what) {
     abort();
   }
 }
+// The row strides of either order: one of them is a single 128-byte row.
+void require_row_strides(int head_stride, int slot_stride, int Hkv, int BS) {
+  require((head_stride == BS * 128 && slot_stride == 128) ||
+              (head_stride == 128 && slot_stride == Hkv * 128),
+          "row strides");
+}
 bool in_range(const void* p, const void* base, size_t bytes) {
   return (const char*)p >= (const char*)base && (const char*)p <= (const char*)base + bytes;
 }
@@ -31,6 +37,7 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
   require(query_group_size == 6 || query_group_size == 8 || query_group_size == 16, "QG");
   require(kv_block_size == 16 || kv_block_size == 32, "BS");
   require(a.o && a.ml && a.es && a.seq_lens && a.st.bt && a.st.q, "partition pointers");
+  require_row_strides(a.st.row_head_stride, a.st.row_slot_stride, a.st.num_kv_heads, kv_block_size);
   require(tq4 ? (a.st.tq4 && a.st.centroids) : (a.st.k && a.st.v && a.st.scales), "format");
   // The launcher's plan: the flat kernel's grid, else one wave per run of partitions.
   const int flat_groups = plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap,
@@ -85,6 +92,7 @@ hipError_t launch_reduce(const ReduceArgs& a, int num_seq_heads, hipStream_t) {
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t) {
   ++g_log.kv_write;
   require(a.num_tokens >= 1 && a.num_kv_heads >= 1 && a.num_slots >= 1, "writer args");
+  require_row_strides(a.row_head_stride, a.row_slot_stride, a.num_kv_heads, a.kv_block_size);
   return hipSuccess;
 }
 

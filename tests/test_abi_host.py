@@ -55,7 +55,7 @@ def test_every_header_is_covered():
 
 
 def test_abi_version_and_status_strings(lib):
-    assert tq.abi_version() == 1
+    assert tq.abi_version() == 2
     for st in range(9):
         assert tq.status_str(st) != "unknown status"
     assert tq.status_str(99) == "unknown status"
@@ -76,10 +76,10 @@ A = 0x10000
 
 
 def call_decode(lib, *, ptrs=None, QG=8, BS=16, G=1, Hkv=2, scale=0.088, S=2, NB=8, MB=4, P=1,
-                maxlen=64, head_dim=128, part=None):
+                maxlen=64, head_dim=128, part=None, layout=0):
     ptrs = ptrs or [A] * 6
     ps = tq.PartialsStruct(*(part or (A, A, A)))
-    ext = tq.Extent(S, NB, MB, P, maxlen, head_dim)
+    ext = tq.Extent(S, NB, MB, P, maxlen, head_dim, layout)
     return lib.tq_decode(*ptrs, ctypes.byref(ps), Hkv, QG, BS, G, scale, ctypes.byref(ext), None)
 
 
@@ -92,6 +92,8 @@ def call_decode(lib, *, ptrs=None, QG=8, BS=16, G=1, Hkv=2, scale=0.088, S=2, NB
     (dict(BS=8), tq.TQ_ERR_UNSUPPORTED),
     (dict(BS=64), tq.TQ_ERR_UNSUPPORTED),
     (dict(head_dim=64), tq.TQ_ERR_UNSUPPORTED),
+    (dict(layout=2), tq.TQ_ERR_UNSUPPORTED),
+    (dict(layout=-1), tq.TQ_ERR_UNSUPPORTED),
     (dict(S=0), tq.TQ_ERR_SHAPE),
     (dict(Hkv=0), tq.TQ_ERR_SHAPE),
     (dict(NB=0), tq.TQ_ERR_SHAPE),
@@ -262,9 +264,9 @@ def test_product_path_does_not_import_the_oracle():
                 assert "oracle.c" not in text and "liboracle" not in text, f
 
 
-def call_kv_write(lib, *, ptrs=None, T=4, Hkv=2, BS=16, NB=8, D=128):
+def call_kv_write(lib, *, ptrs=None, T=4, Hkv=2, BS=16, NB=8, D=128, layout=0):
     ptrs = ptrs or [A] * 6
-    return lib.tq_kv_write(*ptrs, T, Hkv, BS, NB, D, None)
+    return lib.tq_kv_write(*ptrs, T, Hkv, BS, NB, D, layout, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -274,6 +276,8 @@ def call_kv_write(lib, *, ptrs=None, T=4, Hkv=2, BS=16, NB=8, D=128):
     (dict(NB=1 << 30, BS=32), tq.TQ_ERR_SHAPE),
     (dict(BS=8), tq.TQ_ERR_UNSUPPORTED),
     (dict(D=64), tq.TQ_ERR_UNSUPPORTED),
+    (dict(layout=2), tq.TQ_ERR_UNSUPPORTED),
+    (dict(layout=-1), tq.TQ_ERR_UNSUPPORTED),
     (dict(ptrs=[A, A, 0, A, A, A]), tq.TQ_ERR_NULL),
     (dict(ptrs=[A + 4, A, A, A, A, A]), tq.TQ_ERR_MISALIGNED),
     (dict(ptrs=[A, A, A, A, A, A + 8]), tq.TQ_ERR_MISALIGNED),

@@ -24,7 +24,8 @@ def gpu_tq4(inp, path, num_partitions=None, tile_groups=None):
                         num_kv_heads=wl.num_kv_heads, kv_block_size=wl.kv_block_size,
                         num_partitions=P, tile_groups_per_partition=G,
                         softmax_scale=inp.softmax_scale,
-                        max_seq_len=int(inp.seq_lens.max().item()), fused=(path == "fused"))
+                        max_seq_len=int(inp.seq_lens.max().item()), fused=(path == "fused"),
+                        kv_layout=inp.kv_layout)
     torch.cuda.synchronize()
     return out
 
@@ -33,7 +34,7 @@ def oracle_tq4(inp, units=None):
     c = inp.to("cpu")
     return oracle.decode_tq4(c.q, c.cache, c.centroids, c.block_tables, c.seq_lens,
                              inp.softmax_scale, inp.wl.num_kv_heads, inp.wl.kv_block_size,
-                             units=units, nthreads=ORACLE_THREADS)
+                             units=units, nthreads=ORACLE_THREADS, layout=inp.kv_layout)
 
 
 def bits(t):

@@ -22,8 +22,10 @@ Recipe (the same for every workload):
 
 Layouts (all C-contiguous):
   q             bf16   [S][Hkv*QG][D]
-  k_cache       uint8  [NB][Hkv][BS][D]  (e4m3fn codes; one (block, kv head) slice contiguous)
-  v_cache       uint8  [NB][Hkv][BS][D]
+  k_cache       uint8  [NB][Hkv][BS][D]  (e4m3fn codes, kv_layout "head": one (block, kv head)
+                                          slice contiguous), or [NB][BS][Hkv][D] ("slot": the
+                                          page's data-region order; the same values, permuted)
+  v_cache       uint8  the same as k_cache
   kv_scales     fp32   [NB][Hkv][2][BS]  (field 0 = K, field 1 = V)
   block_tables  int32  [S][max_blocks_per_seq]
   seq_lens      int32  [S]
@@ -111,12 +113,21 @@ class Inputs:
     num_partitions: int
     num_blocks: int
     softmax_scale: float
+    kv_layout: str = "head"
 
     def to(self, device) -> "Inputs":
         f = lambda t: t.to(device)  # noqa: E731
         return dataclasses.replace(self, q=f(self.q), k_cache=f(self.k_cache), v_cache=f(self.v_cache),
                                    kv_scales=f(self.kv_scales), block_tables=f(self.block_tables),
                                    seq_lens=f(self.seq_lens))
+
+    def with_layout(self, kv_layout: str) -> "Inputs":
+        """The same inputs with the cache rows in the other order (a permuted copy)."""
+        if kv_layout == self.kv_layout:
+            return self
+        swap = lambda t: t.permute(0, 2, 1, 3).contiguous()  # noqa: E731
+        return dataclasses.replace(self, k_cache=swap(self.k_cache), v_cache=swap(self.v_cache),
+                                   kv_layout=kv_layout)
 
     def kv_bytes(self) -> int:
         """Bytes of live K/V codes plus scales: sum over sequences and kv heads of L * (2*D + 8)."""
@@ -141,8 +152,10 @@ def quantize_rows(x: torch.Tensor):
 
 
 def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
-                softmax_scale: Optional[float] = None, _skip_cache: bool = False) -> Inputs:
-    """Draw the inputs of workload `wl` on `device` (deterministic per device).
+                softmax_scale: Optional[float] = None, _skip_cache: bool = False,
+                kv_layout: str = "head") -> Inputs:
+    """Draw the inputs of workload `wl` on `device` (deterministic per device); kv_layout
+    "slot" gives the same values with the cache rows slot-major.
     _skip_cache: leave the fp8 cache empty (for the 4-bit format's generator)."""
     dev = torch.device(device)
     rng = np.random.default_rng(wl.seed)
@@ -196,9 +209,13 @@ def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
             del x, codes, sc
     if softmax_scale is None:
         softmax_scale = float(np.float32(1.0 / math.sqrt(D)))
-    return Inputs(wl=wl, q=q, k_cache=k_codes, v_cache=v_codes, kv_scales=scales,
-                  block_tables=torch.from_numpy(bt).to(dev), seq_lens=torch.from_numpy(sl).to(dev),
-                  num_partitions=int(num_partitions), num_blocks=NB, softmax_scale=softmax_scale)
+    inp = Inputs(wl=wl, q=q, k_cache=k_codes, v_cache=v_codes, kv_scales=scales,
+                 block_tables=torch.from_numpy(bt).to(dev), seq_lens=torch.from_numpy(sl).to(dev),
+                 num_partitions=int(num_partitions), num_blocks=NB, softmax_scale=softmax_scale)
+    if kv_layout != "head":
+        del k_codes, v_codes
+        inp = inp.with_layout(kv_layout)
+    return inp
 
 
 def small_workload(name="small", num_seqs=3, num_kv_heads=2, query_group_size=8, kv_block_size=16,
@@ -230,13 +247,16 @@ def poison(inp: Inputs, seed: int = 99) -> Inputs:
     bt = inp.block_tables.cpu().numpy().copy()
     sl = inp.seq_lens.cpu().numpy()
     BS = inp.wl.kv_block_size
+    # the slots of a block: dim 2 of a head-major cache, dim 1 of a slot-major one
+    kh = k if inp.kv_layout == "head" else k.transpose(1, 2)
+    vh = v if inp.kv_layout == "head" else v.transpose(1, 2)
     for s, L in enumerate(sl):
         L = int(L)
         nb_used = -(-L // BS)
         if L % BS:
             b = int(bt[s, nb_used - 1])
-            k[b, :, L % BS:] = 0x7F
-            v[b, :, L % BS:] = 0x7F
+            kh[b, :, L % BS:] = 0x7F
+            vh[b, :, L % BS:] = 0x7F
             sc[b, :, :, L % BS:] = float("nan")
         tail = bt.shape[1] - nb_used
         if tail > 0:
@@ -284,13 +304,17 @@ def lloyd_max_normal_16(iters: int = 200) -> np.ndarray:
     return np.asarray(c, dtype=np.float32)
 
 
-def pack_tq4(k_idx: torch.Tensor, v_idx: torch.Tensor, meta_bits: torch.Tensor) -> torch.Tensor:
+def pack_tq4(k_idx: torch.Tensor, v_idx: torch.Tensor, meta_bits: torch.Tensor,
+             kv_layout: str = "head") -> torch.Tensor:
     """Indices uint8 [NB][Hkv][BS][D] (values 0..15) and fp16 meta bits int16
-    [NB][Hkv][3][BS] -> cache uint8 [NB][block_bytes]."""
+    [NB][Hkv][3][BS] -> cache uint8 [NB][block_bytes], the data rows in the order kv_layout
+    names ("head" [Hkv][BS], "slot" [BS][Hkv])."""
     NB, Hkv, BS, D = k_idx.shape
     data = torch.empty((NB, Hkv, BS, D), dtype=torch.uint8, device=k_idx.device)
     data[..., :D // 2] = k_idx[..., 0::2] | (k_idx[..., 1::2] << 4)
     data[..., D // 2:] = v_idx[..., 0::2] | (v_idx[..., 1::2] << 4)
+    if kv_layout != "head":
+        data = data.permute(0, 2, 1, 3).contiguous()
     meta = meta_bits.contiguous().view(torch.uint8).reshape(NB, -1)
     return torch.cat([data.reshape(NB, -1), meta], dim=1).contiguous()
 
@@ -326,6 +350,20 @@ class InputsTq4:
     num_partitions: int
     num_blocks: int
     softmax_scale: float
+    kv_layout: str = "head"
+
+    def with_layout(self, kv_layout: str) -> "InputsTq4":
+        """The same records with the data rows of every block in the other order."""
+        if kv_layout == self.kv_layout:
+            return self
+        wl = self.wl
+        Hkv, BS, D = wl.num_kv_heads, wl.kv_block_size, wl.head_dim
+        NB = self.cache.shape[0]
+        nd = Hkv * BS * D
+        data = self.cache[:, :nd].reshape(NB, *((Hkv, BS) if self.kv_layout == "head" else (BS, Hkv)), D)
+        data = data.permute(0, 2, 1, 3).reshape(NB, nd)
+        return dataclasses.replace(self, cache=torch.cat([data, self.cache[:, nd:]], dim=1).contiguous(),
+                                   kv_layout=kv_layout)
 
     def to(self, device) -> "InputsTq4":
         f = lambda t: t.to(device)  # noqa: E731
@@ -339,7 +377,7 @@ class InputsTq4:
 
 
 def make_inputs_tq4(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
-                    softmax_scale: Optional[float] = None) -> InputsTq4:
+                    softmax_scale: Optional[float] = None, kv_layout: str = "head") -> InputsTq4:
     """Draw the 4-bit-format inputs of workload `wl` on `device` (same lengths, tables and q
     as make_inputs; the cache from the same K/V draws, quantized to the 4-bit record)."""
     dev = torch.device(device)
@@ -357,11 +395,11 @@ def make_inputs_tq4(wl: Workload, device="cpu", seq_lens=None, num_partitions=No
         y = torch.randn((b1 - b0, Hkv, BS, D), generator=gv, device=dev, dtype=torch.float32)
         k_idx, v_idx, meta = quantize_tq4_rows(x, y, cent)
         meta_bits = meta.view(torch.int16).permute(0, 1, 3, 2).contiguous()  # [b][Hkv][3][BS]
-        cache[b0:b1] = pack_tq4(k_idx, v_idx, meta_bits)
+        cache[b0:b1] = pack_tq4(k_idx, v_idx, meta_bits, kv_layout)
         del x, y, k_idx, v_idx, meta, meta_bits
     return InputsTq4(wl=wl, q=base.q, cache=cache, centroids=cent, block_tables=base.block_tables,
                      seq_lens=base.seq_lens, num_partitions=base.num_partitions, num_blocks=NB,
-                     softmax_scale=base.softmax_scale)
+                     softmax_scale=base.softmax_scale, kv_layout=kv_layout)
 
 
 def poison_tq4(inp: InputsTq4, seed: int = 99) -> InputsTq4:
@@ -381,7 +419,8 @@ def poison_tq4(inp: InputsTq4, seed: int = 99) -> InputsTq4:
         if L % BS:
             b = int(bt[s, nb_used - 1])
             blk = cache[b]
-            rows = blk[:data_bytes].view(Hkv, BS, D)
+            rows = blk[:data_bytes].view(Hkv, BS, D) if inp.kv_layout == "head" else \
+                blk[:data_bytes].view(BS, Hkv, D).transpose(0, 1)
             rows[:, L % BS:] = torch.from_numpy(
                 rng.integers(0, 256, size=(Hkv, BS - L % BS, D), dtype=np.uint8)).to(cache.device)
             meta = blk[data_bytes:].view(torch.int16).view(Hkv, TQ4_META_FIELDS, BS)

@@ -234,8 +234,9 @@ tq_status tq_decode_fused_static(const void* q, const uint8_t* k_cache, const ui
                                  int32_t tile_groups_per_partition, float softmax_scale,
                                  const tq_extent* ext, void* stream);
 
-/* Workspace bytes for the fastest split of tq_decode_fused at these sizes (0:
- * it needs none).  Depends on num_seqs, max_seq_len, num_kv_heads and
+/* Workspace bytes for the fastest split of tq_decode_fused at these sizes on a
+ * device of 256 compute units, the largest split the library plans (a device
+ * with fewer CUs uses fewer of them; 0: it needs none).  Depends on num_seqs, max_seq_len, num_kv_heads and
  * query_group_size: with the even split, 256 B-rounded arrival counters (4 B per
  * (s, h)) and two partial slots per workgroup (QG*520 B each). */
 size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,

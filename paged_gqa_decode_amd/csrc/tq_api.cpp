@@ -178,7 +178,9 @@ tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out
   const hipError_t v = maybe_validate(st, seq_lens, kv_block_size, ext, stream);
   if (v != hipSuccess) return hip_status(v);
   const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
-  const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
+  const int cus = tq::device_cu_count();
+  const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len,
+                                               tq::kFlatUnitTokens, cus);
   const size_t cb = counters ? counters : tq::counter_bytes(seq_heads);
   const bool counters_fit = workspace && cb >= tq::counter_bytes(seq_heads) && workspace_bytes >= cb;
   if (flat_groups > 0 && counters_fit &&
@@ -195,7 +197,7 @@ tq_status run_fused(const tq::StreamArgs& st, const int32_t* seq_lens, void* out
                                       static_cast<hipStream_t>(stream)));
   }
   const tq::FusedPlan plan = tq::plan_fused(seq_heads, ext->max_seq_len, query_group_size,
-                                            workspace ? workspace_bytes : 0, counters);
+                                            workspace ? workspace_bytes : 0, counters, cus);
   tq::FusedArgs a{};
   a.st = st;
   a.seq_lens = seq_lens;
@@ -324,6 +326,8 @@ size_t tq_fused_workspace_bytes(const tq_extent* ext, int32_t num_kv_heads,
   if (!ext || ext->num_seqs < 1 || num_kv_heads < 1 || !supported_qg(query_group_size) ||
       ext->max_seq_len < 0)
     return 0;
+  // Sized for a device of kFlatGroupsMax (256) CUs, the most the plans use: a
+  // device with fewer CUs plans fewer workgroups and needs no more bytes.
   const int64_t seq_heads = (int64_t)ext->num_seqs * num_kv_heads;
   const int flat_groups = tq::plan_flat_groups(ext->num_seqs, num_kv_heads, ext->max_seq_len);
   if (flat_groups > 0) return tq::flat_workspace_bytes(seq_heads, flat_groups, query_group_size);

@@ -16,8 +16,9 @@ constexpr int kTokensPerTileGroup = 256;
 constexpr int kFlatWaves = 8;
 constexpr int kFlatSlices = 16;
 constexpr int kFlatMaxSeqs = 64 * kFlatSlices;
-// Workgroups of the flat kernels at most (one per CU), and per lane of a wave
-// that walks them all.
+// Workgroups of the flat kernels at most (one per CU, up to the 256 CUs of an
+// MI355X in its single-partition mode), and per lane of a wave that walks them
+// all.  The grid itself follows the device's CU count (device_cu_count).
 constexpr int kFlatGroupsMax = 256;
 constexpr int kFlatGroupsPerLane = kFlatGroupsMax / 64;
 // Tokens per entry of the flat fused kernel's work list: one 32-token chunk,
@@ -93,7 +94,7 @@ size_t counter_bytes(int64_t seq_heads);
 // Plan for these sizes with `ws_bytes` of workspace (0: none), and the
 // workspace bytes a plan needs (counters first, at a fixed offset).
 FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes,
-                     size_t counters = 0);
+                     size_t counters = 0, int cus = kFlatGroupsMax);
 size_t fused_partial_bytes(int64_t seq_heads, int splits, int query_group_size);
 size_t fused_workspace_bytes(int64_t seq_heads, int splits, int query_group_size);
 // Carve the workspace for `splits` into the pointers of `a`.
@@ -121,12 +122,17 @@ struct FlatArgs {
 // apply), the workspace bytes it needs, and the carving of that workspace.
 // unit_tokens: the tokens of one list entry (a 32-token chunk for the fused path,
 // a partition for the two-kernel path).
+// cus: the device's compute units (one resident workgroup of 8 waves each).
 int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
-                     int unit_tokens = kFlatUnitTokens);
+                     int unit_tokens = kFlatUnitTokens, int cus = kFlatGroupsMax);
 // Workgroups of the flat partition kernel (tq_partition_flat_kernel) for
 // these sizes, or 0 when the per-partition kernel runs instead.
 int plan_partition_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
-                               int partition_tokens, bool tq4);
+                               int partition_tokens, bool tq4, int cus = kFlatGroupsMax);
+
+// Compute units of the current device (hipDeviceAttributeMultiprocessorCount,
+// queried once per device; kFlatGroupsMax if the query fails).
+int device_cu_count();
 size_t flat_partial_bytes(int n_groups, int query_group_size);
 size_t flat_workspace_bytes(int64_t seq_heads, int n_groups, int query_group_size);
 void bind_flat_workspace(FlatArgs* a, void* ws, int64_t seq_heads, int query_group_size,

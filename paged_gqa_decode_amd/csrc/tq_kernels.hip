@@ -507,13 +507,19 @@ constexpr int kTq4MetaStage = 256;
 constexpr int kTq4MetaOff = 2 * kTq4RowStage;
 constexpr int kTq4WaveLds = kTq4MetaOff + 2 * kTq4MetaStage;
 constexpr int kTq4TableEntries = 256;
-// Columns of the wide centroid table: every entry repeated in 32 adjacent
-// dwords, lane l reading the copy in column l % 32, so that the bank a lookup
-// hits follows from the lane whatever the index byte (random index bytes
-// otherwise pile several lanes onto one bank).  32 KiB: the fused flat kernel
-// at QG <= 8 has the room (its staging takes 133 KiB at QG = 16).
+// Columns of the wide centroid tables: every entry repeated in COLS adjacent
+// dwords, lane l reading the copy in column l % COLS, so that the bank a
+// lookup hits follows from the lane whatever the index byte (random index
+// bytes otherwise pile several lanes onto one bank).  32 columns (32 KiB):
+// at most two lanes of a wave on one bank.  16 columns (16 KiB): lanes l and
+// l + 16 share a bank when their entries have the same parity.  The fused
+// flat kernel has room for 32 columns at QG <= 8 and for 16 at QG = 16 (its
+// staging takes 133 KiB there).  The flat partition kernel keeps one column:
+// 32 there measured no faster on the bandwidth workload and 1-3 % slower on
+// shorter batches (building the table costs more than its conflicts).
 constexpr int kTq4WideCols = 32;
-constexpr int tq4_flat_table_cols(int qg, bool tq4) { return tq4 && qg <= 8 ? kTq4WideCols : 1; }
+constexpr int tq4_flat_table_cols(int qg, bool tq4) { return !tq4 ? 1 : (qg <= 8 ? 32 : 16); }
+constexpr int tq4_partition_flat_table_cols(bool tq4) { return 1; }
 
 __device__ __forceinline__ int tq4_row_swz(int row) {
   return (row & 7) ^ ((row >> 3) & 1) ^ ((row >> 2) & 4);
@@ -526,7 +532,7 @@ __device__ __forceinline__ int tq4_row_swz(int row) {
 template <int COLS = 1>
 __device__ __forceinline__ void build_tq4_table(uint32_t* tab, const float* centroids, int tid,
                                                 int nthreads) {
-  static_assert(COLS == 1 || COLS == kTq4WideCols, "table columns");
+  static_assert(COLS == 1 || COLS == 16 || COLS == 32, "table columns");
   for (int i = tid; i < kTq4TableEntries * COLS; i += nthreads) {
     const int x = i / COLS;
     const f16x2 e = {(_Float16)centroids[x & 15], (_Float16)centroids[x >> 4]};
@@ -736,16 +742,18 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
           kop[t][cc] = __builtin_bit_cast(
               f16x8, u32x4{tab[x & 0xFF], tab[(x >> 8) & 0xFF], tab[(x >> 16) & 0xFF], tab[x >> 24]});
         } else {
-          // Entry e's copies start at byte 128 e: each index byte lands there
-          // with one shift and one mask, and the lane's column ORs in.
-          static_assert(COLS * 4 == 128, "wide table row");
+          // Entry e's copies start at byte e * 4 COLS: each index byte lands
+          // there with one shift and one mask, and the lane's column ORs in.
+          static_assert(COLS == 16 || COLS == 32, "wide table row");
+          constexpr int sh = COLS == 32 ? 7 : 6;  // log2 of a row's bytes
+          constexpr uint32_t m = 0xFFu << sh;
           const char* tb = reinterpret_cast<const char*>(tab);
           auto at = [&](uint32_t row) {
             return *reinterpret_cast<const uint32_t*>(tb + (row | tab_col));
           };
           kop[t][cc] = __builtin_bit_cast(
-              f16x8, u32x4{at((x << 7) & 0x7F80u), at((x >> 1) & 0x7F80u), at((x >> 9) & 0x7F80u),
-                           at((x >> 17) & 0x7F80u)});
+              f16x8, u32x4{at((x << sh) & m), at((x >> (8 - sh)) & m), at((x >> (16 - sh)) & m),
+                           at((x >> (24 - sh)) & m)});
         }
       }
     if (c == next_boundary) {
@@ -1663,8 +1671,9 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
 // table and fill the pipeline for only 8 chunks.
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64 * kFlatWaves) void tq_partition_flat_kernel(PartitionArgs a) {
+  constexpr int kTabCols = tq4_partition_flat_table_cols(TQ4);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries * kTabCols : 1];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int W = blockDim.x >> 6;
@@ -1673,7 +1682,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_partition_flat_kernel(Part
   const int E = a.partition_tokens;
   auto len_of = [&](int s) { return clamp_len(a.seq_lens[s], a.len_cap); };
   if constexpr (TQ4) {  // before any return: every thread reaches the barrier
-    build_tq4_table(lds_tab, a.st.centroids, threadIdx.x, blockDim.x);
+    build_tq4_table<kTabCols>(lds_tab, a.st.centroids, threadIdx.x, blockDim.x);
     __syncthreads();
   }
 
@@ -1737,9 +1746,9 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_partition_flat_kernel(Part
     const int t_begin = k0 * E, t_end = min(k1 * E, L);
     WaveState w;
     w.reset();
-    stream_any<QG, BS, TQ4>(a.st, s, h, t_begin, t_end, chunks_per_part, area,
-                            reinterpret_cast<float*>(area + 2 * CHUNK * D), lds_tab, w,
-                            [&](int j, WaveState& ws) { store_partial<QG, TQ4>(a, sh, k0 + j, ws); });
+    stream_any<QG, BS, TQ4, kTabCols>(a.st, s, h, t_begin, t_end, chunks_per_part, area,
+                                      reinterpret_cast<float*>(area + 2 * CHUNK * D), lds_tab, w,
+                                      [&](int j, WaveState& ws) { store_partial<QG, TQ4>(a, sh, k0 + j, ws); });
     const int n_chunks = (t_end - t_begin + CHUNK - 1) / CHUNK;
     store_partial<QG, TQ4>(a, sh, k0 + (n_chunks - 1) / chunks_per_part, w);
     pos += k1 - k0;
@@ -1956,6 +1965,27 @@ __global__ __launch_bounds__(256) void tq_zero_fill_kernel(u32x4* p, uint32_t n1
 
 }  // namespace
 
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static int cus[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();  // must not surface as a later launch's status
+    return kFlatGroupsMax;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      n = kFlatGroupsMax;
+    }
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 hipError_t static_scratch(void** ptr, hipStream_t stream) {
   // One device address per GPU, taken once with that GPU current; the first
   // call on a GPU also enqueues the zero fill of its copy on `stream`, ahead
@@ -2043,7 +2073,8 @@ hipError_t launch_partition_flat_t(const PartitionArgs& a, int n_groups, hipStre
     return hipErrorInvalidValue;
   } else {
     constexpr size_t lds = (size_t)kFlatWaves * kWaveLds;
-    static_assert(lds + kTq4TableEntries * 4 <= 160 * 1024, "LDS per workgroup");
+    static_assert(lds + kTq4TableEntries * 4 * tq4_partition_flat_table_cols(TQ4) + 1024 <= 160 * 1024,
+                  "LDS per workgroup");
     // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
     // the runtime needs none, and must not leak into the launch status.
     static const bool lds_opt_in = [] {
@@ -2064,8 +2095,8 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
   a.num_seqs = num_seqs;
   a.nt_partials = partials_nontemporal(num_seqs, a.st.num_kv_heads, a.num_partitions,
                                        query_group_size, tq4) ? 1 : 0;
-  const int flat_groups =
-      plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap, a.partition_tokens, tq4);
+  const int flat_groups = plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap,
+                                                     a.partition_tokens, tq4, device_cu_count());
   if (flat_groups > 0) {
     a.parts_per_wave = 0;  // unused by the flat kernel
     TQ_DISPATCH(launch_partition_flat_t, query_group_size, kv_block_size, tq4, a, flat_groups, stream);

@@ -66,13 +66,13 @@ void bind_fused_workspace(FusedArgs* a, void* ws, int64_t seq_heads, int query_g
 }
 
 FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, size_t ws_bytes,
-                     size_t counters) {
-  // About kTargetWaves waves on the device (one resident round at two waves
-  // per SIMD; measured best across the workloads), each with at least one tile
+                     size_t counters, int cus) {
+  // About 8 waves per CU on the device (one resident round at two waves per
+  // SIMD; measured best across the workloads), each with at least one tile
   // group of work; at most 8 waves per workgroup (the register budget of
   // __launch_bounds__(512)), then more workgroups per (s, h) if the workspace
   // can hold their partials.
-  constexpr int64_t kTargetWaves = 2048;
+  const int64_t kTargetWaves = (int64_t)kFlatWaves * (cus < 1 ? 1 : cus);
   const int64_t n_tg = max_seq_len > 0 ? (max_seq_len + kTokensPerTileGroup - 1) / kTokensPerTileGroup : 1;
   int64_t waves_per_sh = (kTargetWaves + seq_heads - 1) / seq_heads;
   if (waves_per_sh > n_tg) waves_per_sh = n_tg;
@@ -90,12 +90,13 @@ FusedPlan plan_fused(int64_t seq_heads, int max_seq_len, int query_group_size, s
   return plan;
 }
 
-int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len, int unit_tokens) {
-  // One resident round at two waves per SIMD (256 workgroups of 8 waves, one
-  // per CU), or fewer when the list cannot fill them: at most one wave per list
-  // entry.
-  constexpr int64_t kFlatGroups = kFlatGroupsMax;
-  static_assert(kFlatGroups * kFlatWaves <= 65536, "waves per launch");
+int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len, int unit_tokens,
+                     int cus) {
+  // One resident round at two waves per SIMD (a workgroup of 8 waves per CU,
+  // at most kFlatGroupsMax), or fewer when the list cannot fill them: at most
+  // one wave per list entry.
+  static_assert(int64_t(kFlatGroupsMax) * kFlatWaves <= 65536, "waves per launch");
+  const int64_t kFlatGroups = cus < 1 ? 1 : (cus < kFlatGroupsMax ? cus : kFlatGroupsMax);
   if (num_seqs < 1 || num_seqs > kFlatMaxSeqs || num_kv_heads < 1 || max_seq_len <= 0 ||
       unit_tokens < 1)
     return 0;
@@ -107,15 +108,16 @@ int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len, int un
 }
 
 int plan_partition_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
-                               int partition_tokens, bool tq4) {
+                               int partition_tokens, bool tq4, int cus) {
   // The 4-bit format only, and only when the partitions (bounded by the
   // longest length) fill the resident round at least twice: measured faster
   // than one wave per partition there (7-12 %), slower with fewer partitions
   // than that, and no faster for fp8.
   if (!tq4 || num_seqs < 1 || num_kv_heads < 1 || max_seq_len <= 0 || partition_tokens < 1) return 0;
   const int64_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
-  if (num_seqs * num_kv_heads * parts < 2 * kFlatWaves * kFlatGroupsMax) return 0;
-  return plan_flat_groups(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+  const int64_t groups = cus < 1 ? 1 : (cus < kFlatGroupsMax ? cus : kFlatGroupsMax);
+  if (num_seqs * num_kv_heads * parts < 2 * kFlatWaves * groups) return 0;
+  return plan_flat_groups(num_seqs, num_kv_heads, max_seq_len, partition_tokens, cus);
 }
 
 size_t flat_partial_bytes(int n_groups, int query_group_size) {

@@ -196,6 +196,11 @@ int main() {
     c.layout = TQ_KV_LAYOUT_SLOT_MAJOR;
     run_valid(c);
   }
+  for (int cus : {32, 80, 304}) {  // devices of other sizes (partitioned modes, larger parts)
+    g_log.cus = cus;
+    for (const Case& c : valid) run_valid(c);
+  }
+  g_log.cus = 256;
   run_invalid();
   run_static_limits();
   setenv("TQ_VALIDATE", "1", 1);

@@ -7,5 +7,6 @@ struct LaunchLog {
   bool last_tq4 = false;
   const void* ws = nullptr;  // the workspace the driver passed, to check the carving
   size_t ws_bytes = 0;
+  int cus = 256;  // what the device_cu_count stand-in reports
 };
 extern LaunchLog g_log;

@@ -41,7 +41,7 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
   require(tq4 ? (a.st.tq4 && a.st.centroids) : (a.st.k && a.st.v && a.st.scales), "format");
   // The launcher's plan: the flat kernel's grid, else one wave per run of partitions.
   const int flat_groups = plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap,
-                                                     a.partition_tokens, tq4);
+                                                     a.partition_tokens, tq4, g_log.cus);
   require(flat_groups >= 0 && flat_groups <= 256 && (tq4 || flat_groups == 0), "flat partition plan");
   const bool nt = partials_nontemporal(num_seqs, a.st.num_kv_heads, a.num_partitions,
                                        query_group_size, tq4);
@@ -71,7 +71,8 @@ hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_g
 hipError_t launch_flat(const FlatArgs& a, int query_group_size, int kv_block_size, bool tq4,
                        hipStream_t) {
   ++g_log.flat;
-  require(a.n_groups >= 1 && a.n_groups <= 256 && a.num_seqs >= 1, "flat plan");
+  require(a.n_groups >= 1 && a.n_groups <= 256 && a.n_groups <= g_log.cus && a.num_seqs >= 1,
+          "flat plan");
   require(a.counters && a.ws_o && a.ws_m && a.ws_l, "flat workspace");
   require(query_group_size >= 1 && kv_block_size >= 1, "flat sizes");
   if (g_log.ws) {
@@ -95,6 +96,8 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t) {
   require_row_strides(a.row_head_stride, a.row_slot_stride, a.num_kv_heads, a.kv_block_size);
   return hipSuccess;
 }
+
+int device_cu_count() { return g_log.cus; }
 
 // The static scratch of tq_decode_fused_static: real host memory of the same size, recorded
 // as the workspace so that the launch stand-ins check the carving against it.

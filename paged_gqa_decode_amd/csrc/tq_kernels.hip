@@ -1604,11 +1604,15 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   }
   __syncthreads();
   // The last arrival merges the n partials of workgroups g_first .. g_first +
-  // n - 1 in workgroup order.  First the coefficients c_j = l_j e^{m_j - M} /
-  // sum_j' l_j' e^{m_j' - M} of each query row, one row per wave at a time,
-  // the lanes over j (n <= G <= 256), into LDS (the staging areas are free by
-  // now); then every item thread sums c_j o_j for its 4 columns, eight
-  // partials' loads in flight at once.
+  // n - 1 in workgroup order.  With at most kFlatFewPartials of them, every
+  // item thread loads the max logits, exp sums and its 4 columns of all of
+  // them at once (one round trip) and merges them as lse_merge4_regs does.
+  // Otherwise, first the coefficients c_j = l_j e^{m_j - M} / sum_j' l_j'
+  // e^{m_j' - M} of each query row, one row per wave at a time, the lanes
+  // over j (n <= G <= 256), into LDS (the staging areas are free by now); then
+  // every item thread sums c_j o_j for its 4 columns, eight partials' loads in
+  // flight at once.
+  constexpr int kFlatFewPartials = 8;
   float* coef = reinterpret_cast<float*>(lds_dyn);  // [QG][n]
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
@@ -1617,6 +1621,16 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
       __hip_atomic_store(a.counters + ext_sh[x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int n = count[x], gf = g_first[x], fs = first_slot[x];
     auto rec = [&](int j) -> uint32_t { return 2 * (uint32_t)(gf + j) + (j == 0 ? fs : 0); };
+    if (n <= kFlatFewPartials) {  // uniform over the workgroup
+      if (t < kItems) {
+        const f32x4 o = lse_merge4_regs<kFlatFewPartials>(
+            n, [&](int j) { return ld_coherent4(rs_o, ((rec(j) * QG + item_g) * D + item_col) * 4); },
+            [&](int j) { return ld_coherent1(rs_m, (rec(j) * QG + item_g) * 4); },
+            [&](int j) { return ld_coherent1(rs_l, (rec(j) * QG + item_g) * 4); });
+        store_bf16x4(a.out + ((size_t)ext_sh[x] * QG + item_g) * D + item_col, o);
+      }
+      continue;
+    }
     for (int g = wave; g < QG; g += W) {
       float mj[kFlatGroupsPerLane], lj[kFlatGroupsPerLane];
 #pragma unroll

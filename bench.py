@@ -543,10 +543,10 @@ def main() -> int:
     # tokens scattered into random slots of the same pool; bytes per (token, kv head) row =
     # 512 read (bf16 K and V) + 264 written (fp8 codes and two fp32 scales).
     T = 16384
-    gen = torch.Generator(device=dev).manual_seed(wl.seed + 7)
-    k_new = torch.randn((T, Hkv, 128), generator=gen, device=dev).to(torch.bfloat16)
-    v_new = torch.randn((T, Hkv, 128), generator=gen, device=dev).to(torch.bfloat16)
-    slots = torch.randperm(inp.num_blocks * wl.kv_block_size, generator=gen, device=dev)[:T]
+    wkey = workloads.stream_key(wl.seed, "writer")
+    new_rows = workloads.random_normal(wkey, 0, 2 * T * Hkv * 128, dev).to(torch.bfloat16)
+    k_new, v_new = new_rows.view(2, T, Hkv, 128).unbind(0)
+    slots = workloads.random_permutation(wkey, inp.num_blocks * wl.kv_block_size, dev)[:T]
     slots = slots.to(torch.int32)
     write = lambda: tq.tq_kv_write(k_new, v_new, slots, inp.k_cache, inp.v_cache,  # noqa: E731
                                    inp.kv_scales, kv_layout=args.kv_layout, stream=stream)

@@ -6,11 +6,19 @@ none of the attention arithmetic, so both the HIP path and the fp64 oracle can
 consume what it produces without sharing code with each other.
 
 Recipe (the same for every workload):
-  * numpy ``default_rng(seed)`` draws the sequence lengths, the permutation of
-    the physical block pool and the outlier channels;
-  * torch's generator (seed+1 for q, seed+2 for K, seed+3 for V), on the
-    requested device, draws N(0, 1) values; K and V are drawn in slabs of at
-    most ``SLAB_BLOCKS`` cache blocks, K slab then V slab;
+  * every random number comes from one counter-based generator written here
+    (no library RNG): splitmix64 (Steele, Lea and Flood, "Fast splittable
+    pseudorandom number generators", OOPSLA 2014; the finalizer constants of
+    Vigna's public reference code) applied to key + (i + 1) * 0x9E3779B97F4A7C15
+    for the i-th number of a stream, with one key per (seed, stream);
+    uniforms take the top 53 bits, N(0, 1) values the Box-Muller transform of
+    two uniforms (numbers 2k and 2k + 1 give value k).  The 64-bit stream is
+    the same bits on any device; the normals go through fp64 log / sqrt / cos,
+    whose last-bit rounding may differ between devices;
+  * streams: the sequence lengths (uniform integers), the permutation of the
+    physical block pool (an argsort of random keys), the outlier channels (the
+    first of another argsort), q, K and V (one normal per element, in the
+    element order of [S][Hq][D] and [NB][Hkv][BS][D]);
   * q: bf16 round-to-nearest-even of N(0, 1), optionally with a seeded set of
     outlier (q head, dim) channels multiplied by 20 before rounding;
   * K, V: per (block, slot, kv head) row of head_dim values, scale =
@@ -135,10 +143,83 @@ class Inputs:
         return int(self.seq_lens.to(torch.int64).sum().item()) * self.wl.num_kv_heads * (2 * D + 8)
 
 
-def draw_seq_lens(wl: Workload, rng: np.random.Generator) -> np.ndarray:
+# ----------------------------------------------------------------------------
+# The counter-based generator (splitmix64 on a counter; see the recipe above).
+# ----------------------------------------------------------------------------
+
+SPLITMIX_GAMMA = 0x9E3779B97F4A7C15
+SPLITMIX_M1 = 0xBF58476D1CE4E5B9
+SPLITMIX_M2 = 0x94D049BB133111EB
+_U64 = (1 << 64) - 1
+STREAMS = {"lens": 1, "pool": 2, "outliers": 3, "q": 4, "k": 5, "v": 6, "writer": 7, "poison": 8}
+
+
+def _i64(c: int) -> int:
+    """A 64-bit pattern as the int64 value with the same bits."""
+    c &= _U64
+    return c - (1 << 64) if c >> 63 else c
+
+
+def _shr(z: torch.Tensor, k: int) -> torch.Tensor:
+    """Logical right shift of int64 bit patterns."""
+    return (z >> k) & ((1 << (64 - k)) - 1)
+
+
+def mix64(z: torch.Tensor) -> torch.Tensor:
+    """The splitmix64 finalizer on int64 bit patterns (multiplications wrap mod 2^64)."""
+    z = (z ^ _shr(z, 30)) * _i64(SPLITMIX_M1)
+    z = (z ^ _shr(z, 27)) * _i64(SPLITMIX_M2)
+    return z ^ _shr(z, 31)
+
+
+def mix64_int(z: int) -> int:
+    """The same finalizer on a Python integer."""
+    z &= _U64
+    z = ((z ^ (z >> 30)) * SPLITMIX_M1) & _U64
+    z = ((z ^ (z >> 27)) * SPLITMIX_M2) & _U64
+    return z ^ (z >> 31)
+
+
+def stream_key(seed: int, stream: str) -> int:
+    """The key of one stream of a seed."""
+    return mix64_int((seed << 8) + STREAMS[stream])
+
+
+def random_bits(key: int, start: int, n: int, device) -> torch.Tensor:
+    """Numbers start .. start + n - 1 of the stream with this key, as int64 bit patterns."""
+    i = torch.arange(start + 1, start + n + 1, dtype=torch.int64, device=device)
+    return mix64(i * _i64(SPLITMIX_GAMMA) + _i64(key))
+
+
+def random_uniform(key: int, start: int, n: int, device) -> torch.Tensor:
+    """Uniforms in (0, 1), fp64: (top 53 bits + 0.5) / 2^53."""
+    return (_shr(random_bits(key, start, n, device), 11).to(torch.float64) + 0.5) * 2.0 ** -53
+
+
+def random_normal(key: int, start: int, n: int, device) -> torch.Tensor:
+    """N(0, 1) values start .. start + n - 1, fp64: value k is sqrt(-2 ln u1) cos(2 pi u2)
+    with u1, u2 the uniforms 2k and 2k + 1."""
+    u = random_uniform(key, 2 * start, 2 * n, device).view(n, 2)
+    return torch.sqrt(-2.0 * torch.log(u[:, 0])) * torch.cos(2.0 * math.pi * u[:, 1])
+
+
+def random_permutation(key: int, n: int, device="cpu") -> torch.Tensor:
+    """A permutation of 0 .. n-1 (int64): the stable argsort of n random keys."""
+    b = random_bits(key, 0, n, device)
+    return torch.sort(_shr(b, 1), stable=True).indices
+
+
+def random_ints(key: int, start: int, n: int, hi: int) -> np.ndarray:
+    """n integers in [0, hi) (int64, CPU): the top 53 bits of each number scaled to hi."""
+    u = random_uniform(key, start, n, "cpu").numpy()
+    return np.minimum(np.floor(u * hi), hi - 1).astype(np.int64)
+
+
+def draw_seq_lens(wl: Workload) -> np.ndarray:
     if wl.seq_len_lo == wl.seq_len_hi:
         return np.full(wl.num_seqs, wl.seq_len_lo, dtype=np.int32)
-    return rng.integers(wl.seq_len_lo, wl.seq_len_hi + 1, size=wl.num_seqs).astype(np.int32)
+    span = wl.seq_len_hi - wl.seq_len_lo + 1
+    return (wl.seq_len_lo + random_ints(stream_key(wl.seed, "lens"), 0, wl.num_seqs, span)).astype(np.int32)
 
 
 def quantize_rows(x: torch.Tensor):
@@ -158,15 +239,15 @@ def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
     "slot" gives the same values with the cache rows slot-major.
     _skip_cache: leave the fp8 cache empty (for the 4-bit format's generator)."""
     dev = torch.device(device)
-    rng = np.random.default_rng(wl.seed)
-    sl = draw_seq_lens(wl, rng) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    sl = draw_seq_lens(wl) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
     S, Hkv, QG, D, BS = wl.num_seqs, wl.num_kv_heads, wl.query_group_size, wl.head_dim, wl.kv_block_size
     assert sl.shape == (S,)
     need = [-(-int(L) // BS) for L in sl]
     NB = wl.num_blocks if wl.num_blocks is not None else max(1, sum(need))
     assert NB >= sum(need), "block pool smaller than the sequences need"
     assert max(need) <= wl.max_blocks_per_seq
-    pool = rng.permutation(NB).astype(np.int32) if wl.permute_pool else np.arange(NB, dtype=np.int32)
+    pool = (random_permutation(stream_key(wl.seed, "pool"), NB).numpy().astype(np.int32)
+            if wl.permute_pool else np.arange(NB, dtype=np.int32))
     bt = np.zeros((S, wl.max_blocks_per_seq), dtype=np.int32)
     pos = 0
     for s in range(S):
@@ -177,13 +258,13 @@ def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
     if num_partitions is None:
         num_partitions = max(1, -(-int(sl.max()) // wl.partition_tokens))
 
-    gq = torch.Generator(device=dev).manual_seed(wl.seed + 1)
-    q = torch.randn((S, Hkv * QG, D), generator=gq, device=dev, dtype=torch.float32)
+    q = random_normal(stream_key(wl.seed, "q"), 0, S * Hkv * QG * D, dev).float()
+    q = q.view(S, Hkv * QG, D)
     if wl.outlier_frac > 0:
         n_out = int(round(wl.outlier_frac * Hkv * QG * D))
-        chans = rng.choice(Hkv * QG * D, size=n_out, replace=False)
+        chans = random_permutation(stream_key(wl.seed, "outliers"), Hkv * QG * D)[:n_out]
         mult = torch.ones(Hkv * QG * D, dtype=torch.float32)
-        mult[torch.from_numpy(chans.astype(np.int64))] = wl.outlier_mult
+        mult[chans] = wl.outlier_mult
         q = q * mult.view(1, Hkv * QG, D).to(dev)
     q = q.to(torch.bfloat16)
 
@@ -197,12 +278,12 @@ def make_inputs(wl: Workload, device="cpu", seq_lens=None, num_partitions=None,
     k_codes = torch.empty((NB, Hkv, BS, D), dtype=torch.uint8, device=dev)
     v_codes = torch.empty((NB, Hkv, BS, D), dtype=torch.uint8, device=dev)
     scales = torch.empty((NB, Hkv, 2, BS), dtype=torch.float32, device=dev)
-    gk = torch.Generator(device=dev).manual_seed(wl.seed + 2)
-    gv = torch.Generator(device=dev).manual_seed(wl.seed + 3)
+    row = Hkv * BS * D  # elements per cache block
     for b0 in range(0, NB, SLAB_BLOCKS):
         b1 = min(NB, b0 + SLAB_BLOCKS)
-        for field, (gen, dst) in enumerate(((gk, k_codes), (gv, v_codes))):
-            x = torch.randn((b1 - b0, Hkv, BS, D), generator=gen, device=dev, dtype=torch.float32)
+        for field, (stream, dst) in enumerate((("k", k_codes), ("v", v_codes))):
+            x = random_normal(stream_key(wl.seed, stream), b0 * row, (b1 - b0) * row, dev).float()
+            x = x.view(b1 - b0, Hkv, BS, D)
             codes, sc = quantize_rows(x)
             dst[b0:b1] = codes
             scales[b0:b1, :, field, :] = sc
@@ -240,7 +321,7 @@ def poison(inp: Inputs, seed: int = 99) -> Inputs:
     * block-table entries past ceil(L / BS): other valid block ids of the pool
       (never out of range, so a wrong reader gives wrong numbers, not a fault).
     """
-    rng = np.random.default_rng(seed)
+    key, used = stream_key(seed, "poison"), 0
     k = inp.k_cache.clone()
     v = inp.v_cache.clone()
     sc = inp.kv_scales.clone()
@@ -260,7 +341,8 @@ def poison(inp: Inputs, seed: int = 99) -> Inputs:
             sc[b, :, :, L % BS:] = float("nan")
         tail = bt.shape[1] - nb_used
         if tail > 0:
-            bt[s, nb_used:] = rng.integers(0, inp.num_blocks, size=tail)
+            bt[s, nb_used:] = random_ints(key, used, tail, inp.num_blocks)
+            used += tail
     return dataclasses.replace(inp, k_cache=k, v_cache=v, kv_scales=sc,
                                block_tables=torch.from_numpy(bt).to(inp.block_tables.device))
 
@@ -273,7 +355,7 @@ def poison(inp: Inputs, seed: int = 99) -> Inputs:
 #     the last D/2;
 #   meta [Hkv][3][BS] fp16: K norm, V scale, V zero point.
 # Recipe: q as above (the query arrives already rotated: a rotation of an
-# isotropic Gaussian is one); K rows x ~ N(0, 1): knorm = fp16(|x| / sqrt(D)),
+# isotropic Gaussian is one); K rows x ~ N(0, 1) (the fp8 format's K stream): knorm = fp16(|x| / sqrt(D)),
 # indices = nearest of the 16 centroids to x / knorm; V rows y ~ N(0, 1): zero
 # = fp16(min y), scale = fp16((max y - min y) / 15), indices = round((y - zero)
 # / scale) clamped to [0, 15].  The centroids are those of the 16-level
@@ -387,12 +469,12 @@ def make_inputs_tq4(wl: Workload, device="cpu", seq_lens=None, num_partitions=No
     NB = base.num_blocks
     cent = torch.from_numpy(lloyd_max_normal_16()).to(dev)
     cache = torch.empty((NB, tq4_block_bytes(Hkv, BS, D)), dtype=torch.uint8, device=dev)
-    gk = torch.Generator(device=dev).manual_seed(wl.seed + 2)
-    gv = torch.Generator(device=dev).manual_seed(wl.seed + 3)
+    row = Hkv * BS * D
     for b0 in range(0, NB, SLAB_BLOCKS):
         b1 = min(NB, b0 + SLAB_BLOCKS)
-        x = torch.randn((b1 - b0, Hkv, BS, D), generator=gk, device=dev, dtype=torch.float32)
-        y = torch.randn((b1 - b0, Hkv, BS, D), generator=gv, device=dev, dtype=torch.float32)
+        x = random_normal(stream_key(wl.seed, "k"), b0 * row, (b1 - b0) * row, dev).float()
+        y = random_normal(stream_key(wl.seed, "v"), b0 * row, (b1 - b0) * row, dev).float()
+        x, y = x.view(b1 - b0, Hkv, BS, D), y.view(b1 - b0, Hkv, BS, D)
         k_idx, v_idx, meta = quantize_tq4_rows(x, y, cent)
         meta_bits = meta.view(torch.int16).permute(0, 1, 3, 2).contiguous()  # [b][Hkv][3][BS]
         cache[b0:b1] = pack_tq4(k_idx, v_idx, meta_bits, kv_layout)
@@ -406,7 +488,7 @@ def poison_tq4(inp: InputsTq4, seed: int = 99) -> InputsTq4:
     """Copy of `inp` with garbage wherever a correct reader must not look: the records of
     slots past each sequence's length in its last block get random index bytes and NaN
     meta (fp16 0x7E00); block-table entries past ceil(L / BS) get other valid block ids."""
-    rng = np.random.default_rng(seed)
+    key, used = stream_key(seed, "poison"), 0
     cache = inp.cache.clone()
     bt = inp.block_tables.cpu().numpy().copy()
     sl = inp.seq_lens.cpu().numpy()
@@ -421,12 +503,15 @@ def poison_tq4(inp: InputsTq4, seed: int = 99) -> InputsTq4:
             blk = cache[b]
             rows = blk[:data_bytes].view(Hkv, BS, D) if inp.kv_layout == "head" else \
                 blk[:data_bytes].view(BS, Hkv, D).transpose(0, 1)
-            rows[:, L % BS:] = torch.from_numpy(
-                rng.integers(0, 256, size=(Hkv, BS - L % BS, D), dtype=np.uint8)).to(cache.device)
+            n = Hkv * (BS - L % BS) * D
+            rows[:, L % BS:] = torch.from_numpy(random_ints(key, used, n, 256).astype(np.uint8).reshape(
+                Hkv, BS - L % BS, D)).to(cache.device)
+            used += n
             meta = blk[data_bytes:].view(torch.int16).view(Hkv, TQ4_META_FIELDS, BS)
             meta[:, :, L % BS:] = 0x7E00
         tail = bt.shape[1] - nb_used
         if tail > 0:
-            bt[s, nb_used:] = rng.integers(0, inp.num_blocks, size=tail)
+            bt[s, nb_used:] = random_ints(key, used, tail, inp.num_blocks)
+            used += tail
     return dataclasses.replace(inp, cache=cache,
                                block_tables=torch.from_numpy(bt).to(inp.block_tables.device))

@@ -294,8 +294,8 @@ COUNTER_PASSES = (
               "SQ_INSTS_SALU", "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE")),
 )
 COUNTER_KERNELS = ("tq_flat_kernel", "tq_partition_kernel", "tq_merge_kernel", "tq_kv_write_kernel",
-                   "tq_flat_kernel[tq4]", "tq_partition_flat_kernel[tq4]", "probe_pattern_kernel",
-                   "probe_pattern4_kernel")
+                   "tq_flat_kernel[tq4]", "tq_partition_flat_kernel[tq4]", "tq_partition_kernel[tq4]",
+                   "probe_pattern_kernel", "probe_pattern4_kernel")
 MI355X_XCDS, MI355X_CUS, MI355X_SIMDS = 8, 256, 1024
 
 

@@ -61,6 +61,7 @@ struct PartitionArgs {
   int32_t len_cap;           // device lengths are clamped to [0, len_cap]
   int32_t num_seqs;          // S
   int32_t nt_partials;       // 1: partials stored with the non-temporal bit
+  int32_t rotate;            // 1: an (s, h)'s partition groups in an order rotated by sh
 };
 
 struct FusedArgs {
@@ -69,6 +70,7 @@ struct FusedArgs {
   uint16_t* out;            // bf16 [S][Hkv*QG][128]
   int32_t len_cap;
   int32_t splits;           // workgroups per (s, h), >= 1
+  int32_t rotate;           // 1: an (s, h)'s workgroups in an order rotated by sh
   // Cross-workgroup merge workspace, used when splits > 1.
   int32_t* counters;        // [S*Hkv] arrival counters: 0 on entry, re-armed to 0
   float* ws_o;              // [S*Hkv][splits][QG][128] workgroup partials
@@ -195,6 +197,10 @@ bool partials_nontemporal(int64_t num_seqs, int num_kv_heads, int num_partitions
 
 // Partitions of one (s, h) that one wave of the partition kernel walks.
 int choose_parts_per_wave(int64_t units, int num_partitions);
+
+// Whether the per-unit kernels deal an (s, h)'s workgroups in an order rotated
+// by sh: when `waves` exceed one resident round of two waves per SIMD.
+bool rotate_units(int64_t waves, int cus);
 
 // Enqueue the kernels; each returns the launch status (hipGetLastError after
 // the launch).  launch_partition chooses parts_per_wave and launch_fused the

@@ -1016,9 +1016,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void tq
   const int Hkv = a.st.num_kv_heads;
   const int E = a.partition_tokens;
   const int ppw = a.parts_per_wave;
+  // The partition groups of one (s, h) are consecutive workgroups, which keeps
+  // its partial stores together (an order with (s, h) fastest scattered them
+  // and lost 8 % on the bandwidth workload); with a.rotate their order is
+  // rotated by sh, so that group p of every (s, h) does not land on one XCD
+  // (rotate_units says when).
   const int n_groups = (P + ppw - 1) / ppw;
-  const int pg = blockIdx.x % n_groups;
   const int sh = blockIdx.x / n_groups;
+  const int pg = a.rotate ? (int)((blockIdx.x % n_groups + (unsigned)sh) % (unsigned)n_groups)
+                          : (int)(blockIdx.x % n_groups);
   const int h = sh % Hkv;
   const int s = sh / Hkv;
   const int p0 = pg * ppw;
@@ -1173,8 +1179,11 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
   const int b = lane >> 4;
   const int Hkv = a.st.num_kv_heads;
   const int splits = a.splits;
+  // The workgroups of one (s, h) are consecutive; with a.rotate their split
+  // order is rotated by sh, as in tq_partition_kernel.
   const int sh = blockIdx.x / splits;
-  const int split = blockIdx.x % splits;
+  const int split = a.rotate ? (int)((blockIdx.x % splits + (unsigned)sh) % (unsigned)splits)
+                             : (int)(blockIdx.x % splits);
   const int h = sh % Hkv;
   const int s = sh / Hkv;
   const int L = clamp_len(a.seq_lens[s], a.len_cap);
@@ -2119,6 +2128,7 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
   a.parts_per_wave = choose_parts_per_wave(units, a.num_partitions);
   const int64_t groups = (a.num_partitions + a.parts_per_wave - 1) / a.parts_per_wave;
   const dim3 grid((unsigned)(num_seqs * (int64_t)a.st.num_kv_heads * groups));
+  a.rotate = rotate_units(grid.x, device_cu_count()) ? 1 : 0;
   TQ_DISPATCH(launch_partition_t, query_group_size, kv_block_size, tq4, a, grid, stream);
 }
 
@@ -2138,9 +2148,11 @@ hipError_t launch_fused_t(const FusedArgs& a, unsigned grid, int waves, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_fused(const FusedArgs& a, int num_seqs, int waves, int query_group_size,
+hipError_t launch_fused(const FusedArgs& a_in, int num_seqs, int waves, int query_group_size,
                         int kv_block_size, bool tq4, hipStream_t stream) {
+  FusedArgs a = a_in;
   const unsigned grid = (unsigned)((int64_t)num_seqs * a.st.num_kv_heads * a.splits);
+  a.rotate = rotate_units((int64_t)grid * waves, device_cu_count()) ? 1 : 0;
   TQ_DISPATCH(launch_fused_t, query_group_size, kv_block_size, tq4, a, grid, waves, stream);
 }
 

@@ -25,6 +25,20 @@ int choose_parts_per_wave(int64_t units, int num_partitions) {
   return (int)ppw;
 }
 
+bool rotate_units(int64_t waves, int cus) {
+  // Workgroups go to the 8 XCDs round robin by index.  With an (s, h)'s
+  // partitions on consecutive workgroups and a partition count divisible by
+  // 8, partition p of every (s, h) lands on XCD p % 8, and on ragged batches,
+  // whose high partitions are mostly dead, the XCDs of the low partitions get
+  // up to 1.5x the work.  Rotating each (s, h)'s order by sh spreads them:
+  // measured on the partition kernel, the ragged workload (16384 one-wave
+  // workgroups) 149 -> 119.5 us, the bandwidth workload 414.7 -> 411.5 us; the
+  // long-context one, whose 2048 partitions are all resident at once, lost 8 %
+  // (79.8 -> 86 us), so the rotation is kept for grids beyond one round.
+  const int64_t round = (int64_t)2 * kFlatWaves * (cus < 1 ? 1 : cus);
+  return waves > round;
+}
+
 bool partials_nontemporal(int64_t num_seqs, int num_kv_heads, int num_partitions,
                           int query_group_size, bool tq4) {
   // Measured on the fp8 partition kernel: with 51-136 MB of partials (bound)

@@ -507,19 +507,19 @@ constexpr int kTq4MetaStage = 256;
 constexpr int kTq4MetaOff = 2 * kTq4RowStage;
 constexpr int kTq4WaveLds = kTq4MetaOff + 2 * kTq4MetaStage;
 constexpr int kTq4TableEntries = 256;
-// Columns of the wide centroid tables: every entry repeated in COLS adjacent
-// dwords, lane l reading the copy in column l % COLS, so that the bank a
-// lookup hits follows from the lane whatever the index byte (random index
-// bytes otherwise pile several lanes onto one bank).  32 columns (32 KiB):
-// at most two lanes of a wave on one bank.  16 columns (16 KiB): lanes l and
-// l + 16 share a bank when their entries have the same parity.  The fused
-// flat kernel has room for 32 columns at QG <= 8 and for 16 at QG = 16 (its
-// staging takes 133 KiB there).  The flat partition kernel keeps one column:
-// 32 there measured no faster on the bandwidth workload and 1-3 % slower on
-// shorter batches (building the table costs more than its conflicts).
-constexpr int kTq4WideCols = 32;
-constexpr int tq4_flat_table_cols(int qg, bool tq4) { return !tq4 ? 1 : (qg <= 8 ? 32 : 16); }
-constexpr int tq4_partition_flat_table_cols(bool tq4) { return 1; }
+// The per-lane centroid table of the flat kernels: every entry repeated in 64
+// adjacent dwords (a 256-byte row), lane l reading the copy in column l, so a
+// wave's 64 lookups hit 64 distinct banks whatever the index bytes (random
+// bytes otherwise pile several lanes onto one bank: about 30 % of the cycles
+// of the flat partition kernel with a one-column table).  A lookup's address,
+// index byte n of a dword in bits 8..15 and the lane's column offset in bits
+// 0..7, is one byte permute, the same one VALU op as the one-column table's
+// shift.  64 KiB: the flat kernels have room for it (one workgroup per CU);
+// the kernels of one to eight waves per (s, h) or partition keep one column.
+// Tables of 16 or 32 columns in rows of 64 or 128 bytes (not byte aligned)
+// took a shift and a mask per lookup and gained less.
+constexpr int kTq4LaneCols = 64;
+constexpr int tq4_flat_table_cols(bool tq4) { return tq4 ? kTq4LaneCols : 1; }
 
 __device__ __forceinline__ int tq4_row_swz(int row) {
   return (row & 7) ^ ((row >> 3) & 1) ^ ((row >> 2) & 4);
@@ -532,11 +532,21 @@ __device__ __forceinline__ int tq4_row_swz(int row) {
 template <int COLS = 1>
 __device__ __forceinline__ void build_tq4_table(uint32_t* tab, const float* centroids, int tid,
                                                 int nthreads) {
-  static_assert(COLS == 1 || COLS == 16 || COLS == 32, "table columns");
-  for (int i = tid; i < kTq4TableEntries * COLS; i += nthreads) {
-    const int x = i / COLS;
-    const f16x2 e = {(_Float16)centroids[x & 15], (_Float16)centroids[x >> 4]};
-    tab[i] = __builtin_bit_cast(uint32_t, e);
+  static_assert(COLS == 1 || COLS == kTq4LaneCols, "table columns");
+  if constexpr (COLS == 1) {
+    for (int i = tid; i < kTq4TableEntries; i += nthreads) {
+      const f16x2 e = {(_Float16)centroids[i & 15], (_Float16)centroids[i >> 4]};
+      tab[i] = __builtin_bit_cast(uint32_t, e);
+    }
+  } else {
+    // 16 stores of 4 copies per row.
+    u32x4* t4 = reinterpret_cast<u32x4*>(tab);
+    for (int i = tid; i < kTq4TableEntries * (COLS / 4); i += nthreads) {
+      const int x = i / (COLS / 4);
+      const f16x2 e = {(_Float16)centroids[x & 15], (_Float16)centroids[x >> 4]};
+      const uint32_t v = __builtin_bit_cast(uint32_t, e);
+      t4[i] = u32x4{v, v, v, v};
+    }
   }
 }
 
@@ -580,6 +590,7 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
   constexpr bool kCompact = tq4_compact_softmax(QG);
   const int lane = threadIdx.x & 63;
   const uint32_t tab_col = (uint32_t)(lane & (COLS - 1)) << 2;  // byte offset of the lane's column
+  static_assert(COLS == 1 || COLS == kTq4LaneCols, "table columns");
   const int r = lane & 15;
   const int b = lane >> 4;
   const int Hkv = a.num_kv_heads;
@@ -742,18 +753,15 @@ __device__ __forceinline__ void stream_tokens_tq4(const StreamArgs& a, int s, in
           kop[t][cc] = __builtin_bit_cast(
               f16x8, u32x4{tab[x & 0xFF], tab[(x >> 8) & 0xFF], tab[(x >> 16) & 0xFF], tab[x >> 24]});
         } else {
-          // Entry e's copies start at byte e * 4 COLS: each index byte lands
-          // there with one shift and one mask, and the lane's column ORs in.
-          static_assert(COLS == 16 || COLS == 32, "wide table row");
-          constexpr int sh = COLS == 32 ? 7 : 6;  // log2 of a row's bytes
-          constexpr uint32_t m = 0xFFu << sh;
+          // Entry e's row starts at byte 256 e: v_perm_b32 puts index byte n of
+          // x in bits 8..15 and the lane's column offset (bits 0..7 of tab_col)
+          // below it.
           const char* tb = reinterpret_cast<const char*>(tab);
-          auto at = [&](uint32_t row) {
-            return *reinterpret_cast<const uint32_t*>(tb + (row | tab_col));
+          auto at = [&](uint32_t sel) {
+            return *reinterpret_cast<const uint32_t*>(tb + __builtin_amdgcn_perm(x, tab_col, sel));
           };
           kop[t][cc] = __builtin_bit_cast(
-              f16x8, u32x4{at((x << sh) & m), at((x >> (8 - sh)) & m), at((x >> (16 - sh)) & m),
-                           at((x >> (24 - sh)) & m)});
+              f16x8, u32x4{at(0x0C0C0400u), at(0x0C0C0500u), at(0x0C0C0600u), at(0x0C0C0700u)});
         }
       }
     if (c == next_boundary) {
@@ -1328,14 +1336,32 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 }
 
 
-template <int QG>
+template <int QG, bool TQ4>
 struct FlatLayout {
   // A partial in LDS or the workspace: o [QG][128], then m [16] and l [16].
   static constexpr int kPieceFloats = QG * D + 32;
-  // Per-wave LDS: the staging area (which also holds the last piece), then the
-  // first piece.
-  static constexpr int kArea = kWaveLds + kPieceFloats * 4;
-  static_assert(kPieceFloats * 4 <= kWaveLds, "the last piece must fit the staging area");
+  static constexpr int kPieceBytes = kPieceFloats * 4;
+  static_assert(kPieceBytes <= kWaveLds, "the last piece must fit the staging area");
+  // fp8: per-wave LDS is the staging area (which also holds the last piece),
+  // then the first piece, stored when its segment ends.  4-bit: the per-lane
+  // centroid table takes 64 KiB, so a wave keeps its first piece in registers
+  // until its stream is done and then stores it behind the last piece in its
+  // staging area (QG <= 8), or, where the two do not fit (QG = 16), in the
+  // table's LDS once every wave of the workgroup is past its lookups.
+  static constexpr bool kFirstInRegs = TQ4;
+  static constexpr bool kFirstInStage = TQ4 && 2 * kPieceBytes <= kWaveLds;
+  static constexpr bool kFirstInTable = TQ4 && !kFirstInStage;
+  static constexpr int kArea = TQ4 ? kWaveLds : kWaveLds + kPieceBytes;  // per wave, dynamic
+  // The table's LDS array, in dwords (it also holds the first pieces when kFirstInTable).
+  static constexpr int kTableWords =
+      !TQ4 ? 1
+           : (kFirstInTable && kFlatWaves * kPieceFloats > kTq4TableEntries * kTq4LaneCols
+                  ? kFlatWaves * kPieceFloats
+                  : kTq4TableEntries * kTq4LaneCols);
+  // Byte offset of wave v's first piece: in the dynamic area, or (kFirstInTable) in the table array.
+  static constexpr int first_offset(int v) {
+    return kFirstInTable ? v * kPieceBytes : v * kArea + (TQ4 ? kPieceBytes : kWaveLds);
+  }
 };
 
 // Store the wave's finished partial (rows r < QG) at piece P.
@@ -1356,10 +1382,10 @@ __device__ __forceinline__ void store_piece(float* P, const f32x4 o[8], float m,
 
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
-  using Lay = FlatLayout<QG>;
-  constexpr int kTabCols = tq4_flat_table_cols(QG, TQ4);
+  using Lay = FlatLayout<QG, TQ4>;
+  constexpr int kTabCols = tq4_flat_table_cols(TQ4);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
-  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries * kTabCols : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_tab[Lay::kTableWords];
   __shared__ int piece_sh[2 * kFlatWaves];        // s*Hkv+h of wave v's first (2v) / last
                                                   // (2v+1) piece, -1: none
   __shared__ int piece_ea[2 * kFlatWaves];        // list offset of that (s, h)'s first entry
@@ -1457,9 +1483,12 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
 
   uint8_t* area = lds_dyn + wave * Lay::kArea;
   float* last_piece = reinterpret_cast<float*>(area);
-  float* first_piece = reinterpret_cast<float*>(area + kWaveLds);
+  uint8_t* const first_base = Lay::kFirstInTable ? reinterpret_cast<uint8_t*>(lds_tab) : lds_dyn;
+  float* first_piece = reinterpret_cast<float*>(first_base + Lay::first_offset(wave));
   int f_sh = -1, l_sh = -1, f_n = 0, l_n = 0;
   int f_ea = 0, l_ea = 0;
+  f32x4 f_o[Lay::kFirstInRegs ? 8 : 1];  // the first piece while the stream goes on
+  float f_m = 0.f, f_l = 0.f;
   if (wave < Wu) {  // uniform over the wave
     int h = n > 0 ? (A - base) / n : Hkv;
     int k0 = n > 0 ? (A - base) - h * n : 0;
@@ -1484,7 +1513,14 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
           for (int dblk = 0; dblk < 8; ++dblk) store_bf16x4(dst + out_col<TQ4>(dblk, b), o[dblk]);
         }
       } else if (first_seg) {
-        store_piece<QG, TQ4>(first_piece, o, st.m2 * kLn2, l);
+        if constexpr (Lay::kFirstInRegs) {
+#pragma unroll
+          for (int dblk = 0; dblk < 8; ++dblk) f_o[dblk] = o[dblk];
+          f_m = st.m2 * kLn2;
+          f_l = l;
+        } else {
+          store_piece<QG, TQ4>(first_piece, o, st.m2 * kLn2, l);
+        }
         f_sh = sh;
         f_ea = base + h * n;
         f_n = n;
@@ -1513,6 +1549,8 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
       }
     }
   }
+  if constexpr (Lay::kFirstInStage)
+    if (f_sh >= 0) store_piece<QG, TQ4>(first_piece, f_o, f_m, f_l);
   if (lane == 0) {
     piece_sh[2 * wave] = f_sh;
     piece_ea[2 * wave] = f_ea;
@@ -1522,6 +1560,10 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
     piece_n[2 * wave + 1] = l_n;
   }
   __syncthreads();
+  if constexpr (Lay::kFirstInTable) {  // every wave is past its lookups
+    if (f_sh >= 0) store_piece<QG, TQ4>(first_piece, f_o, f_m, f_l);
+    __syncthreads();
+  }
 
   // Merge the pieces of each (s, h) this workgroup holds.  Piece p = 2v + which
   // is wave v's first (which = 0) or last piece.  The pieces of one (s, h) are
@@ -1529,7 +1571,8 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
   // v1.  Every wave finds the runs alike, lane p reading piece p.  At most two
   // of these (s, h) reach outside the workgroup.
   auto piece = [&](int v, int which) -> const float* {
-    return reinterpret_cast<const float*>(lds_dyn + v * Lay::kArea + (which == 0 ? kWaveLds : 0));
+    return reinterpret_cast<const float*>(which == 0 ? first_base + Lay::first_offset(v)
+                                                     : lds_dyn + v * Lay::kArea);
   };
   const int t = threadIdx.x;
   const int item_g = t / (D / 4);
@@ -1564,8 +1607,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
     if (t < kItems) {
       // Piece j of the run: p0's area for j = 0, else wave v + j's first piece.
       const float* first = piece(v, which);
-      const float* rest = piece(v, 0);
-      auto at = [&](int j) { return j == 0 ? first : rest + j * (Lay::kArea / 4); };
+      auto at = [&](int j) { return j == 0 ? first : piece(v + j, 0); };
       float m, l;
       const f32x4 o = lse_merge4_regs<kFlatWaves>(
           v1 - v + 1,
@@ -1694,7 +1736,7 @@ __global__ __launch_bounds__(64 * kFlatWaves) void tq_flat_kernel(FlatArgs a) {
 // table and fill the pipeline for only 8 chunks.
 template <int QG, int BS, bool TQ4>
 __global__ __launch_bounds__(64 * kFlatWaves) void tq_partition_flat_kernel(PartitionArgs a) {
-  constexpr int kTabCols = tq4_partition_flat_table_cols(TQ4);
+  constexpr int kTabCols = tq4_flat_table_cols(TQ4);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds_dyn[];
   __shared__ __attribute__((aligned(16))) uint32_t lds_tab[TQ4 ? kTq4TableEntries * kTabCols : 1];
   const int lane = threadIdx.x & 63;
@@ -2059,9 +2101,8 @@ hipError_t static_scratch(void** ptr, hipStream_t stream) {
 
 template <int QG, int BS, bool TQ4>
 hipError_t launch_flat_t(const FlatArgs& a, hipStream_t stream) {
-  constexpr size_t lds = (size_t)kFlatWaves * FlatLayout<QG>::kArea;
-  static_assert(lds + (TQ4 ? kTq4TableEntries * 4 * tq4_flat_table_cols(QG, TQ4) : 0) + 1024 <=
-                    160 * 1024,
+  constexpr size_t lds = (size_t)kFlatWaves * FlatLayout<QG, TQ4>::kArea;
+  static_assert(lds + FlatLayout<QG, TQ4>::kTableWords * 4 + 1024 <= 160 * 1024,
                 "LDS per workgroup");
   // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
   // the runtime needs none, and must not leak into the launch status.
@@ -2096,7 +2137,7 @@ hipError_t launch_partition_flat_t(const PartitionArgs& a, int n_groups, hipStre
     return hipErrorInvalidValue;
   } else {
     constexpr size_t lds = (size_t)kFlatWaves * kWaveLds;
-    static_assert(lds + kTq4TableEntries * 4 * tq4_partition_flat_table_cols(TQ4) + 1024 <= 160 * 1024,
+    static_assert(lds + kTq4TableEntries * 4 * tq4_flat_table_cols(TQ4) + 1024 <= 160 * 1024,
                   "LDS per workgroup");
     // Dynamic LDS beyond 64 KiB needs the opt-in, once; an error here only means
     // the runtime needs none, and must not leak into the launch status.

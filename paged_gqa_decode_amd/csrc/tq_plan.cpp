@@ -124,13 +124,16 @@ int plan_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len, int un
 int plan_partition_flat_groups(int64_t num_seqs, int num_kv_heads, int max_seq_len,
                                int partition_tokens, bool tq4, int cus) {
   // The 4-bit format only, and only when the partitions (bounded by the
-  // longest length) fill the resident round at least twice: measured faster
-  // than one wave per partition there (7-12 %), slower with fewer partitions
-  // than that, and no faster for fp8.
+  // longest length) fill the resident round: measured faster than one wave per
+  // partition there (7-12 % with two rounds of partitions or more, 3 % on the
+  // two-kernel step with one round, where its per-lane centroid table spares
+  // the bank conflicts of the one-wave workgroups' table).  With fewer
+  // partitions than waves its workgroups would leave CUs idle.  No faster for
+  // fp8.
   if (!tq4 || num_seqs < 1 || num_kv_heads < 1 || max_seq_len <= 0 || partition_tokens < 1) return 0;
   const int64_t parts = (max_seq_len + partition_tokens - 1) / partition_tokens;
   const int64_t groups = cus < 1 ? 1 : (cus < kFlatGroupsMax ? cus : kFlatGroupsMax);
-  if (num_seqs * num_kv_heads * parts < 2 * kFlatWaves * groups) return 0;
+  if (num_seqs * num_kv_heads * parts < kFlatWaves * groups) return 0;
   return plan_flat_groups(num_seqs, num_kv_heads, max_seq_len, partition_tokens, cus);
 }
 

@@ -171,10 +171,10 @@ def test_tq4_single_tile_group_identity(qg, bs):
 
 
 # Batches whose partitions (bounded by the longest length) fill the device's resident round
-# of 2048 waves at least twice take the flat partition kernel for the 4-bit format; smaller
-# ones take one wave per partition.
+# of 2048 waves take the flat partition kernel for the 4-bit format; smaller ones (here each
+# sequence decoded alone) take one wave per partition.  The last case fills exactly one round.
 FLAT_CASES = [(8, 32, 1, 64, 4, 4096), (16, 16, 2, 48, 8, 6000), (6, 32, 5, 128, 8, 6400),
-              (8, 16, 1, 600, 2, 1024)]
+              (8, 16, 1, 600, 2, 1024), (16, 32, 1, 64, 4, 2048)]
 
 
 @pytest.mark.parametrize("qg,bs,G,S,hkv,max_len", FLAT_CASES,
@@ -189,7 +189,7 @@ def test_tq4_flat_partition_kernel(qg, bs, G, S, hkv, max_len):
     lens[:6] = (max_len, 0, 1, E - 1, E, E + 1)
     lens = tuple(int(x) for x in lens)
     P = -(-max_len // E)
-    assert S * hkv * P >= 2 * 2048 and hkv * P < 2 * 2048
+    assert S * hkv * P >= 2048 and hkv * P < 2048
     wl = workloads.small_workload(name="tq4flat", num_seqs=S, num_kv_heads=hkv, query_group_size=qg,
                                   kv_block_size=bs, seq_lens=lens, tile_groups_per_partition=G,
                                   seed=80 + qg)

@@ -100,6 +100,40 @@ void run_valid(const Case& c) {
   }
 }
 
+// Which partition kernel the two-kernel path plans: the flat one for the 4-bit
+// format once the partitions (bounded by max_seq_len) fill one resident round of
+// 8 waves per CU, one wave per partition otherwise and always for fp8.
+void run_partition_plans() {
+  struct PlanCase {
+    Case c;
+    int cus;
+    bool flat;
+  };
+  const PlanCase cases[] = {
+      {{16, 4, 16, 32, 5, 32, 40960, 14336, 1280}, 256, true},   // 2048 partitions: one round
+      {{16, 4, 16, 32, 5, 32, 40959, 14336, 1280}, 256, true},   // still 32 partitions each
+      {{16, 4, 16, 32, 5, 32, 39680, 14336, 1280}, 256, false},  // 31 each: 1984 < 2048
+      {{1, 4, 16, 32, 5, 32, 40960, 1280, 1280}, 256, false},    // one sequence
+      {{1, 4, 16, 32, 5, 32, 40960, 1280, 1280}, 16, true},      // ... on a 16-CU device
+      {{128, 8, 8, 32, 1, 32, 8192, 32768, 256}, 256, true},
+  };
+  for (const PlanCase& pc : cases) {
+    g_log.cus = pc.cus;
+    const tq_extent e = extent(pc.c);
+    tq_partials part = {(float*)fake(10), (float*)fake(11), (float*)fake(12)};
+    EXPECT(tq4_decode(fake(1), (const uint8_t*)fake(2), (const float*)fake(4),
+                      (const int32_t*)fake(5), (const int32_t*)fake(6), &part, pc.c.Hkv, pc.c.QG,
+                      pc.c.BS, pc.c.G, 0.088f, &e, nullptr) == TQ_OK);
+    EXPECT((g_log.flat_partition_groups > 0) == pc.flat);
+    EXPECT(g_log.flat_partition_groups <= pc.cus);
+    EXPECT(tq_decode(fake(1), (const uint8_t*)fake(2), (const uint8_t*)fake(3), (const float*)fake(4),
+                     (const int32_t*)fake(5), (const int32_t*)fake(6), &part, pc.c.Hkv, pc.c.QG,
+                     pc.c.BS, pc.c.G, 0.088f, &e, nullptr) == TQ_OK);
+    EXPECT(g_log.flat_partition_groups == 0);
+  }
+  g_log.cus = 256;
+}
+
 void run_static_limits() {
   // More (sequence, kv head) pairs than the static counter region holds: refused, no launch.
   const Case c = {1024, 257, 8, 16, 1, 2, 300, 64, 32};
@@ -201,6 +235,7 @@ int main() {
     for (const Case& c : valid) run_valid(c);
   }
   g_log.cus = 256;
+  run_partition_plans();
   run_invalid();
   run_static_limits();
   setenv("TQ_VALIDATE", "1", 1);

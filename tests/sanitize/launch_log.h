@@ -8,5 +8,6 @@ struct LaunchLog {
   const void* ws = nullptr;  // the workspace the driver passed, to check the carving
   size_t ws_bytes = 0;
   int cus = 256;  // what the device_cu_count stand-in reports
+  int flat_partition_groups = -1;  // the flat partition kernel's grid of the last partition launch (0: none)
 };
 extern LaunchLog g_log;

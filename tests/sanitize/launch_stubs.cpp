@@ -43,6 +43,7 @@ hipError_t launch_partition(PartitionArgs a, int num_seqs, int query_group_size,
   const int flat_groups = plan_partition_flat_groups(num_seqs, a.st.num_kv_heads, a.len_cap,
                                                      a.partition_tokens, tq4, g_log.cus);
   require(flat_groups >= 0 && flat_groups <= 256 && (tq4 || flat_groups == 0), "flat partition plan");
+  g_log.flat_partition_groups = flat_groups;
   const bool nt = partials_nontemporal(num_seqs, a.st.num_kv_heads, a.num_partitions,
                                        query_group_size, tq4);
   require(!(nt && tq4), "partial store policy");

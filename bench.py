@@ -89,8 +89,8 @@ def cpu_info():
             "cpus_available": len(os.sched_getaffinity(0))}
 
 
-# The oracle's threads: every CPU this process may use, at most 16 (a one-GPU machine's share of
-# its host's CPUs, whatever the host has in all).
+# The oracle's threads: every CPU this process may use, at most 16 (the CPU share of one GPU
+# on an 8-GPU host, whatever the host has in all).
 CPU_BASELINE_MAX_THREADS = 16
 
 

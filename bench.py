@@ -122,13 +122,22 @@ def cpu_baseline(inp, budget_s: float):
         kv_bytes = sum(int(lens[s]) for s, _ in sel) * KV_BYTES_PER_TOKEN_HEAD
         return kv_bytes / dt / 1e9, dt, sel
 
+    def token_heads(sel):
+        return sum(int(lens[s]) for s, _ in sel)
+
     gbs, dt, sel = sized(threads, budget_s)
     gbs1, dt1, sel1 = sized(1, budget_s / 3)
+    # the whole workload's oracle time at the measured rate (the sample is whole units)
+    total_th = sum(int(lens[s]) for s, _ in units)
+    step_s = dt * total_th / max(token_heads(sel), 1)
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "threads": threads, "cpu_model": info["cpu_model"],
             "physical_cores": info["physical_cores"], "logical_cpus": info["logical_cpus"],
             "cpus_available": info["cpus_available"],
+            "token_heads_per_s": round(token_heads(sel) / dt),
+            "us_per_step": round(step_s * 1e6),
             "one_thread": {"value": round(gbs1, 4), "unit": "GB/s",
+                           "token_heads_per_s": round(token_heads(sel1) / dt1),
                            "sample": f"{len(sel1)} units, {dt1:.1f} s wall"},
             "sample": f"{len(sel)} of {len(units)} (sequence, kv head) units of {wl.name} "
                       f"({int(lens[sel[0][0]])} tokens each, all {wl.query_group_size} query rows), "

@@ -53,10 +53,13 @@ def kernel_sha() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload: str, path_name: str):
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def measured_traffic(workload: str, path_name: str, profiles_dir: str = PROFILES):
     """HBM bytes per launch of the headline kernel from the committed rocprofv3
     counter summary, or None if there is none or the kernel source changed since."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{KERNEL_NAMES[path_name]}_{workload}.json")
+    path = os.path.join(profiles_dir, f"traffic_{KERNEL_NAMES[path_name]}_{workload}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -224,7 +227,7 @@ def _kernel_key(name: str) -> str:
     return key
 
 
-def summarize_rocprof(prof_dir: str, workload: str) -> None:
+def summarize_rocprof(prof_dir: str, workload: str, out_dir: str = PROFILES) -> None:
     """Turn the rocprofv3 output of three profiled bench runs under `prof_dir`
     (trace/: --kernel-trace --stats; fetch/: --pmc FETCH_SIZE; write/: --pmc
     WRITE_SIZE) into the summaries kept under profiles/: per-kernel duration
@@ -254,7 +257,7 @@ def summarize_rocprof(prof_dir: str, workload: str) -> None:
     f_scale = copy_bytes / (fetch["probe_copy_kernel"] * 1024.0)
     w_scale = copy_bytes / (write["probe_copy_kernel"] * 1024.0)
     sha = kernel_sha()
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    os.makedirs(out_dir, exist_ok=True)
     lines = [f"# rocprofv3 kernel statistics, {workload} (bench.py, both decode paths)", "",
              "Commands (run from the repository root; <dir> = an output directory):", "",
              "    " + PROFILE_CMD.format(what="--kernel-trace --stats", sub="trace", wl=workload),
@@ -286,10 +289,10 @@ def summarize_rocprof(prof_dir: str, workload: str) -> None:
                "fetch_scale": round(f_scale, 5), "write_scale": round(w_scale, 5),
                "source": f"profiles/rocprof_{workload}.md"}
         fname = name.replace("[tq4]", "_tq4")
-        with open(os.path.join(ROOT, "profiles", f"traffic_{fname}_{workload}.json"), "w") as f:
+        with open(os.path.join(out_dir, f"traffic_{fname}_{workload}.json"), "w") as f:
             json.dump(rec, f, indent=1)
         lines.append(f"- {name}: {fb / 1e9:.4f} GB fetched + {wb / 1e9:.4f} GB written per launch")
-    with open(os.path.join(ROOT, "profiles", f"rocprof_{workload}.md"), "w") as f:
+    with open(os.path.join(out_dir, f"rocprof_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -308,7 +311,7 @@ COUNTER_KERNELS = ("tq_flat_kernel", "tq_partition_kernel", "tq_merge_kernel", "
 MI355X_XCDS, MI355X_CUS, MI355X_SIMDS = 8, 256, 1024
 
 
-def summarize_counters(prof_dir: str, workload: str) -> None:
+def summarize_counters(prof_dir: str, workload: str, out_dir: str = PROFILES) -> None:
     """Write profiles/counters_<workload>.md from the COUNTER_PASSES runs under prof_dir:
     per kernel, the average over its dispatches of every counter, and ratios derived from
     them (cycles = GRBM_GUI_ACTIVE / 8 XCDs; quad-cycle counters times 4)."""
@@ -353,8 +356,8 @@ def summarize_counters(prof_dir: str, workload: str) -> None:
             f"{pct(a.get('SQ_VALU_MFMA_BUSY_CYCLES', float('nan')) / MI355X_SIMDS / cyc)} | "
             f"{pct(a.get('SQ_LDS_BANK_CONFLICT', float('nan')) / MI355X_CUS / cyc)} | "
             f"{a.get('SQ_INSTS_VALU', float('nan')) / a.get('SQ_WAVES', float('nan')):.0f} |")
-    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", f"counters_{workload}.md"), "w") as f:
+    os.makedirs(out_dir, exist_ok=True)
+    with open(os.path.join(out_dir, f"counters_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 

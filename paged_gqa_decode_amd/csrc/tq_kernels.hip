@@ -486,7 +486,8 @@ __device__ __forceinline__ void stream_tokens(const StreamArgs& a, int s, int h,
 //
 // Per-wave LDS of the 4-bit stream: two 4 KiB row stages and two 256 B
 // metadata stages ([3][32] fp16), in the same 8.5 KiB staging area as the fp8
-// stream's; the 1 KiB centroid table is a workgroup's LDS array of its own.
+// stream's; the centroid table (1 KiB, or 64 KiB per lane in the flat
+// kernels) is a workgroup's LDS array of its own.
 //  * A chunk's 32 rows of 128 B (a whole block's slots of one kv head when
 //    BS = 32, of two blocks when BS = 16) arrive whole, by LDS-direct loads
 //    of 8 rows each, and K is read back from LDS.  Splitting each row between a
@@ -526,9 +527,11 @@ __device__ __forceinline__ int tq4_row_swz(int row) {
 }
 
 // The centroid table, written by threads tid, tid + nthreads, ...: entry x =
-// (f16(c[x & 15]), f16(c[x >> 4])), the first in the low half.  One table
-// serves every wave of a workgroup, at a fixed LDS address, so a lookup's
-// address is the index byte times 4 (one shift) plus a constant offset.
+// (f16(c[x & 15]), f16(c[x >> 4])), the first in the low half, once (COLS =
+// 1) or in each of the 64 columns of row x (COLS = 64).  One table serves
+// every wave of a workgroup, at a fixed LDS address, so a lookup's address is
+// the index byte times 4 (one shift) plus a constant offset, or with 64
+// columns the byte permute described above.
 template <int COLS = 1>
 __device__ __forceinline__ void build_tq4_table(uint32_t* tab, const float* centroids, int tid,
                                                 int nthreads) {
@@ -1307,8 +1310,9 @@ __global__ __launch_bounds__(512) void tq_fused_kernel(FusedArgs a) {
 // one online softmax.  A segment that holds a whole (s, h) is finished by its
 // wave, which writes bf16 out.  Any other segment is a piece: only a wave's
 // first or last segment can be one.  The wave stores a piece's partial (o, m,
-// l) in its LDS area (first piece: a slot of its own; last piece: its staging
-// area, free once the stream is done).  After a barrier the workgroup merges
+// l) in LDS: the last piece in its staging area, free once the stream is done;
+// the first in a slot of its own (fp8) or, for the 4-bit format, held in
+// registers until the stream is done (FlatLayout).  After a barrier the workgroup merges
 // the pieces of each (s, h) it holds, in wave order.  If the (s, h) lies
 // inside the workgroup's range, that merge writes out.  Otherwise (only the
 // workgroup's first or last (s, h) can reach outside) the merged partial goes
